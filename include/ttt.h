@@ -1,0 +1,158 @@
+/*
+ * ttt.h - C ABI of the TTT-E2E prefill library (libttt.so, gfx950 / MI355X).
+ *
+ * What the library computes is the causal prefill with inner adaptation of
+ * "End-to-End Test-Time Training for Long Context" as described in the
+ * zhongzhuzhou.org reading notes (section 7, Algorithm 1; section 5, Eq. 9;
+ * section 3, Eq. 3): a context is read in chunks of b positions through a
+ * pre-norm Transformer with causal sliding-window attention (window k) and
+ * QK-norm.  Each chunk's per-token next-token losses are recorded with the
+ * current fast weights W; then the mean loss of the chunk is differentiated
+ * with respect to W only - the fast SwiGLU MLPs of the last n_update blocks,
+ * each summed with a frozen static SwiGLU on the same pre-MLP norm (notes,
+ * section 6) - and one SGD step W <- W - eta * grad is taken before the next
+ * chunk.  Keys and values of earlier chunks are kept in a bounded ring of the
+ * window and are constants of each step.  Every prefill starts from W_init
+ * (notes, section 7: state of independent documents is never shared).
+ *
+ * All compute runs in the library's own HIP kernels on the given stream.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers point to GPU memory of the current HIP device; host
+ *     pointers are marked "host".
+ *   - Row-major layouts.  "[R,C]" means R rows of C contiguous elements.
+ *   - Element types: tensors marked "wt" are float32 when cfg.dtype ==
+ *     TTT_FP32 and bfloat16 (raw 16-bit storage) when cfg.dtype == TTT_BF16.
+ *   - The caller owns every buffer it passes; the library never frees them.
+ *   - Return value: TTT_OK or a negative ttt_status.  On TTT_EINVAL nothing
+ *     was enqueued.  ttt_last_error() gives a text for the last failure.
+ *   - A handle is not thread-safe; use one handle per stream.
+ */
+#ifndef TTT_H
+#define TTT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TTT_OK = 0,
+  TTT_EINVAL = -1,        /* bad argument: sizes, null pointers, unsupported combination */
+  TTT_ENOMEM = -2,        /* device allocation failed */
+  TTT_EHIP = -3,          /* a HIP runtime call failed (text in ttt_last_error) */
+  TTT_EUNSUPPORTED = -4,  /* shape not supported by the compiled kernels (e.g. head_dim) */
+  TTT_ENONFINITE = -5     /* a recorded loss was NaN or infinite (checked after the prefill) */
+} ttt_status;
+
+typedef enum { TTT_FP32 = 0, TTT_BF16 = 1 } ttt_dtype;
+
+/* Flags for ttt_prefill (and defaults in ttt_config.flags). */
+enum {
+  TTT_NO_UPDATE = 1u << 0,  /* forward-only sliding-window prefill: no backward, no SGD.
+                               Losses equal those of eta = 0. */
+  TTT_NO_GRAPH = 1u << 1    /* launch kernels one by one instead of replaying the
+                               captured per-chunk HIP graph (same results, bit for bit) */
+};
+
+/*
+ * Model and run shape.  Constraints checked by ttt_create (TTT_EINVAL otherwise):
+ *   n_layers >= 1; 0 <= n_update <= n_layers; d_model == n_heads * head_dim;
+ *   d_model, d_ff, vocab multiples of 16; head_dim in {16, 32, 64, 80, 96, 128};
+ *   chunk and window multiples of 64 with window >= chunk (the notes, section 5:
+ *   the window covers at least one chunk); max_tokens >= 1.
+ */
+typedef struct {
+  int32_t n_layers;     /* L */
+  int32_t d_model;      /* d */
+  int32_t n_heads;      /* H */
+  int32_t head_dim;     /* hd */
+  int32_t d_ff;         /* F: hidden size of each SwiGLU (fast and static alike) */
+  int32_t vocab;        /* V */
+  int32_t window;       /* k: query p attends keys j with p-k < j <= p */
+  int32_t chunk;        /* b: positions per inner update */
+  int32_t n_update;     /* n_u: blocks L-n_u .. L-1 carry fast MLPs */
+  float eta;            /* inner SGD step size */
+  float rms_eps;        /* epsilon inside every RMSNorm (block, final, QK-norm) */
+  float rope_theta;     /* rotary base; angle_i = p * theta^(-2i/hd), pairs (i, i+hd/2) */
+  int32_t dtype;        /* ttt_dtype of weights and activations */
+  int64_t max_tokens;   /* largest T accepted by ttt_prefill; sizes the rotary table */
+  uint32_t flags;       /* default flags OR-ed into every ttt_prefill call */
+} ttt_config;
+
+/*
+ * Weights.  The pointer ARRAYS are host memory (one entry per layer, or per
+ * updated block); every tensor they point to is device memory, read only
+ * during ttt_create (the library copies and repacks everything it needs).
+ * Linear maps follow y = x W^T with W stored [out, in].
+ */
+typedef struct {
+  const void *tok_emb;             /* wt [V, d] */
+  const void *lm_head;             /* wt [V, d] (untied output head) */
+  const void *final_norm;          /* wt [d] */
+  const void *const *attn_norm;    /* host array of L; each wt [d] */
+  const void *const *wq;           /* host array of L; each wt [d, d] (heads contiguous in rows) */
+  const void *const *wk;           /* host array of L; each wt [d, d] */
+  const void *const *wv;           /* host array of L; each wt [d, d] */
+  const void *const *wo;           /* host array of L; each wt [d, d] */
+  const void *const *q_norm;       /* host array of L; each wt [hd] (shared by heads) */
+  const void *const *k_norm;       /* host array of L; each wt [hd] */
+  const void *const *mlp_norm;     /* host array of L; each wt [d] */
+  const void *const *w_gate;       /* host array of L; each wt [F, d]  (static SwiGLU) */
+  const void *const *w_up;         /* host array of L; each wt [F, d] */
+  const void *const *w_down;       /* host array of L; each wt [d, F] */
+  const float *const *fast_gate;   /* host array of n_u; each float32 [F, d]: W_init of block L-n_u+u */
+  const float *const *fast_up;     /* host array of n_u; each float32 [F, d] */
+  const float *const *fast_down;   /* host array of n_u; each float32 [d, F] */
+} ttt_weights;
+
+typedef struct ttt_handle ttt_handle;
+
+/*
+ * Creates a handle on the current HIP device: validates cfg, allocates the
+ * bounded state (per-layer key/value rings of k+b rows, activations of one
+ * chunk, fp32 master fast weights) and copies/repacks the weights.
+ * `stream` is a hipStream_t (NULL = default stream); the call synchronises it
+ * before returning.  *out receives the handle (NULL on failure).
+ */
+ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream, ttt_handle **out);
+
+/*
+ * Algorithm 1 of the notes on one sequence.
+ *   d_tokens   device int32 [T+1]: ids x_0..x_T, each in [0, V).
+ *   T          number of scored positions, 0 <= T <= cfg.max_tokens.  The last
+ *              chunk may be short (T % b != 0); its update averages over its own size.
+ *   d_losses   device float32 [T] out: d_losses[p] = -ln p(x_{p+1} | x_0..x_p)
+ *              under the fast weights current at p's chunk, recorded before that
+ *              chunk's update.
+ *   d_fast_out host array of 3*n_u device float32 pointers, or NULL.  If given,
+ *              receives W_N after all ceil(T/b) updates, in the order
+ *              gate[F,d], up[F,d], down[d,F] for block L-n_u, then L-n_u+1, ...
+ *   flags      TTT_NO_UPDATE / TTT_NO_GRAPH, OR-ed with cfg.flags.
+ *   stream     hipStream_t to enqueue on (NULL = default stream).
+ * Starts from W_init and an empty ring every call.  Returns after enqueueing
+ * (no host synchronisation) unless the non-finite check is requested with
+ * ttt_check_finite().  Token ids are not range-checked on the device; ids
+ * outside [0, V) are undefined behaviour.
+ */
+ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float *d_losses,
+                       float *const *d_fast_out, uint32_t flags, void *stream);
+
+/* Synchronises `stream` and returns TTT_ENONFINITE if any loss of the last
+ * prefill on this handle was NaN or infinite, TTT_OK otherwise. */
+ttt_status ttt_check_finite(ttt_handle *h, void *stream);
+
+/* Number of chunks and of kernel launches per chunk of the last prefill (host values). */
+ttt_status ttt_get_stats(const ttt_handle *h, int64_t *chunks_last, int64_t *launches_per_chunk);
+
+/* Text of the last error on this handle (or of the calling thread if h is NULL). */
+const char *ttt_last_error(const ttt_handle *h);
+
+/* Frees everything the handle owns.  Synchronises the device first. NULL is a no-op. */
+void ttt_destroy(ttt_handle *h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TTT_H */

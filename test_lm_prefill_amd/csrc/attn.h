@@ -1,0 +1,31 @@
+// Sliding-window attention over per-layer key/value rings (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+
+// Ring layouts, per layer and head h, R rows (R a multiple of 64; position j
+// lives in row j mod R):
+//   K  [H][R][hd]   rotated, normalised keys
+//   Vt [H][hd][R]   values, transposed (slot-contiguous)
+//   Kt [H][hd][R]   keys transposed     (only layers whose attention is back-propagated)
+//   V  [H][R][hd]   values              (same)
+struct AttnArgs {
+  const void *q;     // [n][d]  rotated, normalised queries of the chunk
+  const void *qt;    // [H][hd][ldt] same, transposed (backward only)
+  const void *dout;  // [n][d]  gradient of the attention output (backward)
+  const void *doutt; // [H][hd][ldt] same, transposed (backward)
+  const void *K, *Vt, *Kt, *V;
+  void *o;           // [n][d]  output (forward)
+  float *lse2;       // [H][ldl] log2-sum-exp of scaled scores per query
+  const float *Dq;   // [H][ldl] rowsum(dO * O) (backward)
+  float *dq;         // [n][d] fp32 (backward)
+  float *dk;         // [n][d] fp32, chunk keys (backward)
+  float *dv;         // [n][d] fp32, chunk values (backward)
+  int n, d, H, R, window, ldl, ldt;
+  const int *pos0;   // absolute position of the chunk's first query (device)
+  float scale;       // 1/sqrt(hd)
+};
+
+hipError_t attn_fwd_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st);
+hipError_t attn_bwd_dq_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st);
+hipError_t attn_bwd_dkdv_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st);
+bool attn_supported_hd(int hd);

@@ -1,0 +1,580 @@
+// Causal sliding-window attention over key/value rings, forward and backward.
+//
+// Query p attends keys j with p - k < j <= p (the window of the reading
+// notes, section 5 and Eq. 1).  Keys of earlier chunks come from the ring and
+// are constants of the inner step; only the chunk's own keys and values get
+// gradients.
+//
+// MFMA orientation (16x16x32 bf16 tiles, see common.h): scores are produced
+// transposed, S^T = K Q^T, so each lane holds 4 keys of one query; that lane
+// layout is exactly the reduction-dim fragment of the next product
+// O^T = V^T P^T once the 32 keys of a step are taken in the order
+// (4g..4g+3, 16+4g..16+4g+3) for lane group g, which is why V (and K for dQ)
+// are read transposed from LDS.  Softmax statistics stay per lane (one query).
+#include "common.h"
+#include "attn.h"
+
+namespace {
+
+constexpr int NT = 256;
+
+// Global -> registers -> LDS copy of a ROWS x COLSP tile (COLSP a multiple of
+// the 16-byte vector), zero outside rows_valid x cols.
+template <typename T, int ROWS, int COLSP> struct TileIO {
+  static constexpr int VE = 16 / sizeof(T);
+  static constexpr int VPR = COLSP / VE;
+  static constexpr int TOT = ROWS * VPR;
+  static constexpr int PER = (TOT + NT - 1) / NT;
+  uint4 v[PER];
+  DEVI void load(const T *g, long gld, int rows_valid, int cols, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int idx = tid + i * NT;
+      int r = idx / VPR, c = (idx % VPR) * VE;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (idx < TOT && r < rows_valid) {
+        if (c + VE <= cols) {
+          x = *reinterpret_cast<const uint4 *>(g + (long)r * gld + c);
+        } else if (c < cols) {
+          T tmp[VE];
+#pragma unroll
+          for (int e = 0; e < VE; ++e) tmp[e] = (c + e < cols) ? g[(long)r * gld + c + e] : T(0);
+          x = *reinterpret_cast<const uint4 *>(tmp);
+        }
+      }
+      v[i] = x;
+    }
+  }
+  DEVI void store(T *sm, int sld, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int idx = tid + i * NT;
+      if (idx < TOT) {
+        int r = idx / VPR, c = (idx % VPR) * VE;
+        *reinterpret_cast<uint4 *>(sm + r * sld + c) = v[i];
+      }
+    }
+  }
+};
+
+template <int HD> struct Dims {
+  static constexpr int HDP = (HD + 31) / 32 * 32;  // reduction length of q.k, zero padded
+  static constexpr int NC = HDP / 32;
+  static constexpr int NH = HD / 16;               // 16-wide output tiles over hd
+};
+
+template <typename T> constexpr int pad_el() { return 16 / (int)sizeof(T); }
+
+// ======================================================================= forward
+// grid (ceil(n/128), H); 4 waves x 32 queries.
+template <typename T, int HD>
+__global__ __launch_bounds__(NT) void attn_fwd_kernel(const AttnArgs a) {
+  constexpr int HDP = Dims<HD>::HDP, NC = Dims<HD>::NC, NH = Dims<HD>::NH;
+  constexpr int LDK = HDP + pad_el<T>(), LDV = 64 + pad_el<T>();
+  __shared__ __align__(16) T smK[2][64 * LDK];
+  __shared__ __align__(16) T smV[2][HD * LDV];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4, g4 = lg * 4;
+  const int h = blockIdx.y, q_lo = blockIdx.x * 128;
+  const int pos0 = *a.pos0;
+  const int qw = q_lo + wave * 32;
+  const T *Q = reinterpret_cast<const T *>(a.q);
+  const T *Kr = reinterpret_cast<const T *>(a.K) + (long)h * a.R * HD;
+  const T *Vr = reinterpret_cast<const T *>(a.Vt) + (long)h * HD * a.R;
+
+  Frag<T> qf[2][NC];
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      int q = qw + qs * 16 + lr, col = c * 32 + lg * 8;
+      if (q < a.n && col < HD)
+        load_frag(qf[qs][c], Q + (long)q * a.d + h * HD + col);
+      else
+        zero_frag(qf[qs][c]);
+    }
+
+  const int p_first = pos0 + q_lo;
+  const int p_last = pos0 + min(q_lo + 127, a.n - 1);
+  const int jt0 = max(0, p_first - a.window + 1) & ~63;
+  const int ntile = (p_last - jt0) / 64 + 1;
+  const int pw_min = pos0 + qw, pw_max = pos0 + qw + 31;
+  const float sl2 = a.scale * LOG2E_F;
+
+  float m_[2] = {-INFINITY, -INFINITY}, l_[2] = {0.f, 0.f};
+  f32x4_v O[NH][2];
+#pragma unroll
+  for (int hs = 0; hs < NH; ++hs)
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) O[hs][qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+
+  TileIO<T, 64, HDP> kio;
+  TileIO<T, HD, 64> vio;
+  kio.load(Kr + (long)(jt0 % a.R) * HD, HD, 64, HD, tid);
+  vio.load(Vr + (jt0 % a.R), a.R, HD, 64, tid);
+  kio.store(smK[0], LDK, tid);
+  vio.store(smV[0], LDV, tid);
+  __syncthreads();
+
+  for (int t = 0; t < ntile; ++t) {
+    const int cur = t & 1;
+    const int jt = jt0 + t * 64;
+    if (t + 1 < ntile) {
+      const int sn = (jt + 64) % a.R;
+      kio.load(Kr + (long)sn * HD, HD, 64, HD, tid);
+      vio.load(Vr + sn, a.R, HD, 64, tid);
+    }
+    const bool any = (jt <= pw_max) && (jt + 63 > pw_min - a.window);
+    const bool full = (jt + 63 <= pw_min) && (jt > pw_max - a.window);
+    if (any) {
+      f32x4_v S[4][2];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) S[ks][qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      const T *sk = smK[cur];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        Frag<T> kf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) load_frag(kf[ks], sk + (ks * 16 + lr) * LDK + c * 32 + lg * 8);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int qs = 0; qs < 2; ++qs) mma(S[ks][qs], kf[ks], qf[qs][c]);
+      }
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const int p = pos0 + qw + qs * 16 + lr;
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float s = S[ks][qs][r] * sl2;
+            if (!full) {
+              int j = jt + ks * 16 + g4 + r;
+              if (j > p || j <= p - a.window) s = -INFINITY;
+            }
+            S[ks][qs][r] = s;
+            mloc = fmaxf(mloc, s);
+          }
+        mloc = group4_max(mloc);
+        const float mnew = fmaxf(m_[qs], mloc);
+        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = exp2f(m_[qs] - muse);
+        m_[qs] = mnew;
+        l_[qs] *= alpha;
+#pragma unroll
+        for (int hs = 0; hs < NH; ++hs) O[hs][qs] *= alpha;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float pv = exp2f(S[ks][qs][r] - muse);
+            S[ks][qs][r] = pv;
+            l_[qs] += pv;
+          }
+      }
+      const T *sv = smV[cur];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        Frag<T> pf[2];
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          float x[8] = {S[2 * c2][qs][0],     S[2 * c2][qs][1],     S[2 * c2][qs][2],     S[2 * c2][qs][3],
+                        S[2 * c2 + 1][qs][0], S[2 * c2 + 1][qs][1], S[2 * c2 + 1][qs][2], S[2 * c2 + 1][qs][3]};
+          pack_frag(pf[qs], x);
+        }
+#pragma unroll
+        for (int hs = 0; hs < NH; ++hs) {
+          Frag<T> vf;
+          const T *row = sv + (hs * 16 + lr) * LDV + c2 * 32 + g4;
+          load_frag2(vf, row, row + 16);
+#pragma unroll
+          for (int qs = 0; qs < 2; ++qs) mma(O[hs][qs], vf, pf[qs]);
+        }
+      }
+    }
+    if (t + 1 < ntile) {
+      kio.store(smK[cur ^ 1], LDK, tid);
+      vio.store(smV[cur ^ 1], LDV, tid);
+    }
+    __syncthreads();
+  }
+
+  T *Out = reinterpret_cast<T *>(a.o);
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const float lt = group4_sum(l_[qs]);
+    const int q = qw + qs * 16 + lr;
+    if (q < a.n) {
+      const float inv = 1.f / lt;
+#pragma unroll
+      for (int hs = 0; hs < NH; ++hs) {
+        float v[4] = {O[hs][qs][0] * inv, O[hs][qs][1] * inv, O[hs][qs][2] * inv, O[hs][qs][3] * inv};
+        store4<T>(Out + (long)q * a.d + h * HD + hs * 16 + g4, v);
+      }
+      if (lg == 0) a.lse2[(long)h * a.ldl + q] = m_[qs] + log2f(lt);
+    }
+  }
+}
+
+// ======================================================================= dQ
+// grid (ceil(n/128), H); 4 waves x 32 queries; loops over the window's keys.
+template <typename T, int HD>
+__global__ __launch_bounds__(NT) void attn_bwd_dq_kernel(const AttnArgs a) {
+  constexpr int HDP = Dims<HD>::HDP, NC = Dims<HD>::NC, NH = Dims<HD>::NH;
+  constexpr int LDK = HDP + pad_el<T>(), LDV = 64 + pad_el<T>();
+  __shared__ __align__(16) T smK[2][64 * LDK];
+  __shared__ __align__(16) T smV[2][64 * LDK];
+  __shared__ __align__(16) T smKt[2][HD * LDV];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4, g4 = lg * 4;
+  const int h = blockIdx.y, q_lo = blockIdx.x * 128;
+  const int pos0 = *a.pos0;
+  const int qw = q_lo + wave * 32;
+  const T *Q = reinterpret_cast<const T *>(a.q);
+  const T *dO = reinterpret_cast<const T *>(a.dout);
+  const T *Kr = reinterpret_cast<const T *>(a.K) + (long)h * a.R * HD;
+  const T *Vr = reinterpret_cast<const T *>(a.V) + (long)h * a.R * HD;
+  const T *Ktr = reinterpret_cast<const T *>(a.Kt) + (long)h * HD * a.R;
+
+  Frag<T> qf[2][NC], df[2][NC];
+  float Lq[2], Dv[2];
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const int q = qw + qs * 16 + lr;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int col = c * 32 + lg * 8;
+      if (q < a.n && col < HD) {
+        load_frag(qf[qs][c], Q + (long)q * a.d + h * HD + col);
+        load_frag(df[qs][c], dO + (long)q * a.d + h * HD + col);
+      } else {
+        zero_frag(qf[qs][c]);
+        zero_frag(df[qs][c]);
+      }
+    }
+    Lq[qs] = q < a.n ? a.lse2[(long)h * a.ldl + q] : 0.f;
+    Dv[qs] = q < a.n ? a.Dq[(long)h * a.ldl + q] : 0.f;
+  }
+
+  const int p_first = pos0 + q_lo;
+  const int p_last = pos0 + min(q_lo + 127, a.n - 1);
+  const int jt0 = max(0, p_first - a.window + 1) & ~63;
+  const int ntile = (p_last - jt0) / 64 + 1;
+  const int pw_min = pos0 + qw, pw_max = pos0 + qw + 31;
+  const float sl2 = a.scale * LOG2E_F;
+
+  f32x4_v dQ[NH][2];
+#pragma unroll
+  for (int hs = 0; hs < NH; ++hs)
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) dQ[hs][qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+
+  TileIO<T, 64, HDP> kio, vio;
+  TileIO<T, HD, 64> ktio;
+  {
+    const int s0 = jt0 % a.R;
+    kio.load(Kr + (long)s0 * HD, HD, 64, HD, tid);
+    vio.load(Vr + (long)s0 * HD, HD, 64, HD, tid);
+    ktio.load(Ktr + s0, a.R, HD, 64, tid);
+    kio.store(smK[0], LDK, tid);
+    vio.store(smV[0], LDK, tid);
+    ktio.store(smKt[0], LDV, tid);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntile; ++t) {
+    const int cur = t & 1;
+    const int jt = jt0 + t * 64;
+    if (t + 1 < ntile) {
+      const int sn = (jt + 64) % a.R;
+      kio.load(Kr + (long)sn * HD, HD, 64, HD, tid);
+      vio.load(Vr + (long)sn * HD, HD, 64, HD, tid);
+      ktio.load(Ktr + sn, a.R, HD, 64, tid);
+    }
+    const bool any = (jt <= pw_max) && (jt + 63 > pw_min - a.window);
+    const bool full = (jt + 63 <= pw_min) && (jt > pw_max - a.window);
+    if (any) {
+      f32x4_v S[4][2], dP[4][2];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          S[ks][qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+          dP[ks][qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        Frag<T> kf[4], vf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          load_frag(kf[ks], smK[cur] + (ks * 16 + lr) * LDK + c * 32 + lg * 8);
+          load_frag(vf[ks], smV[cur] + (ks * 16 + lr) * LDK + c * 32 + lg * 8);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int qs = 0; qs < 2; ++qs) {
+            mma(S[ks][qs], kf[ks], qf[qs][c]);
+            mma(dP[ks][qs], vf[ks], df[qs][c]);
+          }
+      }
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const int p = pos0 + qw + qs * 16 + lr;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            bool ok = true;
+            if (!full) {
+              int j = jt + ks * 16 + g4 + r;
+              ok = (j <= p) && (j > p - a.window);
+            }
+            float pv = ok ? exp2f(S[ks][qs][r] * sl2 - Lq[qs]) : 0.f;
+            S[ks][qs][r] = pv * (dP[ks][qs][r] - Dv[qs]);
+          }
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        Frag<T> sf[2];
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          float x[8] = {S[2 * c2][qs][0],     S[2 * c2][qs][1],     S[2 * c2][qs][2],     S[2 * c2][qs][3],
+                        S[2 * c2 + 1][qs][0], S[2 * c2 + 1][qs][1], S[2 * c2 + 1][qs][2], S[2 * c2 + 1][qs][3]};
+          pack_frag(sf[qs], x);
+        }
+#pragma unroll
+        for (int hs = 0; hs < NH; ++hs) {
+          Frag<T> kt;
+          const T *row = smKt[cur] + (hs * 16 + lr) * LDV + c2 * 32 + g4;
+          load_frag2(kt, row, row + 16);
+#pragma unroll
+          for (int qs = 0; qs < 2; ++qs) mma(dQ[hs][qs], kt, sf[qs]);
+        }
+      }
+    }
+    if (t + 1 < ntile) {
+      kio.store(smK[cur ^ 1], LDK, tid);
+      vio.store(smV[cur ^ 1], LDK, tid);
+      ktio.store(smKt[cur ^ 1], LDV, tid);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const int q = qw + qs * 16 + lr;
+    if (q < a.n) {
+#pragma unroll
+      for (int hs = 0; hs < NH; ++hs) {
+        float v[4] = {dQ[hs][qs][0] * a.scale, dQ[hs][qs][1] * a.scale, dQ[hs][qs][2] * a.scale,
+                      dQ[hs][qs][3] * a.scale};
+        store4<float>(a.dq + (long)q * a.d + h * HD + hs * 16 + g4, v);
+      }
+    }
+  }
+}
+
+// ======================================================================= dK, dV
+// grid (ceil(n/64), H); 4 waves x 16 chunk keys; loops over the chunk's
+// queries at or after the key tile (all inside the window since b <= k).
+template <typename T, int HD>
+__global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(const AttnArgs a) {
+  constexpr int HDP = Dims<HD>::HDP, NC = Dims<HD>::NC, NH = Dims<HD>::NH;
+  constexpr int LDK = HDP + pad_el<T>(), LDV = 64 + pad_el<T>();
+  __shared__ __align__(16) T smQ[64 * LDK];
+  __shared__ __align__(16) T smdO[64 * LDK];
+  __shared__ __align__(16) T smQt[HD * LDV];
+  __shared__ __align__(16) T smdOt[HD * LDV];
+  __shared__ float smL[64], smD[64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4, g4 = lg * 4;
+  const int h = blockIdx.y, k_lo = blockIdx.x * 64;
+  const int pos0 = *a.pos0;
+  const int kw = k_lo + wave * 16;
+  const int key = kw + lr;  // this lane's key (chunk-relative)
+  const T *Q = reinterpret_cast<const T *>(a.q);
+  const T *dO = reinterpret_cast<const T *>(a.dout);
+  const T *Qt = reinterpret_cast<const T *>(a.qt) + (long)h * HD * a.ldt;
+  const T *dOt = reinterpret_cast<const T *>(a.doutt) + (long)h * HD * a.ldt;
+
+  Frag<T> kf[NC], vf[NC];
+  {
+    const long slot = (pos0 + key) % a.R;
+    const T *kr = reinterpret_cast<const T *>(a.K) + ((long)h * a.R + slot) * HD;
+    const T *vr = reinterpret_cast<const T *>(a.V) + ((long)h * a.R + slot) * HD;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int col = c * 32 + lg * 8;
+      if (key < a.n && col < HD) {
+        load_frag(kf[c], kr + col);
+        load_frag(vf[c], vr + col);
+      } else {
+        zero_frag(kf[c]);
+        zero_frag(vf[c]);
+      }
+    }
+  }
+  const float sl2 = a.scale * LOG2E_F;
+  f32x4_v dK[NH], dV[NH];
+#pragma unroll
+  for (int hs = 0; hs < NH; ++hs) {
+    dK[hs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    dV[hs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int qt = k_lo; qt < a.n; qt += 64) {
+    {
+      TileIO<T, 64, HDP> io;
+      io.load(Q + (long)qt * a.d + h * HD, a.d, a.n - qt, HD, tid);
+      io.store(smQ, LDK, tid);
+      io.load(dO + (long)qt * a.d + h * HD, a.d, a.n - qt, HD, tid);
+      io.store(smdO, LDK, tid);
+      TileIO<T, HD, 64> io2;
+      io2.load(Qt + qt, a.ldt, HD, a.n - qt, tid);
+      io2.store(smQt, LDV, tid);
+      io2.load(dOt + qt, a.ldt, HD, a.n - qt, tid);
+      io2.store(smdOt, LDV, tid);
+      if (tid < 64) {
+        const int q = qt + tid;
+        smL[tid] = q < a.n ? a.lse2[(long)h * a.ldl + q] : 0.f;
+        smD[tid] = q < a.n ? a.Dq[(long)h * a.ldl + q] : 0.f;
+      }
+    }
+    __syncthreads();
+    f32x4_v S[4], dP[4];
+#pragma unroll
+    for (int qs = 0; qs < 4; ++qs) {
+      S[qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      dP[qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int qs = 0; qs < 4; ++qs) {
+        Frag<T> qa, da;
+        load_frag(qa, smQ + (qs * 16 + lr) * LDK + c * 32 + lg * 8);
+        load_frag(da, smdO + (qs * 16 + lr) * LDK + c * 32 + lg * 8);
+        mma(S[qs], qa, kf[c]);
+        mma(dP[qs], da, vf[c]);
+      }
+    }
+    // lane holds S[q = qt + 16 qs + g4 + r][key]
+#pragma unroll
+    for (int qs = 0; qs < 4; ++qs)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qi = qs * 16 + g4 + r;
+        const int q = qt + qi;
+        const bool ok = (q < a.n) && (key < a.n) && (q >= key) && (q - key < a.window);
+        float pv = ok ? exp2f(S[qs][r] * sl2 - smL[qi]) : 0.f;
+        S[qs][r] = pv;
+        dP[qs][r] = pv * (dP[qs][r] - smD[qi]);
+      }
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      Frag<T> pf, sf;
+      float x[8] = {S[2 * c2][0], S[2 * c2][1], S[2 * c2][2], S[2 * c2][3],
+                    S[2 * c2 + 1][0], S[2 * c2 + 1][1], S[2 * c2 + 1][2], S[2 * c2 + 1][3]};
+      pack_frag(pf, x);
+      float y[8] = {dP[2 * c2][0], dP[2 * c2][1], dP[2 * c2][2], dP[2 * c2][3],
+                    dP[2 * c2 + 1][0], dP[2 * c2 + 1][1], dP[2 * c2 + 1][2], dP[2 * c2 + 1][3]};
+      pack_frag(sf, y);
+#pragma unroll
+      for (int hs = 0; hs < NH; ++hs) {
+        Frag<T> ao, aq;
+        const T *ro = smdOt + (hs * 16 + lr) * LDV + c2 * 32 + g4;
+        const T *rq = smQt + (hs * 16 + lr) * LDV + c2 * 32 + g4;
+        load_frag2(ao, ro, ro + 16);
+        load_frag2(aq, rq, rq + 16);
+        mma(dV[hs], ao, pf);
+        mma(dK[hs], aq, sf);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (key < a.n) {
+#pragma unroll
+    for (int hs = 0; hs < NH; ++hs) {
+      float v[4] = {dV[hs][0], dV[hs][1], dV[hs][2], dV[hs][3]};
+      store4<float>(a.dv + (long)key * a.d + h * HD + hs * 16 + g4, v);
+      float k4[4] = {dK[hs][0] * a.scale, dK[hs][1] * a.scale, dK[hs][2] * a.scale, dK[hs][3] * a.scale};
+      store4<float>(a.dk + (long)key * a.d + h * HD + hs * 16 + g4, k4);
+    }
+  }
+}
+
+template <typename T, int HD> hipError_t fwd_t(const AttnArgs &a, hipStream_t st) {
+  dim3 grid((a.n + 127) / 128, a.H);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
+template <typename T, int HD> hipError_t dq_t(const AttnArgs &a, hipStream_t st) {
+  dim3 grid((a.n + 127) / 128, a.H);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
+template <typename T, int HD> hipError_t dkdv_t(const AttnArgs &a, hipStream_t st) {
+  dim3 grid((a.n + 63) / 64, a.H);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD>), grid, dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
+
+#define HD_SWITCH(FN, T)                          \
+  switch (hd) {                                   \
+    case 16: return FN<T, 16>(a, st);             \
+    case 32: return FN<T, 32>(a, st);             \
+    case 64: return FN<T, 64>(a, st);             \
+    case 80: return FN<T, 80>(a, st);             \
+    case 96: return FN<T, 96>(a, st);             \
+    case 128: return FN<T, 128>(a, st);           \
+  }                                               \
+  return hipErrorInvalidValue;
+
+// fp32 (the small test workloads) is compiled for head_dim <= 64 only: its
+// double-buffered tiles for larger heads would not fit in 160 KiB of LDS.
+#define HD_SWITCH_F32(FN)                         \
+  switch (hd) {                                   \
+    case 16: return FN<float, 16>(a, st);         \
+    case 32: return FN<float, 32>(a, st);         \
+    case 64: return FN<float, 64>(a, st);         \
+  }                                               \
+  return hipErrorInvalidValue;
+
+hipError_t fwd_hd(bool bf, int hd, const AttnArgs &a, hipStream_t st) {
+  if (bf) { HD_SWITCH(fwd_t, bf16_t) }
+  HD_SWITCH_F32(fwd_t)
+}
+hipError_t dq_hd(bool bf, int hd, const AttnArgs &a, hipStream_t st) {
+  if (bf) { HD_SWITCH(dq_t, bf16_t) }
+  HD_SWITCH_F32(dq_t)
+}
+hipError_t dkdv_hd(bool bf, int hd, const AttnArgs &a, hipStream_t st) {
+  if (bf) { HD_SWITCH(dkdv_t, bf16_t) }
+  HD_SWITCH_F32(dkdv_t)
+}
+
+}  // namespace
+
+bool attn_supported_hd(int hd) { return hd == 16 || hd == 32 || hd == 64 || hd == 80 || hd == 96 || hd == 128; }
+
+hipError_t attn_fwd_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st) {
+  if (a.n <= 0) return hipSuccess;
+  return fwd_hd(dtype == 1, hd, a, st);
+}
+hipError_t attn_bwd_dq_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st) {
+  if (a.n <= 0) return hipSuccess;
+  return dq_hd(dtype == 1, hd, a, st);
+}
+hipError_t attn_bwd_dkdv_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st) {
+  if (a.n <= 0) return hipSuccess;
+  return dkdv_hd(dtype == 1, hd, a, st);
+}

@@ -1,0 +1,123 @@
+// Shared device helpers for the gfx950 kernels of the TTT-E2E prefill.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // raw bfloat16 storage
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+
+#define DEVI __device__ __forceinline__
+
+DEVI float to_f(float x) { return x; }
+DEVI float to_f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+template <typename T> DEVI T from_f(float f);
+template <> DEVI float from_f<float>(float f) { return f; }
+// float -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+template <> DEVI bf16_t from_f<bf16_t>(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+
+// ---------------------------------------------------------------------------
+// MFMA fragments.  A fragment is the 8 consecutive reduction-dim elements one
+// lane feeds to a 16x16 tile product with a 32-long reduction:
+//   lane l holds X[row = l % 16][k = 8 * (l / 16) + j], j = 0..7
+// for both operands; the 16x16 fp32 result has lane l holding
+//   D[row = 4 * (l / 16) + r][col = l % 16], r = 0..3.
+// bf16 uses one v_mfma_f32_16x16x32_bf16; fp32 issues eight
+// v_mfma_f32_16x16x4_f32, instruction j taking element j of every lane
+// group, which sums the same 32 products in another order.
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> { uint4 v; };
+template <> struct Frag<float> { float4 lo, hi; };
+
+DEVI void mma(f32x4_v &acc, const Frag<bf16_t> &a, const Frag<bf16_t> &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a.v),
+                                                __builtin_bit_cast(bf16x8_v, b.v), acc, 0, 0, 0);
+}
+DEVI void mma(f32x4_v &acc, const Frag<float> &a, const Frag<float> &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.z, b.lo.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.w, b.lo.w, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.x, b.hi.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.y, b.hi.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.z, b.hi.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, acc, 0, 0, 0);
+}
+
+// Load a fragment of 8 contiguous elements.
+DEVI void load_frag(Frag<bf16_t> &f, const bf16_t *p) { f.v = *reinterpret_cast<const uint4 *>(p); }
+DEVI void load_frag(Frag<float> &f, const float *p) {
+  f.lo = *reinterpret_cast<const float4 *>(p);
+  f.hi = *reinterpret_cast<const float4 *>(p + 4);
+}
+// Fragment from two runs of 4 contiguous elements (p[0..3], q[0..3]).
+DEVI void load_frag2(Frag<bf16_t> &f, const bf16_t *p, const bf16_t *q) {
+  uint2 a = *reinterpret_cast<const uint2 *>(p);
+  uint2 b = *reinterpret_cast<const uint2 *>(q);
+  f.v = make_uint4(a.x, a.y, b.x, b.y);
+}
+DEVI void load_frag2(Frag<float> &f, const float *p, const float *q) {
+  f.lo = *reinterpret_cast<const float4 *>(p);
+  f.hi = *reinterpret_cast<const float4 *>(q);
+}
+DEVI void zero_frag(Frag<bf16_t> &f) { f.v = make_uint4(0, 0, 0, 0); }
+DEVI void zero_frag(Frag<float> &f) {
+  f.lo = make_float4(0, 0, 0, 0);
+  f.hi = f.lo;
+}
+// Fragment from 8 floats (rounded to T).
+DEVI void pack_frag(Frag<bf16_t> &f, const float *x) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)from_f<bf16_t>(x[2 * i]) | ((uint32_t)from_f<bf16_t>(x[2 * i + 1]) << 16);
+  f.v = make_uint4(w[0], w[1], w[2], w[3]);
+}
+DEVI void pack_frag(Frag<float> &f, const float *x) {
+  f.lo = make_float4(x[0], x[1], x[2], x[3]);
+  f.hi = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+// Store 4 consecutive values (16 bytes fp32, 8 bytes bf16).
+template <typename T> DEVI void store4(T *p, const float *v);
+template <> DEVI void store4<float>(float *p, const float *v) {
+  *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <> DEVI void store4<bf16_t>(bf16_t *p, const float *v) {
+  uint32_t a = (uint32_t)from_f<bf16_t>(v[0]) | ((uint32_t)from_f<bf16_t>(v[1]) << 16);
+  uint32_t b = (uint32_t)from_f<bf16_t>(v[2]) | ((uint32_t)from_f<bf16_t>(v[3]) << 16);
+  *reinterpret_cast<uint2 *>(p) = make_uint2(a, b);
+}
+
+// 16-byte vector of T (8 bf16 or 4 fp32).
+template <typename T> struct Vec16 {
+  static constexpr int N = 16 / sizeof(T);
+};
+
+// ---------------------------------------------------------------------------
+// Wave-level reductions (64 lanes).
+DEVI float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+DEVI float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+// Reduce across the four 16-lane groups (lanes l, l^16, l^32, l^48).
+DEVI float group4_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+DEVI float group4_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+#define LOG2E_F 1.4426950408889634f
+#define LN2_F 0.6931471805599453f

@@ -1,0 +1,67 @@
+// Norm, rotary, embedding, SwiGLU-backward, cross-entropy reduction and
+// small bookkeeping kernels (gfx950).  All launchers enqueue on `st`.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// h[t, :] = E[tok[*pos0 + t], :] as fp32.
+hipError_t embed_launch(int dtype, const void *E, const int *tok, const int *pos0, float *h, int n, int d,
+                        hipStream_t st);
+
+// y = x * r * g, r = (mean(x^2) + eps)^-1/2 per row; optional r_out [n] and x_copy [n, d].
+hipError_t rmsnorm_fwd_launch(int dtype, const float *x, const void *g, void *y, float *r_out, float *x_copy,
+                              int n, int d, float eps, hipStream_t st);
+
+// dh_out = dh_in + r * (g*dy) - x * r^3 * mean(x * g*dy)   (dh_in may be NULL or alias dh_out);
+// also writes dh_t, the same values in the working dtype.
+hipError_t rmsnorm_bwd_launch(int dtype, const float *dy, const float *x, const float *r, const void *g,
+                              const float *dh_in, float *dh_out, void *dh_t, int n, int d, hipStream_t st);
+
+struct RopeArgs {
+  const void *qkv;      // [n][3d] pre-norm q | k | v
+  const void *gq, *gk;  // [hd] QK-norm gains
+  const float2 *cs;     // rotary table [max_pos][hd/2] of (cos, sin) pairs
+  const int *pos0;
+  int n, d, H, hd, R;
+  float eps;
+  // forward outputs
+  void *qh;             // [n][d]
+  void *qht;            // [H][hd][ldt] or NULL
+  void *K, *Vt, *Kt, *V;  // ring planes (Kt, V may be NULL)
+  int ldt;
+  // backward inputs / output
+  const float *dqh, *dkh, *dv;  // [n][d]
+  void *dqkv;           // [n][3d]
+};
+hipError_t qk_rope_fwd_launch(int dtype, const RopeArgs &a, hipStream_t st);
+hipError_t qk_rope_bwd_launch(int dtype, const RopeArgs &a, hipStream_t st);
+
+// Dq[h, q] = sum_i dO[q, h, i] * O[q, h, i];  dOt[h, i, q] = dO[q, h, i].
+hipError_t attn_bwd_pre_launch(int dtype, const void *dO, const void *O, float *Dq, void *dOt, int n, int d,
+                               int H, int hd, int ldl, int ldt, hipStream_t st);
+
+// SwiGLU backward over 16-row interleaved gate/up blocks.  GU [n][ld_gu],
+// dhmid [n][ld_h] (units), dGU [n][ld_gu]; `units` hidden units processed.
+hipError_t swiglu_bwd_launch(int dtype, const void *GU, const void *dhmid, void *dGU, int n, int units,
+                             long ld_gu, long ld_h, hipStream_t st);
+
+// Combines per-row partials (max, sum exp) into lse[m] and
+// losses[*pos0 + m] = lse - zlab[m].
+hipError_t ce_reduce_launch(const float2 *part, int P, const float *zlab, const int *pos0, float *lse,
+                            float *losses, int n, hipStream_t st);
+
+// Rotary table: cs[p][i] = (cos, sin)(p * theta^(-2i/hd)) evaluated in fp64.
+hipError_t rope_table_launch(float2 *cs, long max_pos, int hd, double theta, hipStream_t st);
+
+// dst[r * ld_dst + c] = (T) src[r * ld_src + c]
+hipError_t convert_rows_launch(int dtype, const float *src, long ld_src, void *dst, long ld_dst, int rows, int cols,
+                               hipStream_t st);
+// dst (T) = src (T) copies with row strides.
+hipError_t copy_rows_launch(int dtype, const void *src, long ld_src, void *dst, long ld_dst, int rows, int cols,
+                            hipStream_t st);
+
+hipError_t set_int_launch(int *p, int v, hipStream_t st);
+hipError_t add_int_launch(int *p, int v, hipStream_t st);
+hipError_t zero_launch(void *p, size_t bytes, hipStream_t st);
+// flag |= 1 if any of x[0..n) is not finite.
+hipError_t finite_check_launch(const float *x, long n, int *flag, hipStream_t st);

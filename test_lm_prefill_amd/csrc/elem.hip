@@ -1,0 +1,458 @@
+// Memory-bound kernels of the chunk step: embedding gather, RMSNorm forward /
+// backward, QK-norm + rotary + ring write (and its backward), the attention
+// backward pre-pass, SwiGLU backward and the cross-entropy row reduction.
+// Statistics are accumulated in fp32; inputs/outputs use the working dtype.
+#include "common.h"
+#include "elem.h"
+
+namespace {
+
+template <typename T> DEVI void load4(const T *p, float *v);
+template <> DEVI void load4<float>(const float *p, float *v) {
+  float4 x = *reinterpret_cast<const float4 *>(p);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
+template <> DEVI void load4<bf16_t>(const bf16_t *p, float *v) {
+  uint2 x = *reinterpret_cast<const uint2 *>(p);
+  v[0] = to_f((bf16_t)(x.x & 0xFFFF)); v[1] = to_f((bf16_t)(x.x >> 16));
+  v[2] = to_f((bf16_t)(x.y & 0xFFFF)); v[3] = to_f((bf16_t)(x.y >> 16));
+}
+
+// ----------------------------------------------------------------- embedding
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const T *E, const int *tok, const int *pos0, float *h, int d) {
+  const int t = blockIdx.x;
+  const long row = tok[*pos0 + t];
+  for (int i = threadIdx.x * 4; i < d; i += 1024) {
+    float v[4];
+    load4<T>(E + row * d + i, v);
+    store4<float>(h + (long)t * d + i, v);
+  }
+}
+
+// ----------------------------------------------------------------- RMSNorm
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float *x, const T *g, T *y, float *r_out,
+                                                          float *x_copy, int n, int d, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const float *xr = x + (long)row * d;
+  float ss = 0.f;
+  for (int i = lane * 4; i < d; i += 256) {
+    float4 v = *reinterpret_cast<const float4 *>(xr + i);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  const float r = 1.f / sqrtf(ss / (float)d + eps);
+  for (int i = lane * 4; i < d; i += 256) {
+    float4 v = *reinterpret_cast<const float4 *>(xr + i);
+    float gv[4];
+    load4<T>(g + i, gv);
+    float o[4] = {v.x * r * gv[0], v.y * r * gv[1], v.z * r * gv[2], v.w * r * gv[3]};
+    store4<T>(y + (long)row * d + i, o);
+    if (x_copy) *reinterpret_cast<float4 *>(x_copy + (long)row * d + i) = v;
+  }
+  if (r_out && lane == 0) r_out[row] = r;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float *dy, const float *x, const float *r,
+                                                          const T *g, const float *dh_in, float *dh_out, T *dh_t,
+                                                          int n, int d) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const long o = (long)row * d;
+  float dot = 0.f;
+  for (int i = lane * 4; i < d; i += 256) {
+    float4 a = *reinterpret_cast<const float4 *>(x + o + i);
+    float4 b = *reinterpret_cast<const float4 *>(dy + o + i);
+    float gv[4];
+    load4<T>(g + i, gv);
+    dot += a.x * b.x * gv[0] + a.y * b.y * gv[1] + a.z * b.z * gv[2] + a.w * b.w * gv[3];
+  }
+  dot = wave_sum(dot);
+  const float rr = r[row];
+  const float c = rr * rr * rr * dot / (float)d;
+  for (int i = lane * 4; i < d; i += 256) {
+    float4 a = *reinterpret_cast<const float4 *>(x + o + i);
+    float4 b = *reinterpret_cast<const float4 *>(dy + o + i);
+    float gv[4];
+    load4<T>(g + i, gv);
+    float v[4] = {rr * gv[0] * b.x - a.x * c, rr * gv[1] * b.y - a.y * c, rr * gv[2] * b.z - a.z * c,
+                  rr * gv[3] * b.w - a.w * c};
+    if (dh_in) {
+      float4 p = *reinterpret_cast<const float4 *>(dh_in + o + i);
+      v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
+    }
+    store4<float>(dh_out + o + i, v);
+    store4<T>(dh_t + o + i, v);
+  }
+}
+
+// ----------------------------------------------------------------- QK-norm + rotary (+ ring write)
+// grid (ceil(n/32), H); wave w handles tokens 8w..8w+7 of the block; lane
+// i < hd/2 handles the rotary pair (i, i + hd/2).
+template <typename T>
+__global__ __launch_bounds__(256) void qk_rope_fwd_kernel(const RopeArgs a) {
+  extern __shared__ float sm[];  // [3][hd][33]: Vt, Kt, Qt tiles
+  const int hd = a.hd, half = hd / 2, h = blockIdx.y, t0 = blockIdx.x * 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int pos0 = *a.pos0;
+  const T *qkv = reinterpret_cast<const T *>(a.qkv);
+  const T *gq = reinterpret_cast<const T *>(a.gq);
+  const T *gk = reinterpret_cast<const T *>(a.gk);
+  float *sV = sm, *sK = sm + hd * 33, *sQ = sm + 2 * hd * 33;
+  const bool act = lane < half;
+  const float gqi = act ? to_f(gq[lane]) : 0.f, gqj = act ? to_f(gq[lane + half]) : 0.f;
+  const float gki = act ? to_f(gk[lane]) : 0.f, gkj = act ? to_f(gk[lane + half]) : 0.f;
+  for (int tt = 0; tt < 8; ++tt) {
+    const int tl = wave * 8 + tt, t = t0 + tl;
+    if (t >= a.n) break;
+    const int p = pos0 + t;
+    const long base = (long)t * 3 * a.d + h * hd;
+    float qi = 0, qj = 0, ki = 0, kj = 0, vi = 0, vj = 0;
+    if (act) {
+      qi = to_f(qkv[base + lane]); qj = to_f(qkv[base + lane + half]);
+      ki = to_f(qkv[base + a.d + lane]); kj = to_f(qkv[base + a.d + lane + half]);
+      vi = to_f(qkv[base + 2 * a.d + lane]); vj = to_f(qkv[base + 2 * a.d + lane + half]);
+    }
+    const float sq = wave_sum(qi * qi + qj * qj), sk = wave_sum(ki * ki + kj * kj);
+    const float rq = 1.f / sqrtf(sq / (float)hd + a.eps), rk = 1.f / sqrtf(sk / (float)hd + a.eps);
+    if (act) {
+      const float2 cs = a.cs[(long)p * half + lane];
+      const float qa = qi * rq * gqi, qb = qj * rq * gqj, ka = ki * rk * gki, kb = kj * rk * gkj;
+      const float q1 = qa * cs.x - qb * cs.y, q2 = qa * cs.y + qb * cs.x;
+      const float k1 = ka * cs.x - kb * cs.y, k2 = ka * cs.y + kb * cs.x;
+      T *qh = reinterpret_cast<T *>(a.qh) + (long)t * a.d + h * hd;
+      qh[lane] = from_f<T>(q1);
+      qh[lane + half] = from_f<T>(q2);
+      const long slot = p % a.R;
+      T *kr = reinterpret_cast<T *>(a.K) + ((long)h * a.R + slot) * hd;
+      kr[lane] = from_f<T>(k1);
+      kr[lane + half] = from_f<T>(k2);
+      if (a.V) {
+        T *vr = reinterpret_cast<T *>(a.V) + ((long)h * a.R + slot) * hd;
+        vr[lane] = from_f<T>(vi);
+        vr[lane + half] = from_f<T>(vj);
+      }
+      sV[lane * 33 + tl] = vi; sV[(lane + half) * 33 + tl] = vj;
+      sK[lane * 33 + tl] = k1; sK[(lane + half) * 33 + tl] = k2;
+      sQ[lane * 33 + tl] = q1; sQ[(lane + half) * 33 + tl] = q2;
+    }
+  }
+  __syncthreads();
+  const int cnt = min(32, a.n - t0);
+  for (int idx = threadIdx.x; idx < hd * 32; idx += 256) {
+    const int dim = idx / 32, tl = idx % 32;
+    if (tl >= cnt) continue;
+    const int t = t0 + tl;
+    const long slot = (pos0 + t) % a.R;
+    reinterpret_cast<T *>(a.Vt)[((long)h * hd + dim) * a.R + slot] = from_f<T>(sV[dim * 33 + tl]);
+    if (a.Kt) reinterpret_cast<T *>(a.Kt)[((long)h * hd + dim) * a.R + slot] = from_f<T>(sK[dim * 33 + tl]);
+    if (a.qht) reinterpret_cast<T *>(a.qht)[((long)h * hd + dim) * a.ldt + t] = from_f<T>(sQ[dim * 33 + tl]);
+  }
+}
+
+// grid (ceil(n/4), H): one wave per (token, head).
+template <typename T>
+__global__ __launch_bounds__(256) void qk_rope_bwd_kernel(const RopeArgs a) {
+  const int hd = a.hd, half = hd / 2, h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.n) return;
+  const int p = *a.pos0 + t;
+  const bool act = lane < half;
+  const T *qkv = reinterpret_cast<const T *>(a.qkv);
+  const long base = (long)t * 3 * a.d + h * hd;
+  const long ob = (long)t * a.d + h * hd;
+  float qi = 0, qj = 0, ki = 0, kj = 0, dqi = 0, dqj = 0, dki = 0, dkj = 0;
+  float2 cs = make_float2(1.f, 0.f);
+  float gqi = 0, gqj = 0, gki = 0, gkj = 0;
+  if (act) {
+    qi = to_f(qkv[base + lane]); qj = to_f(qkv[base + lane + half]);
+    ki = to_f(qkv[base + a.d + lane]); kj = to_f(qkv[base + a.d + lane + half]);
+    cs = a.cs[(long)p * half + lane];
+    // transpose of the rotation
+    const float ai = a.dqh[ob + lane], aj = a.dqh[ob + lane + half];
+    dqi = ai * cs.x + aj * cs.y; dqj = -ai * cs.y + aj * cs.x;
+    const float bi = a.dkh[ob + lane], bj = a.dkh[ob + lane + half];
+    dki = bi * cs.x + bj * cs.y; dkj = -bi * cs.y + bj * cs.x;
+    gqi = to_f(reinterpret_cast<const T *>(a.gq)[lane]); gqj = to_f(reinterpret_cast<const T *>(a.gq)[lane + half]);
+    gki = to_f(reinterpret_cast<const T *>(a.gk)[lane]); gkj = to_f(reinterpret_cast<const T *>(a.gk)[lane + half]);
+  }
+  const float sq = wave_sum(qi * qi + qj * qj), sk = wave_sum(ki * ki + kj * kj);
+  const float rq = 1.f / sqrtf(sq / (float)hd + a.eps), rk = 1.f / sqrtf(sk / (float)hd + a.eps);
+  const float gyqi = dqi * gqi, gyqj = dqj * gqj, gyki = dki * gki, gykj = dkj * gkj;
+  const float dotq = wave_sum(qi * gyqi + qj * gyqj), dotk = wave_sum(ki * gyki + kj * gykj);
+  if (act) {
+    const float cq = rq * rq * rq * dotq / (float)hd, ck = rk * rk * rk * dotk / (float)hd;
+    T *o = reinterpret_cast<T *>(a.dqkv) + base;
+    o[lane] = from_f<T>(rq * gyqi - qi * cq);
+    o[lane + half] = from_f<T>(rq * gyqj - qj * cq);
+    o[a.d + lane] = from_f<T>(rk * gyki - ki * ck);
+    o[a.d + lane + half] = from_f<T>(rk * gykj - kj * ck);
+    o[2 * a.d + lane] = from_f<T>(a.dv[ob + lane]);
+    o[2 * a.d + lane + half] = from_f<T>(a.dv[ob + lane + half]);
+  }
+}
+
+// ----------------------------------------------------------------- attention backward pre-pass
+template <typename T>
+__global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const T *dO, const T *O, float *Dq, T *dOt, int n, int d,
+                                                           int hd, int ldl, int ldt) {
+  extern __shared__ float sm[];  // [hd][65]
+  const int h = blockIdx.y, t0 = blockIdx.x * 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int tt = 0; tt < 16; ++tt) {
+    const int tl = wave * 16 + tt, t = t0 + tl;
+    if (t >= n) break;
+    float acc = 0.f;
+    for (int i = lane; i < hd; i += 64) {
+      const float a = to_f(dO[(long)t * d + h * hd + i]);
+      acc += a * to_f(O[(long)t * d + h * hd + i]);
+      sm[i * 65 + tl] = a;
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) Dq[(long)h * ldl + t] = acc;
+  }
+  __syncthreads();
+  const int cnt = min(64, n - t0);
+  for (int idx = threadIdx.x; idx < hd * 64; idx += 256) {
+    const int dim = idx / 64, tl = idx % 64;
+    if (tl < cnt) dOt[((long)h * hd + dim) * ldt + t0 + tl] = from_f<T>(sm[dim * 65 + tl]);
+  }
+}
+
+// ----------------------------------------------------------------- SwiGLU backward
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T *GU, const T *dh, T *dGU, int n, int units, long ld_gu,
+                                                         long ld_h) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = units / 4;
+  if (idx >= (long)n * per_row) return;
+  const int m = idx / per_row, u = (idx % per_row) * 4;
+  const int blk = u / 16, t = u % 16;
+  const long gcol = (long)m * ld_gu + blk * 32 + t, ucol = gcol + 16;
+  float g[4], up[4], dy[4], dg[4], du[4];
+  load4<T>(GU + gcol, g);
+  load4<T>(GU + ucol, up);
+  load4<T>(dh + (long)m * ld_h + u, dy);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float s = 1.f / (1.f + __expf(-g[r]));
+    const float silu = g[r] * s;
+    dg[r] = dy[r] * up[r] * s * (1.f + g[r] * (1.f - s));
+    du[r] = dy[r] * silu;
+  }
+  store4<T>(dGU + gcol, dg);
+  store4<T>(dGU + ucol, du);
+}
+
+// ----------------------------------------------------------------- cross-entropy reduce
+__global__ __launch_bounds__(256) void ce_reduce_kernel(const float2 *part, int P, const float *zlab, const int *pos0,
+                                                        float *lse, float *losses, int n) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= n) return;
+  const float2 *pr = part + (long)m * P;
+  float mx = -INFINITY;
+  for (int i = lane; i < P; i += 64) mx = fmaxf(mx, pr[i].x);
+  mx = wave_max(mx);
+  float s = 0.f;
+  for (int i = lane; i < P; i += 64) {
+    const float2 v = pr[i];
+    if (v.y > 0.f) s += v.y * __expf(v.x - mx);
+  }
+  s = wave_sum(s);
+  if (lane == 0) {
+    const float l = mx + logf(s);
+    lse[m] = l;
+    losses[*pos0 + m] = l - zlab[m];
+  }
+}
+
+__global__ void rope_table_kernel(float2 *cs, long max_pos, int hd, double theta) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const int half = hd / 2;
+  if (idx >= max_pos * half) return;
+  const long p = idx / half;
+  const int i = idx % half;
+  const double inv = pow(theta, -2.0 * (double)i / (double)hd);
+  const double ang = (double)p * inv;
+  cs[idx] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+template <typename T>
+__global__ void convert_rows_kernel(const float *src, long ld_src, T *dst, long ld_dst, int rows, int cols) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)rows * cols) return;
+  const int r = idx / cols, c = idx % cols;
+  dst[(long)r * ld_dst + c] = from_f<T>(src[(long)r * ld_src + c]);
+}
+template <typename T>
+__global__ void copy_rows_kernel(const T *src, long ld_src, T *dst, long ld_dst, int rows, int cols) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)rows * cols) return;
+  const int r = idx / cols, c = idx % cols;
+  dst[(long)r * ld_dst + c] = src[(long)r * ld_src + c];
+}
+
+__global__ void set_int_kernel(int *p, int v) { *p = v; }
+__global__ void add_int_kernel(int *p, int v) { *p += v; }
+__global__ void zero_kernel(uint32_t *p, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (size_t)gridDim.x * 256) p[i] = 0;
+}
+__global__ void finite_check_kernel(const float *x, long n, int *flag) {
+  int bad = 0;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) bad |= !isfinite(x[i]);
+  if (bad) atomicOr(flag, 1);
+}
+
+inline unsigned blocks_for(long n, int per = 256) { return (unsigned)((n + per - 1) / per); }
+
+}  // namespace
+
+#define DT_DISPATCH(dtype, KERNEL, ...)                                   \
+  do {                                                                    \
+    if ((dtype) == 1) {                                                   \
+      KERNEL(bf16_t, __VA_ARGS__);                                        \
+    } else {                                                              \
+      KERNEL(float, __VA_ARGS__);                                         \
+    }                                                                     \
+  } while (0)
+
+hipError_t embed_launch(int dtype, const void *E, const int *tok, const int *pos0, float *h, int n, int d,
+                        hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+#define K_(T, ...) hipLaunchKernelGGL(embed_kernel<T>, dim3(n), dim3(256), 0, st, (const T *)E, tok, pos0, h, d)
+  DT_DISPATCH(dtype, K_, 0);
+#undef K_
+  return hipGetLastError();
+}
+
+hipError_t rmsnorm_fwd_launch(int dtype, const float *x, const void *g, void *y, float *r_out, float *x_copy, int n,
+                              int d, float eps, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+#define K_(T, ...)                                                                                            \
+  hipLaunchKernelGGL(rmsnorm_fwd_kernel<T>, dim3(blocks_for(n, 4)), dim3(256), 0, st, x, (const T *)g, (T *)y, \
+                     r_out, x_copy, n, d, eps)
+  DT_DISPATCH(dtype, K_, 0);
+#undef K_
+  return hipGetLastError();
+}
+
+hipError_t rmsnorm_bwd_launch(int dtype, const float *dy, const float *x, const float *r, const void *g,
+                              const float *dh_in, float *dh_out, void *dh_t, int n, int d, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+#define K_(T, ...)                                                                                               \
+  hipLaunchKernelGGL(rmsnorm_bwd_kernel<T>, dim3(blocks_for(n, 4)), dim3(256), 0, st, dy, x, r, (const T *)g, dh_in, \
+                     dh_out, (T *)dh_t, n, d)
+  DT_DISPATCH(dtype, K_, 0);
+#undef K_
+  return hipGetLastError();
+}
+
+hipError_t qk_rope_fwd_launch(int dtype, const RopeArgs &a, hipStream_t st) {
+  if (a.n <= 0) return hipSuccess;
+  size_t shm = (size_t)3 * a.hd * 33 * sizeof(float);
+  dim3 grid(blocks_for(a.n, 32), a.H);
+#define K_(T, ...) hipLaunchKernelGGL(qk_rope_fwd_kernel<T>, grid, dim3(256), shm, st, a)
+  DT_DISPATCH(dtype, K_, 0);
+#undef K_
+  return hipGetLastError();
+}
+
+hipError_t qk_rope_bwd_launch(int dtype, const RopeArgs &a, hipStream_t st) {
+  if (a.n <= 0) return hipSuccess;
+  dim3 grid(blocks_for(a.n, 4), a.H);
+#define K_(T, ...) hipLaunchKernelGGL(qk_rope_bwd_kernel<T>, grid, dim3(256), 0, st, a)
+  DT_DISPATCH(dtype, K_, 0);
+#undef K_
+  return hipGetLastError();
+}
+
+hipError_t attn_bwd_pre_launch(int dtype, const void *dO, const void *O, float *Dq, void *dOt, int n, int d, int H,
+                               int hd, int ldl, int ldt, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  size_t shm = (size_t)hd * 65 * sizeof(float);
+  dim3 grid(blocks_for(n, 64), H);
+#define K_(T, ...)                                                                                              \
+  hipLaunchKernelGGL(attn_bwd_pre_kernel<T>, grid, dim3(256), shm, st, (const T *)dO, (const T *)O, Dq, (T *)dOt, n, \
+                     d, hd, ldl, ldt)
+  DT_DISPATCH(dtype, K_, 0);
+#undef K_
+  return hipGetLastError();
+}
+
+hipError_t swiglu_bwd_launch(int dtype, const void *GU, const void *dhmid, void *dGU, int n, int units, long ld_gu,
+                             long ld_h, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  long tot = (long)n * (units / 4);
+#define K_(T, ...)                                                                                                  \
+  hipLaunchKernelGGL(swiglu_bwd_kernel<T>, dim3(blocks_for(tot)), dim3(256), 0, st, (const T *)GU, (const T *)dhmid, \
+                     (T *)dGU, n, units, ld_gu, ld_h)
+  DT_DISPATCH(dtype, K_, 0);
+#undef K_
+  return hipGetLastError();
+}
+
+hipError_t ce_reduce_launch(const float2 *part, int P, const float *zlab, const int *pos0, float *lse, float *losses,
+                            int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ce_reduce_kernel, dim3(blocks_for(n, 4)), dim3(256), 0, st, part, P, zlab, pos0, lse, losses, n);
+  return hipGetLastError();
+}
+
+hipError_t rope_table_launch(float2 *cs, long max_pos, int hd, double theta, hipStream_t st) {
+  long tot = max_pos * (hd / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks_for(tot)), dim3(256), 0, st, cs, max_pos, hd, theta);
+  return hipGetLastError();
+}
+
+hipError_t convert_rows_launch(int dtype, const float *src, long ld_src, void *dst, long ld_dst, int rows, int cols,
+                               hipStream_t st) {
+  long tot = (long)rows * cols;
+  if (tot <= 0) return hipSuccess;
+#define K_(T, ...)                                                                                               \
+  hipLaunchKernelGGL(convert_rows_kernel<T>, dim3(blocks_for(tot)), dim3(256), 0, st, src, ld_src, (T *)dst, ld_dst, \
+                     rows, cols)
+  DT_DISPATCH(dtype, K_, 0);
+#undef K_
+  return hipGetLastError();
+}
+
+hipError_t copy_rows_launch(int dtype, const void *src, long ld_src, void *dst, long ld_dst, int rows, int cols,
+                            hipStream_t st) {
+  long tot = (long)rows * cols;
+  if (tot <= 0) return hipSuccess;
+#define K_(T, ...)                                                                                                   \
+  hipLaunchKernelGGL(copy_rows_kernel<T>, dim3(blocks_for(tot)), dim3(256), 0, st, (const T *)src, ld_src, (T *)dst, \
+                     ld_dst, rows, cols)
+  DT_DISPATCH(dtype, K_, 0);
+#undef K_
+  return hipGetLastError();
+}
+
+hipError_t set_int_launch(int *p, int v, hipStream_t st) {
+  hipLaunchKernelGGL(set_int_kernel, dim3(1), dim3(1), 0, st, p, v);
+  return hipGetLastError();
+}
+hipError_t add_int_launch(int *p, int v, hipStream_t st) {
+  hipLaunchKernelGGL(add_int_kernel, dim3(1), dim3(1), 0, st, p, v);
+  return hipGetLastError();
+}
+hipError_t zero_launch(void *p, size_t bytes, hipStream_t st) {
+  size_t words = bytes / 4;
+  if (words == 0) return hipSuccess;
+  unsigned blocks = (unsigned)std::min<size_t>((words + 255) / 256, 8192);
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, st, (uint32_t *)p, words);
+  return hipGetLastError();
+}
+hipError_t finite_check_launch(const float *x, long n, int *flag, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  unsigned blocks = (unsigned)std::min<long>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(finite_check_kernel, dim3(blocks), dim3(256), 0, st, x, n, flag);
+  return hipGetLastError();
+}

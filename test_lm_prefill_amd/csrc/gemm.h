@@ -1,0 +1,51 @@
+// MFMA GEMM for gfx950: C[m, n] = sum_k A[m, k] * B[n, k], fp32 accumulation,
+// with fused epilogues.  Host-side launcher declarations.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+enum GemmEpi {
+  EPI_STORE = 0,     // C (T) = acc
+  EPI_STORE_F32 = 1, // Cf (fp32) = acc
+  EPI_ADD_F32 = 2,   // Cf (fp32) += acc            (residual stream)
+  EPI_SWIGLU = 3,    // C (T)[m, unit] = silu(gate) * up over 16-row interleaved gate/up
+                     // blocks of B; C2 (T, optional) = raw gate/up pre-activations
+  EPI_CE = 4,        // per-row partial (max, sum exp) over the tile's columns and the
+                     // label logit -> part / zlab   (cross-entropy, first pass)
+  EPI_DLOGITS = 5,   // C (T) = (exp(acc - lse[m]) - [n + col_off == label]) * alpha
+  EPI_SGD = 6,       // Cf (fp32 master) -= alpha * acc; C (T) = round(Cf)   (inner SGD)
+};
+
+struct GemmArgs {
+  const void *A;  // A[m, k] at A[m * lda + k] (a_kc) or A[k * lda + m] (!a_kc)
+  const void *B;  // B[n, k] at B[n * ldb + k] (b_kc) or B[k * ldb + n] (!b_kc)
+  long lda, ldb;
+  int M, N, K;
+  void *C;
+  long ldc;
+  float *Cf;
+  long ldcf;
+  void *C2;
+  long ldc2;
+  const float *rowf;  // lse per row (EPI_DLOGITS)
+  const int *rowi;    // labels: label of row m = rowi[*pos0 + m]
+  const int *pos0;
+  float2 *part;       // EPI_CE partials [M][part_ld]
+  int part_ld;
+  float *zlab;        // EPI_CE label logits [M]
+  float alpha;
+  int col_off;
+  // split-K (internal)
+  int ksplit;
+  float *ws;
+};
+
+// dtype: 0 = fp32, 1 = bf16.  a_kc / b_kc select the operand layouts.
+// For EPI_STORE / EPI_STORE_F32 / EPI_ADD_F32 the launcher may split K over
+// several work-groups into `ws` (fp32, ws_elems entries) and reduce in a fixed
+// order, which keeps results deterministic.
+hipError_t gemm_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, float *ws, size_t ws_elems,
+                       hipStream_t st, int force_split = 0);
+
+// Number of fp32 partial entries the launcher may need for an M x N output.
+size_t gemm_ws_elems(int M, int N);

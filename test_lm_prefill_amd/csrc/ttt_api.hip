@@ -1,0 +1,715 @@
+// Host side of libttt: handle, weight packing, the per-chunk step of
+// Algorithm 1 (reading notes, section 7) and its HIP-graph replay.
+//
+// One chunk step, all on one stream, no host synchronisation:
+//   forward  embed -> L x [RMSNorm, QKV GEMM, QK-norm + rotary + ring write,
+//            window attention, O GEMM (+residual), RMSNorm, gate|up GEMM with
+//            fused SwiGLU, down GEMM (+residual)] -> final RMSNorm ->
+//            LM-head GEMM with fused cross-entropy partials -> row reduce
+//            (losses recorded here, before any update: Alg. 1 step 3.3)
+//   backward (skipped with TTT_NO_UPDATE) dlogits slab by slab and dX of the
+//            head -> final RMSNorm backward -> for blocks L-1 .. L-n_u: MLP
+//            backward with the fast-weight gradient GEMMs carrying the SGD
+//            step in their epilogue (Eq. 9), then (above block L-n_u) the
+//            attention sub-block backward; keys/values of earlier chunks are
+//            constants.
+//   counter  the device-side chunk start advances by the chunk size.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/ttt.h"
+#include "attn.h"
+#include "elem.h"
+#include "gemm.h"
+
+namespace {
+
+thread_local std::string g_thread_err;
+
+struct LayerBuf {
+  void *attn_norm = nullptr, *wqkv = nullptr, *wo = nullptr, *q_norm = nullptr, *k_norm = nullptr,
+       *mlp_norm = nullptr;
+  void *wgu = nullptr;  // [2F][d] frozen, [4F][d] updated (fast rows first), gate/up interleaved by 16 rows
+  void *wd = nullptr;   // [d][F] frozen, [d][2F] updated (fast columns first)
+  bool fast = false, bwd_attn = false;
+  int u = -1;
+  void *K = nullptr, *Vt = nullptr, *Kt = nullptr, *V = nullptr;  // ring planes
+};
+
+struct Saved {
+  float *h_in = nullptr, *r1 = nullptr, *lse2 = nullptr, *h1 = nullptr, *r2 = nullptr;
+  void *qkv = nullptr, *qh = nullptr, *qht = nullptr, *o = nullptr, *m = nullptr, *gu = nullptr, *hmid = nullptr;
+};
+
+}  // namespace
+
+struct ttt_handle {
+  ttt_config cfg;
+  int dt = 0;
+  size_t es = 4;
+  int L = 0, d = 0, H = 0, hd = 0, F = 0, V = 0, k = 0, b = 0, nu = 0, R = 0, Vs = 0, P = 0;
+  std::vector<void *> allocs;
+  std::vector<std::pair<void *, size_t>> zero_list;
+  std::string err;
+  // weights
+  void *tok_emb = nullptr, *lm_head = nullptr, *final_norm = nullptr;
+  std::vector<LayerBuf> layers;
+  std::vector<float *> m_gu, m_d, i_gu, i_d;  // fp32 master and initial fast weights
+  // state and scratch
+  int *tok = nullptr, *pos0 = nullptr, *flag = nullptr;
+  float *losses = nullptr;
+  float2 *rope = nullptr;
+  void *ring_base = nullptr;
+  size_t ring_bytes = 0;
+  float *h = nullptr, *lse2 = nullptr, *hf = nullptr, *rf = nullptr, *zlab = nullptr, *lse = nullptr;
+  void *a = nullptr, *qkv = nullptr, *qh = nullptr, *o = nullptr, *m = nullptr, *hmid = nullptr, *nf = nullptr;
+  float2 *part = nullptr;
+  void *dz = nullptr, *dy = nullptr, *dhmid = nullptr, *dgu = nullptr, *dO = nullptr, *dOt = nullptr, *dqkv = nullptr;
+  float *dn = nullptr, *dh = nullptr, *dm = nullptr, *Dq = nullptr, *dq = nullptr, *dk = nullptr, *dv = nullptr,
+        *da = nullptr;
+  float *ws = nullptr;
+  size_t ws_elems = 0;
+  std::vector<Saved> saved;
+  // graphs: [0] update, [1] no-update
+  hipGraphExec_t gexec[2] = {nullptr, nullptr};
+  hipStream_t cap = nullptr;
+  int64_t chunks_last = 0;
+  int64_t launches = 0;
+};
+
+namespace {
+
+struct HipFail {
+  hipError_t e;
+  const char *what;
+};
+
+#define HIPCHK(x)                               \
+  do {                                          \
+    hipError_t e_ = (x);                        \
+    if (e_ != hipSuccess) throw HipFail{e_, #x}; \
+  } while (0)
+
+void *dalloc(ttt_handle *h, size_t bytes, bool zero = true) {
+  void *p = nullptr;
+  if (bytes == 0) bytes = 16;
+  hipError_t e = hipMalloc(&p, bytes);
+  if (e != hipSuccess) throw HipFail{e, "hipMalloc"};
+  h->allocs.push_back(p);
+  if (zero) h->zero_list.push_back({p, bytes});
+  return p;
+}
+
+void gemm(ttt_handle *h, bool akc, bool bkc, int epi, GemmArgs g, hipStream_t st) {
+  HIPCHK(gemm_launch(h->dt, akc, bkc, epi, g, h->ws, h->ws_elems, st));
+  h->launches += 2;
+}
+
+GemmArgs gargs(const void *A, long lda, const void *B, long ldb, int M, int N, int K) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.A = A;
+  g.lda = lda;
+  g.B = B;
+  g.ldb = ldb;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.alpha = 1.f;
+  return g;
+}
+
+char *off(void *p, size_t bytes) { return reinterpret_cast<char *>(p) + bytes; }
+
+// --------------------------------------------------------------------------- the chunk step
+void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
+  const int d = h->d, F = h->F, L = h->L, dt = h->dt;
+  const size_t es = h->es;
+  const float eps = h->cfg.rms_eps;
+  h->launches = 0;
+
+  HIPCHK(embed_launch(dt, h->tok_emb, h->tok, h->pos0, h->h, n, d, st));
+  h->launches++;
+  for (int l = 0; l < L; ++l) {
+    LayerBuf &lw = h->layers[l];
+    Saved *S = (lw.fast && update) ? &h->saved[lw.u] : nullptr;
+    const bool sb = S && lw.bwd_attn;  // attention of this block is back-propagated
+    // --- attention sub-block
+    HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.attn_norm, h->a, sb ? S->r1 : nullptr, sb ? S->h_in : nullptr, n, d, eps,
+                              st));
+    void *qkv = sb ? S->qkv : h->qkv;
+    {
+      GemmArgs g = gargs(h->a, d, lw.wqkv, d, n, 3 * d, d);
+      g.C = qkv;
+      g.ldc = 3 * d;
+      gemm(h, true, true, EPI_STORE, g, st);
+    }
+    void *qh = sb ? S->qh : h->qh;
+    {
+      RopeArgs ra;
+      memset(&ra, 0, sizeof(ra));
+      ra.qkv = qkv;
+      ra.gq = lw.q_norm;
+      ra.gk = lw.k_norm;
+      ra.cs = h->rope;
+      ra.pos0 = h->pos0;
+      ra.n = n;
+      ra.d = d;
+      ra.H = h->H;
+      ra.hd = h->hd;
+      ra.R = h->R;
+      ra.eps = eps;
+      ra.qh = qh;
+      ra.qht = sb ? S->qht : nullptr;
+      ra.K = lw.K;
+      ra.Vt = lw.Vt;
+      ra.Kt = lw.bwd_attn ? lw.Kt : nullptr;
+      ra.V = lw.bwd_attn ? lw.V : nullptr;
+      ra.ldt = h->b;
+      HIPCHK(qk_rope_fwd_launch(dt, ra, st));
+    }
+    void *o = sb ? S->o : h->o;
+    {
+      AttnArgs aa;
+      memset(&aa, 0, sizeof(aa));
+      aa.q = qh;
+      aa.K = lw.K;
+      aa.Vt = lw.Vt;
+      aa.o = o;
+      aa.lse2 = sb ? S->lse2 : h->lse2;
+      aa.n = n;
+      aa.d = d;
+      aa.H = h->H;
+      aa.R = h->R;
+      aa.window = h->k;
+      aa.ldl = h->b;
+      aa.ldt = h->b;
+      aa.pos0 = h->pos0;
+      aa.scale = 1.f / sqrtf((float)h->hd);
+      HIPCHK(attn_fwd_launch(dt, h->hd, aa, st));
+    }
+    {
+      GemmArgs g = gargs(o, d, lw.wo, d, n, d, d);
+      g.Cf = h->h;
+      g.ldcf = d;
+      gemm(h, true, true, EPI_ADD_F32, g, st);
+    }
+    // --- MLP sub-block (fast + static summed on one norm for updated blocks)
+    void *m = S ? S->m : h->m;
+    HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.mlp_norm, m, S ? S->r2 : nullptr, S ? S->h1 : nullptr, n, d, eps, st));
+    const int Fc = lw.fast ? 2 * F : F;  // hidden units of this block
+    void *hm = S ? S->hmid : h->hmid;
+    {
+      GemmArgs g = gargs(m, d, lw.wgu, d, n, 2 * Fc, d);
+      g.C = hm;
+      g.ldc = Fc;
+      g.C2 = S ? S->gu : nullptr;
+      g.ldc2 = 2 * Fc;
+      gemm(h, true, true, EPI_SWIGLU, g, st);
+    }
+    {
+      GemmArgs g = gargs(hm, Fc, lw.wd, Fc, n, d, Fc);
+      g.Cf = h->h;
+      g.ldcf = d;
+      gemm(h, true, true, EPI_ADD_F32, g, st);
+    }
+    h->launches += 4;
+  }
+  // --- head: final norm, LM head + cross-entropy (losses written before any update)
+  HIPCHK(rmsnorm_fwd_launch(dt, h->h, h->final_norm, h->nf, update ? h->rf : nullptr, update ? h->hf : nullptr, n, d,
+                            eps, st));
+  {
+    GemmArgs g = gargs(h->nf, d, h->lm_head, d, n, h->V, d);
+    g.rowi = h->tok + 1;
+    g.pos0 = h->pos0;
+    g.part = h->part;
+    g.part_ld = h->P;
+    g.zlab = h->zlab;
+    gemm(h, true, true, EPI_CE, g, st);
+  }
+  HIPCHK(ce_reduce_launch(h->part, h->P, h->zlab, h->pos0, h->lse, h->losses, n, st));
+  h->launches += 2;
+
+  if (update && h->nu > 0) {
+    // --- dlogits (softmax - onehot)/n, streamed over vocab slabs, and dn = dz W_lm
+    for (int v0 = 0, s = 0; v0 < h->V; v0 += h->Vs, ++s) {
+      const int vs = std::min(h->Vs, h->V - v0);
+      const void *wl = off(h->lm_head, (size_t)v0 * d * es);
+      {
+        GemmArgs g = gargs(h->nf, d, wl, d, n, vs, d);
+        g.C = h->dz;
+        g.ldc = h->Vs;
+        g.rowf = h->lse;
+        g.rowi = h->tok + 1;
+        g.pos0 = h->pos0;
+        g.col_off = v0;
+        g.alpha = 1.f / (float)n;
+        gemm(h, true, true, EPI_DLOGITS, g, st);
+      }
+      {
+        GemmArgs g = gargs(h->dz, h->Vs, wl, d, n, d, vs);
+        g.Cf = h->dn;
+        g.ldcf = d;
+        gemm(h, true, false, s == 0 ? EPI_STORE_F32 : EPI_ADD_F32, g, st);
+      }
+    }
+    HIPCHK(rmsnorm_bwd_launch(dt, h->dn, h->hf, h->rf, h->final_norm, nullptr, h->dh, h->dy, n, d, st));
+    h->launches++;
+    for (int l = L - 1; l >= L - h->nu; --l) {
+      LayerBuf &lw = h->layers[l];
+      Saved &S = h->saved[lw.u];
+      const bool last = (l == L - h->nu);
+      const int Fu = last ? F : 2 * F;  // hidden units whose gradient is needed
+      // dhmid = dy Wd_cat[:, :Fu]
+      {
+        GemmArgs g = gargs(h->dy, d, lw.wd, 2 * F, n, Fu, d);
+        g.C = h->dhmid;
+        g.ldc = 2 * F;
+        gemm(h, true, false, EPI_STORE, g, st);
+      }
+      // dWd_fast = dy^T hmid_fast, fused SGD into the fp32 master and the working copy
+      {
+        GemmArgs g = gargs(h->dy, d, S.hmid, 2 * F, d, F, n);
+        g.Cf = h->m_d[lw.u];
+        g.ldcf = F;
+        g.C = lw.wd;
+        g.ldc = 2 * F;
+        g.alpha = h->cfg.eta;
+        gemm(h, false, false, EPI_SGD, g, st);
+      }
+      HIPCHK(swiglu_bwd_launch(dt, S.gu, h->dhmid, h->dgu, n, Fu, 4 * F, 2 * F, st));
+      if (!last) {
+        GemmArgs g = gargs(h->dgu, 4 * F, lw.wgu, d, n, d, 4 * F);
+        g.Cf = h->dm;
+        g.ldcf = d;
+        gemm(h, true, false, EPI_STORE_F32, g, st);
+      }
+      // dW(gate|up)_fast = dGU_fast^T m, fused SGD
+      {
+        GemmArgs g = gargs(h->dgu, 4 * F, S.m, d, 2 * F, d, n);
+        g.Cf = h->m_gu[lw.u];
+        g.ldcf = d;
+        g.C = lw.wgu;
+        g.ldc = d;
+        g.alpha = h->cfg.eta;
+        gemm(h, false, false, EPI_SGD, g, st);
+      }
+      h->launches++;
+      if (last) break;
+      HIPCHK(rmsnorm_bwd_launch(dt, h->dm, S.h1, S.r2, lw.mlp_norm, h->dh, h->dh, h->dy, n, d, st));
+      // attention sub-block backward
+      {
+        GemmArgs g = gargs(h->dy, d, lw.wo, d, n, d, d);
+        g.C = h->dO;
+        g.ldc = d;
+        gemm(h, true, false, EPI_STORE, g, st);
+      }
+      HIPCHK(attn_bwd_pre_launch(dt, h->dO, S.o, h->Dq, h->dOt, n, d, h->H, h->hd, h->b, h->b, st));
+      {
+        AttnArgs aa;
+        memset(&aa, 0, sizeof(aa));
+        aa.q = S.qh;
+        aa.qt = S.qht;
+        aa.dout = h->dO;
+        aa.doutt = h->dOt;
+        aa.K = lw.K;
+        aa.Vt = lw.Vt;
+        aa.Kt = lw.Kt;
+        aa.V = lw.V;
+        aa.lse2 = S.lse2;
+        aa.Dq = h->Dq;
+        aa.dq = h->dq;
+        aa.dk = h->dk;
+        aa.dv = h->dv;
+        aa.n = n;
+        aa.d = d;
+        aa.H = h->H;
+        aa.R = h->R;
+        aa.window = h->k;
+        aa.ldl = h->b;
+        aa.ldt = h->b;
+        aa.pos0 = h->pos0;
+        aa.scale = 1.f / sqrtf((float)h->hd);
+        HIPCHK(attn_bwd_dq_launch(dt, h->hd, aa, st));
+        HIPCHK(attn_bwd_dkdv_launch(dt, h->hd, aa, st));
+      }
+      {
+        RopeArgs ra;
+        memset(&ra, 0, sizeof(ra));
+        ra.qkv = S.qkv;
+        ra.gq = lw.q_norm;
+        ra.gk = lw.k_norm;
+        ra.cs = h->rope;
+        ra.pos0 = h->pos0;
+        ra.n = n;
+        ra.d = d;
+        ra.H = h->H;
+        ra.hd = h->hd;
+        ra.R = h->R;
+        ra.eps = eps;
+        ra.dqh = h->dq;
+        ra.dkh = h->dk;
+        ra.dv = h->dv;
+        ra.dqkv = h->dqkv;
+        HIPCHK(qk_rope_bwd_launch(dt, ra, st));
+      }
+      {
+        GemmArgs g = gargs(h->dqkv, 3 * d, lw.wqkv, d, n, d, 3 * d);
+        g.Cf = h->da;
+        g.ldcf = d;
+        gemm(h, true, false, EPI_STORE_F32, g, st);
+      }
+      HIPCHK(rmsnorm_bwd_launch(dt, h->da, S.h_in, S.r1, lw.attn_norm, h->dh, h->dh, h->dy, n, d, st));
+      h->launches += 6;
+    }
+  }
+  HIPCHK(add_int_launch(h->pos0, n, st));
+  h->launches++;
+}
+
+// Copies W_init into the fp32 masters and the working-dtype copies.
+void reset_fast(ttt_handle *h, hipStream_t st) {
+  const int d = h->d, F = h->F;
+  for (int l = 0; l < h->L; ++l) {
+    LayerBuf &lw = h->layers[l];
+    if (!lw.fast) continue;
+    HIPCHK(hipMemcpyAsync(h->m_gu[lw.u], h->i_gu[lw.u], (size_t)2 * F * d * 4, hipMemcpyDeviceToDevice, st));
+    HIPCHK(hipMemcpyAsync(h->m_d[lw.u], h->i_d[lw.u], (size_t)d * F * 4, hipMemcpyDeviceToDevice, st));
+    HIPCHK(convert_rows_launch(h->dt, h->i_gu[lw.u], d, lw.wgu, d, 2 * F, d, st));
+    HIPCHK(convert_rows_launch(h->dt, h->i_d[lw.u], F, lw.wd, 2 * F, d, F, st));
+  }
+}
+
+ttt_status fail_hip(ttt_handle *h, const HipFail &f) {
+  char buf[512];
+  snprintf(buf, sizeof(buf), "HIP error %d (%s) in %s", (int)f.e, hipGetErrorString(f.e), f.what);
+  if (h) h->err = buf;
+  g_thread_err = buf;
+  return TTT_EHIP;
+}
+ttt_status fail(ttt_handle *h, ttt_status s, const std::string &msg) {
+  if (h) h->err = msg;
+  g_thread_err = msg;
+  return s;
+}
+
+void free_all(ttt_handle *h) {
+  for (int i = 0; i < 2; ++i)
+    if (h->gexec[i]) hipGraphExecDestroy(h->gexec[i]);
+  if (h->cap) hipStreamDestroy(h->cap);
+  for (void *p : h->allocs) hipFree(p);
+  h->allocs.clear();
+}
+
+// Interleaves gate and up rows in blocks of 16: packed row 32j+t = gate 16j+t, 32j+16+t = up 16j+t.
+void pack_gu(const void *gate, const void *up, void *dst, int F, int d, size_t es, hipStream_t st) {
+  const size_t blk = (size_t)16 * d * es;
+  HIPCHK(hipMemcpy2DAsync(dst, 2 * blk, gate, blk, blk, F / 16, hipMemcpyDeviceToDevice, st));
+  HIPCHK(hipMemcpy2DAsync(off(dst, blk), 2 * blk, up, blk, blk, F / 16, hipMemcpyDeviceToDevice, st));
+}
+
+}  // namespace
+
+// =========================================================================== C ABI
+extern "C" {
+
+ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream, ttt_handle **out) {
+  if (out) *out = nullptr;
+  if (!cfg || !w || !out) return fail(nullptr, TTT_EINVAL, "null argument");
+  const ttt_config c = *cfg;
+  if (c.n_layers < 1 || c.n_update < 0 || c.n_update > c.n_layers)
+    return fail(nullptr, TTT_EINVAL, "n_layers >= 1 and 0 <= n_update <= n_layers required");
+  if (c.n_heads < 1 || c.d_model != c.n_heads * c.head_dim) return fail(nullptr, TTT_EINVAL, "d_model != n_heads * head_dim");
+  if (c.d_model % 16 || c.d_ff % 16 || c.vocab % 16 || c.d_model <= 0 || c.d_ff <= 0 || c.vocab <= 0)
+    return fail(nullptr, TTT_EINVAL, "d_model, d_ff and vocab must be positive multiples of 16");
+  if (!attn_supported_hd(c.head_dim)) return fail(nullptr, TTT_EUNSUPPORTED, "head_dim not in {16,32,64,80,96,128}");
+  if (c.dtype != TTT_FP32 && c.dtype != TTT_BF16) return fail(nullptr, TTT_EINVAL, "dtype");
+  if (c.dtype == TTT_FP32 && c.head_dim > 64) return fail(nullptr, TTT_EUNSUPPORTED, "fp32 supports head_dim <= 64");
+  if (c.chunk <= 0 || c.window <= 0 || c.chunk % 64 || c.window % 64 || c.window < c.chunk)
+    return fail(nullptr, TTT_EINVAL, "chunk and window must be positive multiples of 64 with window >= chunk");
+  if (c.max_tokens < 1 || c.max_tokens > (1ll << 30)) return fail(nullptr, TTT_EINVAL, "max_tokens out of range");
+  if (!(c.rms_eps > 0.f) || !(c.rope_theta > 0.f) || !std::isfinite(c.eta))
+    return fail(nullptr, TTT_EINVAL, "rms_eps, rope_theta must be > 0 and eta finite");
+  if (!w->tok_emb || !w->lm_head || !w->final_norm || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
+      !w->q_norm || !w->k_norm || !w->mlp_norm || !w->w_gate || !w->w_up || !w->w_down)
+    return fail(nullptr, TTT_EINVAL, "null weight pointer");
+  for (int l = 0; l < c.n_layers; ++l)
+    if (!w->attn_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->q_norm[l] || !w->k_norm[l] ||
+        !w->mlp_norm[l] || !w->w_gate[l] || !w->w_up[l] || !w->w_down[l])
+      return fail(nullptr, TTT_EINVAL, "null per-layer weight pointer");
+  if (c.n_update > 0) {
+    if (!w->fast_gate || !w->fast_up || !w->fast_down) return fail(nullptr, TTT_EINVAL, "null fast weight array");
+    for (int u = 0; u < c.n_update; ++u)
+      if (!w->fast_gate[u] || !w->fast_up[u] || !w->fast_down[u]) return fail(nullptr, TTT_EINVAL, "null fast weight");
+  }
+
+  ttt_handle *h = new ttt_handle();
+  h->cfg = c;
+  h->dt = c.dtype == TTT_BF16 ? 1 : 0;
+  h->es = h->dt ? 2 : 4;
+  h->L = c.n_layers;
+  h->d = c.d_model;
+  h->H = c.n_heads;
+  h->hd = c.head_dim;
+  h->F = c.d_ff;
+  h->V = c.vocab;
+  h->k = c.window;
+  h->b = c.chunk;
+  h->nu = c.n_update;
+  h->R = c.window + c.chunk;  // positions s-k+1 .. s+b-1 must coexist; multiple of 64
+  h->Vs = std::min(h->V, 16384);
+  h->P = 2 * ((h->V + 127) / 128);
+  hipStream_t st = (hipStream_t)stream;
+  const int d = h->d, F = h->F, b = h->b, L = h->L, V = h->V;
+  const size_t es = h->es;
+  try {
+    // ---- weights
+    h->tok_emb = dalloc(h, (size_t)V * d * es, false);
+    h->lm_head = dalloc(h, (size_t)V * d * es, false);
+    h->final_norm = dalloc(h, d * es, false);
+    HIPCHK(hipMemcpyAsync(h->tok_emb, w->tok_emb, (size_t)V * d * es, hipMemcpyDeviceToDevice, st));
+    HIPCHK(hipMemcpyAsync(h->lm_head, w->lm_head, (size_t)V * d * es, hipMemcpyDeviceToDevice, st));
+    HIPCHK(hipMemcpyAsync(h->final_norm, w->final_norm, d * es, hipMemcpyDeviceToDevice, st));
+    h->layers.resize(L);
+    h->m_gu.resize(h->nu);
+    h->m_d.resize(h->nu);
+    h->i_gu.resize(h->nu);
+    h->i_d.resize(h->nu);
+    h->saved.resize(h->nu);
+    const size_t plane = (size_t)h->H * h->R * h->hd * es;
+    int nplanes = 0;
+    for (int l = 0; l < L; ++l) {
+      h->layers[l].fast = l >= L - h->nu;
+      h->layers[l].bwd_attn = l > L - h->nu;
+      nplanes += h->layers[l].bwd_attn ? 4 : 2;
+    }
+    h->ring_bytes = plane * nplanes;
+    h->ring_base = dalloc(h, h->ring_bytes);
+    size_t roff = 0;
+    for (int l = 0; l < L; ++l) {
+      LayerBuf &lw = h->layers[l];
+      lw.u = lw.fast ? l - (L - h->nu) : -1;
+      lw.attn_norm = dalloc(h, d * es, false);
+      lw.mlp_norm = dalloc(h, d * es, false);
+      lw.q_norm = dalloc(h, h->hd * es, false);
+      lw.k_norm = dalloc(h, h->hd * es, false);
+      HIPCHK(hipMemcpyAsync(lw.attn_norm, w->attn_norm[l], d * es, hipMemcpyDeviceToDevice, st));
+      HIPCHK(hipMemcpyAsync(lw.mlp_norm, w->mlp_norm[l], d * es, hipMemcpyDeviceToDevice, st));
+      HIPCHK(hipMemcpyAsync(lw.q_norm, w->q_norm[l], h->hd * es, hipMemcpyDeviceToDevice, st));
+      HIPCHK(hipMemcpyAsync(lw.k_norm, w->k_norm[l], h->hd * es, hipMemcpyDeviceToDevice, st));
+      const size_t dd = (size_t)d * d * es;
+      lw.wqkv = dalloc(h, 3 * dd, false);
+      HIPCHK(hipMemcpyAsync(lw.wqkv, w->wq[l], dd, hipMemcpyDeviceToDevice, st));
+      HIPCHK(hipMemcpyAsync(off(lw.wqkv, dd), w->wk[l], dd, hipMemcpyDeviceToDevice, st));
+      HIPCHK(hipMemcpyAsync(off(lw.wqkv, 2 * dd), w->wv[l], dd, hipMemcpyDeviceToDevice, st));
+      lw.wo = dalloc(h, dd, false);
+      HIPCHK(hipMemcpyAsync(lw.wo, w->wo[l], dd, hipMemcpyDeviceToDevice, st));
+      const size_t fd = (size_t)F * d * es;
+      if (!lw.fast) {
+        lw.wgu = dalloc(h, 2 * fd, false);
+        pack_gu(w->w_gate[l], w->w_up[l], lw.wgu, F, d, es, st);
+        lw.wd = dalloc(h, fd, false);
+        HIPCHK(hipMemcpyAsync(lw.wd, w->w_down[l], fd, hipMemcpyDeviceToDevice, st));
+      } else {
+        const int u = lw.u;
+        lw.wgu = dalloc(h, 4 * fd, false);
+        pack_gu(w->w_gate[l], w->w_up[l], off(lw.wgu, 2 * fd), F, d, es, st);  // static rows after the fast ones
+        lw.wd = dalloc(h, 2 * fd, false);
+        HIPCHK(hipMemcpy2DAsync(off(lw.wd, (size_t)F * es), 2 * F * es, w->w_down[l], F * es, F * es, d,
+                                hipMemcpyDeviceToDevice, st));
+        const size_t f32fd = (size_t)F * d * 4;
+        h->m_gu[u] = (float *)dalloc(h, 2 * f32fd);
+        h->m_d[u] = (float *)dalloc(h, f32fd);
+        h->i_gu[u] = (float *)dalloc(h, 2 * f32fd, false);
+        h->i_d[u] = (float *)dalloc(h, f32fd, false);
+        pack_gu(w->fast_gate[u], w->fast_up[u], h->i_gu[u], F, d, 4, st);
+        HIPCHK(hipMemcpyAsync(h->i_d[u], w->fast_down[u], f32fd, hipMemcpyDeviceToDevice, st));
+      }
+      lw.K = off(h->ring_base, roff);
+      roff += plane;
+      lw.Vt = off(h->ring_base, roff);
+      roff += plane;
+      if (lw.bwd_attn) {
+        lw.Kt = off(h->ring_base, roff);
+        roff += plane;
+        lw.V = off(h->ring_base, roff);
+        roff += plane;
+      }
+    }
+    // ---- state and chunk scratch
+    const size_t bd = (size_t)b * d;
+    h->tok = (int *)dalloc(h, (c.max_tokens + 1) * sizeof(int));
+    h->losses = (float *)dalloc(h, c.max_tokens * sizeof(float));
+    h->pos0 = (int *)dalloc(h, 64);
+    h->flag = (int *)dalloc(h, 64);
+    h->rope = (float2 *)dalloc(h, (size_t)c.max_tokens * (h->hd / 2) * sizeof(float2), false);
+    HIPCHK(rope_table_launch(h->rope, c.max_tokens, h->hd, (double)c.rope_theta, st));
+    h->h = (float *)dalloc(h, bd * 4);
+    h->lse2 = (float *)dalloc(h, (size_t)h->H * b * 4);
+    h->a = dalloc(h, bd * es);
+    h->qkv = dalloc(h, 3 * bd * es);
+    h->qh = dalloc(h, bd * es);
+    h->o = dalloc(h, bd * es);
+    h->m = dalloc(h, bd * es);
+    h->hmid = dalloc(h, (size_t)b * (h->nu > 0 ? 2 * F : F) * es);
+    h->nf = dalloc(h, bd * es);
+    h->hf = (float *)dalloc(h, bd * 4);
+    h->rf = (float *)dalloc(h, b * 4);
+    h->zlab = (float *)dalloc(h, b * 4);
+    h->lse = (float *)dalloc(h, b * 4);
+    h->part = (float2 *)dalloc(h, (size_t)b * h->P * sizeof(float2));
+    if (h->nu > 0) {
+      h->dz = dalloc(h, (size_t)b * h->Vs * es);
+      h->dn = (float *)dalloc(h, bd * 4);
+      h->dh = (float *)dalloc(h, bd * 4);
+      h->dy = dalloc(h, bd * es);
+      h->dhmid = dalloc(h, (size_t)b * 2 * F * es);
+      h->dgu = dalloc(h, (size_t)b * 4 * F * es);
+      h->dm = (float *)dalloc(h, bd * 4);
+      h->dO = dalloc(h, bd * es);
+      h->dOt = dalloc(h, bd * es);
+      h->Dq = (float *)dalloc(h, (size_t)h->H * b * 4);
+      h->dq = (float *)dalloc(h, bd * 4);
+      h->dk = (float *)dalloc(h, bd * 4);
+      h->dv = (float *)dalloc(h, bd * 4);
+      h->dqkv = dalloc(h, 3 * bd * es);
+      h->da = (float *)dalloc(h, bd * 4);
+      for (int u = 0; u < h->nu; ++u) {
+        Saved &S = h->saved[u];
+        S.h_in = (float *)dalloc(h, bd * 4);
+        S.r1 = (float *)dalloc(h, b * 4);
+        S.lse2 = (float *)dalloc(h, (size_t)h->H * b * 4);
+        S.h1 = (float *)dalloc(h, bd * 4);
+        S.r2 = (float *)dalloc(h, b * 4);
+        S.qkv = dalloc(h, 3 * bd * es);
+        S.qh = dalloc(h, bd * es);
+        S.qht = dalloc(h, bd * es);
+        S.o = dalloc(h, bd * es);
+        S.m = dalloc(h, bd * es);
+        S.gu = dalloc(h, (size_t)b * 4 * F * es);
+        S.hmid = dalloc(h, (size_t)b * 2 * F * es);
+      }
+    }
+    h->ws_elems = gemm_ws_elems(b, d);
+    h->ws = (float *)dalloc(h, h->ws_elems * 4);
+    // scratch starts as zeros (finite), so masked tile entries never carry NaN
+    HIPCHK(hipStreamSynchronize(st));
+    for (auto &z : h->zero_list) HIPCHK(hipMemsetAsync(z.first, 0, z.second, st));
+    HIPCHK(hipStreamSynchronize(st));
+    HIPCHK(hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking));
+  } catch (const HipFail &f) {
+    ttt_status s = fail_hip(h, f);
+    hipStreamSynchronize(st);
+    free_all(h);
+    delete h;
+    return f.e == hipErrorOutOfMemory ? TTT_ENOMEM : s;
+  }
+  *out = h;
+  return TTT_OK;
+}
+
+ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float *d_losses, float *const *d_fast_out,
+                       uint32_t flags, void *stream) {
+  if (!h) return fail(nullptr, TTT_EINVAL, "null handle");
+  if (T < 0 || T > h->cfg.max_tokens) return fail(h, TTT_EINVAL, "T out of range [0, max_tokens]");
+  if (T > 0 && (!d_tokens || !d_losses)) return fail(h, TTT_EINVAL, "null tokens or losses");
+  if (d_fast_out)
+    for (int i = 0; i < 3 * h->nu; ++i)
+      if (!d_fast_out[i]) return fail(h, TTT_EINVAL, "null entry in d_fast_out");
+  flags |= h->cfg.flags;
+  const bool update = !(flags & TTT_NO_UPDATE) && h->nu > 0;
+  const bool use_graph = !(flags & TTT_NO_GRAPH);
+  hipStream_t st = (hipStream_t)stream;
+  const int b = h->b, d = h->d, F = h->F;
+  try {
+    if (T > 0)
+      HIPCHK(hipMemcpyAsync(h->tok, d_tokens, (size_t)(T + 1) * sizeof(int), hipMemcpyDeviceToDevice, st));
+    HIPCHK(set_int_launch(h->pos0, 0, st));
+    HIPCHK(set_int_launch(h->flag, 0, st));
+    HIPCHK(zero_launch(h->ring_base, h->ring_bytes, st));
+    reset_fast(h, st);
+    const int64_t nfull = T / b;
+    const int tail = (int)(T % b);
+    if (nfull > 0) {
+      hipGraphExec_t ex = nullptr;
+      if (use_graph) {
+        const int gi = update ? 0 : 1;
+        if (!h->gexec[gi]) {
+          // capture one full-chunk step on the private stream
+          hipGraph_t gr = nullptr;
+          HIPCHK(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
+          try {
+            enqueue_chunk(h, b, update, h->cap);
+          } catch (...) {
+            hipStreamEndCapture(h->cap, &gr);
+            if (gr) hipGraphDestroy(gr);
+            throw;
+          }
+          HIPCHK(hipStreamEndCapture(h->cap, &gr));
+          hipError_t e = hipGraphInstantiate(&h->gexec[gi], gr, nullptr, nullptr, 0);
+          hipGraphDestroy(gr);
+          HIPCHK(e);
+        }
+        ex = h->gexec[gi];
+      }
+      for (int64_t c = 0; c < nfull; ++c) {
+        if (ex)
+          HIPCHK(hipGraphLaunch(ex, st));
+        else
+          enqueue_chunk(h, b, update, st);
+      }
+    }
+    if (tail > 0) enqueue_chunk(h, tail, update, st);
+    if (T > 0) {
+      HIPCHK(hipMemcpyAsync(d_losses, h->losses, (size_t)T * sizeof(float), hipMemcpyDeviceToDevice, st));
+      HIPCHK(finite_check_launch(h->losses, T, h->flag, st));
+    }
+    if (d_fast_out) {
+      const size_t blk = (size_t)16 * d * 4;
+      for (int u = 0; u < h->nu; ++u) {
+        HIPCHK(hipMemcpy2DAsync(d_fast_out[3 * u + 0], blk, h->m_gu[u], 2 * blk, blk, F / 16, hipMemcpyDeviceToDevice,
+                                st));
+        HIPCHK(hipMemcpy2DAsync(d_fast_out[3 * u + 1], blk, (char *)h->m_gu[u] + blk, 2 * blk, blk, F / 16,
+                                hipMemcpyDeviceToDevice, st));
+        HIPCHK(hipMemcpyAsync(d_fast_out[3 * u + 2], h->m_d[u], (size_t)d * F * 4, hipMemcpyDeviceToDevice, st));
+      }
+    }
+    h->chunks_last = nfull + (tail > 0 ? 1 : 0);
+  } catch (const HipFail &f) {
+    return fail_hip(h, f);
+  }
+  return TTT_OK;
+}
+
+ttt_status ttt_check_finite(ttt_handle *h, void *stream) {
+  if (!h) return fail(nullptr, TTT_EINVAL, "null handle");
+  int flag = 0;
+  hipError_t e = hipMemcpyAsync(&flag, h->flag, sizeof(int), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(h, HipFail{e, "ttt_check_finite"});
+  return flag ? fail(h, TTT_ENONFINITE, "non-finite loss recorded") : TTT_OK;
+}
+
+ttt_status ttt_get_stats(const ttt_handle *h, int64_t *chunks_last, int64_t *launches_per_chunk) {
+  if (!h) return TTT_EINVAL;
+  if (chunks_last) *chunks_last = h->chunks_last;
+  if (launches_per_chunk) *launches_per_chunk = h->launches;
+  return TTT_OK;
+}
+
+const char *ttt_last_error(const ttt_handle *h) { return h ? h->err.c_str() : g_thread_err.c_str(); }
+
+void ttt_destroy(ttt_handle *h) {
+  if (!h) return;
+  hipDeviceSynchronize();
+  free_all(h);
+  delete h;
+}
+
+}  // extern "C"

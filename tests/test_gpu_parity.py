@@ -1,0 +1,134 @@
+"""GPU path (libttt through its C ABI) against the CPU oracle, element by element.
+
+Tolerances: per-token loss |d| <= 1e-4 (fp32 workloads) and <= 2e-2 (bf16),
+final fast weights rel-L2 <= 1e-2 (bf16).  The change of the fast weights,
+dW = W_N - W_0, is compared too, because W_N alone is dominated by W_0.
+"""
+import numpy as np
+import pytest
+import torch
+
+from ttt_inputs import TTTConfig, get, make_tokens
+
+from gpu_util import compare, fast_init, gpu_session, run_gpu, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+TTT_NO_UPDATE, TTT_NO_GRAPH = 1, 2
+
+
+def mid(hd, dtype="bf16", T=600, n_update=2, L=3, eta=0.5, std=0.02, V=1024, k=256, b=128):
+    H = 4
+    d = H * hd
+    F = {16: 176, 64: 512, 80: 704, 96: 768, 128: 1024}[hd]
+    return TTTConfig(f"mid{hd}_{dtype}", L, d, H, hd, F, V, T, k, b, n_update, eta, dtype, init_std=std)
+
+
+def rand_tokens(n, vocab, seed=3):
+    return np.random.Generator(np.random.PCG64(seed)).integers(0, vocab, size=n).astype(np.int32)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.manual_seed(0)
+
+
+def test_weights_generated_on_device_match_host():
+    from ttt_inputs import make_weights_np, make_weights_torch
+    cfg = mid(64)
+    wt = make_weights_torch(cfg, "cuda")
+    wn = make_weights_np(cfg)
+    for k in ["tok_emb", "l1.wq", "fast0.w_down", "l2.w_up"]:
+        assert np.array_equal(wt[k].float().cpu().numpy(), wn[k]), k
+
+
+def test_tiny_fp32_full_sequence():
+    cfg = get("tiny")
+    say("case: tiny fp32 T=2048")
+    tok = make_tokens(cfg, seed=1)
+    sess, _ = gpu_session(cfg)
+    gl, gf = run_gpu(sess, tok)
+    ol, of, w = run_oracle(cfg, tok)
+    dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, w), "tiny")
+    assert dl <= 1e-4
+    assert wr <= 1e-5
+    assert dwr <= 1e-3
+
+
+@pytest.mark.parametrize("hd", [64, 80, 96])
+def test_mid_bf16_ragged(hd):
+    cfg = mid(hd)
+    say(f"case: mid hd={hd} bf16 T={cfg.seq_len} b={cfg.chunk} k={cfg.window}")
+    tok = rand_tokens(cfg.seq_len + 1, cfg.vocab, seed=hd)
+    sess, _ = gpu_session(cfg)
+    gl, gf = run_gpu(sess, tok)
+    ol, of, w = run_oracle(cfg, tok)
+    dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, w), f"mid{hd}")
+    assert dl <= 2e-2
+    assert wr <= 1e-2
+    assert dwr <= 5e-2
+
+
+def test_mid_fp32_hd64():
+    cfg = mid(64, dtype="fp32")
+    say("case: mid hd=64 fp32")
+    tok = rand_tokens(cfg.seq_len + 1, cfg.vocab, seed=7)
+    sess, _ = gpu_session(cfg)
+    gl, gf = run_gpu(sess, tok)
+    ol, of, w = run_oracle(cfg, tok)
+    dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, w), "mid64 fp32")
+    assert dl <= 1e-4
+    assert dwr <= 1e-3
+
+
+def test_no_update_equals_eta0_and_bitwise_invariants():
+    cfg = mid(80, T=512)
+    say("case: invariants hd=80 bf16 T=512")
+    tok = rand_tokens(cfg.seq_len + 1, cfg.vocab, seed=11)
+    sess, w = gpu_session(cfg)
+    sess0, _ = gpu_session(cfg.with_(eta=0.0), weights=w)
+    l_upd, f1 = run_gpu(sess, tok)
+    l_upd2, f2 = run_gpu(sess, tok)
+    # determinism: two runs bit-identical
+    assert np.array_equal(l_upd, l_upd2)
+    assert all(np.array_equal(a, b) for a, b in zip(f1, f2))
+    # graph replay == launch-by-launch
+    l_ng, f_ng = run_gpu(sess, tok, flags=TTT_NO_GRAPH)
+    assert np.array_equal(l_upd, l_ng)
+    assert all(np.array_equal(a, b) for a, b in zip(f1, f_ng))
+    # NO_UPDATE == eta = 0
+    l_nu, _ = run_gpu(sess, tok, flags=TTT_NO_UPDATE)
+    l_e0, _ = run_gpu(sess0, tok)
+    assert np.array_equal(l_nu, l_e0)
+    # update-after-predict: chunk 0 independent of eta, later chunks not
+    b = cfg.chunk
+    assert np.array_equal(l_upd[:b], l_nu[:b])
+    assert not np.array_equal(l_upd[b:], l_nu[b:])
+    # causality: perturbing tokens after position cut leaves losses[:cut] unchanged
+    cut = 300
+    t2 = tok.copy()
+    t2[cut + 1:] = (t2[cut + 1:] + 5) % cfg.vocab
+    l_c, _ = run_gpu(sess, t2)
+    assert np.array_equal(l_c[:cut], l_upd[:cut])
+    # prefix consistency: a run over the first m chunks reproduces them
+    for m in [1, 2, 3]:
+        l_p, _ = run_gpu(sess, tok[:m * b + 1])
+        assert np.array_equal(l_p, l_upd[:m * b]), m
+
+
+def test_empty_and_single_chunk():
+    cfg = mid(64, T=256)
+    sess, w = gpu_session(cfg)
+    l0, f0 = run_gpu(sess, rand_tokens(1, cfg.vocab))
+    assert len(l0) == 0
+    from ttt_inputs import make_weights_np
+    wn = make_weights_np(cfg)
+    for a, b in zip(f0, fast_init(cfg, wn)):
+        assert np.array_equal(a, b)
+    tok = rand_tokens(cfg.chunk + 1, cfg.vocab, seed=5)
+    gl, gf = run_gpu(sess, tok)
+    ol, of, wn = run_oracle(cfg, tok)
+    dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, wn), "one chunk")
+    assert dl <= 2e-2 and dwr <= 5e-2
