@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""TTT-E2E prefill benchmark on one MI355X.
+
+One step = one full prefill (Algorithm 1 of the reading notes: every chunk's
+forward, loss recording, backward into the fast MLPs and SGD update) over a
+synthetic sequence of T tokens whose ids and weights are already in HBM.
+
+Prints one JSON line: prefill tokens/s (whole job), ms per step, ms per 1K
+tokens, the same for the eta = 0 / no-update sliding-window prefill, MFMA
+utilisation of the whole step against the bf16 dense peak, a roofline entry
+for the dominant kernel class (timed live with HIP events on the prefill's
+stream) and the CPU oracle timed on a bounded sample on this host.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector and matrix)
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kappa_sum(T, k):
+    """sum_{p=0}^{T-1} min(p+1, k): attended keys over all queries (Eq. 1 of the notes)."""
+    if T <= k:
+        return T * (T + 1) // 2
+    return k * (k + 1) // 2 + (T - k) * k
+
+
+def chunk_pair_sum(T, b, k):
+    """sum over chunk keys p of the chunk queries that attend p: min(s+n-p, k) per key."""
+    tot = 0
+    for s in range(0, T, b):
+        n = min(b, T - s)
+        tot += sum(min(n - i, k) for i in range(n))
+    return tot
+
+
+def algorithmic_flops(cfg, T, update=True):
+    """Per-class algorithmic FLOPs of one prefill (multiply-add = 2; no recomputation,
+    padding or masked-tile work counted)."""
+    L, d, F, V, nu, k, b = cfg.n_layers, cfg.d_model, cfg.d_ff, cfg.vocab, cfg.n_update, cfg.window, cfg.chunk
+    ks = kappa_sum(T, k)
+    f = {
+        "gemm_qkv": 6 * d * d * T * L,
+        "attn_fwd": 4 * d * ks * L,
+        "gemm_o_residual": 2 * d * d * T * L,
+        "gemm_gate_up_swiglu": T * ((L - nu) * 4 * d * F + nu * 8 * d * F),
+        "gemm_down_residual": T * ((L - nu) * 2 * d * F + nu * 4 * d * F),
+        "gemm_lmhead_ce": 2 * d * V * T,
+    }
+    if update and nu > 0:
+        nb = nu - 1
+        f.update({
+            "gemm_dn": 2 * d * V * T,
+            "gemm_dhmid": T * (nb * 4 * d * F + 2 * d * F),
+            "gemm_dw_sgd": T * nu * 6 * d * F,
+            "gemm_dm": T * nb * 8 * d * F,
+            "gemm_do": T * nb * 2 * d * d,
+            "gemm_da": T * nb * 6 * d * d,
+            "attn_bwd_dq": nb * 4 * d * ks,
+            "attn_bwd_dkdv": nb * 4 * d * chunk_pair_sum(T, b, k),
+        })
+    return f
+
+
+def gpu_bench(cfg, steps, warmup, profile=True):
+    import torch
+    from ttt_inputs import make_weights_torch, make_tokens
+    from test_lm_prefill_amd import Session
+    from test_lm_prefill_amd.ttt import TTT_NO_UPDATE
+
+    T = cfg.seq_len
+    log(f"[bench] workload {cfg.name}: L={cfg.n_layers} d={cfg.d_model} T={T} b={cfg.chunk} k={cfg.window}")
+    t0 = time.time()
+    w = make_weights_torch(cfg, "cuda", seed=0)
+    tok_np = make_tokens(cfg, seed=1)
+    tok = torch.from_numpy(tok_np).cuda()
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
+    sess = Session(cfg, w, max_tokens=T)
+    stream = torch.cuda.current_stream()
+
+    def timed(flags, K, W):
+        for i in range(W):
+            sess.prefill(tok, flags=flags, want_fast=False, check=False)
+            torch.cuda.synchronize()
+            log(f"[bench] warmup {i + 1}/{W} flags={flags} done")
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            sess.prefill(tok, flags=flags, want_fast=False, check=False)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        log(f"[bench] timed {K} steps flags={flags}: {ms / K:.2f} ms/step")
+        return ms
+
+    ms_ttt = timed(0, steps, warmup)
+    from test_lm_prefill_amd.ttt import ttt_check_finite
+    losses, _ = sess.prefill(tok, want_fast=False, check=True)
+    mean_loss = float(losses.mean().item())
+    ms_swa = timed(TTT_NO_UPDATE, steps, 1)
+
+    ktimes = {}
+    if profile:
+        sess.set_kernel_timing(True)
+        sess.prefill(tok, want_fast=False, check=False)
+        torch.cuda.synchronize()
+        ktimes = sess.kernel_times()
+        sess.set_kernel_timing(False)
+        log("[bench] kernel timing pass done")
+    sess.close()
+    del w
+    torch.cuda.empty_cache()
+    return ms_ttt, ms_swa, ktimes, mean_loss, tok_np
+
+
+def cpu_baseline(cfg, tok_np, n_tokens):
+    """The oracle (numpy fp64) on the first n_tokens positions of the same workload,
+    as one chunk of that size: forward, losses, backward and one update."""
+    from ttt_inputs import make_weights_torch
+    from oracle.ttt_oracle import Oracle
+    import torch
+    t0 = time.time()
+    w = make_weights_torch(cfg, "cuda", seed=0)
+    wn = {k: v.float().cpu().numpy() for k, v in w.items()}
+    del w
+    torch.cuda.empty_cache()
+    log(f"[bench] cpu baseline: weights on host in {time.time() - t0:.1f}s")
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    c = cfg.with_(chunk=n_tokens)
+    orc = Oracle(c, wn)
+    t1 = time.time()
+    orc.prefill(tok_np[:n_tokens + 1])
+    dt = time.time() - t1
+    log(f"[bench] cpu baseline: {n_tokens} tokens in {dt:.1f}s")
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n_tokens} positions of the same sequence as one chunk "
+                      f"(forward, losses, backward, one SGD step), numpy float64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="2.7b_128k")
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: a TTT prefill sequence is a recurrence over chunks and "
+              "independent sequences shard with no communication; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    from ttt_inputs import get
+    cfg = get(args.config)
+    T = cfg.seq_len
+    ms_ttt, ms_swa, kt, mean_loss, tok_np = gpu_bench(cfg, args.steps, args.warmup,
+                                                      profile=not args.no_kernel_timing)
+    ms_step = ms_ttt / args.steps
+    ms_swa_step = ms_swa / args.steps
+    flops = algorithmic_flops(cfg, T, update=True)
+    total_tf = sum(flops.values()) / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    mfma_util = total_tf / (ms_step / 1e3) / peak
+    swa_tf = sum(algorithmic_flops(cfg, T, update=False).values()) / 1e12
+
+    roof = None
+    kernels = {}
+    if kt:
+        tot_prof = sum(v[0] for v in kt.values())
+        for nm, (ms, n) in sorted(kt.items(), key=lambda x: -x[1][0]):
+            if n == 0:
+                continue
+            ent = {"ms": round(ms, 3), "launches": n, "share": round(ms / tot_prof, 4)}
+            if nm in flops and ms > 0:
+                ent["tflops"] = round(flops[nm] / 1e12 / (ms / 1e3), 1)
+                ent["mfma_frac"] = round(flops[nm] / 1e12 / (ms / 1e3) / peak, 4)
+            kernels[nm] = ent
+        dom = max((nm for nm in kernels if nm in flops), key=lambda nm: kernels[nm]["ms"])
+        ms_d, n_d = kt[dom]
+        per_launch = flops[dom] / n_d
+        achieved = per_launch / 1e12 / (ms_d / n_d / 1e3)
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
+                "flop_per_launch": per_launch, "avg_launch_ms": round(ms_d / n_d, 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, tok_np, min(args.cpu_tokens, T))
+    out = {
+        "metric": "TTT prefill tokens/s and ms per 1K tokens at 128K ctx; MFMA util %",
+        "value": round(T * args.steps / (ms_ttt / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "ms_per_1k_tokens": round(ms_step * 1024 / T, 4),
+        "mfma_util_pct": round(100 * mfma_util, 2),
+        "algorithmic_tflop_per_step": round(total_tf, 2),
+        "swa_only": {"ms_per_step": round(ms_swa_step, 3), "ms_per_1k_tokens": round(ms_swa_step * 1024 / T, 4),
+                     "tokens_per_s": round(T / (ms_swa_step / 1e3), 1),
+                     "mfma_util_pct": round(100 * swa_tf / (ms_swa_step / 1e3) / peak, 2)},
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic (seeded Zipf+span-copy ids, seeded random-init weights)",
+        "config": {"workload": cfg.name, "n_layers": cfg.n_layers, "d_model": cfg.d_model, "n_heads": cfg.n_heads,
+                   "d_ff": cfg.d_ff, "vocab": cfg.vocab, "seq_len": T, "window": cfg.window, "chunk": cfg.chunk,
+                   "n_update": cfg.n_update, "eta": cfg.eta},
+        "mean_loss": round(mean_loss, 4),
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

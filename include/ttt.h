@@ -146,6 +146,22 @@ ttt_status ttt_check_finite(ttt_handle *h, void *stream);
 /* Number of chunks and of kernel launches per chunk of the last prefill (host values). */
 ttt_status ttt_get_stats(const ttt_handle *h, int64_t *chunks_last, int64_t *launches_per_chunk);
 
+/*
+ * Kernel timing (diagnostics).  While enabled, ttt_prefill launches kernel by
+ * kernel (no graph replay), brackets every kernel group of a class with HIP
+ * events on the prefill's stream and synchronises after each chunk to add the
+ * elapsed times to per-class totals.  Enabling or disabling clears the totals.
+ * Results are bit-identical to a run without timing.
+ */
+ttt_status ttt_set_kernel_timing(ttt_handle *h, int enable);
+
+/* Number of kernel classes (embed, rmsnorm, gemm_qkv, attn_fwd, ...). */
+int ttt_kernel_class_count(void);
+
+/* Name, summed duration (ms) and launch count of class `cls` since timing was
+ * enabled.  *name points to a static string. */
+ttt_status ttt_get_kernel_time(const ttt_handle *h, int cls, const char **name, double *total_ms, int64_t *count);
+
 /* Text of the last error on this handle (or of the calling thread if h is NULL). */
 const char *ttt_last_error(const ttt_handle *h);
 

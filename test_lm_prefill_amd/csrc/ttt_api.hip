@@ -81,6 +81,13 @@ struct ttt_handle {
   hipStream_t cap = nullptr;
   int64_t chunks_last = 0;
   int64_t launches = 0;
+  // kernel-class timing (diagnostics)
+  bool prof = false;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> ev_cls;
+  int ev_used = 0;
+  double kt_ms[32] = {0};
+  int64_t kt_n[32] = {0};
 };
 
 namespace {
@@ -106,10 +113,6 @@ void *dalloc(ttt_handle *h, size_t bytes, bool zero = true) {
   return p;
 }
 
-void gemm(ttt_handle *h, bool akc, bool bkc, int epi, GemmArgs g, hipStream_t st) {
-  HIPCHK(gemm_launch(h->dt, akc, bkc, epi, g, h->ws, h->ws_elems, st));
-  h->launches += 2;
-}
 
 GemmArgs gargs(const void *A, long lda, const void *B, long ldb, int M, int N, int K) {
   GemmArgs g;
@@ -127,6 +130,61 @@ GemmArgs gargs(const void *A, long lda, const void *B, long ldb, int M, int N, i
 
 char *off(void *p, size_t bytes) { return reinterpret_cast<char *>(p) + bytes; }
 
+enum KClass {
+  K_EMBED, K_RMSNORM, K_GEMM_QKV, K_ROPE, K_ATTN_FWD, K_GEMM_O, K_GEMM_GATE_UP, K_GEMM_DOWN, K_GEMM_HEAD_CE,
+  K_CE_REDUCE, K_GEMM_DLOGITS, K_GEMM_DN, K_RMSNORM_BWD, K_GEMM_DHMID, K_GEMM_DW_SGD, K_SWIGLU_BWD, K_GEMM_DM,
+  K_GEMM_DO, K_ATTN_BWD_PRE, K_ATTN_BWD_DQ, K_ATTN_BWD_DKDV, K_ROPE_BWD, K_GEMM_DA, K_MISC, K_NCLASS
+};
+const char *const kclass_names[K_NCLASS] = {
+    "embed", "rmsnorm", "gemm_qkv", "qknorm_rope_ring", "attn_fwd", "gemm_o_residual", "gemm_gate_up_swiglu",
+    "gemm_down_residual", "gemm_lmhead_ce", "ce_reduce", "gemm_dlogits", "gemm_dn", "rmsnorm_bwd", "gemm_dhmid",
+    "gemm_dw_sgd", "swiglu_bwd", "gemm_dm", "gemm_do", "attn_bwd_pre", "attn_bwd_dq", "attn_bwd_dkdv",
+    "qknorm_rope_bwd", "gemm_da", "misc"};
+
+// Brackets one kernel group with events when kernel timing is on.
+struct Prof {
+  ttt_handle *h;
+  hipStream_t st;
+  int idx = -1;
+  Prof(ttt_handle *h_, int cls, hipStream_t st_) : h(h_), st(st_) {
+    if (!h->prof) return;
+    if ((size_t)(2 * h->ev_used + 2) > h->ev.size()) {
+      hipEvent_t a, b;
+      HIPCHK(hipEventCreate(&a));
+      HIPCHK(hipEventCreate(&b));
+      h->ev.push_back(a);
+      h->ev.push_back(b);
+      h->ev_cls.push_back(0);
+    }
+    idx = h->ev_used++;
+    h->ev_cls[idx] = cls;
+    HIPCHK(hipEventRecord(h->ev[2 * idx], st));
+  }
+  ~Prof() {
+    if (idx >= 0) (void)hipEventRecord(h->ev[2 * idx + 1], st);
+  }
+};
+
+// Adds the recorded intervals of the last chunk to the per-class totals.
+void prof_collect(ttt_handle *h, hipStream_t st) {
+  if (!h->prof || h->ev_used == 0) return;
+  HIPCHK(hipStreamSynchronize(st));
+  for (int i = 0; i < h->ev_used; ++i) {
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, h->ev[2 * i], h->ev[2 * i + 1]));
+    h->kt_ms[h->ev_cls[i]] += ms;
+    h->kt_n[h->ev_cls[i]] += 1;
+  }
+  h->ev_used = 0;
+}
+#define PROF(cls) Prof prof_(h, cls, st)
+
+void gemm(ttt_handle *h, int cls, bool akc, bool bkc, int epi, GemmArgs g, hipStream_t st) {
+  Prof prof_(h, cls, st);
+  HIPCHK(gemm_launch(h->dt, akc, bkc, epi, g, h->ws, h->ws_elems, st));
+  h->launches += 2;
+}
+
 // --------------------------------------------------------------------------- the chunk step
 void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
   const int d = h->d, F = h->F, L = h->L, dt = h->dt;
@@ -134,21 +192,27 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
   const float eps = h->cfg.rms_eps;
   h->launches = 0;
 
-  HIPCHK(embed_launch(dt, h->tok_emb, h->tok, h->pos0, h->h, n, d, st));
+  {
+    PROF(K_EMBED);
+    HIPCHK(embed_launch(dt, h->tok_emb, h->tok, h->pos0, h->h, n, d, st));
+  }
   h->launches++;
   for (int l = 0; l < L; ++l) {
     LayerBuf &lw = h->layers[l];
     Saved *S = (lw.fast && update) ? &h->saved[lw.u] : nullptr;
     const bool sb = S && lw.bwd_attn;  // attention of this block is back-propagated
     // --- attention sub-block
-    HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.attn_norm, h->a, sb ? S->r1 : nullptr, sb ? S->h_in : nullptr, n, d, eps,
-                              st));
+    {
+      PROF(K_RMSNORM);
+      HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.attn_norm, h->a, sb ? S->r1 : nullptr, sb ? S->h_in : nullptr, n, d, eps,
+                                st));
+    }
     void *qkv = sb ? S->qkv : h->qkv;
     {
       GemmArgs g = gargs(h->a, d, lw.wqkv, d, n, 3 * d, d);
       g.C = qkv;
       g.ldc = 3 * d;
-      gemm(h, true, true, EPI_STORE, g, st);
+      gemm(h, K_GEMM_QKV, true, true, EPI_STORE, g, st);
     }
     void *qh = sb ? S->qh : h->qh;
     {
@@ -172,7 +236,10 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       ra.Kt = lw.bwd_attn ? lw.Kt : nullptr;
       ra.V = lw.bwd_attn ? lw.V : nullptr;
       ra.ldt = h->b;
-      HIPCHK(qk_rope_fwd_launch(dt, ra, st));
+      {
+        PROF(K_ROPE);
+        HIPCHK(qk_rope_fwd_launch(dt, ra, st));
+      }
     }
     void *o = sb ? S->o : h->o;
     {
@@ -192,17 +259,23 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       aa.ldt = h->b;
       aa.pos0 = h->pos0;
       aa.scale = 1.f / sqrtf((float)h->hd);
-      HIPCHK(attn_fwd_launch(dt, h->hd, aa, st));
+      {
+        PROF(K_ATTN_FWD);
+        HIPCHK(attn_fwd_launch(dt, h->hd, aa, st));
+      }
     }
     {
       GemmArgs g = gargs(o, d, lw.wo, d, n, d, d);
       g.Cf = h->h;
       g.ldcf = d;
-      gemm(h, true, true, EPI_ADD_F32, g, st);
+      gemm(h, K_GEMM_O, true, true, EPI_ADD_F32, g, st);
     }
     // --- MLP sub-block (fast + static summed on one norm for updated blocks)
     void *m = S ? S->m : h->m;
-    HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.mlp_norm, m, S ? S->r2 : nullptr, S ? S->h1 : nullptr, n, d, eps, st));
+    {
+      PROF(K_RMSNORM);
+      HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.mlp_norm, m, S ? S->r2 : nullptr, S ? S->h1 : nullptr, n, d, eps, st));
+    }
     const int Fc = lw.fast ? 2 * F : F;  // hidden units of this block
     void *hm = S ? S->hmid : h->hmid;
     {
@@ -211,19 +284,22 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       g.ldc = Fc;
       g.C2 = S ? S->gu : nullptr;
       g.ldc2 = 2 * Fc;
-      gemm(h, true, true, EPI_SWIGLU, g, st);
+      gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, g, st);
     }
     {
       GemmArgs g = gargs(hm, Fc, lw.wd, Fc, n, d, Fc);
       g.Cf = h->h;
       g.ldcf = d;
-      gemm(h, true, true, EPI_ADD_F32, g, st);
+      gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g, st);
     }
     h->launches += 4;
   }
   // --- head: final norm, LM head + cross-entropy (losses written before any update)
-  HIPCHK(rmsnorm_fwd_launch(dt, h->h, h->final_norm, h->nf, update ? h->rf : nullptr, update ? h->hf : nullptr, n, d,
-                            eps, st));
+  {
+    PROF(K_RMSNORM);
+    HIPCHK(rmsnorm_fwd_launch(dt, h->h, h->final_norm, h->nf, update ? h->rf : nullptr, update ? h->hf : nullptr, n, d,
+                              eps, st));
+  }
   {
     GemmArgs g = gargs(h->nf, d, h->lm_head, d, n, h->V, d);
     g.rowi = h->tok + 1;
@@ -231,9 +307,12 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
     g.part = h->part;
     g.part_ld = h->P;
     g.zlab = h->zlab;
-    gemm(h, true, true, EPI_CE, g, st);
+    gemm(h, K_GEMM_HEAD_CE, true, true, EPI_CE, g, st);
   }
-  HIPCHK(ce_reduce_launch(h->part, h->P, h->zlab, h->pos0, h->lse, h->losses, n, st));
+  {
+    PROF(K_CE_REDUCE);
+    HIPCHK(ce_reduce_launch(h->part, h->P, h->zlab, h->pos0, h->lse, h->losses, n, st));
+  }
   h->launches += 2;
 
   if (update && h->nu > 0) {
@@ -250,16 +329,19 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         g.pos0 = h->pos0;
         g.col_off = v0;
         g.alpha = 1.f / (float)n;
-        gemm(h, true, true, EPI_DLOGITS, g, st);
+        gemm(h, K_GEMM_DLOGITS, true, true, EPI_DLOGITS, g, st);
       }
       {
         GemmArgs g = gargs(h->dz, h->Vs, wl, d, n, d, vs);
         g.Cf = h->dn;
         g.ldcf = d;
-        gemm(h, true, false, s == 0 ? EPI_STORE_F32 : EPI_ADD_F32, g, st);
+        gemm(h, K_GEMM_DN, true, false, s == 0 ? EPI_STORE_F32 : EPI_ADD_F32, g, st);
       }
     }
-    HIPCHK(rmsnorm_bwd_launch(dt, h->dn, h->hf, h->rf, h->final_norm, nullptr, h->dh, h->dy, n, d, st));
+    {
+      PROF(K_RMSNORM_BWD);
+      HIPCHK(rmsnorm_bwd_launch(dt, h->dn, h->hf, h->rf, h->final_norm, nullptr, h->dh, h->dy, n, d, st));
+    }
     h->launches++;
     for (int l = L - 1; l >= L - h->nu; --l) {
       LayerBuf &lw = h->layers[l];
@@ -271,7 +353,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         GemmArgs g = gargs(h->dy, d, lw.wd, 2 * F, n, Fu, d);
         g.C = h->dhmid;
         g.ldc = 2 * F;
-        gemm(h, true, false, EPI_STORE, g, st);
+        gemm(h, K_GEMM_DHMID, true, false, EPI_STORE, g, st);
       }
       // dWd_fast = dy^T hmid_fast, fused SGD into the fp32 master and the working copy
       {
@@ -281,14 +363,17 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         g.C = lw.wd;
         g.ldc = 2 * F;
         g.alpha = h->cfg.eta;
-        gemm(h, false, false, EPI_SGD, g, st);
+        gemm(h, K_GEMM_DW_SGD, false, false, EPI_SGD, g, st);
       }
-      HIPCHK(swiglu_bwd_launch(dt, S.gu, h->dhmid, h->dgu, n, Fu, 4 * F, 2 * F, st));
+      {
+        PROF(K_SWIGLU_BWD);
+        HIPCHK(swiglu_bwd_launch(dt, S.gu, h->dhmid, h->dgu, n, Fu, 4 * F, 2 * F, st));
+      }
       if (!last) {
         GemmArgs g = gargs(h->dgu, 4 * F, lw.wgu, d, n, d, 4 * F);
         g.Cf = h->dm;
         g.ldcf = d;
-        gemm(h, true, false, EPI_STORE_F32, g, st);
+        gemm(h, K_GEMM_DM, true, false, EPI_STORE_F32, g, st);
       }
       // dW(gate|up)_fast = dGU_fast^T m, fused SGD
       {
@@ -298,19 +383,25 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         g.C = lw.wgu;
         g.ldc = d;
         g.alpha = h->cfg.eta;
-        gemm(h, false, false, EPI_SGD, g, st);
+        gemm(h, K_GEMM_DW_SGD, false, false, EPI_SGD, g, st);
       }
       h->launches++;
       if (last) break;
-      HIPCHK(rmsnorm_bwd_launch(dt, h->dm, S.h1, S.r2, lw.mlp_norm, h->dh, h->dh, h->dy, n, d, st));
+      {
+        PROF(K_RMSNORM_BWD);
+        HIPCHK(rmsnorm_bwd_launch(dt, h->dm, S.h1, S.r2, lw.mlp_norm, h->dh, h->dh, h->dy, n, d, st));
+      }
       // attention sub-block backward
       {
         GemmArgs g = gargs(h->dy, d, lw.wo, d, n, d, d);
         g.C = h->dO;
         g.ldc = d;
-        gemm(h, true, false, EPI_STORE, g, st);
+        gemm(h, K_GEMM_DO, true, false, EPI_STORE, g, st);
       }
-      HIPCHK(attn_bwd_pre_launch(dt, h->dO, S.o, h->Dq, h->dOt, n, d, h->H, h->hd, h->b, h->b, st));
+      {
+        PROF(K_ATTN_BWD_PRE);
+        HIPCHK(attn_bwd_pre_launch(dt, h->dO, S.o, h->Dq, h->dOt, n, d, h->H, h->hd, h->b, h->b, st));
+      }
       {
         AttnArgs aa;
         memset(&aa, 0, sizeof(aa));
@@ -336,8 +427,14 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         aa.ldt = h->b;
         aa.pos0 = h->pos0;
         aa.scale = 1.f / sqrtf((float)h->hd);
-        HIPCHK(attn_bwd_dq_launch(dt, h->hd, aa, st));
-        HIPCHK(attn_bwd_dkdv_launch(dt, h->hd, aa, st));
+        {
+          PROF(K_ATTN_BWD_DQ);
+          HIPCHK(attn_bwd_dq_launch(dt, h->hd, aa, st));
+        }
+        {
+          PROF(K_ATTN_BWD_DKDV);
+          HIPCHK(attn_bwd_dkdv_launch(dt, h->hd, aa, st));
+        }
       }
       {
         RopeArgs ra;
@@ -357,19 +454,28 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         ra.dkh = h->dk;
         ra.dv = h->dv;
         ra.dqkv = h->dqkv;
-        HIPCHK(qk_rope_bwd_launch(dt, ra, st));
+        {
+          PROF(K_ROPE_BWD);
+          HIPCHK(qk_rope_bwd_launch(dt, ra, st));
+        }
       }
       {
         GemmArgs g = gargs(h->dqkv, 3 * d, lw.wqkv, d, n, d, 3 * d);
         g.Cf = h->da;
         g.ldcf = d;
-        gemm(h, true, false, EPI_STORE_F32, g, st);
+        gemm(h, K_GEMM_DA, true, false, EPI_STORE_F32, g, st);
       }
-      HIPCHK(rmsnorm_bwd_launch(dt, h->da, S.h_in, S.r1, lw.attn_norm, h->dh, h->dh, h->dy, n, d, st));
+      {
+        PROF(K_RMSNORM_BWD);
+        HIPCHK(rmsnorm_bwd_launch(dt, h->da, S.h_in, S.r1, lw.attn_norm, h->dh, h->dh, h->dy, n, d, st));
+      }
       h->launches += 6;
     }
   }
-  HIPCHK(add_int_launch(h->pos0, n, st));
+  {
+    PROF(K_MISC);
+    HIPCHK(add_int_launch(h->pos0, n, st));
+  }
   h->launches++;
 }
 
@@ -624,7 +730,7 @@ ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float 
       if (!d_fast_out[i]) return fail(h, TTT_EINVAL, "null entry in d_fast_out");
   flags |= h->cfg.flags;
   const bool update = !(flags & TTT_NO_UPDATE) && h->nu > 0;
-  const bool use_graph = !(flags & TTT_NO_GRAPH);
+  const bool use_graph = !(flags & TTT_NO_GRAPH) && !h->prof;
   hipStream_t st = (hipStream_t)stream;
   const int b = h->b, d = h->d, F = h->F;
   try {
@@ -659,13 +765,18 @@ ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float 
         ex = h->gexec[gi];
       }
       for (int64_t c = 0; c < nfull; ++c) {
-        if (ex)
+        if (ex) {
           HIPCHK(hipGraphLaunch(ex, st));
-        else
+        } else {
           enqueue_chunk(h, b, update, st);
+          prof_collect(h, st);
+        }
       }
     }
-    if (tail > 0) enqueue_chunk(h, tail, update, st);
+    if (tail > 0) {
+      enqueue_chunk(h, tail, update, st);
+      prof_collect(h, st);
+    }
     if (T > 0) {
       HIPCHK(hipMemcpyAsync(d_losses, h->losses, (size_t)T * sizeof(float), hipMemcpyDeviceToDevice, st));
       HIPCHK(finite_check_launch(h->losses, T, h->flag, st));
@@ -703,11 +814,33 @@ ttt_status ttt_get_stats(const ttt_handle *h, int64_t *chunks_last, int64_t *lau
   return TTT_OK;
 }
 
+ttt_status ttt_set_kernel_timing(ttt_handle *h, int enable) {
+  if (!h) return fail(nullptr, TTT_EINVAL, "null handle");
+  h->prof = enable != 0;
+  for (int i = 0; i < K_NCLASS; ++i) {
+    h->kt_ms[i] = 0.0;
+    h->kt_n[i] = 0;
+  }
+  h->ev_used = 0;
+  return TTT_OK;
+}
+
+int ttt_kernel_class_count(void) { return K_NCLASS; }
+
+ttt_status ttt_get_kernel_time(const ttt_handle *h, int cls, const char **name, double *total_ms, int64_t *count) {
+  if (!h || cls < 0 || cls >= K_NCLASS) return TTT_EINVAL;
+  if (name) *name = kclass_names[cls];
+  if (total_ms) *total_ms = h->kt_ms[cls];
+  if (count) *count = h->kt_n[cls];
+  return TTT_OK;
+}
+
 const char *ttt_last_error(const ttt_handle *h) { return h ? h->err.c_str() : g_thread_err.c_str(); }
 
 void ttt_destroy(ttt_handle *h) {
   if (!h) return;
   hipDeviceSynchronize();
+  for (hipEvent_t e : h->ev) hipEventDestroy(e);
   free_all(h);
   delete h;
 }

@@ -15,7 +15,8 @@ TTT_OK, TTT_EINVAL, TTT_ENOMEM, TTT_EHIP, TTT_EUNSUPPORTED, TTT_ENONFINITE = 0, 
 TTT_FP32, TTT_BF16 = 0, 1
 TTT_NO_UPDATE, TTT_NO_GRAPH = 1, 2
 
-EXPORTED = ["ttt_create", "ttt_prefill", "ttt_check_finite", "ttt_get_stats", "ttt_last_error", "ttt_destroy"]
+EXPORTED = ["ttt_create", "ttt_prefill", "ttt_check_finite", "ttt_get_stats", "ttt_set_kernel_timing",
+            "ttt_kernel_class_count", "ttt_get_kernel_time", "ttt_last_error", "ttt_destroy"]
 
 
 class ttt_config(ctypes.Structure):
@@ -63,6 +64,13 @@ def lib():
         L.ttt_check_finite.restype = ctypes.c_int
         L.ttt_get_stats.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
         L.ttt_get_stats.restype = ctypes.c_int
+        L.ttt_set_kernel_timing.argtypes = [ctypes.c_void_p, ctypes.c_int]
+        L.ttt_set_kernel_timing.restype = ctypes.c_int
+        L.ttt_kernel_class_count.argtypes = []
+        L.ttt_kernel_class_count.restype = ctypes.c_int
+        L.ttt_get_kernel_time.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                          ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        L.ttt_get_kernel_time.restype = ctypes.c_int
         L.ttt_last_error.argtypes = [ctypes.c_void_p]
         L.ttt_last_error.restype = ctypes.c_char_p
         L.ttt_destroy.argtypes = [ctypes.c_void_p]
@@ -109,6 +117,21 @@ def ttt_get_stats(handle):
     a, b = ctypes.c_int64(), ctypes.c_int64()
     _check(lib().ttt_get_stats(handle, ctypes.byref(a), ctypes.byref(b)), handle)
     return a.value, b.value
+
+
+def ttt_set_kernel_timing(handle, enable):
+    _check(lib().ttt_set_kernel_timing(handle, 1 if enable else 0), handle)
+
+
+def ttt_kernel_class_count():
+    return lib().ttt_kernel_class_count()
+
+
+def ttt_get_kernel_time(handle, cls):
+    """Returns (name, total_ms, launches) of kernel class `cls`."""
+    nm, ms, n = ctypes.c_char_p(), ctypes.c_double(), ctypes.c_int64()
+    _check(lib().ttt_get_kernel_time(handle, cls, ctypes.byref(nm), ctypes.byref(ms), ctypes.byref(n)), handle)
+    return nm.value.decode(), ms.value, n.value
 
 
 def ttt_last_error(handle=None):
@@ -188,6 +211,17 @@ class Session:
 
     def stats(self):
         return ttt_get_stats(self.handle)
+
+    def kernel_times(self):
+        """{class name: (total ms, launches)} collected while kernel timing was on."""
+        out = {}
+        for c in range(ttt_kernel_class_count()):
+            nm, ms, n = ttt_get_kernel_time(self.handle, c)
+            out[nm] = (ms, n)
+        return out
+
+    def set_kernel_timing(self, enable):
+        ttt_set_kernel_timing(self.handle, enable)
 
     def close(self):
         if self.handle:
