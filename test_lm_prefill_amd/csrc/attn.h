@@ -23,7 +23,16 @@ struct AttnArgs {
   int n, d, H, R, window, ldl, ldt;
   const int *pos0;   // absolute position of the chunk's first query (device)
   float scale;       // 1/sqrt(hd)
+  // key-range split (forward and dQ): nsplit work-groups share one query tile;
+  // their partial results go to ws (fp32) and are merged in a fixed order.
+  int nsplit;
+  float *ws;         // forward: [nsplit][n][d] outputs then [nsplit][H][ldl] log2-sum-exp; dQ: [nsplit][n][d]
 };
+
+// Work-space floats the forward / dQ passes need for `nsplit` splits.
+size_t attn_ws_floats(int nsplit, int n, int d, int H, int ldl);
+// Split count that gives the GPU enough work-groups for this shape.
+int attn_pick_split(int n, int H, int window, int chunk);
 
 hipError_t attn_fwd_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st);
 hipError_t attn_bwd_dq_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st);

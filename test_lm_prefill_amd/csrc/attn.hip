@@ -11,6 +11,8 @@
 // O^T = V^T P^T once the 32 keys of a step are taken in the order
 // (4g..4g+3, 16+4g..16+4g+3) for lane group g, which is why V (and K for dQ)
 // are read transposed from LDS.  Softmax statistics stay per lane (one query).
+#include <algorithm>
+
 #include "common.h"
 #include "attn.h"
 
@@ -57,6 +59,77 @@ template <typename T, int ROWS, int COLSP> struct TileIO {
   }
 };
 
+// Branch-free variant for tiles whose rows are all valid and whose valid
+// columns (COLS) are known at compile time: every lane loads from an
+// in-bounds address and zeroes the padding columns with a select, so the
+// compiler emits straight-line loads.
+template <typename T, int ROWS, int COLSP, int COLS> struct FullTile {
+  static constexpr int VE = 16 / sizeof(T);
+  static constexpr int VPR = COLSP / VE;
+  static constexpr int TOT = ROWS * VPR;
+  static constexpr int PER = (TOT + NT - 1) / NT;
+  uint4 v[PER];
+  DEVI void load(const T *g, long gld, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NT;
+      const int r = idx / VPR, c = (idx % VPR) * VE;
+      const bool ok = (idx < TOT) && (c < COLS);
+      const uint32_t o = ok ? (uint32_t)(r * (int)gld + c) : 0u;  // element offset (< 2^31)
+      const uint4 x = *reinterpret_cast<const uint4 *>(g + o);
+      v[i] = ok ? x : make_uint4(0, 0, 0, 0);
+    }
+  }
+  DEVI void store(T *sm, int sld, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NT;
+      if (TOT % NT == 0 || idx < TOT) {
+        const int r = idx / VPR, c = (idx % VPR) * VE;
+        *reinterpret_cast<uint4 *>(sm + r * sld + c) = v[i];
+      }
+    }
+  }
+};
+
+// Ring tile loader through a buffer descriptor: per-lane byte offsets are
+// computed once and the tile position enters as the scalar offset, so the
+// prefetch of the next tile never waits on registers the current tile reuses.
+// Columns at or past COLS (padding) read an offset beyond the extent -> 0.
+template <typename T, int ROWS, int COLSP, int COLS> struct RingTile {
+  static constexpr int VE = 16 / sizeof(T);
+  static constexpr int VPR = COLSP / VE;
+  static constexpr int TOT = ROWS * VPR;
+  static constexpr int PER = (TOT + NT - 1) / NT;
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t voff[PER];
+  uint4 v[PER];
+  DEVI void init(const T *plane, uint32_t plane_bytes, int gld, int tid) {
+    rs = __builtin_amdgcn_make_buffer_rsrc((void *)plane, (short)0, plane_bytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NT;
+      const int r = idx / VPR, c = (idx % VPR) * VE;
+      voff[i] = (idx < TOT && c < COLS) ? (uint32_t)((r * gld + c) * (int)sizeof(T)) : 0x7FFFFF00u;
+    }
+  }
+  DEVI void load(int soff_bytes) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], soff_bytes, 0));
+  }
+  DEVI void store(T *sm, int sld, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NT;
+      if (TOT % NT == 0 || idx < TOT) {
+        const int r = idx / VPR, c = (idx % VPR) * VE;
+        *reinterpret_cast<uint4 *>(sm + r * sld + c) = v[i];
+      }
+    }
+  }
+};
+
 template <int HD> struct Dims {
   static constexpr int HDP = (HD + 31) / 32 * 32;  // reduction length of q.k, zero padded
   static constexpr int NC = HDP / 32;
@@ -94,11 +167,18 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const AttnArgs a) {
       else
         zero_frag(qf[qs][c]);
     }
+  // the query fragments are complete before the tile loop, so its waits need
+  // only cover the tile prefetch
+  __builtin_amdgcn_s_waitcnt(0);
 
   const int p_first = pos0 + q_lo;
   const int p_last = pos0 + min(q_lo + 127, a.n - 1);
-  const int jt0 = max(0, p_first - a.window + 1) & ~63;
-  const int ntile = (p_last - jt0) / 64 + 1;
+  const int jtw = max(0, p_first - a.window + 1) & ~63;
+  const int ntw = (p_last - jtw) / 64 + 1;
+  const int sp = blockIdx.z;
+  const int t_lo = ntw * sp / a.nsplit, t_hi = ntw * (sp + 1) / a.nsplit;
+  const int jt0 = jtw + 64 * t_lo;
+  const int ntile = t_hi - t_lo;
   const int pw_min = pos0 + qw, pw_max = pos0 + qw + 31;
   const float sl2 = a.scale * LOG2E_F;
 
@@ -109,12 +189,17 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) O[hs][qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
 
-  TileIO<T, 64, HDP> kio;
-  TileIO<T, HD, 64> vio;
-  kio.load(Kr + (long)(jt0 % a.R) * HD, HD, 64, HD, tid);
-  vio.load(Vr + (jt0 % a.R), a.R, HD, 64, tid);
-  kio.store(smK[0], LDK, tid);
-  vio.store(smV[0], LDV, tid);
+  const uint32_t plane = (uint32_t)((long)a.R * HD * sizeof(T));
+  RingTile<T, 64, HDP, HD> kio;
+  RingTile<T, HD, 64, 64> vio;
+  kio.init(Kr, plane, HD, tid);
+  vio.init(Vr, plane, a.R, tid);
+  if (ntile > 0) {
+    kio.load((jt0 % a.R) * HD * (int)sizeof(T));
+    vio.load((jt0 % a.R) * (int)sizeof(T));
+    kio.store(smK[0], LDK, tid);
+    vio.store(smV[0], LDV, tid);
+  }
   __syncthreads();
 
   for (int t = 0; t < ntile; ++t) {
@@ -122,8 +207,8 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const AttnArgs a) {
     const int jt = jt0 + t * 64;
     if (t + 1 < ntile) {
       const int sn = (jt + 64) % a.R;
-      kio.load(Kr + (long)sn * HD, HD, 64, HD, tid);
-      vio.load(Vr + sn, a.R, HD, 64, tid);
+      kio.load(sn * HD * (int)sizeof(T));
+      vio.load(sn * (int)sizeof(T));
     }
     const bool any = (jt <= pw_max) && (jt + 63 > pw_min - a.window);
     const bool full = (jt + 63 <= pw_min) && (jt > pw_max - a.window);
@@ -163,7 +248,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const AttnArgs a) {
         mloc = group4_max(mloc);
         const float mnew = fmaxf(m_[qs], mloc);
         const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = exp2f(m_[qs] - muse);
+        const float alpha = fast_exp2(m_[qs] - muse);
         m_[qs] = mnew;
         l_[qs] *= alpha;
 #pragma unroll
@@ -172,7 +257,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const AttnArgs a) {
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float pv = exp2f(S[ks][qs][r] - muse);
+            float pv = fast_exp2(S[ks][qs][r] - muse);
             S[ks][qs][r] = pv;
             l_[qs] += pv;
           }
@@ -210,15 +295,64 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const AttnArgs a) {
     const float lt = group4_sum(l_[qs]);
     const int q = qw + qs * 16 + lr;
     if (q < a.n) {
-      const float inv = 1.f / lt;
+      // a split may see no key of this query: weight 0 in the merge
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float lse = lt > 0.f ? m_[qs] + log2f(lt) : -INFINITY;
+      if (a.nsplit == 1) {
 #pragma unroll
-      for (int hs = 0; hs < NH; ++hs) {
-        float v[4] = {O[hs][qs][0] * inv, O[hs][qs][1] * inv, O[hs][qs][2] * inv, O[hs][qs][3] * inv};
-        store4<T>(Out + (long)q * a.d + h * HD + hs * 16 + g4, v);
+        for (int hs = 0; hs < NH; ++hs) {
+          float v[4] = {O[hs][qs][0] * inv, O[hs][qs][1] * inv, O[hs][qs][2] * inv, O[hs][qs][3] * inv};
+          store4<T>(Out + (long)q * a.d + h * HD + hs * 16 + g4, v);
+        }
+        if (lg == 0) a.lse2[(long)h * a.ldl + q] = lse;
+      } else {
+        float *po = a.ws + (long)sp * a.n * a.d;
+#pragma unroll
+        for (int hs = 0; hs < NH; ++hs) {
+          float v[4] = {O[hs][qs][0] * inv, O[hs][qs][1] * inv, O[hs][qs][2] * inv, O[hs][qs][3] * inv};
+          store4<float>(po + (long)q * a.d + h * HD + hs * 16 + g4, v);
+        }
+        if (lg == 0) a.ws[(long)a.nsplit * a.n * a.d + ((long)sp * a.H + h) * a.ldl + q] = lse;
       }
-      if (lg == 0) a.lse2[(long)h * a.ldl + q] = m_[qs] + log2f(lt);
     }
   }
+}
+
+// out[q, h, :] = sum_s 2^(lse_s - lse) O_s[q, h, :],  lse = log2 sum_s 2^lse_s  (fixed order in s).
+template <typename T>
+__global__ __launch_bounds__(256) void attn_fwd_merge_kernel(const AttnArgs a, int hd) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const int dq4 = a.d / 4;
+  if (idx >= (long)a.n * dq4) return;
+  const int q = idx / dq4, col = (idx % dq4) * 4, h = col / hd;
+  const float *L = a.ws + (long)a.nsplit * a.n * a.d;
+  float mx = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) mx = fmaxf(mx, L[((long)s * a.H + h) * a.ldl + q]);
+  float den = 0.f, v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float ls = L[((long)s * a.H + h) * a.ldl + q];
+    const float w = (ls == -INFINITY) ? 0.f : exp2f(ls - mx);
+    den += w;
+    const float4 o = *reinterpret_cast<const float4 *>(a.ws + ((long)s * a.n + q) * a.d + col);
+    v[0] += w * o.x; v[1] += w * o.y; v[2] += w * o.z; v[3] += w * o.w;
+  }
+  const float inv = 1.f / den;
+  v[0] *= inv; v[1] *= inv; v[2] *= inv; v[3] *= inv;
+  store4<T>(reinterpret_cast<T *>(a.o) + (long)q * a.d + col, v);
+  if (col % hd == 0) a.lse2[(long)h * a.ldl + q] = mx + log2f(den);
+}
+
+// dq[q, :] = scale-free sum over splits of the partial dQ (fixed order).
+__global__ __launch_bounds__(256) void attn_dq_merge_kernel(const AttnArgs a) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const long tot = (long)a.n * a.d / 4;
+  if (idx >= tot) return;
+  float4 acc = reinterpret_cast<const float4 *>(a.ws)[idx];
+  for (int s = 1; s < a.nsplit; ++s) {
+    const float4 x = reinterpret_cast<const float4 *>(a.ws + (long)s * a.n * a.d)[idx];
+    acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+  }
+  reinterpret_cast<float4 *>(a.dq)[idx] = acc;
 }
 
 // ======================================================================= dQ
@@ -261,11 +395,16 @@ __global__ __launch_bounds__(NT) void attn_bwd_dq_kernel(const AttnArgs a) {
     Lq[qs] = q < a.n ? a.lse2[(long)h * a.ldl + q] : 0.f;
     Dv[qs] = q < a.n ? a.Dq[(long)h * a.ldl + q] : 0.f;
   }
+  __builtin_amdgcn_s_waitcnt(0);
 
   const int p_first = pos0 + q_lo;
   const int p_last = pos0 + min(q_lo + 127, a.n - 1);
-  const int jt0 = max(0, p_first - a.window + 1) & ~63;
-  const int ntile = (p_last - jt0) / 64 + 1;
+  const int jtw = max(0, p_first - a.window + 1) & ~63;
+  const int ntw = (p_last - jtw) / 64 + 1;
+  const int sp = blockIdx.z;
+  const int t_lo = ntw * sp / a.nsplit, t_hi = ntw * (sp + 1) / a.nsplit;
+  const int jt0 = jtw + 64 * t_lo;
+  const int ntile = t_hi - t_lo;
   const int pw_min = pos0 + qw, pw_max = pos0 + qw + 31;
   const float sl2 = a.scale * LOG2E_F;
 
@@ -275,13 +414,17 @@ __global__ __launch_bounds__(NT) void attn_bwd_dq_kernel(const AttnArgs a) {
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) dQ[hs][qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
 
-  TileIO<T, 64, HDP> kio, vio;
-  TileIO<T, HD, 64> ktio;
-  {
+  const uint32_t plane = (uint32_t)((long)a.R * HD * sizeof(T));
+  RingTile<T, 64, HDP, HD> kio, vio;
+  RingTile<T, HD, 64, 64> ktio;
+  kio.init(Kr, plane, HD, tid);
+  vio.init(Vr, plane, HD, tid);
+  ktio.init(Ktr, plane, a.R, tid);
+  if (ntile > 0) {
     const int s0 = jt0 % a.R;
-    kio.load(Kr + (long)s0 * HD, HD, 64, HD, tid);
-    vio.load(Vr + (long)s0 * HD, HD, 64, HD, tid);
-    ktio.load(Ktr + s0, a.R, HD, 64, tid);
+    kio.load(s0 * HD * (int)sizeof(T));
+    vio.load(s0 * HD * (int)sizeof(T));
+    ktio.load(s0 * (int)sizeof(T));
     kio.store(smK[0], LDK, tid);
     vio.store(smV[0], LDK, tid);
     ktio.store(smKt[0], LDV, tid);
@@ -293,9 +436,9 @@ __global__ __launch_bounds__(NT) void attn_bwd_dq_kernel(const AttnArgs a) {
     const int jt = jt0 + t * 64;
     if (t + 1 < ntile) {
       const int sn = (jt + 64) % a.R;
-      kio.load(Kr + (long)sn * HD, HD, 64, HD, tid);
-      vio.load(Vr + (long)sn * HD, HD, 64, HD, tid);
-      ktio.load(Ktr + sn, a.R, HD, 64, tid);
+      kio.load(sn * HD * (int)sizeof(T));
+      vio.load(sn * HD * (int)sizeof(T));
+      ktio.load(sn * (int)sizeof(T));
     }
     const bool any = (jt <= pw_max) && (jt + 63 > pw_min - a.window);
     const bool full = (jt + 63 <= pw_min) && (jt > pw_max - a.window);
@@ -336,7 +479,7 @@ __global__ __launch_bounds__(NT) void attn_bwd_dq_kernel(const AttnArgs a) {
               int j = jt + ks * 16 + g4 + r;
               ok = (j <= p) && (j > p - a.window);
             }
-            float pv = ok ? exp2f(S[ks][qs][r] * sl2 - Lq[qs]) : 0.f;
+            float pv = ok ? fast_exp2(S[ks][qs][r] * sl2 - Lq[qs]) : 0.f;
             S[ks][qs][r] = pv * (dP[ks][qs][r] - Dv[qs]);
           }
       }
@@ -375,7 +518,8 @@ __global__ __launch_bounds__(NT) void attn_bwd_dq_kernel(const AttnArgs a) {
       for (int hs = 0; hs < NH; ++hs) {
         float v[4] = {dQ[hs][qs][0] * a.scale, dQ[hs][qs][1] * a.scale, dQ[hs][qs][2] * a.scale,
                       dQ[hs][qs][3] * a.scale};
-        store4<float>(a.dq + (long)q * a.d + h * HD + hs * 16 + g4, v);
+        float *dst = a.nsplit == 1 ? a.dq : a.ws + (long)sp * a.n * a.d;
+        store4<float>(dst + (long)q * a.d + h * HD + hs * 16 + g4, v);
       }
     }
   }
@@ -474,7 +618,7 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(const AttnArgs a) {
         const int qi = qs * 16 + g4 + r;
         const int q = qt + qi;
         const bool ok = (q < a.n) && (key < a.n) && (q >= key) && (q - key < a.window);
-        float pv = ok ? exp2f(S[qs][r] * sl2 - smL[qi]) : 0.f;
+        float pv = ok ? fast_exp2(S[qs][r] * sl2 - smL[qi]) : 0.f;
         S[qs][r] = pv;
         dP[qs][r] = pv * (dP[qs][r] - smD[qi]);
       }
@@ -513,13 +657,21 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(const AttnArgs a) {
 }
 
 template <typename T, int HD> hipError_t fwd_t(const AttnArgs &a, hipStream_t st) {
-  dim3 grid((a.n + 127) / 128, a.H);
+  dim3 grid((a.n + 127) / 128, a.H, a.nsplit);
   hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(NT), 0, st, a);
+  if (a.nsplit > 1) {
+    const long tot = (long)a.n * a.d / 4;
+    hipLaunchKernelGGL((attn_fwd_merge_kernel<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, a, HD);
+  }
   return hipGetLastError();
 }
 template <typename T, int HD> hipError_t dq_t(const AttnArgs &a, hipStream_t st) {
-  dim3 grid((a.n + 127) / 128, a.H);
+  dim3 grid((a.n + 127) / 128, a.H, a.nsplit);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, dim3(NT), 0, st, a);
+  if (a.nsplit > 1) {
+    const long tot = (long)a.n * a.d / 4;
+    hipLaunchKernelGGL(attn_dq_merge_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 template <typename T, int HD> hipError_t dkdv_t(const AttnArgs &a, hipStream_t st) {
@@ -563,6 +715,20 @@ hipError_t dkdv_hd(bool bf, int hd, const AttnArgs &a, hipStream_t st) {
 }
 
 }  // namespace
+
+size_t attn_ws_floats(int nsplit, int n, int d, int H, int ldl) {
+  return (size_t)nsplit * n * d + (size_t)nsplit * H * ldl;
+}
+
+int attn_pick_split(int n, int H, int window, int chunk) {
+  // aim for two resident work-groups per CU (256 CUs) while every split keeps
+  // at least 8 key tiles of 64
+  const long wg = (long)((n + 127) / 128) * H;
+  int s = (int)((512 + wg - 1) / wg);
+  const int tiles = (window + chunk) / 64;
+  s = std::min(s, std::max(1, tiles / 8));
+  return std::max(1, std::min(s, 8));
+}
 
 bool attn_supported_hd(int hd) { return hd == 16 || hd == 32 || hd == 64 || hd == 80 || hd == 96 || hd == 128; }
 

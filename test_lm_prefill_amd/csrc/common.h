@@ -107,17 +107,28 @@ DEVI float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
-// Reduce across the four 16-lane groups (lanes l, l^16, l^32, l^48).
+// Reduce across the four 16-lane groups (lanes l, l^16, l^32, l^48) with the
+// gfx950 row-swap moves (VALU, no LDS traffic): permlane16_swap of a value
+// with itself yields, in its two results, the value of lane l and of lane
+// l^16; permlane32_swap likewise pairs lane l with l^32.
+DEVI float xor16_pair_max(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 DEVI float group4_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  v = xor16_pair_max(v);
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 DEVI float group4_sum(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
+// 2^x with one v_exp_f32 (results below the normal range flush to zero,
+// which softmax weights tolerate).
+DEVI float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 #define LOG2E_F 1.4426950408889634f
 #define LN2_F 0.6931471805599453f

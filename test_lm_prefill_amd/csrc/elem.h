@@ -60,6 +60,12 @@ hipError_t convert_rows_launch(int dtype, const float *src, long ld_src, void *d
 hipError_t copy_rows_launch(int dtype, const void *src, long ld_src, void *dst, long ld_dst, int rows, int cols,
                             hipStream_t st);
 
+// dst[c * ldd + r] = r < R ? src[r * lds + c] : 0 for r < Rpad, c < C.  The
+// destination has the working dtype; the source is fp32 when src_f32 (always
+// in fp32 mode), else the working dtype.
+hipError_t transpose_launch(int dtype, bool src_f32, const void *src, long lds, void *dst, long ldd, int R, int Rpad,
+                            int C, hipStream_t st);
+
 hipError_t set_int_launch(int *p, int v, hipStream_t st);
 hipError_t add_int_launch(int *p, int v, hipStream_t st);
 hipError_t zero_launch(void *p, size_t bytes, hipStream_t st);

@@ -299,6 +299,25 @@ __global__ void copy_rows_kernel(const T *src, long ld_src, T *dst, long ld_dst,
   dst[(long)r * ld_dst + c] = src[(long)r * ld_src + c];
 }
 
+// dst[c * ldd + r] = r < R ? src[r * lds + c] : 0   for r < Rpad, c < C
+// (64 x 64 tiles through LDS; both global sides coalesced).
+template <typename S, typename D>
+__global__ __launch_bounds__(256) void transpose_kernel(const S *src, long lds, D *dst, long ldd, int R, int Rpad,
+                                                        int C) {
+  __shared__ float tile[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < R && c < C) ? to_f(src[(long)r * lds + c]) : 0.f;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < C && r < Rpad) dst[(long)c * ldd + r] = from_f<D>(tile[tx][i]);
+  }
+}
+
 __global__ void set_int_kernel(int *p, int v) { *p = v; }
 __global__ void add_int_kernel(int *p, int v) { *p += v; }
 __global__ void zero_kernel(uint32_t *p, size_t words) {
@@ -432,6 +451,24 @@ hipError_t copy_rows_launch(int dtype, const void *src, long ld_src, void *dst, 
                      ld_dst, rows, cols)
   DT_DISPATCH(dtype, K_, 0);
 #undef K_
+  return hipGetLastError();
+}
+
+hipError_t transpose_launch(int dtype, bool src_f32, const void *src, long lds, void *dst, long ldd, int R, int Rpad,
+                            int C, hipStream_t st) {
+  if (Rpad <= 0 || C <= 0) return hipSuccess;
+  dim3 grid((C + 63) / 64, (Rpad + 63) / 64);
+  if (dtype == 1) {
+    if (src_f32)
+      hipLaunchKernelGGL((transpose_kernel<float, bf16_t>), grid, dim3(256), 0, st, (const float *)src, lds,
+                         (bf16_t *)dst, ldd, R, Rpad, C);
+    else
+      hipLaunchKernelGGL((transpose_kernel<bf16_t, bf16_t>), grid, dim3(256), 0, st, (const bf16_t *)src, lds,
+                         (bf16_t *)dst, ldd, R, Rpad, C);
+  } else {
+    hipLaunchKernelGGL((transpose_kernel<float, float>), grid, dim3(256), 0, st, (const float *)src, lds,
+                       (float *)dst, ldd, R, Rpad, C);
+  }
   return hipGetLastError();
 }
 

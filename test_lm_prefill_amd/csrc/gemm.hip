@@ -16,6 +16,8 @@
 // offset(i % 8) + i / 8, giving every XCD a contiguous run of tiles in
 // m-fastest order; the tiles sharing one block of B (the weights) then sit on
 // one XCD and share its L2.
+#include <algorithm>
+
 #include "common.h"
 #include "gemm.h"
 
@@ -383,19 +385,27 @@ hipError_t reduce_launch(int epi, const GemmArgs &g, int S, hipStream_t st) {
 
 size_t gemm_ws_elems(int M, int N) { return (size_t)8 * M * N; }
 
+hipError_t gemm_dma_launch(int epi, const GemmArgs &g, int bn, hipStream_t st);
+
 hipError_t gemm_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, float *ws, size_t ws_elems,
                        hipStream_t st, int force_split) {
+  const bool dma = dtype == 1 && a_kc && b_kc && g.K % 64 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0;
   int split = 1;
   if (epi == EPI_STORE || epi == EPI_STORE_F32 || epi == EPI_ADD_F32) {
-    int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
     if (force_split > 0) {
       split = force_split;
+    } else if (dma) {
+      // split only when the tiles leave CUs idle: aim for ~400 work-groups,
+      // each split at least eight 64-deep steps (the fp32 partial traffic of a
+      // split costs about as much as a short K range saves)
+      if (tiles < 256) split = std::min(std::min((400 + tiles - 1) / tiles, g.K / (8 * BK)), 4);
     } else if (tiles < 256 && g.K >= 4 * BK) {
       split = (2 * 256 + tiles - 1) / tiles;
       split = min(split, g.K / (2 * BK));
       split = min(split, 8);
-      if (split < 2) split = 1;
     }
+    if (split < 2) split = 1;
     if (split > 1) {
       // each split must own at least one BK step
       int per = ((g.K + split - 1) / split + BK - 1) / BK * BK;
@@ -405,8 +415,12 @@ hipError_t gemm_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, flo
   }
   g.ksplit = split;
   g.ws = ws;
-  hipError_t e = dtype == 1 ? dispatch_layout<bf16_t>(a_kc, b_kc, epi, g, st, split)
-                            : dispatch_layout<float>(a_kc, b_kc, epi, g, st, split);
+  hipError_t e;
+  if (dma)
+    e = gemm_dma_launch(epi, g, 128, st);
+  else
+    e = dtype == 1 ? dispatch_layout<bf16_t>(a_kc, b_kc, epi, g, st, split)
+                   : dispatch_layout<float>(a_kc, b_kc, epi, g, st, split);
   if (e != hipSuccess || split == 1) return e;
   return dtype == 1 ? reduce_launch<bf16_t>(epi, g, split, st) : reduce_launch<float>(epi, g, split, st);
 }

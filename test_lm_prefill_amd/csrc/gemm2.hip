@@ -1,0 +1,292 @@
+// bf16 MFMA GEMM for gfx950 with operands streamed straight into LDS
+// (used for every bf16 GEMM whose operands are both k-contiguous).
+//
+// C[m, n] = sum_k A[m, k] B[n, k], both operands stored with k contiguous
+// (activations A [M][lda], weights B [N][ldb]).  Work-group tile BN (weight
+// rows) x 128 (tokens) x 64 (k), 256 threads = 4 waves in a 2 x 2 grid; each
+// wave owns (BN/2) x 64 outputs as 16x16 tiles of v_mfma_f32_16x16x32_bf16.
+//
+// Loads: buffer_load_dwordx4 ... lds writes each lane's 16 bytes directly to
+// LDS at (base + 16 * lane), so one instruction fills 1 KiB = 8 tile rows of
+// 128 bytes.  The lane -> global chunk mapping applies an XOR swizzle
+// (chunk ^ ((row >> 1) & 7)) so that the fragment reads (16 consecutive rows,
+// one 16-byte chunk) hit 64 distinct banks.  Per-lane byte offsets are loop
+// invariant; the k position enters through the scalar offset.  Rows outside
+// the matrix get an offset beyond the buffer's extent, which the hardware
+// returns as zeros.  STAGES tiles are in flight; each thread waits on its own
+// vector-memory counter for the oldest tile, then a barrier publishes it.
+#include "common.h"
+#include "gemm.h"
+
+namespace ttt_g2 {
+
+constexpr int BM = 128, BK = 64, NT = 256;
+constexpr uint32_t OOB = 0x7FFFFF00u;
+constexpr int RSRC_W3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+
+template <int BN> struct G2 {
+  static constexpr int ROWS = BN + BM;        // tile rows per stage (weights then tokens)
+  static constexpr int SBYTES = ROWS * 128;   // bytes per LDS stage
+  static constexpr int CPT = ROWS / 32;       // 16-byte chunks each thread moves per tile
+  static constexpr int WN = BN / 2;           // wave tile along n
+  static constexpr int NI = WN / 16;
+};
+
+DEVI int swz(int row) { return (row >> 1) & 7; }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N> DEVI void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+DEVI int remap_tile2(int i, int T) {
+  int q = T / 8, rem = T % 8;
+  int x = i % 8, j = i / 8;
+  return x * q + min(x, rem) + j;
+}
+
+template <int BN, int EPI, typename Acc>
+DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, int wm, int wn, int lr, int lq) {
+  constexpr int NI = G2<BN>::NI, WN = G2<BN>::WN;
+  // ------------------------------------------------------------- epilogues
+  // lane holds C[m][n .. n+3] for m = m0 + wm*64 + 16 j + lr, n = n0 + wn*WN + 16 i + 4 lq
+  const int g4 = lq * 4;
+  if constexpr (EPI == EPI_CE) {
+    const int lab_base = *g.pos0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wm * 64 + j * 16 + lr;
+      const int lab = (m < g.M) ? g.rowi[lab_base + m] : -1;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = n0 + wn * WN + i * 16 + g4 + r;
+          if (n < g.N) mx = fmaxf(mx, acc[i][j][r]);
+        }
+      mx = group4_max(mx);
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = n0 + wn * WN + i * 16 + g4 + r;
+          if (n < g.N) {
+            s += fast_exp2((acc[i][j][r] - mx) * LOG2E_F);
+            if (n + g.col_off == lab) g.zlab[m] = acc[i][j][r];
+          }
+        }
+      s = group4_sum(s);
+      if (m < g.M && lq == 0) g.part[(long)m * g.part_ld + tn * 2 + wn] = make_float2(mx, s);
+    }
+    return;
+  }
+  if constexpr (EPI == EPI_SWIGLU) {
+    bf16_t *Hm = reinterpret_cast<bf16_t *>(g.C);
+    bf16_t *GU = reinterpret_cast<bf16_t *>(g.C2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wm * 64 + j * 16 + lr;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int i = 0; i < NI; i += 2) {
+        const int nb = n0 + wn * WN + i * 16;  // gate block start; up block is nb + 16
+        if (nb >= g.N) continue;
+        const int unit = (nb >> 1) + g4;
+        float hv[4], gv[4], uv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          gv[r] = acc[i][j][r];
+          uv[r] = acc[i + 1][j][r];
+          hv[r] = gv[r] / (1.f + __expf(-gv[r])) * uv[r];
+        }
+        store4<bf16_t>(Hm + (long)m * g.ldc + unit, hv);
+        if (GU) {
+          store4<bf16_t>(GU + (long)m * g.ldc2 + nb + g4, gv);
+          store4<bf16_t>(GU + (long)m * g.ldc2 + nb + 16 + g4, uv);
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wm * 64 + j * 16 + lr;
+    if (m >= g.M) continue;
+    int lab = -1;
+    float lse = 0.f;
+    if constexpr (EPI == EPI_DLOGITS) {
+      lab = g.rowi[*g.pos0 + m];
+      lse = g.rowf[m];
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int n = n0 + wn * WN + i * 16 + g4;
+      if (n >= g.N) continue;
+      float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      if constexpr (EPI == EPI_STORE) {
+        store4<bf16_t>(reinterpret_cast<bf16_t *>(g.C) + (long)m * g.ldc + n, v);
+      } else if constexpr (EPI == EPI_STORE_F32) {
+        store4<float>(g.Cf + (long)m * g.ldcf + n, v);
+      } else if constexpr (EPI == EPI_ADD_F32) {
+        float4 *p = reinterpret_cast<float4 *>(g.Cf + (long)m * g.ldcf + n);
+        float4 o = *p;
+        *p = make_float4(o.x + v[0], o.y + v[1], o.z + v[2], o.w + v[3]);
+      } else if constexpr (EPI == 100) {  // split-K partial
+        store4<float>(g.ws + ((long)blockIdx.z * g.M + m) * g.N + n, v);
+      } else if constexpr (EPI == EPI_DLOGITS) {
+        float d[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __expf(v[r] - lse);
+          d[r] = (p - ((n + r + g.col_off == lab) ? 1.f : 0.f)) * g.alpha;
+        }
+        store4<bf16_t>(reinterpret_cast<bf16_t *>(g.C) + (long)m * g.ldc + n, d);
+      } else if constexpr (EPI == EPI_SGD) {
+        float4 *pw = reinterpret_cast<float4 *>(g.Cf + (long)m * g.ldcf + n);
+        const float4 w = *pw;
+        float nw[4] = {w.x - g.alpha * v[0], w.y - g.alpha * v[1], w.z - g.alpha * v[2], w.w - g.alpha * v[3]};
+        *pw = make_float4(nw[0], nw[1], nw[2], nw[3]);
+        store4<bf16_t>(reinterpret_cast<bf16_t *>(g.C) + (long)m * g.ldc + n, nw);
+      }
+    }
+  }
+}
+
+// Direct-to-LDS streaming of one k-tile (both operands) by one wave.
+template <int BN> struct G3Issue {
+  static constexpr int CPW = G2<BN>::ROWS / 8 / 4;  // 1 KiB chunks per wave
+  __amdgpu_buffer_rsrc_t rw, rx;
+  uint32_t voff[CPW];
+  int wave, kbeg;
+  char *sm;
+  DEVI void init(const GemmArgs &g, int wave_, int lane, int n0, int m0, int kb, char *sm_) {
+    const uint32_t wbytes = (uint32_t)(((long)(g.N - 1) * g.ldb + g.K) * 2);
+    const uint32_t xbytes = (uint32_t)(((long)(g.M - 1) * g.lda + g.K) * 2);
+    rw = __builtin_amdgcn_make_buffer_rsrc((void *)g.B, (short)0, wbytes, RSRC_W3);
+    rx = __builtin_amdgcn_make_buffer_rsrc((void *)g.A, (short)0, xbytes, RSRC_W3);
+    wave = wave_;
+    kbeg = kb;
+    sm = sm_;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int j = wave * CPW + c;
+      const int row = j * 8 + (lane >> 3);
+      const int kc = (lane & 7) ^ swz(row);
+      if (row < BN) {
+        const int gr = n0 + row;
+        voff[c] = gr < g.N ? (uint32_t)(((long)gr * g.ldb + kc * 8) * 2) : OOB;
+      } else {
+        const int gr = m0 + row - BN;
+        voff[c] = gr < g.M ? (uint32_t)(((long)gr * g.lda + kc * 8) * 2) : OOB;
+      }
+    }
+  }
+  DEVI void run(int kt) const {
+    const int soff = (kbeg + kt * BK) * 2;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int j = wave * CPW + c;
+      lds_void *dst = (lds_void *)(sm + j * 1024);
+      if (j * 8 < BN)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, voff[c], soff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, dst, 16, voff[c], soff, 0, 0);
+    }
+  }
+};
+
+// One LDS stage filled by direct-to-LDS loads: every wave first
+// reads all fragments of the tile into registers, a barrier frees the stage,
+// the next tile is streamed into it while the MFMAs run on registers.
+// Latency is hidden by the other work-groups resident on the CU.
+template <int BN>
+__global__ __launch_bounds__(NT) void gemm3_kernel(const GemmArgs g, int epi) {
+  using C = G2<BN>;
+  constexpr int SBYTES = C::SBYTES, NI = C::NI, WN = C::WN;
+  constexpr int CPW = C::ROWS / 8 / 4;  // 1 KiB chunks per wave
+  __shared__ __align__(1024) char sm[SBYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int mt = (g.M + BM - 1) / BM, ntl = (g.N + BN - 1) / BN;
+  const int tile = remap_tile2(blockIdx.x, mt * ntl);
+  const int tm = tile % mt, tn = tile / mt;
+  const int m0 = tm * BM, n0 = tn * BN;
+  int kbeg = 0, kend = g.K;
+  if (g.ksplit > 1) {
+    const int per = ((g.K + g.ksplit - 1) / g.ksplit + BK - 1) / BK * BK;
+    kbeg = blockIdx.z * per;
+    kend = min(g.K, kbeg + per);
+  }
+  const int nk = (kend - kbeg + BK - 1) / BK;
+  G3Issue<BN> is;
+  is.init(g, wave, lane, n0, m0, kbeg, sm);
+  f32x4_v acc[NI][4];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  const int lr = lane & 15, lq = lane >> 4;
+  if (nk > 0) is.run(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vm<0>();
+    __syncthreads();
+    Frag<bf16_t> fw[2][NI], fx[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int kc = ks * 4 + lq;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row = wn * WN + i * 16 + lr;
+        fw[ks][i].v = *reinterpret_cast<const uint4 *>(sm + row * 128 + ((kc ^ swz(row)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = BN + wm * 64 + j * 16 + lr;
+        fx[ks][j].v = *reinterpret_cast<const uint4 *>(sm + row * 128 + ((kc ^ swz(row)) << 4));
+      }
+    }
+    __syncthreads();
+    if (kt + 1 < nk) is.run(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mma(acc[i][j], fw[ks][i], fx[ks][j]);
+  }
+  switch (epi) {
+    case EPI_STORE: gemm2_epilogue<BN, EPI_STORE>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+    case EPI_STORE_F32: gemm2_epilogue<BN, EPI_STORE_F32>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+    case EPI_ADD_F32: gemm2_epilogue<BN, EPI_ADD_F32>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+    case EPI_SWIGLU: gemm2_epilogue<BN, EPI_SWIGLU>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+    case EPI_CE: gemm2_epilogue<BN, EPI_CE>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+    case EPI_DLOGITS: gemm2_epilogue<BN, EPI_DLOGITS>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+    case EPI_SGD: gemm2_epilogue<BN, EPI_SGD>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+    default: gemm2_epilogue<BN, 100>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+  }
+}
+
+template <int BN> hipError_t launch3(int epi, const GemmArgs &g, hipStream_t st) {
+  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm3_kernel<BN>), dim3(tiles, 1, g.ksplit), dim3(NT), 0, st, g, g.ksplit > 1 ? 100 : epi);
+  return hipGetLastError();
+}
+
+}  // namespace ttt_g2
+using namespace ttt_g2;
+
+// Chooses the weight-tile height and the K split for a bf16 GEMM with both
+// operands k-contiguous and K a multiple of 64, then launches it.  `split` > 1
+// writes fp32 partials to g.ws for the caller's fixed-order reduction.
+// bf16, both operands k-contiguous with 16-byte aligned rows, K a multiple
+// of 64.  g.ksplit > 1 writes fp32 partials to g.ws (the caller reduces).
+hipError_t gemm_dma_launch(int epi, const GemmArgs &g, int bn, hipStream_t st) {
+  return bn == 256 ? launch3<256>(epi, g, st) : launch3<128>(epi, g, st);
+}

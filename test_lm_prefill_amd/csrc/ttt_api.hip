@@ -40,6 +40,11 @@ struct LayerBuf {
   bool fast = false, bwd_attn = false;
   int u = -1;
   void *K = nullptr, *Vt = nullptr, *Kt = nullptr, *V = nullptr;  // ring planes
+  // transposed working copies used by the backward GEMMs (k-contiguous operands)
+  void *wdT = nullptr;    // [2F][d]  (fast units first), updated layers
+  void *wguT = nullptr;   // [d][4F], updated layers
+  void *woT = nullptr;    // [d][d], layers whose attention is back-propagated
+  void *wqkvT = nullptr;  // [d][3d], same
 };
 
 struct Saved {
@@ -71,10 +76,14 @@ struct ttt_handle {
   void *a = nullptr, *qkv = nullptr, *qh = nullptr, *o = nullptr, *m = nullptr, *hmid = nullptr, *nf = nullptr;
   float2 *part = nullptr;
   void *dz = nullptr, *dy = nullptr, *dhmid = nullptr, *dgu = nullptr, *dO = nullptr, *dOt = nullptr, *dqkv = nullptr;
+  void *lm_headT = nullptr;                                  // [d][V]
+  void *dyT = nullptr, *hmidT = nullptr, *dguT = nullptr, *mT = nullptr;  // [rows][b], zero past the chunk
   float *dn = nullptr, *dh = nullptr, *dm = nullptr, *Dq = nullptr, *dq = nullptr, *dk = nullptr, *dv = nullptr,
         *da = nullptr;
   float *ws = nullptr;
   size_t ws_elems = 0;
+  int attn_split = 1;
+  float *attn_ws = nullptr;
   std::vector<Saved> saved;
   // graphs: [0] update, [1] no-update
   hipGraphExec_t gexec[2] = {nullptr, nullptr};
@@ -133,13 +142,13 @@ char *off(void *p, size_t bytes) { return reinterpret_cast<char *>(p) + bytes; }
 enum KClass {
   K_EMBED, K_RMSNORM, K_GEMM_QKV, K_ROPE, K_ATTN_FWD, K_GEMM_O, K_GEMM_GATE_UP, K_GEMM_DOWN, K_GEMM_HEAD_CE,
   K_CE_REDUCE, K_GEMM_DLOGITS, K_GEMM_DN, K_RMSNORM_BWD, K_GEMM_DHMID, K_GEMM_DW_SGD, K_SWIGLU_BWD, K_GEMM_DM,
-  K_GEMM_DO, K_ATTN_BWD_PRE, K_ATTN_BWD_DQ, K_ATTN_BWD_DKDV, K_ROPE_BWD, K_GEMM_DA, K_MISC, K_NCLASS
+  K_GEMM_DO, K_ATTN_BWD_PRE, K_ATTN_BWD_DQ, K_ATTN_BWD_DKDV, K_ROPE_BWD, K_GEMM_DA, K_TRANSPOSE, K_MISC, K_NCLASS
 };
 const char *const kclass_names[K_NCLASS] = {
     "embed", "rmsnorm", "gemm_qkv", "qknorm_rope_ring", "attn_fwd", "gemm_o_residual", "gemm_gate_up_swiglu",
     "gemm_down_residual", "gemm_lmhead_ce", "ce_reduce", "gemm_dlogits", "gemm_dn", "rmsnorm_bwd", "gemm_dhmid",
     "gemm_dw_sgd", "swiglu_bwd", "gemm_dm", "gemm_do", "attn_bwd_pre", "attn_bwd_dq", "attn_bwd_dkdv",
-    "qknorm_rope_bwd", "gemm_da", "misc"};
+    "qknorm_rope_bwd", "gemm_da", "transpose", "misc"};
 
 // Brackets one kernel group with events when kernel timing is on.
 struct Prof {
@@ -259,6 +268,8 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       aa.ldt = h->b;
       aa.pos0 = h->pos0;
       aa.scale = 1.f / sqrtf((float)h->hd);
+      aa.nsplit = h->attn_split;
+      aa.ws = h->attn_ws;
       {
         PROF(K_ATTN_FWD);
         HIPCHK(attn_fwd_launch(dt, h->hd, aa, st));
@@ -316,12 +327,12 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
   h->launches += 2;
 
   if (update && h->nu > 0) {
+    const int np = (n + 63) / 64 * 64;  // token count padded for the weight-gradient GEMMs
     // --- dlogits (softmax - onehot)/n, streamed over vocab slabs, and dn = dz W_lm
     for (int v0 = 0, s = 0; v0 < h->V; v0 += h->Vs, ++s) {
       const int vs = std::min(h->Vs, h->V - v0);
-      const void *wl = off(h->lm_head, (size_t)v0 * d * es);
       {
-        GemmArgs g = gargs(h->nf, d, wl, d, n, vs, d);
+        GemmArgs g = gargs(h->nf, d, off(h->lm_head, (size_t)v0 * d * es), d, n, vs, d);
         g.C = h->dz;
         g.ldc = h->Vs;
         g.rowf = h->lse;
@@ -332,10 +343,11 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         gemm(h, K_GEMM_DLOGITS, true, true, EPI_DLOGITS, g, st);
       }
       {
-        GemmArgs g = gargs(h->dz, h->Vs, wl, d, n, d, vs);
+        // B[n = model dim][k = vocab] from the transposed head [d][V]
+        GemmArgs g = gargs(h->dz, h->Vs, off(h->lm_headT, (size_t)v0 * es), h->V, n, d, vs);
         g.Cf = h->dn;
         g.ldcf = d;
-        gemm(h, K_GEMM_DN, true, false, s == 0 ? EPI_STORE_F32 : EPI_ADD_F32, g, st);
+        gemm(h, K_GEMM_DN, true, true, s == 0 ? EPI_STORE_F32 : EPI_ADD_F32, g, st);
       }
     }
     {
@@ -348,44 +360,62 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       Saved &S = h->saved[lw.u];
       const bool last = (l == L - h->nu);
       const int Fu = last ? F : 2 * F;  // hidden units whose gradient is needed
-      // dhmid = dy Wd_cat[:, :Fu]
+      // dhmid = dy Wd_cat[:, :Fu]  (B from the transposed [2F][d] copy)
       {
-        GemmArgs g = gargs(h->dy, d, lw.wd, 2 * F, n, Fu, d);
+        GemmArgs g = gargs(h->dy, d, lw.wdT, d, n, Fu, d);
         g.C = h->dhmid;
         g.ldc = 2 * F;
-        gemm(h, K_GEMM_DHMID, true, false, EPI_STORE, g, st);
+        gemm(h, K_GEMM_DHMID, true, true, EPI_STORE, g, st);
       }
-      // dWd_fast = dy^T hmid_fast, fused SGD into the fp32 master and the working copy
       {
-        GemmArgs g = gargs(h->dy, d, S.hmid, 2 * F, d, F, n);
+        PROF(K_TRANSPOSE);
+        HIPCHK(transpose_launch(dt, false, h->dy, d, h->dyT, h->b, n, np, d, st));
+        HIPCHK(transpose_launch(dt, false, S.hmid, 2 * F, h->hmidT, h->b, n, np, F, st));
+      }
+      // dWd_fast = dy^T hmid_fast over the chunk's tokens, SGD fused into the epilogue
+      {
+        GemmArgs g = gargs(h->dyT, h->b, h->hmidT, h->b, d, F, np);
         g.Cf = h->m_d[lw.u];
         g.ldcf = F;
         g.C = lw.wd;
         g.ldc = 2 * F;
         g.alpha = h->cfg.eta;
-        gemm(h, K_GEMM_DW_SGD, false, false, EPI_SGD, g, st);
+        gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st);
+      }
+      {
+        PROF(K_TRANSPOSE);
+        HIPCHK(transpose_launch(dt, true, h->m_d[lw.u], F, lw.wdT, d, d, d, F, st));
       }
       {
         PROF(K_SWIGLU_BWD);
         HIPCHK(swiglu_bwd_launch(dt, S.gu, h->dhmid, h->dgu, n, Fu, 4 * F, 2 * F, st));
       }
       if (!last) {
-        GemmArgs g = gargs(h->dgu, 4 * F, lw.wgu, d, n, d, 4 * F);
+        GemmArgs g = gargs(h->dgu, 4 * F, lw.wguT, 4 * F, n, d, 4 * F);
         g.Cf = h->dm;
         g.ldcf = d;
-        gemm(h, K_GEMM_DM, true, false, EPI_STORE_F32, g, st);
+        gemm(h, K_GEMM_DM, true, true, EPI_STORE_F32, g, st);
       }
-      // dW(gate|up)_fast = dGU_fast^T m, fused SGD
       {
-        GemmArgs g = gargs(h->dgu, 4 * F, S.m, d, 2 * F, d, n);
+        PROF(K_TRANSPOSE);
+        HIPCHK(transpose_launch(dt, false, h->dgu, 4 * F, h->dguT, h->b, n, np, 2 * F, st));
+        HIPCHK(transpose_launch(dt, false, S.m, d, h->mT, h->b, n, np, d, st));
+      }
+      // dW(gate|up)_fast = dGU_fast^T m, SGD fused
+      {
+        GemmArgs g = gargs(h->dguT, h->b, h->mT, h->b, 2 * F, d, np);
         g.Cf = h->m_gu[lw.u];
         g.ldcf = d;
         g.C = lw.wgu;
         g.ldc = d;
         g.alpha = h->cfg.eta;
-        gemm(h, K_GEMM_DW_SGD, false, false, EPI_SGD, g, st);
+        gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st);
       }
-      h->launches++;
+      {
+        PROF(K_TRANSPOSE);
+        HIPCHK(transpose_launch(dt, true, h->m_gu[lw.u], d, lw.wguT, 4 * F, 2 * F, 2 * F, d, st));
+      }
+      h->launches += 7;
       if (last) break;
       {
         PROF(K_RMSNORM_BWD);
@@ -393,10 +423,10 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       }
       // attention sub-block backward
       {
-        GemmArgs g = gargs(h->dy, d, lw.wo, d, n, d, d);
+        GemmArgs g = gargs(h->dy, d, lw.woT, d, n, d, d);
         g.C = h->dO;
         g.ldc = d;
-        gemm(h, K_GEMM_DO, true, false, EPI_STORE, g, st);
+        gemm(h, K_GEMM_DO, true, true, EPI_STORE, g, st);
       }
       {
         PROF(K_ATTN_BWD_PRE);
@@ -427,6 +457,8 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         aa.ldt = h->b;
         aa.pos0 = h->pos0;
         aa.scale = 1.f / sqrtf((float)h->hd);
+        aa.nsplit = h->attn_split;
+        aa.ws = h->attn_ws;
         {
           PROF(K_ATTN_BWD_DQ);
           HIPCHK(attn_bwd_dq_launch(dt, h->hd, aa, st));
@@ -460,10 +492,10 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         }
       }
       {
-        GemmArgs g = gargs(h->dqkv, 3 * d, lw.wqkv, d, n, d, 3 * d);
+        GemmArgs g = gargs(h->dqkv, 3 * d, lw.wqkvT, 3 * d, n, d, 3 * d);
         g.Cf = h->da;
         g.ldcf = d;
-        gemm(h, K_GEMM_DA, true, false, EPI_STORE_F32, g, st);
+        gemm(h, K_GEMM_DA, true, true, EPI_STORE_F32, g, st);
       }
       {
         PROF(K_RMSNORM_BWD);
@@ -489,6 +521,9 @@ void reset_fast(ttt_handle *h, hipStream_t st) {
     HIPCHK(hipMemcpyAsync(h->m_d[lw.u], h->i_d[lw.u], (size_t)d * F * 4, hipMemcpyDeviceToDevice, st));
     HIPCHK(convert_rows_launch(h->dt, h->i_gu[lw.u], d, lw.wgu, d, 2 * F, d, st));
     HIPCHK(convert_rows_launch(h->dt, h->i_d[lw.u], F, lw.wd, 2 * F, d, F, st));
+    // transposed working copies for the backward GEMMs: Wd_cat^T [2F][d], Wgu_cat^T [d][4F]
+    HIPCHK(transpose_launch(h->dt, false, lw.wd, 2 * F, lw.wdT, d, d, d, 2 * F, st));
+    HIPCHK(transpose_launch(h->dt, false, lw.wgu, d, lw.wguT, 4 * F, 4 * F, 4 * F, d, st));
   }
 }
 
@@ -637,6 +672,16 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
         pack_gu(w->fast_gate[u], w->fast_up[u], h->i_gu[u], F, d, 4, st);
         HIPCHK(hipMemcpyAsync(h->i_d[u], w->fast_down[u], f32fd, hipMemcpyDeviceToDevice, st));
       }
+      if (lw.fast && h->nu > 0) {
+        lw.wdT = dalloc(h, 2 * fd, false);
+        lw.wguT = dalloc(h, 4 * fd, false);
+      }
+      if (lw.bwd_attn) {
+        lw.woT = dalloc(h, dd, false);
+        lw.wqkvT = dalloc(h, 3 * dd, false);
+        HIPCHK(transpose_launch(h->dt, false, lw.wo, d, lw.woT, d, d, d, d, st));
+        HIPCHK(transpose_launch(h->dt, false, lw.wqkv, d, lw.wqkvT, 3 * d, 3 * d, 3 * d, d, st));
+      }
       lw.K = off(h->ring_base, roff);
       roff += plane;
       lw.Vt = off(h->ring_base, roff);
@@ -701,6 +746,16 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
         S.gu = dalloc(h, (size_t)b * 4 * F * es);
         S.hmid = dalloc(h, (size_t)b * 2 * F * es);
       }
+    }
+    h->attn_split = attn_pick_split(b, h->H, h->k, b);
+    h->attn_ws = (float *)dalloc(h, attn_ws_floats(h->attn_split, b, d, h->H, b) * 4);
+    if (h->nu > 0) {
+      h->lm_headT = dalloc(h, (size_t)V * d * es, false);
+      HIPCHK(transpose_launch(h->dt, false, h->lm_head, d, h->lm_headT, V, V, V, d, st));
+      h->dyT = dalloc(h, bd * es);
+      h->mT = dalloc(h, bd * es);
+      h->hmidT = dalloc(h, (size_t)b * F * es);
+      h->dguT = dalloc(h, (size_t)b * 2 * F * es);
     }
     h->ws_elems = gemm_ws_elems(b, d);
     h->ws = (float *)dalloc(h, h->ws_elems * 4);

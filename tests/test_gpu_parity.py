@@ -132,3 +132,17 @@ def test_empty_and_single_chunk():
     ol, of, wn = run_oracle(cfg, tok)
     dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, wn), "one chunk")
     assert dl <= 2e-2 and dwr <= 5e-2
+
+
+@pytest.mark.parametrize("hd", [64, 80])
+def test_long_window_split_attention(hd):
+    """A window of 1024 with 128-token chunks: the attention passes split the
+    key range over several work-groups and the ring wraps (T > k + b)."""
+    cfg = mid(hd, T=1700, k=1024, b=128, L=2)
+    say(f"case: long window hd={hd} T={cfg.seq_len} k={cfg.window} b={cfg.chunk}")
+    tok = rand_tokens(cfg.seq_len + 1, cfg.vocab, seed=100 + hd)
+    sess, _ = gpu_session(cfg)
+    gl, gf = run_gpu(sess, tok)
+    ol, of, w = run_oracle(cfg, tok)
+    dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, w), f"longwin{hd}")
+    assert dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
