@@ -37,4 +37,7 @@ int attn_pick_split(int n, int H, int window, int chunk);
 hipError_t attn_fwd_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st);
 hipError_t attn_bwd_dq_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st);
 hipError_t attn_bwd_dkdv_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st);
+// Combines the key-range splits (no-op when nsplit == 1): forward outputs and
+// log-sum-exp (dq = false) or the dQ partial sums (dq = true).
+hipError_t attn_merge_launch(int dtype, int hd, bool dq, const AttnArgs &a, hipStream_t st);
 bool attn_supported_hd(int hd);

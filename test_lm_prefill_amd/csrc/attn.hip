@@ -659,19 +659,11 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(const AttnArgs a) {
 template <typename T, int HD> hipError_t fwd_t(const AttnArgs &a, hipStream_t st) {
   dim3 grid((a.n + 127) / 128, a.H, a.nsplit);
   hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(NT), 0, st, a);
-  if (a.nsplit > 1) {
-    const long tot = (long)a.n * a.d / 4;
-    hipLaunchKernelGGL((attn_fwd_merge_kernel<T>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, a, HD);
-  }
   return hipGetLastError();
 }
 template <typename T, int HD> hipError_t dq_t(const AttnArgs &a, hipStream_t st) {
   dim3 grid((a.n + 127) / 128, a.H, a.nsplit);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, dim3(NT), 0, st, a);
-  if (a.nsplit > 1) {
-    const long tot = (long)a.n * a.d / 4;
-    hipLaunchKernelGGL(attn_dq_merge_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, a);
-  }
   return hipGetLastError();
 }
 template <typename T, int HD> hipError_t dkdv_t(const AttnArgs &a, hipStream_t st) {
@@ -740,6 +732,19 @@ hipError_t attn_bwd_dq_launch(int dtype, int hd, const AttnArgs &a, hipStream_t 
   if (a.n <= 0) return hipSuccess;
   return dq_hd(dtype == 1, hd, a, st);
 }
+hipError_t attn_merge_launch(int dtype, int hd, bool dq, const AttnArgs &a, hipStream_t st) {
+  if (a.n <= 0 || a.nsplit <= 1) return hipSuccess;
+  const long tot = (long)a.n * a.d / 4;
+  const dim3 grid((unsigned)((tot + 255) / 256));
+  if (dq)
+    hipLaunchKernelGGL(attn_dq_merge_kernel, grid, dim3(256), 0, st, a);
+  else if (dtype == 1)
+    hipLaunchKernelGGL((attn_fwd_merge_kernel<bf16_t>), grid, dim3(256), 0, st, a, hd);
+  else
+    hipLaunchKernelGGL((attn_fwd_merge_kernel<float>), grid, dim3(256), 0, st, a, hd);
+  return hipGetLastError();
+}
+
 hipError_t attn_bwd_dkdv_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st) {
   if (a.n <= 0) return hipSuccess;
   return dkdv_hd(dtype == 1, hd, a, st);

@@ -387,9 +387,12 @@ size_t gemm_ws_elems(int M, int N) { return (size_t)8 * M * N; }
 
 hipError_t gemm_dma_launch(int epi, const GemmArgs &g, int bn, hipStream_t st);
 
-hipError_t gemm_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, float *ws, size_t ws_elems,
-                       hipStream_t st, int force_split) {
-  const bool dma = dtype == 1 && a_kc && b_kc && g.K % 64 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0;
+static bool use_dma(int dtype, bool a_kc, bool b_kc, const GemmArgs &g) {
+  return dtype == 1 && a_kc && b_kc && g.K % 64 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0;
+}
+
+int gemm_plan(int dtype, bool a_kc, bool b_kc, int epi, const GemmArgs &g, size_t ws_elems, int force_split) {
+  const bool dma = use_dma(dtype, a_kc, b_kc, g);
   int split = 1;
   if (epi == EPI_STORE || epi == EPI_STORE_F32 || epi == EPI_ADD_F32) {
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
@@ -413,14 +416,28 @@ hipError_t gemm_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, flo
     }
     if (split > 1 && (size_t)split * g.M * g.N > ws_elems) split = 1;
   }
+  return split;
+}
+
+hipError_t gemm_main_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, float *ws, int split,
+                            hipStream_t st) {
   g.ksplit = split;
   g.ws = ws;
-  hipError_t e;
-  if (dma)
-    e = gemm_dma_launch(epi, g, 128, st);
-  else
-    e = dtype == 1 ? dispatch_layout<bf16_t>(a_kc, b_kc, epi, g, st, split)
-                   : dispatch_layout<float>(a_kc, b_kc, epi, g, st, split);
-  if (e != hipSuccess || split == 1) return e;
+  if (use_dma(dtype, a_kc, b_kc, g)) return gemm_dma_launch(epi, g, 128, st);
+  return dtype == 1 ? dispatch_layout<bf16_t>(a_kc, b_kc, epi, g, st, split)
+                    : dispatch_layout<float>(a_kc, b_kc, epi, g, st, split);
+}
+
+hipError_t gemm_reduce_launch(int dtype, int epi, GemmArgs g, float *ws, int split, hipStream_t st) {
+  if (split <= 1) return hipSuccess;
+  g.ws = ws;
   return dtype == 1 ? reduce_launch<bf16_t>(epi, g, split, st) : reduce_launch<float>(epi, g, split, st);
+}
+
+hipError_t gemm_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, float *ws, size_t ws_elems,
+                       hipStream_t st, int force_split) {
+  const int split = gemm_plan(dtype, a_kc, b_kc, epi, g, ws_elems, force_split);
+  hipError_t e = gemm_main_launch(dtype, a_kc, b_kc, epi, g, ws, split, st);
+  if (e != hipSuccess) return e;
+  return gemm_reduce_launch(dtype, epi, g, ws, split, st);
 }

@@ -142,13 +142,13 @@ char *off(void *p, size_t bytes) { return reinterpret_cast<char *>(p) + bytes; }
 enum KClass {
   K_EMBED, K_RMSNORM, K_GEMM_QKV, K_ROPE, K_ATTN_FWD, K_GEMM_O, K_GEMM_GATE_UP, K_GEMM_DOWN, K_GEMM_HEAD_CE,
   K_CE_REDUCE, K_GEMM_DLOGITS, K_GEMM_DN, K_RMSNORM_BWD, K_GEMM_DHMID, K_GEMM_DW_SGD, K_SWIGLU_BWD, K_GEMM_DM,
-  K_GEMM_DO, K_ATTN_BWD_PRE, K_ATTN_BWD_DQ, K_ATTN_BWD_DKDV, K_ROPE_BWD, K_GEMM_DA, K_TRANSPOSE, K_MISC, K_NCLASS
+  K_GEMM_DO, K_ATTN_BWD_PRE, K_ATTN_BWD_DQ, K_ATTN_BWD_DKDV, K_ROPE_BWD, K_GEMM_DA, K_TRANSPOSE, K_SPLITK_REDUCE, K_ATTN_MERGE, K_MISC, K_NCLASS
 };
 const char *const kclass_names[K_NCLASS] = {
     "embed", "rmsnorm", "gemm_qkv", "qknorm_rope_ring", "attn_fwd", "gemm_o_residual", "gemm_gate_up_swiglu",
     "gemm_down_residual", "gemm_lmhead_ce", "ce_reduce", "gemm_dlogits", "gemm_dn", "rmsnorm_bwd", "gemm_dhmid",
     "gemm_dw_sgd", "swiglu_bwd", "gemm_dm", "gemm_do", "attn_bwd_pre", "attn_bwd_dq", "attn_bwd_dkdv",
-    "qknorm_rope_bwd", "gemm_da", "transpose", "misc"};
+    "qknorm_rope_bwd", "gemm_da", "transpose", "splitk_reduce", "attn_merge", "misc"};
 
 // Brackets one kernel group with events when kernel timing is on.
 struct Prof {
@@ -189,9 +189,16 @@ void prof_collect(ttt_handle *h, hipStream_t st) {
 #define PROF(cls) Prof prof_(h, cls, st)
 
 void gemm(ttt_handle *h, int cls, bool akc, bool bkc, int epi, GemmArgs g, hipStream_t st) {
-  Prof prof_(h, cls, st);
-  HIPCHK(gemm_launch(h->dt, akc, bkc, epi, g, h->ws, h->ws_elems, st));
-  h->launches += 2;
+  const int split = gemm_plan(h->dt, akc, bkc, epi, g, h->ws_elems);
+  {
+    Prof prof_(h, cls, st);
+    HIPCHK(gemm_main_launch(h->dt, akc, bkc, epi, g, h->ws, split, st));
+  }
+  if (split > 1) {
+    Prof prof_(h, K_SPLITK_REDUCE, st);
+    HIPCHK(gemm_reduce_launch(h->dt, epi, g, h->ws, split, st));
+  }
+  h->launches += split > 1 ? 2 : 1;
 }
 
 // --------------------------------------------------------------------------- the chunk step
@@ -273,6 +280,10 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       {
         PROF(K_ATTN_FWD);
         HIPCHK(attn_fwd_launch(dt, h->hd, aa, st));
+      }
+      if (aa.nsplit > 1) {
+        PROF(K_ATTN_MERGE);
+        HIPCHK(attn_merge_launch(dt, h->hd, false, aa, st));
       }
     }
     {
@@ -462,6 +473,10 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         {
           PROF(K_ATTN_BWD_DQ);
           HIPCHK(attn_bwd_dq_launch(dt, h->hd, aa, st));
+        }
+        if (aa.nsplit > 1) {
+          PROF(K_ATTN_MERGE);
+          HIPCHK(attn_merge_launch(dt, h->hd, true, aa, st));
         }
         {
           PROF(K_ATTN_BWD_DKDV);
