@@ -14,6 +14,7 @@ stream) and the CPU oracle timed on a bounded sample on this host.
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -129,6 +130,62 @@ def gpu_bench(cfg, steps, warmup, profile=True):
     return ms_ttt, ms_swa, ktimes, mean_loss, tok_np
 
 
+def profile_pass(cfg):
+    """For hardware-counter runs: one kernel of known traffic, then one prefill.
+
+    The calibration is torch's elementwise negation of 2**28 fp32 values, which
+    reads 1 GiB and writes 1 GiB once each; a counter's reading for it gives the
+    scale from counter units to bytes.
+    """
+    import torch
+    from ttt_inputs import make_weights_torch, make_tokens
+    from test_lm_prefill_amd import Session
+    w = make_weights_torch(cfg, "cuda", seed=0)
+    tok = torch.from_numpy(make_tokens(cfg, seed=1)).cuda()
+    sess = Session(cfg, w, max_tokens=cfg.seq_len)
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    log("[bench] calibration kernel done")
+    sess.prefill(tok, want_fast=False, check=False)
+    torch.cuda.synchronize()
+    log("[bench] profile prefill done")
+    sess.close()
+    print(json.dumps({"profile_pass": cfg.name, "calibration_bytes_read": n * 4, "calibration_bytes_written": n * 4}),
+          flush=True)
+
+
+def source_digest(paths):
+    import hashlib
+    hsh = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            hsh.update(f.read())
+    return hsh.hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from the counter runs kept under profiles/, or None when
+    none is stored for this kernel and workload or its sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"^- (\w+): (\S+)", line.strip())
+            if m:
+                fields[m.group(1)] = m.group(2)
+    srcs = fields.get("sources", "").split(",")
+    if not srcs or fields.get("digest") != source_digest(srcs):
+        return None
+    return float(fields["bytes_per_launch"])
+
+
 def cpu_baseline(cfg, tok_np, n_tokens):
     """The oracle (numpy fp64) on the first n_tokens positions of the same workload,
     as one chunk of that size: forward, losses, backward and one update."""
@@ -166,6 +223,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="run a calibration kernel and one prefill only (for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: a TTT prefill sequence is a recurrence over chunks and "
@@ -173,6 +232,9 @@ def main():
         sys.exit(2)
     from ttt_inputs import get
     cfg = get(args.config)
+    if args.profile_pass:
+        profile_pass(cfg)
+        return
     T = cfg.seq_len
     ms_ttt, ms_swa, kt, mean_loss, tok_np = gpu_bench(cfg, args.steps, args.warmup,
                                                       profile=not args.no_kernel_timing)
@@ -200,8 +262,9 @@ def main():
         ms_d, n_d = kt[dom]
         per_launch = flops[dom] / n_d
         achieved = per_launch / 1e12 / (ms_d / n_d / 1e3)
+        traffic = stored_traffic(dom, cfg.name)
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
                 "flop_per_launch": per_launch, "avg_launch_ms": round(ms_d / n_d, 4)}
     cpu = None
     if not args.no_cpu_baseline:

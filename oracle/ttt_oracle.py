@@ -273,11 +273,12 @@ class Oracle:
         return grads
 
     # ---------------------------------------------------------------- Algorithm 1
-    def prefill(self, tokens, eta=None, no_update=False, W_init=None, return_trace=False):
+    def prefill(self, tokens, eta=None, no_update=False, W_init=None, return_trace=False, progress=None):
         """Run Algorithm 1 on ids x_0..x_T; returns (losses[T], W_N[, trace]).
 
         Position p (0 <= p < T) predicts x_{p+1}; chunk i holds positions
         [i*b, min((i+1)*b, T)).  With no_update the SGD step is skipped.
+        ``progress(s0, n)``, if given, is called after each chunk (reporting only).
         """
         c = self.cfg
         eta = c.eta if eta is None else eta
@@ -301,6 +302,8 @@ class Oracle:
                 G = self.chunk_grad(W, saved)
                 W = [[sgd_step(w, g, eta) for w, g in zip(ws, gs)] for ws, gs in zip(W, G)]
             cache = new_cache
+            if progress is not None:
+                progress(s0, n)
         if return_trace:
             return losses, W, trace
         return losses, W
