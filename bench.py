@@ -135,7 +135,9 @@ def profile_pass(cfg):
 
     The calibration is torch's elementwise negation of 2**28 fp32 values, which
     reads 1 GiB and writes 1 GiB once each; a counter's reading for it gives the
-    scale from counter units to bytes.
+    scale from counter units to bytes.  The prefill launches its kernels one by
+    one (no graph replay; the kernels are the same), because the profiler's
+    counter collection does not follow graph launches.
     """
     import torch
     from ttt_inputs import make_weights_torch, make_tokens
@@ -151,7 +153,8 @@ def profile_pass(cfg):
     torch.cuda.synchronize()
     del src, dst
     log("[bench] calibration kernel done")
-    sess.prefill(tok, want_fast=False, check=False)
+    from test_lm_prefill_amd.ttt import TTT_NO_GRAPH
+    sess.prefill(tok, flags=TTT_NO_GRAPH, want_fast=False, check=False)
     torch.cuda.synchronize()
     log("[bench] profile prefill done")
     sess.close()

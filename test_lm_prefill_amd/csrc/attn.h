@@ -23,6 +23,7 @@ struct AttnArgs {
   int n, d, H, R, window, ldl, ldt;
   const int *pos0;   // absolute position of the chunk's first query (device)
   float scale;       // 1/sqrt(hd)
+  float sbound;      // forward: bound of scale * q.k in log2 units (bf16 bounded kernel), 0 = none
   // key-range split (forward and dQ): nsplit work-groups share one query tile;
   // their partial results go to ws (fp32) and are merged in a fixed order.
   int nsplit;
@@ -31,8 +32,14 @@ struct AttnArgs {
 
 // Work-space floats the forward / dQ passes need for `nsplit` splits.
 size_t attn_ws_floats(int nsplit, int n, int d, int H, int ldl);
-// Split count that gives the GPU enough work-groups for this shape.
+// Split count that gives the GPU enough work-groups for this shape (dQ pass,
+// and the forward when it runs without a score bound).
 int attn_pick_split(int n, int H, int window, int chunk);
+// The forward's split count: the bounded kernel covers 256 queries per work-group.
+int attn_fwd_split(int dtype, float sbound, int hd, int n, int H, int window, int chunk);
+// Largest score bound (log2 units) the bounded forward accepts: 2^-2B must
+// stay a normal fp32 number with room for sums.
+constexpr float ATTN_MAX_SBOUND = 48.f;
 
 hipError_t attn_fwd_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st);
 hipError_t attn_bwd_dq_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st);

@@ -355,6 +355,270 @@ __global__ __launch_bounds__(256) void attn_dq_merge_kernel(const AttnArgs a) {
   reinterpret_cast<float4 *>(a.dq)[idx] = acc;
 }
 
+// ======================================================= forward, bf16, bounded
+// 64 queries per wave, 4 waves (256 queries) per work-group; grid
+// (ceil(n/256), H, nsplit).  Key tiles of 32 are streamed from the rings
+// straight into one LDS stage (buffer_load ... lds).  Each wave reads all
+// fragments of the tile into registers, a barrier frees the stage, the next
+// tile is streamed into it while the MFMAs and the softmax run on registers;
+// latency is covered by the second resident work-group of the CU.
+//
+// Softmax without a running maximum: with QK-norm every query and key has
+// Euclidean norm at most max|g| * sqrt(hd), so a scaled score never exceeds
+// B = max|g_q| max|g_k| sqrt(hd) (in log2 units: times log2 e), a per-layer
+// constant the host derives from the gains.  p = 2^(s - B) then lies in
+// (2^-2B, 1] and needs no rescaling of the output accumulators; the log2-sum-
+// exp is B + log2(sum p).  The host uses this kernel only when 2B stays far
+// inside the fp32 exponent range.
+//
+// LDS layouts (16-byte chunks):
+//   K tile  [32 keys][KCH = 4 * ceil(hd/32) chunks], chunk c of key row r at
+//           position c ^ X(r); chunks at or past hd/8 read as zero (the q.k
+//           reduction is padded to a multiple of 32).
+//   V^T tile [hd rows][4 chunks of 8 keys], chunk c of row r at c ^ ((r>>1)&3).
+// Score tiles take key rows in the order 8*(i/4) + 4*ks + i%4 (i = MFMA row,
+// ks = which of the two 16-row tiles), so each lane ends up with 8
+// consecutive keys of one query: exactly one 16-byte V^T fragment for the
+// P V product.  With these swizzles each 16-lane phase of a fragment read
+// touches every bank group twice (no conflicts).
+template <int HD> struct F2 {
+  static constexpr int NC = (HD + 31) / 32;   // 32-deep steps of q.k
+  static constexpr int KCH = 4 * NC;          // chunks per K row in LDS
+  static constexpr int RC = HD / 8;           // chunks holding data
+  static constexpr int NH = HD / 16;          // 16-row output tiles over hd
+  static constexpr int KB = 32 * KCH * 16;    // bytes of a K tile
+  static constexpr int VB = HD * 4 * 16;      // bytes of a V^T tile
+  static constexpr int KINS = KB / 1024;      // 1 KiB DMA instructions per K tile
+  static constexpr int INS = (KB + VB) / 1024;
+  static constexpr int IPW = (INS + 3) / 4;   // per wave
+};
+
+template <int KCH> DEVI int kswz(int row) {
+  int x = ((row >> 1) & 1) | (((row >> 3) & 1) << 1);
+  if (KCH % 8 == 0) x |= (row & 1) << 2;
+  return x;
+}
+
+template <int HD> struct F2Issue {
+  using C = F2<HD>;
+  __amdgpu_buffer_rsrc_t rk, rv;
+  uint32_t voff[C::IPW];
+  int j0;
+  DEVI void init(const bf16_t *Kp, const bf16_t *Vtp, int R, int wave, int lane) {
+    rk = __builtin_amdgcn_make_buffer_rsrc((void *)Kp, (short)0, (uint32_t)R * HD * 2, BUF_RSRC_W3);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void *)Vtp, (short)0, (uint32_t)R * HD * 2, BUF_RSRC_W3);
+    j0 = wave * C::IPW;
+#pragma unroll
+    for (int c = 0; c < C::IPW; ++c) {
+      const int j = min(j0 + c, C::INS - 1);  // the last wave repeats the last chunk (same bytes)
+      if (j < C::KINS) {
+        const int s = j * 64 + lane, row = s / C::KCH, ch = (s % C::KCH) ^ kswz<C::KCH>(row);
+        voff[c] = ch < C::RC ? (uint32_t)(row * HD * 2 + ch * 16) : BUF_OOB;
+      } else {
+        const int s = (j - C::KINS) * 64 + lane, row = s / 4, ch = (s % 4) ^ ((row >> 1) & 3);
+        voff[c] = (uint32_t)(row * R * 2 + ch * 16);
+      }
+    }
+  }
+  // Streams the tile whose first key sits in ring slot `slot0` into `stage`.
+  DEVI void run(char *stage, int slot0) const {
+#pragma unroll
+    for (int c = 0; c < C::IPW; ++c) {
+      const int j = min(j0 + c, C::INS - 1);
+      const bool isk = j < C::KINS;  // uniform across the wave
+      lds_void *dst = (lds_void *)(stage + j * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? rk : rv, dst, 16, voff[c], isk ? slot0 * HD * 2 : slot0 * 2, 0, 0);
+    }
+  }
+};
+
+template <int HD> struct F2State {
+  using C = F2<HD>;
+  Frag<bf16_t> qf[4][C::NC];
+  f32x4_v O[C::NH][4];
+  float lsum[4];
+  int kb[2], vb;  // per-lane byte offsets of the fragment reads (kb by parity of the 32-dim step)
+};
+
+// Tiles t0 .. t1-1 of 32 keys.  FULL tiles have every (query, key) pair of
+// the work-group inside the window; otherwise each wave skips the MFMAs of a
+// tile none of its queries sees and masks the rest.  Every wave takes part in
+// the streaming and the barriers of every tile.
+template <int HD, bool FULL>
+DEVI void fwd2_range(F2State<HD> &st, const F2Issue<HD> &is, char *stage, int t0, int t1, int ntile, int jt0,
+                     int pq, int lr, int lg, const AttnArgs &a) {
+  using C = F2<HD>;
+  const float sl2 = a.scale * LOG2E_F, B = a.sbound;
+  for (int t = t0; t < t1; ++t) {
+    const int jt = jt0 + 32 * t;
+    wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    Frag<bf16_t> kf[2][C::NC], vf[C::NH];
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        kf[ks][c].v = *reinterpret_cast<const uint4 *>(stage + st.kb[c & 1] + (4 * ks * C::KCH + 4 * c) * 16);
+#pragma unroll
+    for (int hs = 0; hs < C::NH; ++hs)
+      vf[hs].v = *reinterpret_cast<const uint4 *>(stage + C::KB + st.vb + hs * 16 * 64);
+    lds_barrier();
+    if (t + 1 < ntile) is.run(stage, (jt + 32) % a.R);
+    if (!FULL && !((jt <= pq + 63) && (jt + 31 > pq - a.window))) continue;
+    f32x4_v S[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int qs = 0; qs < 4; ++qs) S[ks][qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int qs = 0; qs < 4; ++qs) mma(S[ks][qs], kf[ks][c], st.qf[qs][c]);
+    Frag<bf16_t> pf[4];
+#pragma unroll
+    for (int qs = 0; qs < 4; ++qs) {
+      const int p = pq + qs * 16 + lr;
+      float x[8];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float e = fast_exp2(__builtin_fmaf(S[ks][qs][r], sl2, -B));
+          if (!FULL) {
+            const int j = jt + 8 * lg + 4 * ks + r;
+            e = (j > p || j <= p - a.window) ? 0.f : e;
+          }
+          x[4 * ks + r] = e;
+          st.lsum[qs] += e;
+        }
+      pack_frag(pf[qs], x);
+    }
+#pragma unroll
+    for (int hs = 0; hs < C::NH; ++hs)
+#pragma unroll
+      for (int qs = 0; qs < 4; ++qs) mma(st.O[hs][qs], vf[hs], pf[qs]);
+  }
+}
+
+template <int HD>
+__global__ __launch_bounds__(NT, 2) void attn_fwd2_kernel(const AttnArgs a) {
+  using C = F2<HD>;
+  __shared__ __align__(1024) char stage[C::KB + C::VB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4, g4 = lg * 4;
+  // Work-groups are dealt to the 8 XCDs round-robin by linear index; remap so
+  // that each XCD gets a contiguous range of (head, split, query block): the
+  // query blocks of one head and key range run side by side on one XCD and
+  // share its L2 for the key/value tiles.
+  int qb, h, sp;
+  {
+    const int gx = gridDim.x, total = gx * gridDim.y * gridDim.z;
+    const int i = blockIdx.x + gx * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int q8 = total / 8, rem = total % 8, x = i % 8;
+    const int m = x * q8 + min(x, rem) + i / 8;
+    qb = m % gx;
+    sp = (m / gx) % a.nsplit;
+    h = m / (gx * a.nsplit);
+  }
+  const int q_lo = qb * 256;
+  const int pos0 = *a.pos0;
+  const int qw = q_lo + wave * 64;
+  const bf16_t *Q = reinterpret_cast<const bf16_t *>(a.q);
+
+  F2State<HD> st;
+#pragma unroll
+  for (int qs = 0; qs < 4; ++qs)
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) {
+      const int q = qw + qs * 16 + lr, col = c * 32 + lg * 8;
+      if (q < a.n && col < HD)
+        load_frag(st.qf[qs][c], Q + (long)q * a.d + h * HD + col);
+      else
+        zero_frag(st.qf[qs][c]);
+    }
+#pragma unroll
+  for (int qs = 0; qs < 4; ++qs) {
+    st.lsum[qs] = 0.f;
+#pragma unroll
+    for (int hs = 0; hs < C::NH; ++hs) st.O[hs][qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  }
+  {
+    // K row of MFMA row lr in the first 16-key tile; chunk 4c + lg of it sits
+    // at 4c + (lg ^ x) + (x & 4) for even c and 4c + (lg ^ x) - (x & 4) for
+    // odd c (x & 4 is nonzero only when KCH is a multiple of 8); the key rows
+    // 4ks + r0 have the same x.
+    const int r0 = 8 * (lr >> 2) + (lr & 3), x0 = kswz<C::KCH>(r0);
+    const int base = r0 * C::KCH + (lg ^ (x0 & 3));
+    st.kb[0] = (base + (x0 & 4)) * 16;
+    st.kb[1] = (base - (x0 & 4)) * 16;
+    st.vb = (lr * 4 + (lg ^ ((lr >> 1) & 3))) * 16;
+  }
+  // the query fragments are complete before the tile loop, so its waits
+  // count only the tile stream
+  __builtin_amdgcn_s_waitcnt(0);
+
+  const int p_first = pos0 + q_lo;
+  const int p_last = pos0 + min(q_lo + 255, a.n - 1);
+  const int jtw = max(0, p_first - a.window + 1) & ~31;
+  const int ntw = (p_last - jtw) / 32 + 1;
+  const int t_lo = ntw * sp / a.nsplit, t_hi = ntw * (sp + 1) / a.nsplit;
+  const int jt0 = jtw + 32 * t_lo;
+  const int ntile = t_hi - t_lo;
+  const int pq = pos0 + qw;
+
+  F2Issue<HD> is;
+  is.init(reinterpret_cast<const bf16_t *>(a.K) + (long)h * a.R * HD,
+          reinterpret_cast<const bf16_t *>(a.Vt) + (long)h * HD * a.R, a.R, wave, lane);
+  // tiles [f0, f1) are full for all four waves: every key at or before the
+  // work-group's first query and inside its last query's window
+  int f0, f1;
+  {
+    const int lo = pos0 + q_lo + 255 - a.window + 1;  // smallest key of the last query's window
+    f0 = lo <= jt0 ? 0 : (lo - jt0 + 31) / 32;
+    f1 = p_first - 31 < jt0 ? 0 : (p_first - 31 - jt0) / 32 + 1;
+    f0 = min(f0, ntile);
+    f1 = min(max(f1, f0), ntile);
+  }
+  if (ntile > 0) is.run(stage, jt0 % a.R);
+  fwd2_range<HD, false>(st, is, stage, 0, f0, ntile, jt0, pq, lr, lg, a);
+  fwd2_range<HD, true>(st, is, stage, f0, f1, ntile, jt0, pq, lr, lg, a);
+  fwd2_range<HD, false>(st, is, stage, f1, ntile, ntile, jt0, pq, lr, lg, a);
+
+  bf16_t *Out = reinterpret_cast<bf16_t *>(a.o);
+#pragma unroll
+  for (int qs = 0; qs < 4; ++qs) {
+    const float lt = group4_sum(st.lsum[qs]);
+    const int q = qw + qs * 16 + lr;
+    if (q < a.n) {
+      // a split may see no key of this query: weight 0 in the merge
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float lse = lt > 0.f ? a.sbound + log2f(lt) : -INFINITY;
+      if (a.nsplit == 1) {
+#pragma unroll
+        for (int hs = 0; hs < C::NH; ++hs) {
+          float v[4] = {st.O[hs][qs][0] * inv, st.O[hs][qs][1] * inv, st.O[hs][qs][2] * inv,
+                        st.O[hs][qs][3] * inv};
+          store4<bf16_t>(Out + (long)q * a.d + h * HD + hs * 16 + g4, v);
+        }
+        if (lg == 0) a.lse2[(long)h * a.ldl + q] = lse;
+      } else {
+        float *po = a.ws + (long)sp * a.n * a.d;
+#pragma unroll
+        for (int hs = 0; hs < C::NH; ++hs) {
+          float v[4] = {st.O[hs][qs][0] * inv, st.O[hs][qs][1] * inv, st.O[hs][qs][2] * inv,
+                        st.O[hs][qs][3] * inv};
+          store4<float>(po + (long)q * a.d + h * HD + hs * 16 + g4, v);
+        }
+        if (lg == 0) a.ws[(long)a.nsplit * a.n * a.d + ((long)sp * a.H + h) * a.ldl + q] = lse;
+      }
+    }
+  }
+}
+
 // ======================================================================= dQ
 // grid (ceil(n/128), H); 4 waves x 32 queries; loops over the window's keys.
 template <typename T, int HD>
@@ -661,6 +925,11 @@ template <typename T, int HD> hipError_t fwd_t(const AttnArgs &a, hipStream_t st
   hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(NT), 0, st, a);
   return hipGetLastError();
 }
+template <int HD> hipError_t fwd2_t(const AttnArgs &a, hipStream_t st) {
+  dim3 grid((a.n + 255) / 256, a.H, a.nsplit);
+  hipLaunchKernelGGL((attn_fwd2_kernel<HD>), grid, dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
 template <typename T, int HD> hipError_t dq_t(const AttnArgs &a, hipStream_t st) {
   dim3 grid((a.n + 127) / 128, a.H, a.nsplit);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, dim3(NT), 0, st, a);
@@ -693,7 +962,23 @@ template <typename T, int HD> hipError_t dkdv_t(const AttnArgs &a, hipStream_t s
   }                                               \
   return hipErrorInvalidValue;
 
+// The bounded forward keeps 64 queries' outputs per wave in registers, which
+// fits head dims up to 96.
+bool bounded(int dtype, float sbound, int hd) {
+  return dtype == 1 && hd <= 96 && sbound > 0.f && sbound <= ATTN_MAX_SBOUND;
+}
+
 hipError_t fwd_hd(bool bf, int hd, const AttnArgs &a, hipStream_t st) {
+  if (bf && bounded(1, a.sbound, hd)) {
+    switch (hd) {
+      case 16: return fwd2_t<16>(a, st);
+      case 32: return fwd2_t<32>(a, st);
+      case 64: return fwd2_t<64>(a, st);
+      case 80: return fwd2_t<80>(a, st);
+      case 96: return fwd2_t<96>(a, st);
+    }
+    return hipErrorInvalidValue;
+  }
   if (bf) { HD_SWITCH(fwd_t, bf16_t) }
   HD_SWITCH_F32(fwd_t)
 }
@@ -719,6 +1004,15 @@ int attn_pick_split(int n, int H, int window, int chunk) {
   int s = (int)((512 + wg - 1) / wg);
   const int tiles = (window + chunk) / 64;
   s = std::min(s, std::max(1, tiles / 8));
+  return std::max(1, std::min(s, 8));
+}
+
+int attn_fwd_split(int dtype, float sbound, int hd, int n, int H, int window, int chunk) {
+  if (!bounded(dtype, sbound, hd)) return attn_pick_split(n, H, window, chunk);
+  const long wg = (long)((n + 255) / 256) * H;
+  int s = (int)((512 + wg - 1) / wg);
+  const int tiles = (window + chunk) / 32;
+  s = std::min(s, std::max(1, tiles / 16));
   return std::max(1, std::min(s, 8));
 }
 

@@ -66,13 +66,16 @@ DEVI void zero_frag(Frag<float> &f) {
   f.lo = make_float4(0, 0, 0, 0);
   f.hi = f.lo;
 }
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+DEVI uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{a, b}, bf16x2_v));
+}
 // Fragment from 8 floats (rounded to T).
 DEVI void pack_frag(Frag<bf16_t> &f, const float *x) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = (uint32_t)from_f<bf16_t>(x[2 * i]) | ((uint32_t)from_f<bf16_t>(x[2 * i + 1]) << 16);
-  f.v = make_uint4(w[0], w[1], w[2], w[3]);
+  f.v = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                   pack_bf16x2(x[6], x[7]));
 }
 DEVI void pack_frag(Frag<float> &f, const float *x) {
   f.lo = make_float4(x[0], x[1], x[2], x[3]);
@@ -85,9 +88,7 @@ template <> DEVI void store4<float>(float *p, const float *v) {
   *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 template <> DEVI void store4<bf16_t>(bf16_t *p, const float *v) {
-  uint32_t a = (uint32_t)from_f<bf16_t>(v[0]) | ((uint32_t)from_f<bf16_t>(v[1]) << 16);
-  uint32_t b = (uint32_t)from_f<bf16_t>(v[2]) | ((uint32_t)from_f<bf16_t>(v[3]) << 16);
-  *reinterpret_cast<uint2 *>(p) = make_uint2(a, b);
+  *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
 // 16-byte vector of T (8 bf16 or 4 fp32).
@@ -129,6 +130,24 @@ DEVI float group4_sum(float v) {
 // 2^x with one v_exp_f32 (results below the normal range flush to zero,
 // which softmax weights tolerate).
 DEVI float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N> DEVI void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// Wait for this wave's LDS operations, then join the work-group barrier
+// (unlike __syncthreads, no wait on outstanding global loads).
+DEVI void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+// Raw buffer descriptor word 3 for gfx9-family 32-bit data; offsets at or past
+// the extent read as zero (BUF_OOB is such an offset for any real extent).
+constexpr int BUF_RSRC_W3 = 0x00020000;
+constexpr uint32_t BUF_OOB = 0x7FFFFF00u;
 
 #define LOG2E_F 1.4426950408889634f
 #define LN2_F 0.6931471805599453f

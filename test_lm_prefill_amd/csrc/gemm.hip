@@ -385,7 +385,7 @@ hipError_t reduce_launch(int epi, const GemmArgs &g, int S, hipStream_t st) {
 
 size_t gemm_ws_elems(int M, int N) { return (size_t)8 * M * N; }
 
-hipError_t gemm_dma_launch(int epi, const GemmArgs &g, int bn, hipStream_t st);
+hipError_t gemm_dma_launch(int epi, const GemmArgs &g, hipStream_t st);
 
 static bool use_dma(int dtype, bool a_kc, bool b_kc, const GemmArgs &g) {
   return dtype == 1 && a_kc && b_kc && g.K % 64 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0;
@@ -423,7 +423,7 @@ hipError_t gemm_main_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g
                             hipStream_t st) {
   g.ksplit = split;
   g.ws = ws;
-  if (use_dma(dtype, a_kc, b_kc, g)) return gemm_dma_launch(epi, g, 128, st);
+  if (use_dma(dtype, a_kc, b_kc, g)) return gemm_dma_launch(epi, g, st);
   return dtype == 1 ? dispatch_layout<bf16_t>(a_kc, b_kc, epi, g, st, split)
                     : dispatch_layout<float>(a_kc, b_kc, epi, g, st, split);
 }

@@ -2,9 +2,9 @@
 // (used for every bf16 GEMM whose operands are both k-contiguous).
 //
 // C[m, n] = sum_k A[m, k] B[n, k], both operands stored with k contiguous
-// (activations A [M][lda], weights B [N][ldb]).  Work-group tile BN (weight
+// (activations A [M][lda], weights B [N][ldb]).  Work-group tile 128 (weight
 // rows) x 128 (tokens) x 64 (k), 256 threads = 4 waves in a 2 x 2 grid; each
-// wave owns (BN/2) x 64 outputs as 16x16 tiles of v_mfma_f32_16x16x32_bf16.
+// wave owns 64 x 64 outputs as 16x16 tiles of v_mfma_f32_16x16x32_bf16.
 //
 // Loads: buffer_load_dwordx4 ... lds writes each lane's 16 bytes directly to
 // LDS at (base + 16 * lane), so one instruction fills 1 KiB = 8 tile rows of
@@ -13,16 +13,17 @@
 // one 16-byte chunk) hit 64 distinct banks.  Per-lane byte offsets are loop
 // invariant; the k position enters through the scalar offset.  Rows outside
 // the matrix get an offset beyond the buffer's extent, which the hardware
-// returns as zeros.  STAGES tiles are in flight; each thread waits on its own
-// vector-memory counter for the oldest tile, then a barrier publishes it.
+// returns as zeros.  Two LDS stages: while one k-step is multiplied from
+// registers the next two are in flight; each thread waits on its own
+// vector-memory counter for the oldest, then a barrier publishes it.
 #include "common.h"
 #include "gemm.h"
 
 namespace ttt_g2 {
 
 constexpr int BM = 128, BK = 64, NT = 256;
-constexpr uint32_t OOB = 0x7FFFFF00u;
-constexpr int RSRC_W3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+constexpr uint32_t OOB = BUF_OOB;
+constexpr int RSRC_W3 = BUF_RSRC_W3;
 
 template <int BN> struct G2 {
   static constexpr int ROWS = BN + BM;        // tile rows per stage (weights then tokens)
@@ -34,13 +35,6 @@ template <int BN> struct G2 {
 
 DEVI int swz(int row) { return (row >> 1) & 7; }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N> DEVI void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 DEVI int remap_tile2(int i, int T) {
   int q = T / 8, rem = T % 8;
@@ -186,12 +180,12 @@ template <int BN> struct G3Issue {
       }
     }
   }
-  DEVI void run(int kt) const {
+  DEVI void run(int kt, int stage_off = 0) const {
     const int soff = (kbeg + kt * BK) * 2;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int j = wave * CPW + c;
-      lds_void *dst = (lds_void *)(sm + j * 1024);
+      lds_void *dst = (lds_void *)(sm + stage_off + j * 1024);
       if (j * 8 < BN)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, voff[c], soff, 0, 0);
       else
@@ -200,24 +194,75 @@ template <int BN> struct G3Issue {
   }
 };
 
-// One LDS stage filled by direct-to-LDS loads: every wave first
-// reads all fragments of the tile into registers, a barrier frees the stage,
-// the next tile is streamed into it while the MFMAs run on registers.
-// Latency is hidden by the other work-groups resident on the CU.
-template <int BN>
-__global__ __launch_bounds__(NT) void gemm3_kernel(const GemmArgs g, int epi) {
-  using C = G2<BN>;
-  constexpr int SBYTES = C::SBYTES, NI = C::NI, WN = C::WN;
-  constexpr int CPW = C::ROWS / 8 / 4;  // 1 KiB chunks per wave
-  __shared__ __align__(1024) char sm[SBYTES];
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+
+// All sixteen fragments of one 64-deep k-step of a 128 x 128 tile (4 weight
+// and 4 token 16-row fragments for each 32-deep half), read in one block that
+// ends by waiting for its own reads.  Written as one asm block on purpose: the
+// compiler then does not treat the reads as possibly aliasing the
+// direct-to-LDS writes still in flight into the other stage (it would wait for
+// those before every read).  Visibility of the stage is ordered by the
+// caller's explicit vector-memory wait and barrier.
+DEVI void read_step_128(Frag<bf16_t> (&fw)[2][4], Frag<bf16_t> (&fx)[2][4], uint32_t w0, uint32_t w1, uint32_t x0,
+                        uint32_t x1) {
+  v4i_t a0, a1, a2, a3, b0, b1, b2, b3, c0, c1, c2, c3, d0, d1, d2, d3;
+  asm volatile(
+      "ds_read_b128 %0, %16\n"
+      "ds_read_b128 %1, %16 offset:2048\n"
+      "ds_read_b128 %2, %16 offset:4096\n"
+      "ds_read_b128 %3, %16 offset:6144\n"
+      "ds_read_b128 %4, %17\n"
+      "ds_read_b128 %5, %17 offset:2048\n"
+      "ds_read_b128 %6, %17 offset:4096\n"
+      "ds_read_b128 %7, %17 offset:6144\n"
+      "ds_read_b128 %8, %18\n"
+      "ds_read_b128 %9, %18 offset:2048\n"
+      "ds_read_b128 %10, %18 offset:4096\n"
+      "ds_read_b128 %11, %18 offset:6144\n"
+      "ds_read_b128 %12, %19\n"
+      "ds_read_b128 %13, %19 offset:2048\n"
+      "ds_read_b128 %14, %19 offset:4096\n"
+      "ds_read_b128 %15, %19 offset:6144\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(c0),
+        "=&v"(c1), "=&v"(c2), "=&v"(c3), "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3)
+      : "v"(w0), "v"(w1), "v"(x0), "v"(x1)
+      : "memory");
+  fw[0][0].v = __builtin_bit_cast(uint4, a0);
+  fw[0][1].v = __builtin_bit_cast(uint4, a1);
+  fw[0][2].v = __builtin_bit_cast(uint4, a2);
+  fw[0][3].v = __builtin_bit_cast(uint4, a3);
+  fw[1][0].v = __builtin_bit_cast(uint4, b0);
+  fw[1][1].v = __builtin_bit_cast(uint4, b1);
+  fw[1][2].v = __builtin_bit_cast(uint4, b2);
+  fw[1][3].v = __builtin_bit_cast(uint4, b3);
+  fx[0][0].v = __builtin_bit_cast(uint4, c0);
+  fx[0][1].v = __builtin_bit_cast(uint4, c1);
+  fx[0][2].v = __builtin_bit_cast(uint4, c2);
+  fx[0][3].v = __builtin_bit_cast(uint4, c3);
+  fx[1][0].v = __builtin_bit_cast(uint4, d0);
+  fx[1][1].v = __builtin_bit_cast(uint4, d1);
+  fx[1][2].v = __builtin_bit_cast(uint4, d2);
+  fx[1][3].v = __builtin_bit_cast(uint4, d3);
+}
+
+// Two LDS stages, 128 x 128 tile: while step kt is multiplied from registers,
+// the tiles of steps kt+1 and kt+2 are in flight.  Per step: wait for this
+// wave's loads of step kt, barrier, read the step's fragments, barrier (the
+// stage is free), stream step kt+2 into it, MFMAs.
+__global__ __launch_bounds__(NT, 2) void gemm5_kernel(const GemmArgs g, int epi) {
+  using C = G2<128>;
+  constexpr int SBYTES = C::SBYTES;
+  constexpr int CPW = C::ROWS / 8 / 4;  // 1 KiB chunks per wave and stage
+  __shared__ __align__(1024) char sm[2 * SBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  const int mt = (g.M + BM - 1) / BM, ntl = (g.N + BN - 1) / BN;
+  const int mt = (g.M + BM - 1) / BM, ntl = (g.N + 127) / 128;
   const int tile = remap_tile2(blockIdx.x, mt * ntl);
   const int tm = tile % mt, tn = tile / mt;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = tn * 128;
   int kbeg = 0, kend = g.K;
   if (g.ksplit > 1) {
     const int per = ((g.K + g.ksplit - 1) / g.ksplit + BK - 1) / BK * BK;
@@ -225,68 +270,62 @@ __global__ __launch_bounds__(NT) void gemm3_kernel(const GemmArgs g, int epi) {
     kend = min(g.K, kbeg + per);
   }
   const int nk = (kend - kbeg + BK - 1) / BK;
-  G3Issue<BN> is;
+  G3Issue<128> is;
   is.init(g, wave, lane, n0, m0, kbeg, sm);
-  f32x4_v acc[NI][4];
+  f32x4_v acc[4][4];
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   const int lr = lane & 15, lq = lane >> 4;
-  if (nk > 0) is.run(0);
+  // fragment byte offsets within a stage (rows differ by multiples of 16, which
+  // keep the swizzle of the lane's first row)
+  const int rw = wn * 64 + lr, rx = 128 + wm * 64 + lr;
+  const uint32_t aw0 = rw * 128 + (((0 + lq) ^ swz(rw)) << 4), aw1 = rw * 128 + (((4 + lq) ^ swz(rw)) << 4);
+  const uint32_t ax0 = rx * 128 + (((0 + lq) ^ swz(rx)) << 4), ax1 = rx * 128 + (((4 + lq) ^ swz(rx)) << 4);
+  const uint32_t smb = (uint32_t)(uintptr_t)(lds_void *)sm;
+  if (nk > 0) is.run(0, 0);
+  if (nk > 1) is.run(1, SBYTES);
   for (int kt = 0; kt < nk; ++kt) {
-    wait_vm<0>();
-    __syncthreads();
-    Frag<bf16_t> fw[2][NI], fx[2][4];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int kc = ks * 4 + lq;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int row = wn * WN + i * 16 + lr;
-        fw[ks][i].v = *reinterpret_cast<const uint4 *>(sm + row * 128 + ((kc ^ swz(row)) << 4));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = BN + wm * 64 + j * 16 + lr;
-        fx[ks][j].v = *reinterpret_cast<const uint4 *>(sm + row * 128 + ((kc ^ swz(row)) << 4));
-      }
-    }
-    __syncthreads();
-    if (kt + 1 < nk) is.run(kt + 1);
+    if (kt + 1 < nk)
+      wait_vm<CPW>();
+    else
+      wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    const uint32_t so = smb + (kt & 1) * SBYTES;
+    Frag<bf16_t> fw[2][4], fx[2][4];
+    read_step_128(fw, fx, so + aw0, so + aw1, so + ax0, so + ax1);
+    __builtin_amdgcn_s_barrier();
+    if (kt + 2 < nk) is.run(kt + 2, (kt & 1) * SBYTES);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) mma(acc[i][j], fw[ks][i], fx[ks][j]);
   }
   switch (epi) {
-    case EPI_STORE: gemm2_epilogue<BN, EPI_STORE>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
-    case EPI_STORE_F32: gemm2_epilogue<BN, EPI_STORE_F32>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
-    case EPI_ADD_F32: gemm2_epilogue<BN, EPI_ADD_F32>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
-    case EPI_SWIGLU: gemm2_epilogue<BN, EPI_SWIGLU>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
-    case EPI_CE: gemm2_epilogue<BN, EPI_CE>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
-    case EPI_DLOGITS: gemm2_epilogue<BN, EPI_DLOGITS>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
-    case EPI_SGD: gemm2_epilogue<BN, EPI_SGD>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
-    default: gemm2_epilogue<BN, 100>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+    case EPI_STORE: gemm2_epilogue<128, EPI_STORE>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+    case EPI_STORE_F32: gemm2_epilogue<128, EPI_STORE_F32>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+    case EPI_ADD_F32: gemm2_epilogue<128, EPI_ADD_F32>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+    case EPI_SWIGLU: gemm2_epilogue<128, EPI_SWIGLU>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+    case EPI_CE: gemm2_epilogue<128, EPI_CE>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+    case EPI_DLOGITS: gemm2_epilogue<128, EPI_DLOGITS>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+    case EPI_SGD: gemm2_epilogue<128, EPI_SGD>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
+    default: gemm2_epilogue<128, 100>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
   }
 }
 
-template <int BN> hipError_t launch3(int epi, const GemmArgs &g, hipStream_t st) {
-  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm3_kernel<BN>), dim3(tiles, 1, g.ksplit), dim3(NT), 0, st, g, g.ksplit > 1 ? 100 : epi);
+hipError_t launch5(int epi, const GemmArgs &g, hipStream_t st) {
+  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + 127) / 128);
+  hipLaunchKernelGGL(gemm5_kernel, dim3(tiles, 1, g.ksplit), dim3(NT), 0, st, g, g.ksplit > 1 ? 100 : epi);
   return hipGetLastError();
 }
 
 }  // namespace ttt_g2
 using namespace ttt_g2;
 
-// Chooses the weight-tile height and the K split for a bf16 GEMM with both
-// operands k-contiguous and K a multiple of 64, then launches it.  `split` > 1
-// writes fp32 partials to g.ws for the caller's fixed-order reduction.
-// bf16, both operands k-contiguous with 16-byte aligned rows, K a multiple
-// of 64.  g.ksplit > 1 writes fp32 partials to g.ws (the caller reduces).
-hipError_t gemm_dma_launch(int epi, const GemmArgs &g, int bn, hipStream_t st) {
-  return bn == 256 ? launch3<256>(epi, g, st) : launch3<128>(epi, g, st);
-}
+// bf16, both operands k-contiguous with 16-byte aligned rows, K a multiple of
+// 64.  g.ksplit > 1 writes fp32 partials to g.ws (the caller reduces them in a
+// fixed order).
+hipError_t gemm_dma_launch(int epi, const GemmArgs &g, hipStream_t st) { return launch5(epi, g, st); }

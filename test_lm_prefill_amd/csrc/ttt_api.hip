@@ -39,6 +39,8 @@ struct LayerBuf {
   void *wd = nullptr;   // [d][F] frozen, [d][2F] updated (fast columns first)
   bool fast = false, bwd_attn = false;
   int u = -1;
+  float sbound = 0.f;  // bound of the scaled scores (log2 units) for the bounded forward, 0 = none
+  int fsplit = 1;      // key-range split of the forward
   void *K = nullptr, *Vt = nullptr, *Kt = nullptr, *V = nullptr;  // ring planes
   // transposed working copies used by the backward GEMMs (k-contiguous operands)
   void *wdT = nullptr;    // [2F][d]  (fast units first), updated layers
@@ -275,7 +277,8 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       aa.ldt = h->b;
       aa.pos0 = h->pos0;
       aa.scale = 1.f / sqrtf((float)h->hd);
-      aa.nsplit = h->attn_split;
+      aa.nsplit = lw.fsplit;
+      aa.sbound = lw.sbound;
       aa.ws = h->attn_ws;
       {
         PROF(K_ATTN_FWD);
@@ -570,6 +573,31 @@ void pack_gu(const void *gate, const void *up, void *dst, int F, int d, size_t e
   HIPCHK(hipMemcpy2DAsync(off(dst, blk), 2 * blk, up, blk, blk, F / 16, hipMemcpyDeviceToDevice, st));
 }
 
+// Bound of scale * q.k in log2 units for one layer: with QK-norm every row has
+// Euclidean norm at most max|gain| * sqrt(hd), so |q.k| / sqrt(hd) is at most
+// max|g_q| * max|g_k| * sqrt(hd).  Returns 0 (no bound) for fp32 or when the
+// bound is too large for the bounded forward.
+float score_bound(ttt_handle *h, const void *gq, const void *gk, hipStream_t st) {
+  if (h->dt != 1) return 0.f;
+  std::vector<uint16_t> q(h->hd), k(h->hd);
+  HIPCHK(hipMemcpyAsync(q.data(), gq, h->hd * 2, hipMemcpyDeviceToHost, st));
+  HIPCHK(hipMemcpyAsync(k.data(), gk, h->hd * 2, hipMemcpyDeviceToHost, st));
+  HIPCHK(hipStreamSynchronize(st));
+  auto mx = [](const std::vector<uint16_t> &v) {
+    float m = 0.f;
+    for (uint16_t x : v) {
+      uint32_t u = (uint32_t)x << 16;
+      float f;
+      std::memcpy(&f, &u, 4);
+      m = std::max(m, std::fabs(f));
+    }
+    return m;
+  };
+  // 1% headroom for the bf16 rounding of the normalised rows
+  const double b = 1.01 * mx(q) * mx(k) * std::sqrt((double)h->hd) * 1.4426950408889634;
+  return (b > 0.0 && b <= ATTN_MAX_SBOUND) ? (float)b : 0.f;
+}
+
 }  // namespace
 
 // =========================================================================== C ABI
@@ -659,6 +687,8 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
       HIPCHK(hipMemcpyAsync(lw.mlp_norm, w->mlp_norm[l], d * es, hipMemcpyDeviceToDevice, st));
       HIPCHK(hipMemcpyAsync(lw.q_norm, w->q_norm[l], h->hd * es, hipMemcpyDeviceToDevice, st));
       HIPCHK(hipMemcpyAsync(lw.k_norm, w->k_norm[l], h->hd * es, hipMemcpyDeviceToDevice, st));
+      lw.sbound = score_bound(h, w->q_norm[l], w->k_norm[l], st);
+      lw.fsplit = attn_fwd_split(h->dt, lw.sbound, h->hd, b, h->H, h->k, b);
       const size_t dd = (size_t)d * d * es;
       lw.wqkv = dalloc(h, 3 * dd, false);
       HIPCHK(hipMemcpyAsync(lw.wqkv, w->wq[l], dd, hipMemcpyDeviceToDevice, st));
@@ -763,7 +793,11 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
       }
     }
     h->attn_split = attn_pick_split(b, h->H, h->k, b);
-    h->attn_ws = (float *)dalloc(h, attn_ws_floats(h->attn_split, b, d, h->H, b) * 4);
+    {
+      int smax = h->attn_split;
+      for (const LayerBuf &lw : h->layers) smax = std::max(smax, lw.fsplit);
+      h->attn_ws = (float *)dalloc(h, attn_ws_floats(smax, b, d, h->H, b) * 4);
+    }
     if (h->nu > 0) {
       h->lm_headT = dalloc(h, (size_t)V * d * es, false);
       HIPCHK(transpose_launch(h->dt, false, h->lm_head, d, h->lm_headT, V, V, V, d, st));

@@ -57,7 +57,7 @@ def test_tiny_fp32_full_sequence():
     assert dwr <= 1e-3
 
 
-@pytest.mark.parametrize("hd", [64, 80, 96])
+@pytest.mark.parametrize("hd", [64, 80, 96, 128])
 def test_mid_bf16_ragged(hd):
     cfg = mid(hd)
     say(f"case: mid hd={hd} bf16 T={cfg.seq_len} b={cfg.chunk} k={cfg.window}")
@@ -145,4 +145,42 @@ def test_long_window_split_attention(hd):
     gl, gf = run_gpu(sess, tok)
     ol, of, w = run_oracle(cfg, tok)
     dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, w), f"longwin{hd}")
+    assert dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
+
+
+def _with_gains(cfg, gq, gk):
+    """Weights of cfg with QK-norm gains replaced (bf16-exact values)."""
+    from ttt_inputs import make_weights_np, make_weights_torch
+    from ttt_inputs.weights import round_bf16_np
+    wt = make_weights_torch(cfg, "cuda")
+    wn = make_weights_np(cfg)
+    for l in range(cfg.n_layers):
+        for nm, g in ((f"l{l}.q_norm", gq(l)), (f"l{l}.k_norm", gk(l))):
+            g = round_bf16_np(np.asarray(g, dtype=np.float32))
+            wn[nm] = g
+            wt[nm] = torch.from_numpy(g).to(device="cuda", dtype=wt[nm].dtype)
+    return wt, wn
+
+
+@pytest.mark.parametrize("case", ["varied", "large"])
+def test_qk_gains_score_bound(case):
+    """The forward uses a fixed softmax offset derived from the QK-norm gains
+    when that bound is small ("varied": gains in [0.5, 1.5]) and the running
+    maximum otherwise ("large": one q gain of 8 puts the bound past its limit
+    while the scores stay moderate, so bf16 keeps the usual tolerance)."""
+    cfg = mid(64, T=700, k=256, b=128)
+    rng = np.random.Generator(np.random.PCG64(11))
+    if case == "varied":
+        gq = lambda l: rng.uniform(0.5, 1.5, cfg.head_dim)
+        gk = lambda l: rng.uniform(0.5, 1.5, cfg.head_dim)
+    else:
+        gq = lambda l: np.concatenate([[8.0], np.ones(cfg.head_dim - 1)])
+        gk = lambda l: np.ones(cfg.head_dim)
+    wt, wn = _with_gains(cfg, gq, gk)
+    say(f"case: qk gains {case} T={cfg.seq_len}")
+    tok = rand_tokens(cfg.seq_len + 1, cfg.vocab, seed=77)
+    sess, _ = gpu_session(cfg, weights=wt)
+    gl, gf = run_gpu(sess, tok)
+    ol, of, _ = run_oracle(cfg, tok, weights_np=wn)
+    dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, wn), f"gains-{case}")
     assert dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
