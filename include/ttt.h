@@ -62,6 +62,8 @@ enum {
  *   d_model, d_ff, vocab multiples of 16; head_dim in {16, 32, 64, 80, 96, 128};
  *   chunk and window multiples of 64 with window >= chunk (the notes, section 5:
  *   the window covers at least one chunk); max_tokens >= 1.
+ * Shapes outside the compiled kernels give TTT_EUNSUPPORTED: head_dim not in the
+ * set above, head_dim > 64 with fp32, d_model > 8192.
  */
 typedef struct {
   int32_t n_layers;     /* L */

@@ -619,6 +619,232 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd2_kernel(const AttnArgs a) {
   }
 }
 
+// ======================================================= dQ, bf16, 32-key tiles
+// 32 queries per wave, 4 waves (128 queries) per work-group; grid
+// (ceil(n/128), H, nsplit), remapped so that each XCD gets whole heads.  Key
+// tiles of 32 stream from the rings straight into one LDS stage: K and V
+// [32 keys][KCH chunks] (rows in the same swizzled layout as the forward's K
+// tile) and K^T [hd rows][4 chunks].  Every wave reads all fragments of the
+// tile into registers, a barrier frees the stage, the next tile streams in
+// while the MFMAs run:
+//   S^T = K Q^T, dP^T = V dO^T (lane: 8 consecutive keys of one query),
+//   p = 2^(s * scale * log2 e - lse2), dS = p (dP - D),
+//   dQ^T += K^T dS^T.
+template <int HD> struct Q2 {
+  static constexpr int NC = (HD + 31) / 32;
+  static constexpr int KCH = 4 * NC;
+  static constexpr int RC = HD / 8;
+  static constexpr int NH = HD / 16;
+  static constexpr int KB = 32 * KCH * 16;  // bytes of a K (or V) tile
+  static constexpr int TB = HD * 4 * 16;    // bytes of a K^T tile
+  static constexpr int KINS = KB / 1024;
+  static constexpr int INS = (2 * KB + TB) / 1024;
+  static constexpr int IPW = (INS + 3) / 4;
+};
+
+template <int HD> struct Q2Issue {
+  using C = Q2<HD>;
+  __amdgpu_buffer_rsrc_t rk, rv, rt;
+  uint32_t voff[C::IPW];
+  int j0;
+  DEVI void init(const bf16_t *Kp, const bf16_t *Vp, const bf16_t *Ktp, int R, int wave, int lane) {
+    const uint32_t bytes = (uint32_t)R * HD * 2;
+    rk = __builtin_amdgcn_make_buffer_rsrc((void *)Kp, (short)0, bytes, BUF_RSRC_W3);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void *)Vp, (short)0, bytes, BUF_RSRC_W3);
+    rt = __builtin_amdgcn_make_buffer_rsrc((void *)Ktp, (short)0, bytes, BUF_RSRC_W3);
+    j0 = wave * C::IPW;
+#pragma unroll
+    for (int c = 0; c < C::IPW; ++c) {
+      const int j = min(j0 + c, C::INS - 1);  // the last wave repeats the last chunk (same bytes)
+      if (j < 2 * C::KINS) {
+        const int s = (j % C::KINS) * 64 + lane, row = s / C::KCH, ch = (s % C::KCH) ^ kswz<C::KCH>(row);
+        voff[c] = ch < C::RC ? (uint32_t)(row * HD * 2 + ch * 16) : BUF_OOB;
+      } else {
+        const int s = (j - 2 * C::KINS) * 64 + lane, row = s / 4, ch = (s % 4) ^ ((row >> 1) & 3);
+        voff[c] = (uint32_t)(row * R * 2 + ch * 16);
+      }
+    }
+  }
+  DEVI void run(char *stage, int slot0) const {
+#pragma unroll
+    for (int c = 0; c < C::IPW; ++c) {
+      const int j = min(j0 + c, C::INS - 1);
+      const int part = j < C::KINS ? 0 : (j < 2 * C::KINS ? 1 : 2);  // uniform across the wave
+      lds_void *dst = (lds_void *)(stage + j * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(part == 0 ? rk : (part == 1 ? rv : rt), dst, 16, voff[c],
+                                               part == 2 ? slot0 * 2 : slot0 * HD * 2, 0, 0);
+    }
+  }
+};
+
+template <int HD> struct Q2State {
+  using C = Q2<HD>;
+  Frag<bf16_t> qf[2][C::NC], df[2][C::NC];
+  f32x4_v dQ[C::NH][2];
+  float Lq[2], Dv[2];
+  int kb[2], vb;
+};
+
+template <int HD, bool FULL>
+DEVI void dq2_range(Q2State<HD> &st, const Q2Issue<HD> &is, char *stage, int t0, int t1, int ntile, int jt0,
+                    int pq, int lr, int lg, const AttnArgs &a) {
+  using C = Q2<HD>;
+  const float sl2 = a.scale * LOG2E_F;
+  for (int t = t0; t < t1; ++t) {
+    const int jt = jt0 + 32 * t;
+    wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    Frag<bf16_t> kf[2][C::NC], vf[2][C::NC], tf[C::NH];
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int o = st.kb[c & 1] + (4 * ks * C::KCH + 4 * c) * 16;
+        kf[ks][c].v = *reinterpret_cast<const uint4 *>(stage + o);
+        vf[ks][c].v = *reinterpret_cast<const uint4 *>(stage + C::KB + o);
+      }
+#pragma unroll
+    for (int hs = 0; hs < C::NH; ++hs)
+      tf[hs].v = *reinterpret_cast<const uint4 *>(stage + 2 * C::KB + st.vb + hs * 16 * 64);
+    lds_barrier();
+    if (t + 1 < ntile) is.run(stage, (jt + 32) % a.R);
+    if (!FULL && !((jt <= pq + 31) && (jt + 31 > pq - a.window))) continue;
+    f32x4_v S[2][2], P[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        S[ks][qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+        P[ks][qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          mma(S[ks][qs], kf[ks][c], st.qf[qs][c]);
+          mma(P[ks][qs], vf[ks][c], st.df[qs][c]);
+        }
+    Frag<bf16_t> sf[2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const int p = pq + qs * 16 + lr;
+      float x[8];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float e = fast_exp2(__builtin_fmaf(S[ks][qs][r], sl2, -st.Lq[qs]));
+          if (!FULL) {
+            const int j = jt + 8 * lg + 4 * ks + r;
+            e = (j > p || j <= p - a.window) ? 0.f : e;
+          }
+          x[4 * ks + r] = e * (P[ks][qs][r] - st.Dv[qs]);
+        }
+      pack_frag(sf[qs], x);
+    }
+#pragma unroll
+    for (int hs = 0; hs < C::NH; ++hs)
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) mma(st.dQ[hs][qs], tf[hs], sf[qs]);
+  }
+}
+
+template <int HD>
+__global__ __launch_bounds__(NT, 2) void attn_bwd_dq2_kernel(const AttnArgs a) {
+  using C = Q2<HD>;
+  __shared__ __align__(1024) char stage[2 * C::KB + C::TB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4, g4 = lg * 4;
+  int qb, h, sp;
+  {
+    const int gx = gridDim.x, total = gx * gridDim.y * gridDim.z;
+    const int i = blockIdx.x + gx * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int q8 = total / 8, rem = total % 8, x = i % 8;
+    const int m = x * q8 + min(x, rem) + i / 8;
+    qb = m % gx;
+    sp = (m / gx) % a.nsplit;
+    h = m / (gx * a.nsplit);
+  }
+  const int q_lo = qb * 128;
+  const int pos0 = *a.pos0;
+  const int qw = q_lo + wave * 32;
+  const bf16_t *Q = reinterpret_cast<const bf16_t *>(a.q);
+  const bf16_t *dO = reinterpret_cast<const bf16_t *>(a.dout);
+
+  Q2State<HD> st;
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const int q = qw + qs * 16 + lr;
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) {
+      const int col = c * 32 + lg * 8;
+      if (q < a.n && col < HD) {
+        load_frag(st.qf[qs][c], Q + (long)q * a.d + h * HD + col);
+        load_frag(st.df[qs][c], dO + (long)q * a.d + h * HD + col);
+      } else {
+        zero_frag(st.qf[qs][c]);
+        zero_frag(st.df[qs][c]);
+      }
+    }
+    st.Lq[qs] = q < a.n ? a.lse2[(long)h * a.ldl + q] : 0.f;
+    st.Dv[qs] = q < a.n ? a.Dq[(long)h * a.ldl + q] : 0.f;
+#pragma unroll
+    for (int hs = 0; hs < C::NH; ++hs) st.dQ[hs][qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  }
+  {
+    const int r0 = 8 * (lr >> 2) + (lr & 3), x0 = kswz<C::KCH>(r0);
+    const int base = r0 * C::KCH + (lg ^ (x0 & 3));
+    st.kb[0] = (base + (x0 & 4)) * 16;
+    st.kb[1] = (base - (x0 & 4)) * 16;
+    st.vb = (lr * 4 + (lg ^ ((lr >> 1) & 3))) * 16;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  const int p_first = pos0 + q_lo;
+  const int p_last = pos0 + min(q_lo + 127, a.n - 1);
+  const int jtw = max(0, p_first - a.window + 1) & ~31;
+  const int ntw = (p_last - jtw) / 32 + 1;
+  const int t_lo = ntw * sp / a.nsplit, t_hi = ntw * (sp + 1) / a.nsplit;
+  const int jt0 = jtw + 32 * t_lo;
+  const int ntile = t_hi - t_lo;
+  const int pq = pos0 + qw;
+
+  Q2Issue<HD> is;
+  is.init(reinterpret_cast<const bf16_t *>(a.K) + (long)h * a.R * HD,
+          reinterpret_cast<const bf16_t *>(a.V) + (long)h * a.R * HD,
+          reinterpret_cast<const bf16_t *>(a.Kt) + (long)h * HD * a.R, a.R, wave, lane);
+  int f0, f1;
+  {
+    const int lo = pos0 + q_lo + 127 - a.window + 1;
+    f0 = lo <= jt0 ? 0 : (lo - jt0 + 31) / 32;
+    f1 = p_first - 31 < jt0 ? 0 : (p_first - 31 - jt0) / 32 + 1;
+    f0 = min(f0, ntile);
+    f1 = min(max(f1, f0), ntile);
+  }
+  if (ntile > 0) is.run(stage, jt0 % a.R);
+  dq2_range<HD, false>(st, is, stage, 0, f0, ntile, jt0, pq, lr, lg, a);
+  dq2_range<HD, true>(st, is, stage, f0, f1, ntile, jt0, pq, lr, lg, a);
+  dq2_range<HD, false>(st, is, stage, f1, ntile, ntile, jt0, pq, lr, lg, a);
+
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const int q = qw + qs * 16 + lr;
+    if (q < a.n) {
+#pragma unroll
+      for (int hs = 0; hs < C::NH; ++hs) {
+        float v[4] = {st.dQ[hs][qs][0] * a.scale, st.dQ[hs][qs][1] * a.scale, st.dQ[hs][qs][2] * a.scale,
+                      st.dQ[hs][qs][3] * a.scale};
+        float *dst = a.nsplit == 1 ? a.dq : a.ws + (long)sp * a.n * a.d;
+        store4<float>(dst + (long)q * a.d + h * HD + hs * 16 + g4, v);
+      }
+    }
+  }
+}
+
 // ======================================================================= dQ
 // grid (ceil(n/128), H); 4 waves x 32 queries; loops over the window's keys.
 template <typename T, int HD>
@@ -930,6 +1156,11 @@ template <int HD> hipError_t fwd2_t(const AttnArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((attn_fwd2_kernel<HD>), grid, dim3(NT), 0, st, a);
   return hipGetLastError();
 }
+template <int HD> hipError_t dq2_t(const AttnArgs &a, hipStream_t st) {
+  dim3 grid((a.n + 127) / 128, a.H, a.nsplit);
+  hipLaunchKernelGGL((attn_bwd_dq2_kernel<HD>), grid, dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
 template <typename T, int HD> hipError_t dq_t(const AttnArgs &a, hipStream_t st) {
   dim3 grid((a.n + 127) / 128, a.H, a.nsplit);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, dim3(NT), 0, st, a);
@@ -983,7 +1214,17 @@ hipError_t fwd_hd(bool bf, int hd, const AttnArgs &a, hipStream_t st) {
   HD_SWITCH_F32(fwd_t)
 }
 hipError_t dq_hd(bool bf, int hd, const AttnArgs &a, hipStream_t st) {
-  if (bf) { HD_SWITCH(dq_t, bf16_t) }
+  if (bf) {
+    switch (hd) {
+      case 16: return dq2_t<16>(a, st);
+      case 32: return dq2_t<32>(a, st);
+      case 64: return dq2_t<64>(a, st);
+      case 80: return dq2_t<80>(a, st);
+      case 96: return dq2_t<96>(a, st);
+      case 128: return dq_t<bf16_t, 128>(a, st);  // 32 queries' dQ of hd 128 per wave exceed the registers
+    }
+    return hipErrorInvalidValue;
+  }
   HD_SWITCH_F32(dq_t)
 }
 hipError_t dkdv_hd(bool bf, int hd, const AttnArgs &a, hipStream_t st) {

@@ -18,7 +18,7 @@ hipError_t rmsnorm_bwd_launch(int dtype, const float *dy, const float *x, const 
                               const float *dh_in, float *dh_out, void *dh_t, int n, int d, hipStream_t st);
 
 struct RopeArgs {
-  const void *qkv;      // [n][3d] pre-norm q | k | v
+  const float *qkv;     // [n][3d] pre-norm q | k | v (fp32: the GEMM output is not rounded before the norm)
   const void *gq, *gk;  // [hd] QK-norm gains
   const float2 *cs;     // rotary table [max_pos][hd/2] of (cos, sin) pairs
   const int *pos0;
@@ -53,9 +53,11 @@ hipError_t ce_reduce_launch(const float2 *part, int P, const float *zlab, const 
 // Rotary table: cs[p][i] = (cos, sin)(p * theta^(-2i/hd)) evaluated in fp64.
 hipError_t rope_table_launch(float2 *cs, long max_pos, int hd, double theta, hipStream_t st);
 
-// dst[r * ld_dst + c] = (T) src[r * ld_src + c]
+// dst[r * ld_dst + c] = hi = (T) src[r * ld_src + c]; when lo is given also
+// lo[r * ld_lo + c] = (T) (src - hi), so that hi + lo carries the fp32 value to
+// about 16 significant bits in bf16.
 hipError_t convert_rows_launch(int dtype, const float *src, long ld_src, void *dst, long ld_dst, int rows, int cols,
-                               hipStream_t st);
+                               hipStream_t st, void *lo = nullptr, long ld_lo = 0);
 // dst (T) = src (T) copies with row strides.
 hipError_t copy_rows_launch(int dtype, const void *src, long ld_src, void *dst, long ld_dst, int rows, int cols,
                             hipStream_t st);

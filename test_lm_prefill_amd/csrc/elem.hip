@@ -31,32 +31,42 @@ __global__ __launch_bounds__(256) void embed_kernel(const T *E, const int *tok, 
 }
 
 // ----------------------------------------------------------------- RMSNorm
-template <typename T>
+// One wave per row; the row stays in registers (NV float4 per lane, d <= 256 NV)
+// so x (and dy) are read from HBM once.  Four rows per 256-thread block.
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float *x, const T *g, T *y, float *r_out,
                                                           float *x_copy, int n, int d, float eps) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n) return;
-  const float *xr = x + (long)row * d;
+  const long o = (long)row * d;
+  float4 v[NV];
   float ss = 0.f;
-  for (int i = lane * 4; i < d; i += 256) {
-    float4 v = *reinterpret_cast<const float4 *>(xr + i);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int i = (k * 64 + lane) * 4;
+    v[k] = i < d ? *reinterpret_cast<const float4 *>(x + o + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
   }
   ss = wave_sum(ss);
   const float r = 1.f / sqrtf(ss / (float)d + eps);
-  for (int i = lane * 4; i < d; i += 256) {
-    float4 v = *reinterpret_cast<const float4 *>(xr + i);
-    float gv[4];
-    load4<T>(g + i, gv);
-    float o[4] = {v.x * r * gv[0], v.y * r * gv[1], v.z * r * gv[2], v.w * r * gv[3]};
-    store4<T>(y + (long)row * d + i, o);
-    if (x_copy) *reinterpret_cast<float4 *>(x_copy + (long)row * d + i) = v;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int i = (k * 64 + lane) * 4;
+    if (i < d) {
+      float gv[4];
+      load4<T>(g + i, gv);
+      float out[4] = {v[k].x * r * gv[0], v[k].y * r * gv[1], v[k].z * r * gv[2], v[k].w * r * gv[3]};
+      store4<T>(y + o + i, out);
+      if (x_copy) *reinterpret_cast<float4 *>(x_copy + o + i) = v[k];
+    }
   }
   if (r_out && lane == 0) r_out[row] = r;
 }
 
-template <typename T>
+// dx = r g dy - x r^3 mean(x g dy) (+ dh_in); written fp32 (dh_out) and in the
+// working dtype (dh_t, the next GEMM's operand).
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float *dy, const float *x, const float *r,
                                                           const T *g, const float *dh_in, float *dh_out, T *dh_t,
                                                           int n, int d) {
@@ -64,30 +74,39 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float *dy, const
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n) return;
   const long o = (long)row * d;
+  float4 xa[NV], gy[NV];
   float dot = 0.f;
-  for (int i = lane * 4; i < d; i += 256) {
-    float4 a = *reinterpret_cast<const float4 *>(x + o + i);
-    float4 b = *reinterpret_cast<const float4 *>(dy + o + i);
-    float gv[4];
-    load4<T>(g + i, gv);
-    dot += a.x * b.x * gv[0] + a.y * b.y * gv[1] + a.z * b.z * gv[2] + a.w * b.w * gv[3];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int i = (k * 64 + lane) * 4;
+    if (i < d) {
+      xa[k] = *reinterpret_cast<const float4 *>(x + o + i);
+      const float4 b = *reinterpret_cast<const float4 *>(dy + o + i);
+      float gv[4];
+      load4<T>(g + i, gv);
+      gy[k] = make_float4(b.x * gv[0], b.y * gv[1], b.z * gv[2], b.w * gv[3]);
+    } else {
+      xa[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      gy[k] = xa[k];
+    }
+    dot += xa[k].x * gy[k].x + xa[k].y * gy[k].y + xa[k].z * gy[k].z + xa[k].w * gy[k].w;
   }
   dot = wave_sum(dot);
   const float rr = r[row];
   const float c = rr * rr * rr * dot / (float)d;
-  for (int i = lane * 4; i < d; i += 256) {
-    float4 a = *reinterpret_cast<const float4 *>(x + o + i);
-    float4 b = *reinterpret_cast<const float4 *>(dy + o + i);
-    float gv[4];
-    load4<T>(g + i, gv);
-    float v[4] = {rr * gv[0] * b.x - a.x * c, rr * gv[1] * b.y - a.y * c, rr * gv[2] * b.z - a.z * c,
-                  rr * gv[3] * b.w - a.w * c};
-    if (dh_in) {
-      float4 p = *reinterpret_cast<const float4 *>(dh_in + o + i);
-      v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int i = (k * 64 + lane) * 4;
+    if (i < d) {
+      float v[4] = {rr * gy[k].x - xa[k].x * c, rr * gy[k].y - xa[k].y * c, rr * gy[k].z - xa[k].z * c,
+                    rr * gy[k].w - xa[k].w * c};
+      if (dh_in) {
+        const float4 p = *reinterpret_cast<const float4 *>(dh_in + o + i);
+        v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
+      }
+      store4<float>(dh_out + o + i, v);
+      store4<T>(dh_t + o + i, v);
     }
-    store4<float>(dh_out + o + i, v);
-    store4<T>(dh_t + o + i, v);
   }
 }
 
@@ -100,7 +119,7 @@ __global__ __launch_bounds__(256) void qk_rope_fwd_kernel(const RopeArgs a) {
   const int hd = a.hd, half = hd / 2, h = blockIdx.y, t0 = blockIdx.x * 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int pos0 = *a.pos0;
-  const T *qkv = reinterpret_cast<const T *>(a.qkv);
+  const float *qkv = reinterpret_cast<const float *>(a.qkv);
   const T *gq = reinterpret_cast<const T *>(a.gq);
   const T *gk = reinterpret_cast<const T *>(a.gk);
   float *sV = sm, *sK = sm + hd * 33, *sQ = sm + 2 * hd * 33;
@@ -114,9 +133,9 @@ __global__ __launch_bounds__(256) void qk_rope_fwd_kernel(const RopeArgs a) {
     const long base = (long)t * 3 * a.d + h * hd;
     float qi = 0, qj = 0, ki = 0, kj = 0, vi = 0, vj = 0;
     if (act) {
-      qi = to_f(qkv[base + lane]); qj = to_f(qkv[base + lane + half]);
-      ki = to_f(qkv[base + a.d + lane]); kj = to_f(qkv[base + a.d + lane + half]);
-      vi = to_f(qkv[base + 2 * a.d + lane]); vj = to_f(qkv[base + 2 * a.d + lane + half]);
+      qi = qkv[base + lane]; qj = qkv[base + lane + half];
+      ki = qkv[base + a.d + lane]; kj = qkv[base + a.d + lane + half];
+      vi = qkv[base + 2 * a.d + lane]; vj = qkv[base + 2 * a.d + lane + half];
     }
     const float sq = wave_sum(qi * qi + qj * qj), sk = wave_sum(ki * ki + kj * kj);
     const float rq = 1.f / sqrtf(sq / (float)hd + a.eps), rk = 1.f / sqrtf(sk / (float)hd + a.eps);
@@ -164,15 +183,15 @@ __global__ __launch_bounds__(256) void qk_rope_bwd_kernel(const RopeArgs a) {
   if (t >= a.n) return;
   const int p = *a.pos0 + t;
   const bool act = lane < half;
-  const T *qkv = reinterpret_cast<const T *>(a.qkv);
+  const float *qkv = reinterpret_cast<const float *>(a.qkv);
   const long base = (long)t * 3 * a.d + h * hd;
   const long ob = (long)t * a.d + h * hd;
   float qi = 0, qj = 0, ki = 0, kj = 0, dqi = 0, dqj = 0, dki = 0, dkj = 0;
   float2 cs = make_float2(1.f, 0.f);
   float gqi = 0, gqj = 0, gki = 0, gkj = 0;
   if (act) {
-    qi = to_f(qkv[base + lane]); qj = to_f(qkv[base + lane + half]);
-    ki = to_f(qkv[base + a.d + lane]); kj = to_f(qkv[base + a.d + lane + half]);
+    qi = qkv[base + lane]; qj = qkv[base + lane + half];
+    ki = qkv[base + a.d + lane]; kj = qkv[base + a.d + lane + half];
     cs = a.cs[(long)p * half + lane];
     // transpose of the rotation
     const float ai = a.dqh[ob + lane], aj = a.dqh[ob + lane + half];
@@ -285,11 +304,15 @@ __global__ void rope_table_kernel(float2 *cs, long max_pos, int hd, double theta
 }
 
 template <typename T>
-__global__ void convert_rows_kernel(const float *src, long ld_src, T *dst, long ld_dst, int rows, int cols) {
+__global__ void convert_rows_kernel(const float *src, long ld_src, T *dst, long ld_dst, T *lo, long ld_lo, int rows,
+                                    int cols) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long)rows * cols) return;
   const int r = idx / cols, c = idx % cols;
-  dst[(long)r * ld_dst + c] = from_f<T>(src[(long)r * ld_src + c]);
+  const float x = src[(long)r * ld_src + c];
+  const T hi = from_f<T>(x);
+  dst[(long)r * ld_dst + c] = hi;
+  if (lo) lo[(long)r * ld_lo + c] = from_f<T>(x - to_f(hi));
 }
 template <typename T>
 __global__ void copy_rows_kernel(const T *src, long ld_src, T *dst, long ld_dst, int rows, int cols) {
@@ -351,25 +374,44 @@ hipError_t embed_launch(int dtype, const void *E, const int *tok, const int *pos
   return hipGetLastError();
 }
 
+// Row width classes (float4 per lane): d <= 256 NV.
+#define NV_DISPATCH(d, CALL)                   \
+  if ((d) <= 256) { CALL(1); }                 \
+  else if ((d) <= 512) { CALL(2); }            \
+  else if ((d) <= 1024) { CALL(4); }           \
+  else if ((d) <= 2048) { CALL(8); }           \
+  else if ((d) <= 3072) { CALL(12); }          \
+  else if ((d) <= 4096) { CALL(16); }          \
+  else if ((d) <= 8192) { CALL(32); }          \
+  else return hipErrorInvalidValue;
+
 hipError_t rmsnorm_fwd_launch(int dtype, const float *x, const void *g, void *y, float *r_out, float *x_copy, int n,
                               int d, float eps, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-#define K_(T, ...)                                                                                            \
-  hipLaunchKernelGGL(rmsnorm_fwd_kernel<T>, dim3(blocks_for(n, 4)), dim3(256), 0, st, x, (const T *)g, (T *)y, \
-                     r_out, x_copy, n, d, eps)
-  DT_DISPATCH(dtype, K_, 0);
-#undef K_
+#define CALL_(NV)                                                                                                  \
+  if (dtype == 1)                                                                                                  \
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<bf16_t, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, x,             \
+                       (const bf16_t *)g, (bf16_t *)y, r_out, x_copy, n, d, eps);                                  \
+  else                                                                                                             \
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<float, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, x,              \
+                       (const float *)g, (float *)y, r_out, x_copy, n, d, eps);
+  NV_DISPATCH(d, CALL_)
+#undef CALL_
   return hipGetLastError();
 }
 
 hipError_t rmsnorm_bwd_launch(int dtype, const float *dy, const float *x, const float *r, const void *g,
                               const float *dh_in, float *dh_out, void *dh_t, int n, int d, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-#define K_(T, ...)                                                                                               \
-  hipLaunchKernelGGL(rmsnorm_bwd_kernel<T>, dim3(blocks_for(n, 4)), dim3(256), 0, st, dy, x, r, (const T *)g, dh_in, \
-                     dh_out, (T *)dh_t, n, d)
-  DT_DISPATCH(dtype, K_, 0);
-#undef K_
+#define CALL_(NV)                                                                                                  \
+  if (dtype == 1)                                                                                                  \
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<bf16_t, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, dy, x, r,      \
+                       (const bf16_t *)g, dh_in, dh_out, (bf16_t *)dh_t, n, d);                                    \
+  else                                                                                                             \
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<float, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, dy, x, r,       \
+                       (const float *)g, dh_in, dh_out, (float *)dh_t, n, d);
+  NV_DISPATCH(d, CALL_)
+#undef CALL_
   return hipGetLastError();
 }
 
@@ -431,12 +473,12 @@ hipError_t rope_table_launch(float2 *cs, long max_pos, int hd, double theta, hip
 }
 
 hipError_t convert_rows_launch(int dtype, const float *src, long ld_src, void *dst, long ld_dst, int rows, int cols,
-                               hipStream_t st) {
+                               hipStream_t st, void *lo, long ld_lo) {
   long tot = (long)rows * cols;
   if (tot <= 0) return hipSuccess;
 #define K_(T, ...)                                                                                               \
   hipLaunchKernelGGL(convert_rows_kernel<T>, dim3(blocks_for(tot)), dim3(256), 0, st, src, ld_src, (T *)dst, ld_dst, \
-                     rows, cols)
+                     (T *)lo, ld_lo, rows, cols)
   DT_DISPATCH(dtype, K_, 0);
 #undef K_
   return hipGetLastError();

@@ -13,7 +13,8 @@ enum GemmEpi {
   EPI_CE = 4,        // per-row partial (max, sum exp) over the tile's columns and the
                      // label logit -> part / zlab   (cross-entropy, first pass)
   EPI_DLOGITS = 5,   // C (T) = (exp(acc - lse[m]) - [n + col_off == label]) * alpha
-  EPI_SGD = 6,       // Cf (fp32 master) -= alpha * acc; C (T) = round(Cf)   (inner SGD)
+  EPI_SGD = 6,       // Cf (fp32 master) -= alpha * acc; C (T) = hi = round(Cf) and, when C2 is
+                     // set, C2 (T) = round(Cf - hi): the working copy as hi + lo (inner SGD)
 };
 
 struct GemmArgs {
@@ -35,6 +36,11 @@ struct GemmArgs {
   float *zlab;        // EPI_CE label logits [M]
   float alpha;
   int col_off;
+  // > 0: A is [M][a_kwrap] and its reduction index is taken modulo a_kwrap, so
+  // the product runs over [A | A | ...] and K may span several weight blocks
+  // that multiply the same activations (a multiple of 64, or of 8 for the
+  // generic kernel)
+  int a_kwrap;
   // split-K (internal)
   int ksplit;
   float *ws;

@@ -39,7 +39,7 @@ template <typename T> struct Stage {
 
 // ---- global -> registers
 template <typename T, bool KC>
-DEVI void load_tile(Stage<T> &st, const T *X, long ld, int rows, int K, int r0, int k0, int tid) {
+DEVI void load_tile(Stage<T> &st, const T *X, long ld, int rows, int K, int r0, int k0, int tid, int kwrap = 0) {
   constexpr int VE = Cfg<T>::VE;
   if constexpr (KC) {
     constexpr int VPR = BK / VE;  // vectors per row
@@ -48,8 +48,9 @@ DEVI void load_tile(Stage<T> &st, const T *X, long ld, int rows, int K, int r0, 
       int v = tid + NT * i;
       int r = v / VPR, c = (v % VPR) * VE;
       int gr = r0 + r, gk = k0 + c;
+      const int ck = kwrap > 0 ? gk % kwrap : gk;  // column read (a vector never straddles the wrap)
       if (gr < rows && gk < K)
-        st.v[i] = *reinterpret_cast<const uint4 *>(X + (long)gr * ld + gk);
+        st.v[i] = *reinterpret_cast<const uint4 *>(X + (long)gr * ld + ck);
       else
         st.v[i] = make_uint4(0, 0, 0, 0);
     }
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const GemmArgs g) {
   Stage<T> sa, sb;
   const int nk = (kend - kbeg + BK - 1) / BK;
   if (nk > 0) {
-    load_tile<T, AK>(sa, A, g.lda, g.M, kend, m0, kbeg, tid);
+    load_tile<T, AK>(sa, A, g.lda, g.M, kend, m0, kbeg, tid, g.a_kwrap);
     load_tile<T, BKc>(sb, B, g.ldb, g.N, kend, n0, kbeg, tid);
     store_tile<T, AK>(sa, smA[0], tid);
     store_tile<T, BKc>(sb, smB[0], tid);
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const GemmArgs g) {
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) {
-      load_tile<T, AK>(sa, A, g.lda, g.M, kend, m0, kbeg + (kt + 1) * BK, tid);
+      load_tile<T, AK>(sa, A, g.lda, g.M, kend, m0, kbeg + (kt + 1) * BK, tid, g.a_kwrap);
       load_tile<T, BKc>(sb, B, g.ldb, g.N, kend, n0, kbeg + (kt + 1) * BK, tid);
     }
     const T *pa = smA[cur];
@@ -298,6 +299,12 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const GemmArgs g) {
         float nw[4] = {w.x - g.alpha * v[0], w.y - g.alpha * v[1], w.z - g.alpha * v[2], w.w - g.alpha * v[3]};
         *pw = make_float4(nw[0], nw[1], nw[2], nw[3]);
         store4<T>(reinterpret_cast<T *>(g.C) + (long)m * g.ldc + n, nw);
+        if (g.C2) {
+          float lo[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) lo[r] = nw[r] - to_f(from_f<T>(nw[r]));
+          store4<T>(reinterpret_cast<T *>(g.C2) + (long)m * g.ldc2 + n, lo);
+        }
       }
     }
   }
@@ -388,7 +395,7 @@ size_t gemm_ws_elems(int M, int N) { return (size_t)8 * M * N; }
 hipError_t gemm_dma_launch(int epi, const GemmArgs &g, hipStream_t st);
 
 static bool use_dma(int dtype, bool a_kc, bool b_kc, const GemmArgs &g) {
-  return dtype == 1 && a_kc && b_kc && g.K % 64 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0;
+  return dtype == 1 && a_kc && b_kc && g.K % 64 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.a_kwrap % 64 == 0;
 }
 
 int gemm_plan(int dtype, bool a_kc, bool b_kc, int epi, const GemmArgs &g, size_t ws_elems, int force_split) {
@@ -423,6 +430,8 @@ hipError_t gemm_main_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g
                             hipStream_t st) {
   g.ksplit = split;
   g.ws = ws;
+  // the wrapped activation operand must be k-contiguous, whole 16-byte vectors
+  if (g.a_kwrap < 0 || (g.a_kwrap > 0 && (!a_kc || g.a_kwrap % 8 != 0))) return hipErrorInvalidValue;
   if (use_dma(dtype, a_kc, b_kc, g)) return gemm_dma_launch(epi, g, st);
   return dtype == 1 ? dispatch_layout<bf16_t>(a_kc, b_kc, epi, g, st, split)
                     : dispatch_layout<float>(a_kc, b_kc, epi, g, st, split);

@@ -146,6 +146,12 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
         float nw[4] = {w.x - g.alpha * v[0], w.y - g.alpha * v[1], w.z - g.alpha * v[2], w.w - g.alpha * v[3]};
         *pw = make_float4(nw[0], nw[1], nw[2], nw[3]);
         store4<bf16_t>(reinterpret_cast<bf16_t *>(g.C) + (long)m * g.ldc + n, nw);
+        if (g.C2) {
+          float lo[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) lo[r] = nw[r] - to_f(from_f<bf16_t>(nw[r]));
+          store4<bf16_t>(reinterpret_cast<bf16_t *>(g.C2) + (long)m * g.ldc2 + n, lo);
+        }
       }
     }
   }
@@ -156,15 +162,17 @@ template <int BN> struct G3Issue {
   static constexpr int CPW = G2<BN>::ROWS / 8 / 4;  // 1 KiB chunks per wave
   __amdgpu_buffer_rsrc_t rw, rx;
   uint32_t voff[CPW];
-  int wave, kbeg;
+  int wave, kbeg, kwrap;
   char *sm;
   DEVI void init(const GemmArgs &g, int wave_, int lane, int n0, int m0, int kb, char *sm_) {
+    const int ka = g.a_kwrap > 0 ? g.a_kwrap : g.K;  // columns of A
     const uint32_t wbytes = (uint32_t)(((long)(g.N - 1) * g.ldb + g.K) * 2);
-    const uint32_t xbytes = (uint32_t)(((long)(g.M - 1) * g.lda + g.K) * 2);
+    const uint32_t xbytes = (uint32_t)(((long)(g.M - 1) * g.lda + ka) * 2);
     rw = __builtin_amdgcn_make_buffer_rsrc((void *)g.B, (short)0, wbytes, RSRC_W3);
     rx = __builtin_amdgcn_make_buffer_rsrc((void *)g.A, (short)0, xbytes, RSRC_W3);
     wave = wave_;
     kbeg = kb;
+    kwrap = g.a_kwrap;
     sm = sm_;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
@@ -180,16 +188,20 @@ template <int BN> struct G3Issue {
       }
     }
   }
+  // Streams k-step kt (64 deep) of both operands into the stage at stage_off.
+  // A's column is the step's k modulo kwrap (k-steps never straddle the wrap).
   DEVI void run(int kt, int stage_off = 0) const {
-    const int soff = (kbeg + kt * BK) * 2;
+    const int k = kbeg + kt * BK;
+    const int soff_w = k * 2;
+    const int soff_x = (kwrap > 0 ? k % kwrap : k) * 2;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int j = wave * CPW + c;
       lds_void *dst = (lds_void *)(sm + stage_off + j * 1024);
       if (j * 8 < BN)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, voff[c], soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, voff[c], soff_w, 0, 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, dst, 16, voff[c], soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, dst, 16, voff[c], soff_x, 0, 0);
     }
   }
 };

@@ -35,8 +35,14 @@ thread_local std::string g_thread_err;
 struct LayerBuf {
   void *attn_norm = nullptr, *wqkv = nullptr, *wo = nullptr, *q_norm = nullptr, *k_norm = nullptr,
        *mlp_norm = nullptr;
-  void *wgu = nullptr;  // [2F][d] frozen, [4F][d] updated (fast rows first), gate/up interleaved by 16 rows
-  void *wd = nullptr;   // [d][F] frozen, [d][2F] updated (fast columns first)
+  // gate/up rows interleaved by 16.  Frozen layers: [2F][d].  Updated layers:
+  // fast rows [2F][2d] holding the bf16 working copy as hi | lo (hi = round(W),
+  // lo = round(W - hi), so hi + lo carries the fp32 master to ~16 bits and the
+  // small inner updates are not lost to bf16 rounding), then static rows
+  // [2F][d] at element offset 4Fd.
+  void *wgu = nullptr;
+  // Frozen layers: [d][F].  Updated layers: [d][3F] = fast hi | static | fast lo.
+  void *wd = nullptr;
   bool fast = false, bwd_attn = false;
   int u = -1;
   float sbound = 0.f;  // bound of the scaled scores (log2 units) for the bounded forward, 0 = none
@@ -51,7 +57,8 @@ struct LayerBuf {
 
 struct Saved {
   float *h_in = nullptr, *r1 = nullptr, *lse2 = nullptr, *h1 = nullptr, *r2 = nullptr;
-  void *qkv = nullptr, *qh = nullptr, *qht = nullptr, *o = nullptr, *m = nullptr, *gu = nullptr, *hmid = nullptr;
+  float *qkv = nullptr;  // [b][3d] fp32
+  void *qh = nullptr, *qht = nullptr, *o = nullptr, *m = nullptr, *gu = nullptr, *hmid = nullptr;
 };
 
 }  // namespace
@@ -75,7 +82,8 @@ struct ttt_handle {
   void *ring_base = nullptr;
   size_t ring_bytes = 0;
   float *h = nullptr, *lse2 = nullptr, *hf = nullptr, *rf = nullptr, *zlab = nullptr, *lse = nullptr;
-  void *a = nullptr, *qkv = nullptr, *qh = nullptr, *o = nullptr, *m = nullptr, *hmid = nullptr, *nf = nullptr;
+  float *qkv = nullptr;  // [b][3d] fp32
+  void *a = nullptr, *qh = nullptr, *o = nullptr, *m = nullptr, *hmid = nullptr, *nf = nullptr;
   float2 *part = nullptr;
   void *dz = nullptr, *dy = nullptr, *dhmid = nullptr, *dgu = nullptr, *dO = nullptr, *dOt = nullptr, *dqkv = nullptr;
   void *lm_headT = nullptr;                                  // [d][V]
@@ -225,12 +233,12 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.attn_norm, h->a, sb ? S->r1 : nullptr, sb ? S->h_in : nullptr, n, d, eps,
                                 st));
     }
-    void *qkv = sb ? S->qkv : h->qkv;
+    float *qkv = sb ? S->qkv : h->qkv;  // fp32: q, k, v are normalised / cached without a bf16 rounding first
     {
       GemmArgs g = gargs(h->a, d, lw.wqkv, d, n, 3 * d, d);
-      g.C = qkv;
-      g.ldc = 3 * d;
-      gemm(h, K_GEMM_QKV, true, true, EPI_STORE, g, st);
+      g.Cf = qkv;
+      g.ldcf = 3 * d;
+      gemm(h, K_GEMM_QKV, true, true, EPI_STORE_F32, g, st);
     }
     void *qh = sb ? S->qh : h->qh;
     {
@@ -301,23 +309,40 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       PROF(K_RMSNORM);
       HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.mlp_norm, m, S ? S->r2 : nullptr, S ? S->h1 : nullptr, n, d, eps, st));
     }
-    const int Fc = lw.fast ? 2 * F : F;  // hidden units of this block
-    void *hm = S ? S->hmid : h->hmid;
-    {
-      GemmArgs g = gargs(m, d, lw.wgu, d, n, 2 * Fc, d);
+    void *hm = S ? S->hmid : h->hmid;  // hidden units: F (frozen) or 2F = fast then static
+    if (!lw.fast) {
+      GemmArgs g = gargs(m, d, lw.wgu, d, n, 2 * F, d);
       g.C = hm;
-      g.ldc = Fc;
-      g.C2 = S ? S->gu : nullptr;
-      g.ldc2 = 2 * Fc;
+      g.ldc = F;
       gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, g, st);
+      GemmArgs g2 = gargs(hm, F, lw.wd, F, n, d, F);
+      g2.Cf = h->h;
+      g2.ldcf = d;
+      gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st);
+    } else {
+      // fast units [0, F): bf16 runs the reduction over [m | m] x [hi | lo]
+      GemmArgs g = gargs(m, d, lw.wgu, 2 * d, n, 2 * F, dt == 1 ? 2 * d : d);
+      g.a_kwrap = dt == 1 ? d : 0;
+      g.C = hm;
+      g.ldc = 2 * F;
+      g.C2 = S ? S->gu : nullptr;
+      g.ldc2 = 4 * F;
+      gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, g, st);
+      // static units [F, 2F)
+      GemmArgs gs = gargs(m, d, off(lw.wgu, (size_t)4 * F * d * es), d, n, 2 * F, d);
+      gs.C = off(hm, (size_t)F * es);
+      gs.ldc = 2 * F;
+      gs.C2 = S ? off(S->gu, (size_t)2 * F * es) : nullptr;
+      gs.ldc2 = 4 * F;
+      gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, gs, st);
+      // down: [fast | static | fast] units x [hi | static | lo] columns (bf16)
+      GemmArgs g2 = gargs(hm, 2 * F, lw.wd, 3 * F, n, d, dt == 1 ? 3 * F : 2 * F);
+      g2.a_kwrap = dt == 1 ? 2 * F : 0;
+      g2.Cf = h->h;
+      g2.ldcf = d;
+      gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st);
     }
-    {
-      GemmArgs g = gargs(hm, Fc, lw.wd, Fc, n, d, Fc);
-      g.Cf = h->h;
-      g.ldcf = d;
-      gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g, st);
-    }
-    h->launches += 4;
+    h->launches += lw.fast ? 5 : 4;
   }
   // --- head: final norm, LM head + cross-entropy (losses written before any update)
   {
@@ -391,8 +416,10 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         GemmArgs g = gargs(h->dyT, h->b, h->hmidT, h->b, d, F, np);
         g.Cf = h->m_d[lw.u];
         g.ldcf = F;
-        g.C = lw.wd;
-        g.ldc = 2 * F;
+        g.C = lw.wd;  // hi columns [0, F)
+        g.ldc = 3 * F;
+        g.C2 = dt == 1 ? off(lw.wd, (size_t)2 * F * es) : nullptr;  // lo columns [2F, 3F)
+        g.ldc2 = 3 * F;
         g.alpha = h->cfg.eta;
         gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st);
       }
@@ -420,8 +447,10 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         GemmArgs g = gargs(h->dguT, h->b, h->mT, h->b, 2 * F, d, np);
         g.Cf = h->m_gu[lw.u];
         g.ldcf = d;
-        g.C = lw.wgu;
-        g.ldc = d;
+        g.C = lw.wgu;  // hi columns of the fast rows
+        g.ldc = 2 * d;
+        g.C2 = dt == 1 ? off(lw.wgu, (size_t)d * es) : nullptr;  // lo columns
+        g.ldc2 = 2 * d;
         g.alpha = h->cfg.eta;
         gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st);
       }
@@ -537,11 +566,15 @@ void reset_fast(ttt_handle *h, hipStream_t st) {
     if (!lw.fast) continue;
     HIPCHK(hipMemcpyAsync(h->m_gu[lw.u], h->i_gu[lw.u], (size_t)2 * F * d * 4, hipMemcpyDeviceToDevice, st));
     HIPCHK(hipMemcpyAsync(h->m_d[lw.u], h->i_d[lw.u], (size_t)d * F * 4, hipMemcpyDeviceToDevice, st));
-    HIPCHK(convert_rows_launch(h->dt, h->i_gu[lw.u], d, lw.wgu, d, 2 * F, d, st));
-    HIPCHK(convert_rows_launch(h->dt, h->i_d[lw.u], F, lw.wd, 2 * F, d, F, st));
+    HIPCHK(convert_rows_launch(h->dt, h->i_gu[lw.u], d, lw.wgu, 2 * d, 2 * F, d, st, off(lw.wgu, (size_t)d * h->es),
+                               2 * d));
+    HIPCHK(convert_rows_launch(h->dt, h->i_d[lw.u], F, lw.wd, 3 * F, d, F, st, off(lw.wd, (size_t)2 * F * h->es),
+                               3 * F));
     // transposed working copies for the backward GEMMs: Wd_cat^T [2F][d], Wgu_cat^T [d][4F]
-    HIPCHK(transpose_launch(h->dt, false, lw.wd, 2 * F, lw.wdT, d, d, d, 2 * F, st));
-    HIPCHK(transpose_launch(h->dt, false, lw.wgu, d, lw.wguT, 4 * F, 4 * F, 4 * F, d, st));
+    HIPCHK(transpose_launch(h->dt, false, lw.wd, 3 * F, lw.wdT, d, d, d, 2 * F, st));  // fast hi, static
+    HIPCHK(transpose_launch(h->dt, false, lw.wgu, 2 * d, lw.wguT, 4 * F, 2 * F, 2 * F, d, st));  // fast hi rows
+    HIPCHK(transpose_launch(h->dt, false, off(lw.wgu, (size_t)4 * F * d * h->es), d, off(lw.wguT, (size_t)2 * F * h->es),
+                            4 * F, 2 * F, 2 * F, d, st));  // static rows
   }
 }
 
@@ -615,6 +648,7 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
   if (!attn_supported_hd(c.head_dim)) return fail(nullptr, TTT_EUNSUPPORTED, "head_dim not in {16,32,64,80,96,128}");
   if (c.dtype != TTT_FP32 && c.dtype != TTT_BF16) return fail(nullptr, TTT_EINVAL, "dtype");
   if (c.dtype == TTT_FP32 && c.head_dim > 64) return fail(nullptr, TTT_EUNSUPPORTED, "fp32 supports head_dim <= 64");
+  if (c.d_model > 8192) return fail(nullptr, TTT_EUNSUPPORTED, "d_model > 8192");
   if (c.chunk <= 0 || c.window <= 0 || c.chunk % 64 || c.window % 64 || c.window < c.chunk)
     return fail(nullptr, TTT_EINVAL, "chunk and window must be positive multiples of 64 with window >= chunk");
   if (c.max_tokens < 1 || c.max_tokens > (1ll << 30)) return fail(nullptr, TTT_EINVAL, "max_tokens out of range");
@@ -704,10 +738,10 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
         HIPCHK(hipMemcpyAsync(lw.wd, w->w_down[l], fd, hipMemcpyDeviceToDevice, st));
       } else {
         const int u = lw.u;
-        lw.wgu = dalloc(h, 4 * fd, false);
-        pack_gu(w->w_gate[l], w->w_up[l], off(lw.wgu, 2 * fd), F, d, es, st);  // static rows after the fast ones
-        lw.wd = dalloc(h, 2 * fd, false);
-        HIPCHK(hipMemcpy2DAsync(off(lw.wd, (size_t)F * es), 2 * F * es, w->w_down[l], F * es, F * es, d,
+        lw.wgu = dalloc(h, 6 * fd, false);
+        pack_gu(w->w_gate[l], w->w_up[l], off(lw.wgu, 4 * fd), F, d, es, st);  // static rows after fast hi|lo
+        lw.wd = dalloc(h, 3 * fd, false);
+        HIPCHK(hipMemcpy2DAsync(off(lw.wd, (size_t)F * es), 3 * F * es, w->w_down[l], F * es, F * es, d,
                                 hipMemcpyDeviceToDevice, st));
         const size_t f32fd = (size_t)F * d * 4;
         h->m_gu[u] = (float *)dalloc(h, 2 * f32fd);
@@ -749,7 +783,7 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     h->h = (float *)dalloc(h, bd * 4);
     h->lse2 = (float *)dalloc(h, (size_t)h->H * b * 4);
     h->a = dalloc(h, bd * es);
-    h->qkv = dalloc(h, 3 * bd * es);
+    h->qkv = (float *)dalloc(h, 3 * bd * 4);
     h->qh = dalloc(h, bd * es);
     h->o = dalloc(h, bd * es);
     h->m = dalloc(h, bd * es);
@@ -783,7 +817,7 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
         S.lse2 = (float *)dalloc(h, (size_t)h->H * b * 4);
         S.h1 = (float *)dalloc(h, bd * 4);
         S.r2 = (float *)dalloc(h, b * 4);
-        S.qkv = dalloc(h, 3 * bd * es);
+        S.qkv = (float *)dalloc(h, 3 * bd * 4);
         S.qh = dalloc(h, bd * es);
         S.qht = dalloc(h, bd * es);
         S.o = dalloc(h, bd * es);
