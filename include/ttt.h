@@ -63,7 +63,8 @@ enum {
  *   chunk and window multiples of 64 with window >= chunk (the notes, section 5:
  *   the window covers at least one chunk); max_tokens >= 1.
  * Shapes outside the compiled kernels give TTT_EUNSUPPORTED: head_dim not in the
- * set above, head_dim > 64 with fp32, d_model > 8192.
+ * set above, head_dim > 64 with fp32, d_model > 8192, and in bf16 mode d_model
+ * or d_ff not a multiple of 64.
  */
 typedef struct {
   int32_t n_layers;     /* L */

@@ -35,6 +35,13 @@ def build(verbose=False):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr[-4000:])
+    # every kernel launch needs its host-side stub; a template instantiation
+    # whose stub the compiler did not emit would only fail when loaded
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("kernel launch stubs missing from the library:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -24,6 +24,8 @@ struct AttnArgs {
   const int *pos0;   // absolute position of the chunk's first query (device)
   float scale;       // 1/sqrt(hd)
   float sbound;      // forward: bound of scale * q.k in log2 units (bf16 bounded kernel), 0 = none
+  int fwd_f16;       // forward operands q, K, Vt are fp16 (bounded kernel only; needs sbound <= 14.5)
+  int o_f16;         // forward output o (and its merge) is fp16
   // key-range split (forward and dQ): nsplit work-groups share one query tile;
   // their partial results go to ws (fp32) and are merged in a fixed order.
   int nsplit;
@@ -40,6 +42,9 @@ int attn_fwd_split(int dtype, float sbound, int hd, int n, int H, int window, in
 // Largest score bound (log2 units) the bounded forward accepts: 2^-2B must
 // stay a normal fp32 number with room for sums.
 constexpr float ATTN_MAX_SBOUND = 48.f;
+// Whether the bounded forward can keep q, k, v and the weights in fp16: its
+// weights 2^(s - B + 15) stay normal fp16 numbers while B <= 14.5.
+bool attn_fwd_f16_ok(int dtype, float sbound, int hd);
 
 hipError_t attn_fwd_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st);
 hipError_t attn_bwd_dq_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st);

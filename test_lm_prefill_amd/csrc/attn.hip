@@ -140,7 +140,7 @@ template <typename T> constexpr int pad_el() { return 16 / (int)sizeof(T); }
 
 // ======================================================================= forward
 // grid (ceil(n/128), H); 4 waves x 32 queries.
-template <typename T, int HD>
+template <typename T, int HD, typename TO>
 __global__ __launch_bounds__(NT) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int HDP = Dims<HD>::HDP, NC = Dims<HD>::NC, NH = Dims<HD>::NH;
   constexpr int LDK = HDP + pad_el<T>(), LDV = 64 + pad_el<T>();
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const AttnArgs a) {
     __syncthreads();
   }
 
-  T *Out = reinterpret_cast<T *>(a.o);
+  TO *Out = reinterpret_cast<TO *>(a.o);
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
     const float lt = group4_sum(l_[qs]);
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
         for (int hs = 0; hs < NH; ++hs) {
           float v[4] = {O[hs][qs][0] * inv, O[hs][qs][1] * inv, O[hs][qs][2] * inv, O[hs][qs][3] * inv};
-          store4<T>(Out + (long)q * a.d + h * HD + hs * 16 + g4, v);
+          store4<TO>(Out + (long)q * a.d + h * HD + hs * 16 + g4, v);
         }
         if (lg == 0) a.lse2[(long)h * a.ldl + q] = lse;
       } else {
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256) void attn_dq_merge_kernel(const AttnArgs a) {
   reinterpret_cast<float4 *>(a.dq)[idx] = acc;
 }
 
-// ======================================================= forward, bf16, bounded
+// ======================================================= forward, 16-bit, bounded
 // 64 queries per wave, 4 waves (256 queries) per work-group; grid
 // (ceil(n/256), H, nsplit).  Key tiles of 32 are streamed from the rings
 // straight into one LDS stage (buffer_load ... lds).  Each wave reads all
@@ -371,6 +371,12 @@ __global__ __launch_bounds__(256) void attn_dq_merge_kernel(const AttnArgs a) {
 // exp is B + log2(sum p).  The host uses this kernel only when 2B stays far
 // inside the fp32 exponent range.
 //
+// Operand type TF: bf16, or fp16 (three more mantissa bits for q, k, v and p;
+// same MFMA rate).  With fp16, p is taken as 2^(s - B + 15): at most 2^15 (the
+// scores overshoot B by rounding only), and for B <= 14.5 every weight, even of
+// a query whose scores all sit at -B, stays a normal fp16 number.  The output O
+// is written as fp16 (the O projection's operand) or the working dtype.
+//
 // LDS layouts (16-byte chunks):
 //   K tile  [32 keys][KCH = 4 * ceil(hd/32) chunks], chunk c of key row r at
 //           position c ^ X(r); chunks at or past hd/8 read as zero (the q.k
@@ -381,6 +387,10 @@ __global__ __launch_bounds__(256) void attn_dq_merge_kernel(const AttnArgs a) {
 // consecutive keys of one query: exactly one 16-byte V^T fragment for the
 // P V product.  With these swizzles each 16-lane phase of a fragment read
 // touches every bank group twice (no conflicts).
+// log2 offset of the softmax weights kept in fp16 (none for bf16)
+template <typename TF> struct P16Off { static constexpr float v = 0.f; };
+template <> struct P16Off<f16_t> { static constexpr float v = 15.f; };
+
 template <int HD> struct F2 {
   static constexpr int NC = (HD + 31) / 32;   // 32-deep steps of q.k
   static constexpr int KCH = 4 * NC;          // chunks per K row in LDS
@@ -404,7 +414,7 @@ template <int HD> struct F2Issue {
   __amdgpu_buffer_rsrc_t rk, rv;
   uint32_t voff[C::IPW];
   int j0;
-  DEVI void init(const bf16_t *Kp, const bf16_t *Vtp, int R, int wave, int lane) {
+  DEVI void init(const void *Kp, const void *Vtp, int R, int wave, int lane) {
     rk = __builtin_amdgcn_make_buffer_rsrc((void *)Kp, (short)0, (uint32_t)R * HD * 2, BUF_RSRC_W3);
     rv = __builtin_amdgcn_make_buffer_rsrc((void *)Vtp, (short)0, (uint32_t)R * HD * 2, BUF_RSRC_W3);
     j0 = wave * C::IPW;
@@ -432,9 +442,9 @@ template <int HD> struct F2Issue {
   }
 };
 
-template <int HD> struct F2State {
+template <int HD, typename TF> struct F2State {
   using C = F2<HD>;
-  Frag<bf16_t> qf[4][C::NC];
+  Frag<TF> qf[4][C::NC];
   f32x4_v O[C::NH][4];
   float lsum[4];
   int kb[2], vb;  // per-lane byte offsets of the fragment reads (kb by parity of the 32-dim step)
@@ -444,16 +454,16 @@ template <int HD> struct F2State {
 // the work-group inside the window; otherwise each wave skips the MFMAs of a
 // tile none of its queries sees and masks the rest.  Every wave takes part in
 // the streaming and the barriers of every tile.
-template <int HD, bool FULL>
-DEVI void fwd2_range(F2State<HD> &st, const F2Issue<HD> &is, char *stage, int t0, int t1, int ntile, int jt0,
+template <int HD, typename TF, bool FULL>
+DEVI void fwd2_range(F2State<HD, TF> &st, const F2Issue<HD> &is, char *stage, int t0, int t1, int ntile, int jt0,
                      int pq, int lr, int lg, const AttnArgs &a) {
   using C = F2<HD>;
-  const float sl2 = a.scale * LOG2E_F, B = a.sbound;
+  const float sl2 = a.scale * LOG2E_F, B = a.sbound - P16Off<TF>::v;
   for (int t = t0; t < t1; ++t) {
     const int jt = jt0 + 32 * t;
     wait_vm<0>();
     __builtin_amdgcn_s_barrier();
-    Frag<bf16_t> kf[2][C::NC], vf[C::NH];
+    Frag<TF> kf[2][C::NC], vf[C::NH];
 #pragma unroll
     for (int c = 0; c < C::NC; ++c)
 #pragma unroll
@@ -476,7 +486,7 @@ DEVI void fwd2_range(F2State<HD> &st, const F2Issue<HD> &is, char *stage, int t0
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int qs = 0; qs < 4; ++qs) mma(S[ks][qs], kf[ks][c], st.qf[qs][c]);
-    Frag<bf16_t> pf[4];
+    Frag<TF> pf[4];
 #pragma unroll
     for (int qs = 0; qs < 4; ++qs) {
       const int p = pq + qs * 16 + lr;
@@ -502,7 +512,7 @@ DEVI void fwd2_range(F2State<HD> &st, const F2Issue<HD> &is, char *stage, int t0
   }
 }
 
-template <int HD>
+template <int HD, typename TF, typename TO>
 __global__ __launch_bounds__(NT, 2) void attn_fwd2_kernel(const AttnArgs a) {
   using C = F2<HD>;
   __shared__ __align__(1024) char stage[C::KB + C::VB];
@@ -527,9 +537,9 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd2_kernel(const AttnArgs a) {
   const int q_lo = qb * 256;
   const int pos0 = *a.pos0;
   const int qw = q_lo + wave * 64;
-  const bf16_t *Q = reinterpret_cast<const bf16_t *>(a.q);
+  const TF *Q = reinterpret_cast<const TF *>(a.q);
 
-  F2State<HD> st;
+  F2State<HD, TF> st;
 #pragma unroll
   for (int qs = 0; qs < 4; ++qs)
 #pragma unroll
@@ -571,8 +581,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd2_kernel(const AttnArgs a) {
   const int pq = pos0 + qw;
 
   F2Issue<HD> is;
-  is.init(reinterpret_cast<const bf16_t *>(a.K) + (long)h * a.R * HD,
-          reinterpret_cast<const bf16_t *>(a.Vt) + (long)h * HD * a.R, a.R, wave, lane);
+  is.init(reinterpret_cast<const TF *>(a.K) + (long)h * a.R * HD, reinterpret_cast<const TF *>(a.Vt) + (long)h * HD * a.R,
+          a.R, wave, lane);
   // tiles [f0, f1) are full for all four waves: every key at or before the
   // work-group's first query and inside its last query's window
   int f0, f1;
@@ -584,11 +594,11 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd2_kernel(const AttnArgs a) {
     f1 = min(max(f1, f0), ntile);
   }
   if (ntile > 0) is.run(stage, jt0 % a.R);
-  fwd2_range<HD, false>(st, is, stage, 0, f0, ntile, jt0, pq, lr, lg, a);
-  fwd2_range<HD, true>(st, is, stage, f0, f1, ntile, jt0, pq, lr, lg, a);
-  fwd2_range<HD, false>(st, is, stage, f1, ntile, ntile, jt0, pq, lr, lg, a);
+  fwd2_range<HD, TF, false>(st, is, stage, 0, f0, ntile, jt0, pq, lr, lg, a);
+  fwd2_range<HD, TF, true>(st, is, stage, f0, f1, ntile, jt0, pq, lr, lg, a);
+  fwd2_range<HD, TF, false>(st, is, stage, f1, ntile, ntile, jt0, pq, lr, lg, a);
 
-  bf16_t *Out = reinterpret_cast<bf16_t *>(a.o);
+  TO *Out = reinterpret_cast<TO *>(a.o);
 #pragma unroll
   for (int qs = 0; qs < 4; ++qs) {
     const float lt = group4_sum(st.lsum[qs]);
@@ -596,13 +606,13 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd2_kernel(const AttnArgs a) {
     if (q < a.n) {
       // a split may see no key of this query: weight 0 in the merge
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const float lse = lt > 0.f ? a.sbound + log2f(lt) : -INFINITY;
+      const float lse = lt > 0.f ? a.sbound - P16Off<TF>::v + log2f(lt) : -INFINITY;
       if (a.nsplit == 1) {
 #pragma unroll
         for (int hs = 0; hs < C::NH; ++hs) {
           float v[4] = {st.O[hs][qs][0] * inv, st.O[hs][qs][1] * inv, st.O[hs][qs][2] * inv,
                         st.O[hs][qs][3] * inv};
-          store4<bf16_t>(Out + (long)q * a.d + h * HD + hs * 16 + g4, v);
+          store4<TO>(Out + (long)q * a.d + h * HD + hs * 16 + g4, v);
         }
         if (lg == 0) a.lse2[(long)h * a.ldl + q] = lse;
       } else {
@@ -1148,12 +1158,32 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(const AttnArgs a) {
 
 template <typename T, int HD> hipError_t fwd_t(const AttnArgs &a, hipStream_t st) {
   dim3 grid((a.n + 127) / 128, a.H, a.nsplit);
-  hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(NT), 0, st, a);
+  // bf16 mode hands the O projection an fp16 operand; fp32 mode keeps fp32
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((attn_fwd_kernel<T, HD, f16_t>), grid, dim3(NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<T, HD, T>), grid, dim3(NT), 0, st, a);
   return hipGetLastError();
 }
+// explicit instantiations: clang otherwise may not emit the host launch stubs
+#define FWD2_INST(HD)                                                          \
+  template __global__ void attn_fwd2_kernel<HD, f16_t, f16_t>(const AttnArgs); \
+  template __global__ void attn_fwd2_kernel<HD, bf16_t, f16_t>(const AttnArgs);
+FWD2_INST(16)
+FWD2_INST(32)
+FWD2_INST(64)
+FWD2_INST(80)
+FWD2_INST(96)
+#undef FWD2_INST
+
 template <int HD> hipError_t fwd2_t(const AttnArgs &a, hipStream_t st) {
   dim3 grid((a.n + 255) / 256, a.H, a.nsplit);
-  hipLaunchKernelGGL((attn_fwd2_kernel<HD>), grid, dim3(NT), 0, st, a);
+  // bf16 mode always hands the O projection an fp16 operand
+  if (!a.o_f16) return hipErrorInvalidValue;
+  if (a.fwd_f16)
+    hipLaunchKernelGGL((attn_fwd2_kernel<HD, f16_t, f16_t>), grid, dim3(NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_fwd2_kernel<HD, bf16_t, f16_t>), grid, dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 template <int HD> hipError_t dq2_t(const AttnArgs &a, hipStream_t st) {
@@ -1257,6 +1287,8 @@ int attn_fwd_split(int dtype, float sbound, int hd, int n, int H, int window, in
   return std::max(1, std::min(s, 8));
 }
 
+bool attn_fwd_f16_ok(int dtype, float sbound, int hd) { return bounded(dtype, sbound, hd) && sbound <= 14.5f; }
+
 bool attn_supported_hd(int hd) { return hd == 16 || hd == 32 || hd == 64 || hd == 80 || hd == 96 || hd == 128; }
 
 hipError_t attn_fwd_launch(int dtype, int hd, const AttnArgs &a, hipStream_t st) {
@@ -1273,6 +1305,8 @@ hipError_t attn_merge_launch(int dtype, int hd, bool dq, const AttnArgs &a, hipS
   const dim3 grid((unsigned)((tot + 255) / 256));
   if (dq)
     hipLaunchKernelGGL(attn_dq_merge_kernel, grid, dim3(256), 0, st, a);
+  else if (a.o_f16)
+    hipLaunchKernelGGL((attn_fwd_merge_kernel<f16_t>), grid, dim3(256), 0, st, a, hd);
   else if (dtype == 1)
     hipLaunchKernelGGL((attn_fwd_merge_kernel<bf16_t>), grid, dim3(256), 0, st, a, hd);
   else

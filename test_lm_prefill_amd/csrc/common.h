@@ -4,18 +4,26 @@
 #include <stdint.h>
 
 typedef uint16_t bf16_t;  // raw bfloat16 storage
+// raw IEEE half storage (a distinct type so that templates can tell it from bf16)
+struct f16_t {
+  uint16_t x;
+};
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_v __attribute__((ext_vector_type(8)));
 typedef float f32x4_v __attribute__((ext_vector_type(4)));
 
 #define DEVI __device__ __forceinline__
 
 DEVI float to_f(float x) { return x; }
 DEVI float to_f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+DEVI float to_f(f16_t x) { return (float)__builtin_bit_cast(_Float16, x.x); }
 
 template <typename T> DEVI T from_f(float f);
 template <> DEVI float from_f<float>(float f) { return f; }
 // float -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 template <> DEVI bf16_t from_f<bf16_t>(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+// float -> half, round to nearest even.
+template <> DEVI f16_t from_f<f16_t>(float f) { return f16_t{__builtin_bit_cast(uint16_t, (_Float16)f)}; }
 
 // ---------------------------------------------------------------------------
 // MFMA fragments.  A fragment is the 8 consecutive reduction-dim elements one
@@ -26,13 +34,19 @@ template <> DEVI bf16_t from_f<bf16_t>(float f) { return __builtin_bit_cast(bf16
 // bf16 uses one v_mfma_f32_16x16x32_bf16; fp32 issues eight
 // v_mfma_f32_16x16x4_f32, instruction j taking element j of every lane
 // group, which sums the same 32 products in another order.
+// f16 (v_mfma_f32_16x16x32_f16) has the same layout and rate as bf16.
 template <typename T> struct Frag;
 template <> struct Frag<bf16_t> { uint4 v; };
+template <> struct Frag<f16_t> { uint4 v; };
 template <> struct Frag<float> { float4 lo, hi; };
 
 DEVI void mma(f32x4_v &acc, const Frag<bf16_t> &a, const Frag<bf16_t> &b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a.v),
                                                 __builtin_bit_cast(bf16x8_v, b.v), acc, 0, 0, 0);
+}
+DEVI void mma(f32x4_v &acc, const Frag<f16_t> &a, const Frag<f16_t> &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_v, a.v), __builtin_bit_cast(f16x8_v, b.v),
+                                               acc, 0, 0, 0);
 }
 DEVI void mma(f32x4_v &acc, const Frag<float> &a, const Frag<float> &b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, acc, 0, 0, 0);
@@ -47,6 +61,7 @@ DEVI void mma(f32x4_v &acc, const Frag<float> &a, const Frag<float> &b) {
 
 // Load a fragment of 8 contiguous elements.
 DEVI void load_frag(Frag<bf16_t> &f, const bf16_t *p) { f.v = *reinterpret_cast<const uint4 *>(p); }
+DEVI void load_frag(Frag<f16_t> &f, const f16_t *p) { f.v = *reinterpret_cast<const uint4 *>(p); }
 DEVI void load_frag(Frag<float> &f, const float *p) {
   f.lo = *reinterpret_cast<const float4 *>(p);
   f.hi = *reinterpret_cast<const float4 *>(p + 4);
@@ -62,6 +77,7 @@ DEVI void load_frag2(Frag<float> &f, const float *p, const float *q) {
   f.hi = *reinterpret_cast<const float4 *>(q);
 }
 DEVI void zero_frag(Frag<bf16_t> &f) { f.v = make_uint4(0, 0, 0, 0); }
+DEVI void zero_frag(Frag<f16_t> &f) { f.v = make_uint4(0, 0, 0, 0); }
 DEVI void zero_frag(Frag<float> &f) {
   f.lo = make_float4(0, 0, 0, 0);
   f.hi = f.lo;
@@ -72,10 +88,18 @@ typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 DEVI uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{a, b}, bf16x2_v));
 }
+typedef _Float16 f16x2_v __attribute__((ext_vector_type(2)));
+// Two floats -> two halves (round to nearest even) in one v_cvt_pk_f16_f32.
+DEVI uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{a, b}, f16x2_v));
+}
 // Fragment from 8 floats (rounded to T).
 DEVI void pack_frag(Frag<bf16_t> &f, const float *x) {
   f.v = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                    pack_bf16x2(x[6], x[7]));
+}
+DEVI void pack_frag(Frag<f16_t> &f, const float *x) {
+  f.v = make_uint4(pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]), pack_f16x2(x[4], x[5]), pack_f16x2(x[6], x[7]));
 }
 DEVI void pack_frag(Frag<float> &f, const float *x) {
   f.lo = make_float4(x[0], x[1], x[2], x[3]);
@@ -89,6 +113,9 @@ template <> DEVI void store4<float>(float *p, const float *v) {
 }
 template <> DEVI void store4<bf16_t>(bf16_t *p, const float *v) {
   *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+template <> DEVI void store4<f16_t>(f16_t *p, const float *v) {
+  *reinterpret_cast<uint2 *>(p) = make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]));
 }
 
 // 16-byte vector of T (8 bf16 or 4 fp32).

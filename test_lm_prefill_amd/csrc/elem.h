@@ -9,8 +9,10 @@ hipError_t embed_launch(int dtype, const void *E, const int *tok, const int *pos
                         hipStream_t st);
 
 // y = x * r * g, r = (mean(x^2) + eps)^-1/2 per row; optional r_out [n] and x_copy [n, d].
+// g has the working dtype; y too, or fp16 when y_f16 (bf16 mode's forward GEMM operand).
+// d <= 8192.
 hipError_t rmsnorm_fwd_launch(int dtype, const float *x, const void *g, void *y, float *r_out, float *x_copy,
-                              int n, int d, float eps, hipStream_t st);
+                              int n, int d, float eps, hipStream_t st, bool y_f16 = false);
 
 // dh_out = dh_in + r * (g*dy) - x * r^3 * mean(x * g*dy)   (dh_in may be NULL or alias dh_out);
 // also writes dh_t, the same values in the working dtype.
@@ -25,9 +27,15 @@ struct RopeArgs {
   int n, d, H, hd, R;
   float eps;
   // forward outputs
-  void *qh;             // [n][d]
+  void *qh;             // [n][d] forward type
+  void *qhb;            // [n][d] working-dtype copy of qh (backward) or NULL
   void *qht;            // [H][hd][ldt] or NULL
-  void *K, *Vt, *Kt, *V;  // ring planes (Kt, V may be NULL)
+  // ring planes: K [H][R][hd] and Vt [H][hd][R] in the forward type (fp16 when
+  // fwd_f16, else the working dtype), used by the forward attention and the
+  // score recomputation; Kb [H][R][hd], Kt [H][hd][R] and V [H][R][hd] in the
+  // working dtype for the backward (each may be NULL)
+  void *K, *Vt, *Kb, *Kt, *V;
+  int fwd_f16;          // qh, K and Vt are fp16
   int ldt;
   // backward inputs / output
   const float *dqh, *dkh, *dv;  // [n][d]
@@ -37,8 +45,9 @@ hipError_t qk_rope_fwd_launch(int dtype, const RopeArgs &a, hipStream_t st);
 hipError_t qk_rope_bwd_launch(int dtype, const RopeArgs &a, hipStream_t st);
 
 // Dq[h, q] = sum_i dO[q, h, i] * O[q, h, i];  dOt[h, i, q] = dO[q, h, i].
+// O is fp16 when o_f16 (the forward output), else the working dtype.
 hipError_t attn_bwd_pre_launch(int dtype, const void *dO, const void *O, float *Dq, void *dOt, int n, int d,
-                               int H, int hd, int ldl, int ldt, hipStream_t st);
+                               int H, int hd, int ldl, int ldt, hipStream_t st, bool o_f16);
 
 // SwiGLU backward over 16-row interleaved gate/up blocks.  GU [n][ld_gu],
 // dhmid [n][ld_h] (units), dGU [n][ld_gu]; `units` hidden units processed.
@@ -55,7 +64,7 @@ hipError_t rope_table_launch(float2 *cs, long max_pos, int hd, double theta, hip
 
 // dst[r * ld_dst + c] = hi = (T) src[r * ld_src + c]; when lo is given also
 // lo[r * ld_lo + c] = (T) (src - hi), so that hi + lo carries the fp32 value to
-// about 16 significant bits in bf16.
+// about 16 (bf16) or 22 (fp16) significant bits.  dtype 2 writes fp16.
 hipError_t convert_rows_launch(int dtype, const float *src, long ld_src, void *dst, long ld_dst, int rows, int cols,
                                hipStream_t st, void *lo = nullptr, long ld_lo = 0);
 // dst (T) = src (T) copies with row strides.
@@ -63,10 +72,14 @@ hipError_t copy_rows_launch(int dtype, const void *src, long ld_src, void *dst, 
                             hipStream_t st);
 
 // dst[c * ldd + r] = r < R ? src[r * lds + c] : 0 for r < Rpad, c < C.  The
-// destination has the working dtype; the source is fp32 when src_f32 (always
-// in fp32 mode), else the working dtype.
-hipError_t transpose_launch(int dtype, bool src_f32, const void *src, long lds, void *dst, long ldd, int R, int Rpad,
+// destination has the working dtype; the source is fp32 (SRC_F32, always in
+// fp32 mode), the working dtype (SRC_WORK) or fp16 (SRC_F16, bf16 mode).
+enum { SRC_F32 = 0, SRC_WORK = 1, SRC_F16 = 2 };
+hipError_t transpose_launch(int dtype, int src_kind, const void *src, long lds, void *dst, long ldd, int R, int Rpad,
                             int C, hipStream_t st);
+// dst (fp16) = src (bf16), exactly for the weight magnitudes in use (|x| in the
+// fp16 normal range), with row strides.
+hipError_t bf16_to_f16_launch(const void *src, long lds, void *dst, long ldd, int rows, int cols, hipStream_t st);
 
 hipError_t set_int_launch(int *p, int v, hipStream_t st);
 hipError_t add_int_launch(int *p, int v, hipStream_t st);

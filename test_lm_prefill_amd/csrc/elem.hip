@@ -12,6 +12,11 @@ template <> DEVI void load4<float>(const float *p, float *v) {
   float4 x = *reinterpret_cast<const float4 *>(p);
   v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
 }
+template <> DEVI void load4<f16_t>(const f16_t *p, float *v) {
+  uint2 x = *reinterpret_cast<const uint2 *>(p);
+  v[0] = to_f(f16_t{(uint16_t)(x.x & 0xFFFF)}); v[1] = to_f(f16_t{(uint16_t)(x.x >> 16)});
+  v[2] = to_f(f16_t{(uint16_t)(x.y & 0xFFFF)}); v[3] = to_f(f16_t{(uint16_t)(x.y >> 16)});
+}
 template <> DEVI void load4<bf16_t>(const bf16_t *p, float *v) {
   uint2 x = *reinterpret_cast<const uint2 *>(p);
   v[0] = to_f((bf16_t)(x.x & 0xFFFF)); v[1] = to_f((bf16_t)(x.x >> 16));
@@ -33,8 +38,8 @@ __global__ __launch_bounds__(256) void embed_kernel(const T *E, const int *tok, 
 // ----------------------------------------------------------------- RMSNorm
 // One wave per row; the row stays in registers (NV float4 per lane, d <= 256 NV)
 // so x (and dy) are read from HBM once.  Four rows per 256-thread block.
-template <typename T, int NV>
-__global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float *x, const T *g, T *y, float *r_out,
+template <typename T, typename TY, int NV>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float *x, const T *g, TY *y, float *r_out,
                                                           float *x_copy, int n, int d, float eps) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -57,7 +62,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float *x, const 
       float gv[4];
       load4<T>(g + i, gv);
       float out[4] = {v[k].x * r * gv[0], v[k].y * r * gv[1], v[k].z * r * gv[2], v[k].w * r * gv[3]};
-      store4<T>(y + o + i, out);
+      store4<TY>(y + o + i, out);
       if (x_copy) *reinterpret_cast<float4 *>(x_copy + o + i) = v[k];
     }
   }
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float *dy, const
 // ----------------------------------------------------------------- QK-norm + rotary (+ ring write)
 // grid (ceil(n/32), H); wave w handles tokens 8w..8w+7 of the block; lane
 // i < hd/2 handles the rotary pair (i, i + hd/2).
-template <typename T>
+template <typename T, typename TF>
 __global__ __launch_bounds__(256) void qk_rope_fwd_kernel(const RopeArgs a) {
   extern __shared__ float sm[];  // [3][hd][33]: Vt, Kt, Qt tiles
   const int hd = a.hd, half = hd / 2, h = blockIdx.y, t0 = blockIdx.x * 32;
@@ -144,13 +149,23 @@ __global__ __launch_bounds__(256) void qk_rope_fwd_kernel(const RopeArgs a) {
       const float qa = qi * rq * gqi, qb = qj * rq * gqj, ka = ki * rk * gki, kb = kj * rk * gkj;
       const float q1 = qa * cs.x - qb * cs.y, q2 = qa * cs.y + qb * cs.x;
       const float k1 = ka * cs.x - kb * cs.y, k2 = ka * cs.y + kb * cs.x;
-      T *qh = reinterpret_cast<T *>(a.qh) + (long)t * a.d + h * hd;
-      qh[lane] = from_f<T>(q1);
-      qh[lane + half] = from_f<T>(q2);
+      TF *qh = reinterpret_cast<TF *>(a.qh) + (long)t * a.d + h * hd;
+      qh[lane] = from_f<TF>(q1);
+      qh[lane + half] = from_f<TF>(q2);
+      if (a.qhb) {
+        T *qb = reinterpret_cast<T *>(a.qhb) + (long)t * a.d + h * hd;
+        qb[lane] = from_f<T>(q1);
+        qb[lane + half] = from_f<T>(q2);
+      }
       const long slot = p % a.R;
-      T *kr = reinterpret_cast<T *>(a.K) + ((long)h * a.R + slot) * hd;
-      kr[lane] = from_f<T>(k1);
-      kr[lane + half] = from_f<T>(k2);
+      TF *kr = reinterpret_cast<TF *>(a.K) + ((long)h * a.R + slot) * hd;
+      kr[lane] = from_f<TF>(k1);
+      kr[lane + half] = from_f<TF>(k2);
+      if (a.Kb) {
+        T *kb = reinterpret_cast<T *>(a.Kb) + ((long)h * a.R + slot) * hd;
+        kb[lane] = from_f<T>(k1);
+        kb[lane + half] = from_f<T>(k2);
+      }
       if (a.V) {
         T *vr = reinterpret_cast<T *>(a.V) + ((long)h * a.R + slot) * hd;
         vr[lane] = from_f<T>(vi);
@@ -168,7 +183,7 @@ __global__ __launch_bounds__(256) void qk_rope_fwd_kernel(const RopeArgs a) {
     if (tl >= cnt) continue;
     const int t = t0 + tl;
     const long slot = (pos0 + t) % a.R;
-    reinterpret_cast<T *>(a.Vt)[((long)h * hd + dim) * a.R + slot] = from_f<T>(sV[dim * 33 + tl]);
+    reinterpret_cast<TF *>(a.Vt)[((long)h * hd + dim) * a.R + slot] = from_f<TF>(sV[dim * 33 + tl]);
     if (a.Kt) reinterpret_cast<T *>(a.Kt)[((long)h * hd + dim) * a.R + slot] = from_f<T>(sK[dim * 33 + tl]);
     if (a.qht) reinterpret_cast<T *>(a.qht)[((long)h * hd + dim) * a.ldt + t] = from_f<T>(sQ[dim * 33 + tl]);
   }
@@ -218,8 +233,8 @@ __global__ __launch_bounds__(256) void qk_rope_bwd_kernel(const RopeArgs a) {
 }
 
 // ----------------------------------------------------------------- attention backward pre-pass
-template <typename T>
-__global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const T *dO, const T *O, float *Dq, T *dOt, int n, int d,
+template <typename T, typename TO>
+__global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const T *dO, const TO *O, float *Dq, T *dOt, int n, int d,
                                                            int hd, int ldl, int ldt) {
   extern __shared__ float sm[];  // [hd][65]
   const int h = blockIdx.y, t0 = blockIdx.x * 64;
@@ -341,6 +356,13 @@ __global__ __launch_bounds__(256) void transpose_kernel(const S *src, long lds, 
   }
 }
 
+__global__ void bf16_to_f16_kernel(const bf16_t *src, long lds, f16_t *dst, long ldd, int rows, int cols) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)rows * cols) return;
+  const int r = idx / cols, c = idx % cols;
+  dst[(long)r * ldd + c] = from_f<f16_t>(to_f(src[(long)r * lds + c]));
+}
+
 __global__ void set_int_kernel(int *p, int v) { *p = v; }
 __global__ void add_int_kernel(int *p, int v) { *p += v; }
 __global__ void zero_kernel(uint32_t *p, size_t words) {
@@ -386,14 +408,18 @@ hipError_t embed_launch(int dtype, const void *E, const int *tok, const int *pos
   else return hipErrorInvalidValue;
 
 hipError_t rmsnorm_fwd_launch(int dtype, const float *x, const void *g, void *y, float *r_out, float *x_copy, int n,
-                              int d, float eps, hipStream_t st) {
+                              int d, float eps, hipStream_t st, bool y_f16) {
+  if (y_f16 && dtype != 1) return hipErrorInvalidValue;
   if (n <= 0) return hipSuccess;
 #define CALL_(NV)                                                                                                  \
-  if (dtype == 1)                                                                                                  \
-    hipLaunchKernelGGL((rmsnorm_fwd_kernel<bf16_t, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, x,             \
+  if (dtype == 1 && y_f16)                                                                                         \
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<bf16_t, f16_t, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, x,      \
+                       (const bf16_t *)g, (f16_t *)y, r_out, x_copy, n, d, eps);                                   \
+  else if (dtype == 1)                                                                                             \
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<bf16_t, bf16_t, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, x,     \
                        (const bf16_t *)g, (bf16_t *)y, r_out, x_copy, n, d, eps);                                  \
   else                                                                                                             \
-    hipLaunchKernelGGL((rmsnorm_fwd_kernel<float, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, x,              \
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<float, float, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, x,       \
                        (const float *)g, (float *)y, r_out, x_copy, n, d, eps);
   NV_DISPATCH(d, CALL_)
 #undef CALL_
@@ -419,7 +445,11 @@ hipError_t qk_rope_fwd_launch(int dtype, const RopeArgs &a, hipStream_t st) {
   if (a.n <= 0) return hipSuccess;
   size_t shm = (size_t)3 * a.hd * 33 * sizeof(float);
   dim3 grid(blocks_for(a.n, 32), a.H);
-#define K_(T, ...) hipLaunchKernelGGL(qk_rope_fwd_kernel<T>, grid, dim3(256), shm, st, a)
+#define K_(T, ...)                                                                     \
+  if (a.fwd_f16)                                                                       \
+    hipLaunchKernelGGL((qk_rope_fwd_kernel<T, f16_t>), grid, dim3(256), shm, st, a);  \
+  else                                                                                 \
+    hipLaunchKernelGGL((qk_rope_fwd_kernel<T, T>), grid, dim3(256), shm, st, a)
   DT_DISPATCH(dtype, K_, 0);
 #undef K_
   return hipGetLastError();
@@ -435,13 +465,17 @@ hipError_t qk_rope_bwd_launch(int dtype, const RopeArgs &a, hipStream_t st) {
 }
 
 hipError_t attn_bwd_pre_launch(int dtype, const void *dO, const void *O, float *Dq, void *dOt, int n, int d, int H,
-                               int hd, int ldl, int ldt, hipStream_t st) {
+                               int hd, int ldl, int ldt, hipStream_t st, bool o_f16) {
   if (n <= 0) return hipSuccess;
   size_t shm = (size_t)hd * 65 * sizeof(float);
   dim3 grid(blocks_for(n, 64), H);
-#define K_(T, ...)                                                                                              \
-  hipLaunchKernelGGL(attn_bwd_pre_kernel<T>, grid, dim3(256), shm, st, (const T *)dO, (const T *)O, Dq, (T *)dOt, n, \
-                     d, hd, ldl, ldt)
+#define K_(T, ...)                                                                                                \
+  if (o_f16)                                                                                                      \
+    hipLaunchKernelGGL((attn_bwd_pre_kernel<T, f16_t>), grid, dim3(256), shm, st, (const T *)dO, (const f16_t *)O, \
+                       Dq, (T *)dOt, n, d, hd, ldl, ldt);                                                         \
+  else                                                                                                            \
+    hipLaunchKernelGGL((attn_bwd_pre_kernel<T, T>), grid, dim3(256), shm, st, (const T *)dO, (const T *)O, Dq,     \
+                       (T *)dOt, n, d, hd, ldl, ldt)
   DT_DISPATCH(dtype, K_, 0);
 #undef K_
   return hipGetLastError();
@@ -476,6 +510,11 @@ hipError_t convert_rows_launch(int dtype, const float *src, long ld_src, void *d
                                hipStream_t st, void *lo, long ld_lo) {
   long tot = (long)rows * cols;
   if (tot <= 0) return hipSuccess;
+  if (dtype == 2) {
+    hipLaunchKernelGGL(convert_rows_kernel<f16_t>, dim3(blocks_for(tot)), dim3(256), 0, st, src, ld_src, (f16_t *)dst,
+                       ld_dst, (f16_t *)lo, ld_lo, rows, cols);
+    return hipGetLastError();
+  }
 #define K_(T, ...)                                                                                               \
   hipLaunchKernelGGL(convert_rows_kernel<T>, dim3(blocks_for(tot)), dim3(256), 0, st, src, ld_src, (T *)dst, ld_dst, \
                      (T *)lo, ld_lo, rows, cols)
@@ -496,13 +535,16 @@ hipError_t copy_rows_launch(int dtype, const void *src, long ld_src, void *dst, 
   return hipGetLastError();
 }
 
-hipError_t transpose_launch(int dtype, bool src_f32, const void *src, long lds, void *dst, long ldd, int R, int Rpad,
+hipError_t transpose_launch(int dtype, int src_kind, const void *src, long lds, void *dst, long ldd, int R, int Rpad,
                             int C, hipStream_t st) {
   if (Rpad <= 0 || C <= 0) return hipSuccess;
   dim3 grid((C + 63) / 64, (Rpad + 63) / 64);
   if (dtype == 1) {
-    if (src_f32)
+    if (src_kind == SRC_F32)
       hipLaunchKernelGGL((transpose_kernel<float, bf16_t>), grid, dim3(256), 0, st, (const float *)src, lds,
+                         (bf16_t *)dst, ldd, R, Rpad, C);
+    else if (src_kind == SRC_F16)
+      hipLaunchKernelGGL((transpose_kernel<f16_t, bf16_t>), grid, dim3(256), 0, st, (const f16_t *)src, lds,
                          (bf16_t *)dst, ldd, R, Rpad, C);
     else
       hipLaunchKernelGGL((transpose_kernel<bf16_t, bf16_t>), grid, dim3(256), 0, st, (const bf16_t *)src, lds,
@@ -511,6 +553,14 @@ hipError_t transpose_launch(int dtype, bool src_f32, const void *src, long lds, 
     hipLaunchKernelGGL((transpose_kernel<float, float>), grid, dim3(256), 0, st, (const float *)src, lds,
                        (float *)dst, ldd, R, Rpad, C);
   }
+  return hipGetLastError();
+}
+
+hipError_t bf16_to_f16_launch(const void *src, long lds, void *dst, long ldd, int rows, int cols, hipStream_t st) {
+  const long tot = (long)rows * cols;
+  if (tot <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bf16_to_f16_kernel, dim3(blocks_for(tot)), dim3(256), 0, st, (const bf16_t *)src, lds,
+                     (f16_t *)dst, ldd, rows, cols);
   return hipGetLastError();
 }
 

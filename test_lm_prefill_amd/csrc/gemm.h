@@ -41,12 +41,17 @@ struct GemmArgs {
   // that multiply the same activations (a multiple of 64, or of 8 for the
   // generic kernel)
   int a_kwrap;
+  // 16-bit outputs (C, and C2 of EPI_SGD) are written as fp16 instead of bf16;
+  // EPI_SWIGLU's C2 (pre-activations kept for the backward) stays bf16
+  int c_f16;
   // split-K (internal)
   int ksplit;
   float *ws;
 };
 
-// dtype: 0 = fp32, 1 = bf16.  a_kc / b_kc select the operand layouts.
+// dtype (operand type): 0 = fp32, 1 = bf16, 2 = fp16.  a_kc / b_kc select the
+// operand layouts.  fp16 operands need the streaming kernel's shapes (both
+// k-contiguous, K and a_kwrap multiples of 64, leading dimensions multiples of 8).
 // For EPI_STORE / EPI_STORE_F32 / EPI_ADD_F32 the launcher may split K over
 // several work-groups into `ws` (fp32, ws_elems entries) and reduce in a fixed
 // order, which keeps results deterministic.

@@ -392,10 +392,11 @@ hipError_t reduce_launch(int epi, const GemmArgs &g, int S, hipStream_t st) {
 
 size_t gemm_ws_elems(int M, int N) { return (size_t)8 * M * N; }
 
-hipError_t gemm_dma_launch(int epi, const GemmArgs &g, hipStream_t st);
+hipError_t gemm_dma_launch(bool f16, int epi, const GemmArgs &g, hipStream_t st);
 
 static bool use_dma(int dtype, bool a_kc, bool b_kc, const GemmArgs &g) {
-  return dtype == 1 && a_kc && b_kc && g.K % 64 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.a_kwrap % 64 == 0;
+  return (dtype == 1 || dtype == 2) && a_kc && b_kc && g.K % 64 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+         g.a_kwrap % 64 == 0;
 }
 
 int gemm_plan(int dtype, bool a_kc, bool b_kc, int epi, const GemmArgs &g, size_t ws_elems, int force_split) {
@@ -432,7 +433,8 @@ hipError_t gemm_main_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g
   g.ws = ws;
   // the wrapped activation operand must be k-contiguous, whole 16-byte vectors
   if (g.a_kwrap < 0 || (g.a_kwrap > 0 && (!a_kc || g.a_kwrap % 8 != 0))) return hipErrorInvalidValue;
-  if (use_dma(dtype, a_kc, b_kc, g)) return gemm_dma_launch(epi, g, st);
+  if (use_dma(dtype, a_kc, b_kc, g)) return gemm_dma_launch(dtype == 2, epi, g, st);
+  if (dtype == 2 || g.c_f16) return hipErrorInvalidValue;
   return dtype == 1 ? dispatch_layout<bf16_t>(a_kc, b_kc, epi, g, st, split)
                     : dispatch_layout<float>(a_kc, b_kc, epi, g, st, split);
 }
@@ -440,7 +442,8 @@ hipError_t gemm_main_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g
 hipError_t gemm_reduce_launch(int dtype, int epi, GemmArgs g, float *ws, int split, hipStream_t st) {
   if (split <= 1) return hipSuccess;
   g.ws = ws;
-  return dtype == 1 ? reduce_launch<bf16_t>(epi, g, split, st) : reduce_launch<float>(epi, g, split, st);
+  if (g.c_f16) return reduce_launch<f16_t>(epi, g, split, st);
+  return dtype == 0 ? reduce_launch<float>(epi, g, split, st) : reduce_launch<bf16_t>(epi, g, split, st);
 }
 
 hipError_t gemm_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, float *ws, size_t ws_elems,

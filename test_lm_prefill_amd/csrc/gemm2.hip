@@ -42,6 +42,14 @@ DEVI int remap_tile2(int i, int T) {
   return x * q + min(x, rem) + j;
 }
 
+// 16-bit output in the type the caller asked for (fp16 or bf16).
+DEVI void store_c4(const GemmArgs &g, void *base, long off, const float *v) {
+  if (g.c_f16)
+    store4<f16_t>(reinterpret_cast<f16_t *>(base) + off, v);
+  else
+    store4<bf16_t>(reinterpret_cast<bf16_t *>(base) + off, v);
+}
+
 template <int BN, int EPI, typename Acc>
 DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, int wm, int wn, int lr, int lq) {
   constexpr int NI = G2<BN>::NI, WN = G2<BN>::WN;
@@ -80,7 +88,6 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
     return;
   }
   if constexpr (EPI == EPI_SWIGLU) {
-    bf16_t *Hm = reinterpret_cast<bf16_t *>(g.C);
     bf16_t *GU = reinterpret_cast<bf16_t *>(g.C2);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -98,7 +105,7 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
           uv[r] = acc[i + 1][j][r];
           hv[r] = gv[r] / (1.f + __expf(-gv[r])) * uv[r];
         }
-        store4<bf16_t>(Hm + (long)m * g.ldc + unit, hv);
+        store_c4(g, g.C, (long)m * g.ldc + unit, hv);
         if (GU) {
           store4<bf16_t>(GU + (long)m * g.ldc2 + nb + g4, gv);
           store4<bf16_t>(GU + (long)m * g.ldc2 + nb + 16 + g4, uv);
@@ -123,7 +130,7 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
       if (n >= g.N) continue;
       float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
       if constexpr (EPI == EPI_STORE) {
-        store4<bf16_t>(reinterpret_cast<bf16_t *>(g.C) + (long)m * g.ldc + n, v);
+        store_c4(g, g.C, (long)m * g.ldc + n, v);
       } else if constexpr (EPI == EPI_STORE_F32) {
         store4<float>(g.Cf + (long)m * g.ldcf + n, v);
       } else if constexpr (EPI == EPI_ADD_F32) {
@@ -139,18 +146,19 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
           const float p = __expf(v[r] - lse);
           d[r] = (p - ((n + r + g.col_off == lab) ? 1.f : 0.f)) * g.alpha;
         }
-        store4<bf16_t>(reinterpret_cast<bf16_t *>(g.C) + (long)m * g.ldc + n, d);
+        store_c4(g, g.C, (long)m * g.ldc + n, d);
       } else if constexpr (EPI == EPI_SGD) {
         float4 *pw = reinterpret_cast<float4 *>(g.Cf + (long)m * g.ldcf + n);
         const float4 w = *pw;
         float nw[4] = {w.x - g.alpha * v[0], w.y - g.alpha * v[1], w.z - g.alpha * v[2], w.w - g.alpha * v[3]};
         *pw = make_float4(nw[0], nw[1], nw[2], nw[3]);
-        store4<bf16_t>(reinterpret_cast<bf16_t *>(g.C) + (long)m * g.ldc + n, nw);
+        store_c4(g, g.C, (long)m * g.ldc + n, nw);
         if (g.C2) {
           float lo[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) lo[r] = nw[r] - to_f(from_f<bf16_t>(nw[r]));
-          store4<bf16_t>(reinterpret_cast<bf16_t *>(g.C2) + (long)m * g.ldc2 + n, lo);
+          for (int r = 0; r < 4; ++r)
+            lo[r] = nw[r] - (g.c_f16 ? to_f(from_f<f16_t>(nw[r])) : to_f(from_f<bf16_t>(nw[r])));
+          store_c4(g, g.C2, (long)m * g.ldc2 + n, lo);
         }
       }
     }
@@ -215,7 +223,8 @@ typedef int v4i_t __attribute__((ext_vector_type(4)));
 // direct-to-LDS writes still in flight into the other stage (it would wait for
 // those before every read).  Visibility of the stage is ordered by the
 // caller's explicit vector-memory wait and barrier.
-DEVI void read_step_128(Frag<bf16_t> (&fw)[2][4], Frag<bf16_t> (&fx)[2][4], uint32_t w0, uint32_t w1, uint32_t x0,
+template <typename TI>
+DEVI void read_step_128(Frag<TI> (&fw)[2][4], Frag<TI> (&fx)[2][4], uint32_t w0, uint32_t w1, uint32_t x0,
                         uint32_t x1) {
   v4i_t a0, a1, a2, a3, b0, b1, b2, b3, c0, c1, c2, c3, d0, d1, d2, d3;
   asm volatile(
@@ -262,6 +271,7 @@ DEVI void read_step_128(Frag<bf16_t> (&fw)[2][4], Frag<bf16_t> (&fx)[2][4], uint
 // the tiles of steps kt+1 and kt+2 are in flight.  Per step: wait for this
 // wave's loads of step kt, barrier, read the step's fragments, barrier (the
 // stage is free), stream step kt+2 into it, MFMAs.
+template <typename TI>
 __global__ __launch_bounds__(NT, 2) void gemm5_kernel(const GemmArgs g, int epi) {
   using C = G2<128>;
   constexpr int SBYTES = C::SBYTES;
@@ -305,8 +315,8 @@ __global__ __launch_bounds__(NT, 2) void gemm5_kernel(const GemmArgs g, int epi)
       wait_vm<0>();
     __builtin_amdgcn_s_barrier();
     const uint32_t so = smb + (kt & 1) * SBYTES;
-    Frag<bf16_t> fw[2][4], fx[2][4];
-    read_step_128(fw, fx, so + aw0, so + aw1, so + ax0, so + ax1);
+    Frag<TI> fw[2][4], fx[2][4];
+    read_step_128<TI>(fw, fx, so + aw0, so + aw1, so + ax0, so + ax1);
     __builtin_amdgcn_s_barrier();
     if (kt + 2 < nk) is.run(kt + 2, (kt & 1) * SBYTES);
 #pragma unroll
@@ -328,9 +338,12 @@ __global__ __launch_bounds__(NT, 2) void gemm5_kernel(const GemmArgs g, int epi)
   }
 }
 
-hipError_t launch5(int epi, const GemmArgs &g, hipStream_t st) {
+template __global__ void gemm5_kernel<bf16_t>(const GemmArgs, int);
+template __global__ void gemm5_kernel<f16_t>(const GemmArgs, int);
+
+template <typename TI> hipError_t launch5(int epi, const GemmArgs &g, hipStream_t st) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + 127) / 128);
-  hipLaunchKernelGGL(gemm5_kernel, dim3(tiles, 1, g.ksplit), dim3(NT), 0, st, g, g.ksplit > 1 ? 100 : epi);
+  hipLaunchKernelGGL((gemm5_kernel<TI>), dim3(tiles, 1, g.ksplit), dim3(NT), 0, st, g, g.ksplit > 1 ? 100 : epi);
   return hipGetLastError();
 }
 
@@ -340,4 +353,6 @@ using namespace ttt_g2;
 // bf16, both operands k-contiguous with 16-byte aligned rows, K a multiple of
 // 64.  g.ksplit > 1 writes fp32 partials to g.ws (the caller reduces them in a
 // fixed order).
-hipError_t gemm_dma_launch(int epi, const GemmArgs &g, hipStream_t st) { return launch5(epi, g, st); }
+hipError_t gemm_dma_launch(bool f16, int epi, const GemmArgs &g, hipStream_t st) {
+  return f16 ? launch5<f16_t>(epi, g, st) : launch5<bf16_t>(epi, g, st);
+}

@@ -47,7 +47,10 @@ struct LayerBuf {
   int u = -1;
   float sbound = 0.f;  // bound of the scaled scores (log2 units) for the bounded forward, 0 = none
   int fsplit = 1;      // key-range split of the forward
-  void *K = nullptr, *Vt = nullptr, *Kt = nullptr, *V = nullptr;  // ring planes
+  bool fwd16 = false;  // attention forward operands (q, ring K and V^T) are fp16
+  // ring planes: K, Vt in the attention forward's type; Kb (bf16 copy of K when the
+  // forward is fp16), Kt, V in the working dtype for the backward
+  void *K = nullptr, *Vt = nullptr, *Kb = nullptr, *Kt = nullptr, *V = nullptr;
   // transposed working copies used by the backward GEMMs (k-contiguous operands)
   void *wdT = nullptr;    // [2F][d]  (fast units first), updated layers
   void *wguT = nullptr;   // [d][4F], updated layers
@@ -58,7 +61,8 @@ struct LayerBuf {
 struct Saved {
   float *h_in = nullptr, *r1 = nullptr, *lse2 = nullptr, *h1 = nullptr, *r2 = nullptr;
   float *qkv = nullptr;  // [b][3d] fp32
-  void *qh = nullptr, *qht = nullptr, *o = nullptr, *m = nullptr, *gu = nullptr, *hmid = nullptr;
+  // qh: forward q (attention forward type); qhb / qht: working-dtype copies for the backward
+  void *qh = nullptr, *qhb = nullptr, *qht = nullptr, *o = nullptr, *m = nullptr, *gu = nullptr, *hmid = nullptr;
 };
 
 }  // namespace
@@ -198,15 +202,17 @@ void prof_collect(ttt_handle *h, hipStream_t st) {
 }
 #define PROF(cls) Prof prof_(h, cls, st)
 
-void gemm(ttt_handle *h, int cls, bool akc, bool bkc, int epi, GemmArgs g, hipStream_t st) {
-  const int split = gemm_plan(h->dt, akc, bkc, epi, g, h->ws_elems);
+// fwd: the operands are forward activations and weights, fp16 in bf16 mode
+void gemm(ttt_handle *h, int cls, bool akc, bool bkc, int epi, GemmArgs g, hipStream_t st, bool fwd = false) {
+  const int odt = (fwd && h->dt == 1) ? 2 : h->dt;
+  const int split = gemm_plan(odt, akc, bkc, epi, g, h->ws_elems);
   {
     Prof prof_(h, cls, st);
-    HIPCHK(gemm_main_launch(h->dt, akc, bkc, epi, g, h->ws, split, st));
+    HIPCHK(gemm_main_launch(odt, akc, bkc, epi, g, h->ws, split, st));
   }
   if (split > 1) {
     Prof prof_(h, K_SPLITK_REDUCE, st);
-    HIPCHK(gemm_reduce_launch(h->dt, epi, g, h->ws, split, st));
+    HIPCHK(gemm_reduce_launch(odt, epi, g, h->ws, split, st));
   }
   h->launches += split > 1 ? 2 : 1;
 }
@@ -216,6 +222,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
   const int d = h->d, F = h->F, L = h->L, dt = h->dt;
   const size_t es = h->es;
   const float eps = h->cfg.rms_eps;
+  const bool f16 = dt == 1;  // bf16 mode: forward activations and weights are fp16
   h->launches = 0;
 
   {
@@ -231,14 +238,14 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
     {
       PROF(K_RMSNORM);
       HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.attn_norm, h->a, sb ? S->r1 : nullptr, sb ? S->h_in : nullptr, n, d, eps,
-                                st));
+                                st, f16));
     }
     float *qkv = sb ? S->qkv : h->qkv;  // fp32: q, k, v are normalised / cached without a bf16 rounding first
     {
       GemmArgs g = gargs(h->a, d, lw.wqkv, d, n, 3 * d, d);
       g.Cf = qkv;
       g.ldcf = 3 * d;
-      gemm(h, K_GEMM_QKV, true, true, EPI_STORE_F32, g, st);
+      gemm(h, K_GEMM_QKV, true, true, EPI_STORE_F32, g, st, true);
     }
     void *qh = sb ? S->qh : h->qh;
     {
@@ -256,11 +263,14 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       ra.R = h->R;
       ra.eps = eps;
       ra.qh = qh;
+      ra.qhb = (sb && lw.fwd16) ? S->qhb : nullptr;
       ra.qht = sb ? S->qht : nullptr;
       ra.K = lw.K;
       ra.Vt = lw.Vt;
+      ra.Kb = lw.bwd_attn ? lw.Kb : nullptr;
       ra.Kt = lw.bwd_attn ? lw.Kt : nullptr;
       ra.V = lw.bwd_attn ? lw.V : nullptr;
+      ra.fwd_f16 = lw.fwd16;
       ra.ldt = h->b;
       {
         PROF(K_ROPE);
@@ -287,6 +297,8 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       aa.scale = 1.f / sqrtf((float)h->hd);
       aa.nsplit = lw.fsplit;
       aa.sbound = lw.sbound;
+      aa.fwd_f16 = lw.fwd16;
+      aa.o_f16 = f16;
       aa.ws = h->attn_ws;
       {
         PROF(K_ATTN_FWD);
@@ -301,24 +313,25 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       GemmArgs g = gargs(o, d, lw.wo, d, n, d, d);
       g.Cf = h->h;
       g.ldcf = d;
-      gemm(h, K_GEMM_O, true, true, EPI_ADD_F32, g, st);
+      gemm(h, K_GEMM_O, true, true, EPI_ADD_F32, g, st, true);
     }
     // --- MLP sub-block (fast + static summed on one norm for updated blocks)
     void *m = S ? S->m : h->m;
     {
       PROF(K_RMSNORM);
-      HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.mlp_norm, m, S ? S->r2 : nullptr, S ? S->h1 : nullptr, n, d, eps, st));
+      HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.mlp_norm, m, S ? S->r2 : nullptr, S ? S->h1 : nullptr, n, d, eps, st, f16));
     }
     void *hm = S ? S->hmid : h->hmid;  // hidden units: F (frozen) or 2F = fast then static
     if (!lw.fast) {
       GemmArgs g = gargs(m, d, lw.wgu, d, n, 2 * F, d);
       g.C = hm;
       g.ldc = F;
-      gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, g, st);
+      g.c_f16 = f16;
+      gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, g, st, true);
       GemmArgs g2 = gargs(hm, F, lw.wd, F, n, d, F);
       g2.Cf = h->h;
       g2.ldcf = d;
-      gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st);
+      gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st, true);
     } else {
       // fast units [0, F): bf16 runs the reduction over [m | m] x [hi | lo]
       GemmArgs g = gargs(m, d, lw.wgu, 2 * d, n, 2 * F, dt == 1 ? 2 * d : d);
@@ -327,20 +340,22 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       g.ldc = 2 * F;
       g.C2 = S ? S->gu : nullptr;
       g.ldc2 = 4 * F;
-      gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, g, st);
+      g.c_f16 = f16;
+      gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, g, st, true);
       // static units [F, 2F)
       GemmArgs gs = gargs(m, d, off(lw.wgu, (size_t)4 * F * d * es), d, n, 2 * F, d);
       gs.C = off(hm, (size_t)F * es);
       gs.ldc = 2 * F;
       gs.C2 = S ? off(S->gu, (size_t)2 * F * es) : nullptr;
       gs.ldc2 = 4 * F;
-      gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, gs, st);
+      gs.c_f16 = f16;
+      gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, gs, st, true);
       // down: [fast | static | fast] units x [hi | static | lo] columns (bf16)
       GemmArgs g2 = gargs(hm, 2 * F, lw.wd, 3 * F, n, d, dt == 1 ? 3 * F : 2 * F);
       g2.a_kwrap = dt == 1 ? 2 * F : 0;
       g2.Cf = h->h;
       g2.ldcf = d;
-      gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st);
+      gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st, true);
     }
     h->launches += lw.fast ? 5 : 4;
   }
@@ -348,7 +363,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
   {
     PROF(K_RMSNORM);
     HIPCHK(rmsnorm_fwd_launch(dt, h->h, h->final_norm, h->nf, update ? h->rf : nullptr, update ? h->hf : nullptr, n, d,
-                              eps, st));
+                              eps, st, f16));
   }
   {
     GemmArgs g = gargs(h->nf, d, h->lm_head, d, n, h->V, d);
@@ -357,7 +372,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
     g.part = h->part;
     g.part_ld = h->P;
     g.zlab = h->zlab;
-    gemm(h, K_GEMM_HEAD_CE, true, true, EPI_CE, g, st);
+    gemm(h, K_GEMM_HEAD_CE, true, true, EPI_CE, g, st, true);
   }
   {
     PROF(K_CE_REDUCE);
@@ -379,7 +394,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         g.pos0 = h->pos0;
         g.col_off = v0;
         g.alpha = 1.f / (float)n;
-        gemm(h, K_GEMM_DLOGITS, true, true, EPI_DLOGITS, g, st);
+        gemm(h, K_GEMM_DLOGITS, true, true, EPI_DLOGITS, g, st, true);  // logits recomputed as in the forward
       }
       {
         // B[n = model dim][k = vocab] from the transposed head [d][V]
@@ -408,8 +423,8 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       }
       {
         PROF(K_TRANSPOSE);
-        HIPCHK(transpose_launch(dt, false, h->dy, d, h->dyT, h->b, n, np, d, st));
-        HIPCHK(transpose_launch(dt, false, S.hmid, 2 * F, h->hmidT, h->b, n, np, F, st));
+        HIPCHK(transpose_launch(dt, SRC_WORK, h->dy, d, h->dyT, h->b, n, np, d, st));
+        HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, S.hmid, 2 * F, h->hmidT, h->b, n, np, F, st));
       }
       // dWd_fast = dy^T hmid_fast over the chunk's tokens, SGD fused into the epilogue
       {
@@ -420,12 +435,13 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         g.ldc = 3 * F;
         g.C2 = dt == 1 ? off(lw.wd, (size_t)2 * F * es) : nullptr;  // lo columns [2F, 3F)
         g.ldc2 = 3 * F;
+        g.c_f16 = f16;
         g.alpha = h->cfg.eta;
         gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st);
       }
       {
         PROF(K_TRANSPOSE);
-        HIPCHK(transpose_launch(dt, true, h->m_d[lw.u], F, lw.wdT, d, d, d, F, st));
+        HIPCHK(transpose_launch(dt, SRC_F32, h->m_d[lw.u], F, lw.wdT, d, d, d, F, st));
       }
       {
         PROF(K_SWIGLU_BWD);
@@ -439,8 +455,8 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       }
       {
         PROF(K_TRANSPOSE);
-        HIPCHK(transpose_launch(dt, false, h->dgu, 4 * F, h->dguT, h->b, n, np, 2 * F, st));
-        HIPCHK(transpose_launch(dt, false, S.m, d, h->mT, h->b, n, np, d, st));
+        HIPCHK(transpose_launch(dt, SRC_WORK, h->dgu, 4 * F, h->dguT, h->b, n, np, 2 * F, st));
+        HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, S.m, d, h->mT, h->b, n, np, d, st));
       }
       // dW(gate|up)_fast = dGU_fast^T m, SGD fused
       {
@@ -451,12 +467,13 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         g.ldc = 2 * d;
         g.C2 = dt == 1 ? off(lw.wgu, (size_t)d * es) : nullptr;  // lo columns
         g.ldc2 = 2 * d;
+        g.c_f16 = f16;
         g.alpha = h->cfg.eta;
         gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st);
       }
       {
         PROF(K_TRANSPOSE);
-        HIPCHK(transpose_launch(dt, true, h->m_gu[lw.u], d, lw.wguT, 4 * F, 2 * F, 2 * F, d, st));
+        HIPCHK(transpose_launch(dt, SRC_F32, h->m_gu[lw.u], d, lw.wguT, 4 * F, 2 * F, 2 * F, d, st));
       }
       h->launches += 7;
       if (last) break;
@@ -473,16 +490,16 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       }
       {
         PROF(K_ATTN_BWD_PRE);
-        HIPCHK(attn_bwd_pre_launch(dt, h->dO, S.o, h->Dq, h->dOt, n, d, h->H, h->hd, h->b, h->b, st));
+        HIPCHK(attn_bwd_pre_launch(dt, h->dO, S.o, h->Dq, h->dOt, n, d, h->H, h->hd, h->b, h->b, st, f16));
       }
       {
         AttnArgs aa;
         memset(&aa, 0, sizeof(aa));
-        aa.q = S.qh;
+        aa.q = lw.fwd16 ? S.qhb : S.qh;  // working-dtype copies for the backward
         aa.qt = S.qht;
         aa.dout = h->dO;
         aa.doutt = h->dOt;
-        aa.K = lw.K;
+        aa.K = lw.fwd16 ? lw.Kb : lw.K;
         aa.Vt = lw.Vt;
         aa.Kt = lw.Kt;
         aa.V = lw.V;
@@ -558,22 +575,25 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
   h->launches++;
 }
 
-// Copies W_init into the fp32 masters and the working-dtype copies.
+// Copies W_init into the fp32 masters, the forward copies (hi | lo; fp16 in
+// bf16 mode) and the transposed working-dtype copies of the backward.
 void reset_fast(ttt_handle *h, hipStream_t st) {
   const int d = h->d, F = h->F;
+  const int fdt = h->dt == 1 ? 2 : h->dt;            // forward copy type
+  const int fsrc = h->dt == 1 ? SRC_F16 : SRC_WORK;  // ... as a transpose source
   for (int l = 0; l < h->L; ++l) {
     LayerBuf &lw = h->layers[l];
     if (!lw.fast) continue;
     HIPCHK(hipMemcpyAsync(h->m_gu[lw.u], h->i_gu[lw.u], (size_t)2 * F * d * 4, hipMemcpyDeviceToDevice, st));
     HIPCHK(hipMemcpyAsync(h->m_d[lw.u], h->i_d[lw.u], (size_t)d * F * 4, hipMemcpyDeviceToDevice, st));
-    HIPCHK(convert_rows_launch(h->dt, h->i_gu[lw.u], d, lw.wgu, 2 * d, 2 * F, d, st, off(lw.wgu, (size_t)d * h->es),
+    HIPCHK(convert_rows_launch(fdt, h->i_gu[lw.u], d, lw.wgu, 2 * d, 2 * F, d, st, off(lw.wgu, (size_t)d * h->es),
                                2 * d));
-    HIPCHK(convert_rows_launch(h->dt, h->i_d[lw.u], F, lw.wd, 3 * F, d, F, st, off(lw.wd, (size_t)2 * F * h->es),
+    HIPCHK(convert_rows_launch(fdt, h->i_d[lw.u], F, lw.wd, 3 * F, d, F, st, off(lw.wd, (size_t)2 * F * h->es),
                                3 * F));
     // transposed working copies for the backward GEMMs: Wd_cat^T [2F][d], Wgu_cat^T [d][4F]
-    HIPCHK(transpose_launch(h->dt, false, lw.wd, 3 * F, lw.wdT, d, d, d, 2 * F, st));  // fast hi, static
-    HIPCHK(transpose_launch(h->dt, false, lw.wgu, 2 * d, lw.wguT, 4 * F, 2 * F, 2 * F, d, st));  // fast hi rows
-    HIPCHK(transpose_launch(h->dt, false, off(lw.wgu, (size_t)4 * F * d * h->es), d, off(lw.wguT, (size_t)2 * F * h->es),
+    HIPCHK(transpose_launch(h->dt, fsrc, lw.wd, 3 * F, lw.wdT, d, d, d, 2 * F, st));  // fast hi, static
+    HIPCHK(transpose_launch(h->dt, fsrc, lw.wgu, 2 * d, lw.wguT, 4 * F, 2 * F, 2 * F, d, st));  // fast hi rows
+    HIPCHK(transpose_launch(h->dt, fsrc, off(lw.wgu, (size_t)4 * F * d * h->es), d, off(lw.wguT, (size_t)2 * F * h->es),
                             4 * F, 2 * F, 2 * F, d, st));  // static rows
   }
 }
@@ -649,6 +669,8 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
   if (c.dtype != TTT_FP32 && c.dtype != TTT_BF16) return fail(nullptr, TTT_EINVAL, "dtype");
   if (c.dtype == TTT_FP32 && c.head_dim > 64) return fail(nullptr, TTT_EUNSUPPORTED, "fp32 supports head_dim <= 64");
   if (c.d_model > 8192) return fail(nullptr, TTT_EUNSUPPORTED, "d_model > 8192");
+  if (c.dtype == TTT_BF16 && (c.d_model % 64 || c.d_ff % 64))
+    return fail(nullptr, TTT_EUNSUPPORTED, "bf16 mode needs d_model and d_ff multiples of 64");
   if (c.chunk <= 0 || c.window <= 0 || c.chunk % 64 || c.window % 64 || c.window < c.chunk)
     return fail(nullptr, TTT_EINVAL, "chunk and window must be positive multiples of 64 with window >= chunk");
   if (c.max_tokens < 1 || c.max_tokens > (1ll << 30)) return fail(nullptr, TTT_EINVAL, "max_tokens out of range");
@@ -703,9 +725,12 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     const size_t plane = (size_t)h->H * h->R * h->hd * es;
     int nplanes = 0;
     for (int l = 0; l < L; ++l) {
-      h->layers[l].fast = l >= L - h->nu;
-      h->layers[l].bwd_attn = l > L - h->nu;
-      nplanes += h->layers[l].bwd_attn ? 4 : 2;
+      LayerBuf &lw = h->layers[l];
+      lw.fast = l >= L - h->nu;
+      lw.bwd_attn = l > L - h->nu;
+      lw.sbound = score_bound(h, w->q_norm[l], w->k_norm[l], st);
+      lw.fwd16 = attn_fwd_f16_ok(h->dt, lw.sbound, h->hd);
+      nplanes += 2 + (lw.bwd_attn ? (lw.fwd16 ? 3 : 2) : 0);
     }
     h->ring_bytes = plane * nplanes;
     h->ring_base = dalloc(h, h->ring_bytes);
@@ -721,7 +746,6 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
       HIPCHK(hipMemcpyAsync(lw.mlp_norm, w->mlp_norm[l], d * es, hipMemcpyDeviceToDevice, st));
       HIPCHK(hipMemcpyAsync(lw.q_norm, w->q_norm[l], h->hd * es, hipMemcpyDeviceToDevice, st));
       HIPCHK(hipMemcpyAsync(lw.k_norm, w->k_norm[l], h->hd * es, hipMemcpyDeviceToDevice, st));
-      lw.sbound = score_bound(h, w->q_norm[l], w->k_norm[l], st);
       lw.fsplit = attn_fwd_split(h->dt, lw.sbound, h->hd, b, h->H, h->k, b);
       const size_t dd = (size_t)d * d * es;
       lw.wqkv = dalloc(h, 3 * dd, false);
@@ -758,14 +782,30 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
       if (lw.bwd_attn) {
         lw.woT = dalloc(h, dd, false);
         lw.wqkvT = dalloc(h, 3 * dd, false);
-        HIPCHK(transpose_launch(h->dt, false, lw.wo, d, lw.woT, d, d, d, d, st));
-        HIPCHK(transpose_launch(h->dt, false, lw.wqkv, d, lw.wqkvT, 3 * d, 3 * d, 3 * d, d, st));
+        HIPCHK(transpose_launch(h->dt, SRC_WORK, lw.wo, d, lw.woT, d, d, d, d, st));
+        HIPCHK(transpose_launch(h->dt, SRC_WORK, lw.wqkv, d, lw.wqkvT, 3 * d, 3 * d, 3 * d, d, st));
+      }
+      if (h->dt == 1) {
+        // the forward GEMMs take fp16 operands: convert the forward copies in place
+        // (the fast hi | lo rows and columns are written by reset_fast)
+        HIPCHK(bf16_to_f16_launch(lw.wqkv, 3 * d, lw.wqkv, 3 * d, 1, 3 * d * d, st));
+        HIPCHK(bf16_to_f16_launch(lw.wo, d, lw.wo, d, 1, d * d, st));
+        void *gus = lw.fast ? off(lw.wgu, 4 * fd) : lw.wgu;
+        HIPCHK(bf16_to_f16_launch(gus, d, gus, d, 2 * F, d, st));
+        if (lw.fast)
+          HIPCHK(bf16_to_f16_launch(off(lw.wd, (size_t)F * es), 3 * F, off(lw.wd, (size_t)F * es), 3 * F, d, F, st));
+        else
+          HIPCHK(bf16_to_f16_launch(lw.wd, F, lw.wd, F, d, F, st));
       }
       lw.K = off(h->ring_base, roff);
       roff += plane;
       lw.Vt = off(h->ring_base, roff);
       roff += plane;
       if (lw.bwd_attn) {
+        if (lw.fwd16) {
+          lw.Kb = off(h->ring_base, roff);
+          roff += plane;
+        }
         lw.Kt = off(h->ring_base, roff);
         roff += plane;
         lw.V = off(h->ring_base, roff);
@@ -819,6 +859,7 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
         S.r2 = (float *)dalloc(h, b * 4);
         S.qkv = (float *)dalloc(h, 3 * bd * 4);
         S.qh = dalloc(h, bd * es);
+        if (h->layers[h->L - h->nu + u].fwd16) S.qhb = dalloc(h, bd * es);
         S.qht = dalloc(h, bd * es);
         S.o = dalloc(h, bd * es);
         S.m = dalloc(h, bd * es);
@@ -834,12 +875,14 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     }
     if (h->nu > 0) {
       h->lm_headT = dalloc(h, (size_t)V * d * es, false);
-      HIPCHK(transpose_launch(h->dt, false, h->lm_head, d, h->lm_headT, V, V, V, d, st));
+      HIPCHK(transpose_launch(h->dt, SRC_WORK, h->lm_head, d, h->lm_headT, V, V, V, d, st));
       h->dyT = dalloc(h, bd * es);
       h->mT = dalloc(h, bd * es);
       h->hmidT = dalloc(h, (size_t)b * F * es);
       h->dguT = dalloc(h, (size_t)b * 2 * F * es);
     }
+    // the LM head's forward copy (cross-entropy and the recomputed logits) is fp16 in bf16 mode
+    if (h->dt == 1) HIPCHK(bf16_to_f16_launch(h->lm_head, d, h->lm_head, d, 1, V * d, st));
     h->ws_elems = gemm_ws_elems(b, d);
     h->ws = (float *)dalloc(h, h->ws_elems * 4);
     // scratch starts as zeros (finite), so masked tile entries never carry NaN

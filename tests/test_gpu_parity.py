@@ -20,7 +20,7 @@ TTT_NO_UPDATE, TTT_NO_GRAPH = 1, 2
 def mid(hd, dtype="bf16", T=600, n_update=2, L=3, eta=0.5, std=0.02, V=1024, k=256, b=128):
     H = 4
     d = H * hd
-    F = {16: 176, 64: 512, 80: 704, 96: 768, 128: 1024}[hd]
+    F = {16: 192, 64: 512, 80: 704, 96: 768, 128: 1024}[hd]
     return TTTConfig(f"mid{hd}_{dtype}", L, d, H, hd, F, V, T, k, b, n_update, eta, dtype, init_std=std)
 
 
