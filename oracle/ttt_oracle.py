@@ -130,37 +130,45 @@ class Oracle:
         return [{"pos": np.zeros(0, dtype=np.int64), "k": z, "v": z} for _ in range(self.L)]
 
     # ---------------------------------------------------------------- attention
+    def window_mask(self, pos_q, pos_k):
+        """Causal sliding window: query p sees keys j with p-k < j <= p."""
+        return (pos_k[None, :] <= pos_q[:, None]) & (pos_k[None, :] > pos_q[:, None] - self.cfg.window)
+
+    def head_probs(self, q_h, K_h, valid):
+        """Softmax over the visible keys of one head: P = softmax(q k^T / sqrt(hd))."""
+        s = (q_h @ K_h.T) * (1.0 / np.sqrt(self.cfg.head_dim))
+        s = np.where(valid, s, -np.inf)
+        s = s - np.max(s, axis=-1, keepdims=True)
+        e = np.exp(s)
+        return e / np.sum(e, axis=-1, keepdims=True)
+
     def attention(self, qh, pos_q, K, V, pos_k):
-        """Causal sliding-window attention: query p sees keys j with p-k < j <= p."""
+        """Causal sliding-window attention of the chunk's queries over K, V."""
         c = self.cfg
-        scale = 1.0 / np.sqrt(c.head_dim)
-        valid = (pos_k[None, :] <= pos_q[:, None]) & (pos_k[None, :] > pos_q[:, None] - c.window)
+        valid = self.window_mask(pos_q, pos_k)
         self.key_count += int(valid.sum())
         o = np.empty_like(qh)
-        P = np.empty((c.n_heads, len(pos_q), len(pos_k)), dtype=self.dt)
         for h in range(c.n_heads):
-            s = (qh[:, h, :] @ K[:, h, :].T) * scale
-            s = np.where(valid, s, -np.inf)
-            s = s - np.max(s, axis=-1, keepdims=True)
-            e = np.exp(s)
-            P[h] = e / np.sum(e, axis=-1, keepdims=True)
-            o[:, h, :] = P[h] @ V[:, h, :]
-        return o, P
+            o[:, h, :] = self.head_probs(qh[:, h, :], K[:, h, :], valid) @ V[:, h, :]
+        return o
 
-    def attention_bwd(self, do, qh, K, V, P, n_old):
+    def attention_bwd(self, do, qh, K, V, pos_q, pos_k, n_old):
         """Gradients w.r.t. the queries and the chunk's own keys/values.
 
-        Keys and values of earlier chunks (the first n_old rows of K, V) are
-        constants of the current step, so only the chunk rows get gradients.
+        The probabilities are recomputed head by head with the forward's own
+        function (nothing of size heads x queries x keys is kept).  Keys and
+        values of earlier chunks (the first n_old rows of K, V) are constants of
+        the current step, so only the chunk rows get gradients.
         """
         c = self.cfg
         scale = 1.0 / np.sqrt(c.head_dim)
+        valid = self.window_mask(pos_q, pos_k)
         dq = np.empty_like(qh)
         nk = K.shape[0] - n_old
         dk = np.empty((nk, c.n_heads, c.head_dim), dtype=self.dt)
         dv = np.empty_like(dk)
         for h in range(c.n_heads):
-            Ph = P[h]
+            Ph = self.head_probs(qh[:, h, :], K[:, h, :], valid)
             dP = do[:, h, :] @ V[:, h, :].T
             Drow = np.sum(Ph * dP, axis=-1, keepdims=True)
             dS = Ph * (dP - Drow)
@@ -170,10 +178,12 @@ class Oracle:
         return dq, dk, dv
 
     # ---------------------------------------------------------------- one chunk
-    def chunk_forward(self, W, cache, x_in, labels, pos0, keep=True):
+    def chunk_forward(self, W, cache, x_in, labels, pos0, consume=False):
         """Forward of one chunk with fast weights W and attention state `cache`.
 
-        Returns (losses, saved, new_cache).  `cache` is not modified.
+        Returns (losses, saved, new_cache).  `cache` is not modified unless
+        `consume` is set: then each layer's old entry is dropped once the layer
+        is done (the caller hands the state over; only memory use changes).
         """
         c = self.cfg
         n = len(x_in)
@@ -197,7 +207,7 @@ class Oracle:
             K = np.concatenate([cache[l]["k"], kh], axis=0)
             V = np.concatenate([cache[l]["v"], v], axis=0)
             pos_k = np.concatenate([cache[l]["pos"], pos])
-            o, P = self.attention(qh, pos, K, V, pos_k)
+            o = self.attention(qh, pos, K, V, pos_k)
             h1 = h + o.reshape(n, -1) @ self.p(pre + "wo").T
             m, r2 = rmsnorm(h1, self.p(pre + "mlp_norm"), eps)
             ys, acts_s = swiglu(m, self.p(pre + "w_gate"), self.p(pre + "w_up"), self.p(pre + "w_down"))
@@ -210,12 +220,14 @@ class Oracle:
             h = h1 + y
             if l >= self.first_fast:
                 saved["layers"][l] = dict(h_in=h_in, r1=r1, q=q, k=k, v=v, rq=rq, rk=rk, qh=qh,
-                                          K=K, V=V, P=P, n_old=len(cache[l]["pos"]), o=o,
+                                          K=K, V=V, pos_k=pos_k, n_old=len(cache[l]["pos"]), o=o,
                                           h1=h1, r2=r2, m=m, acts_s=acts_s, acts_f=acts_f)
             # Alg. 1 step 3.6: keep only what the window still needs.
             nxt = pos0 + n
             keep_mask = pos_k > nxt - c.window
             new_cache.append({"pos": pos_k[keep_mask], "k": K[keep_mask], "v": V[keep_mask]})
+            if consume:
+                cache[l] = None
         nf, rf = rmsnorm(h, self.p("final_norm"), eps)
         z = nf @ self.p("lm_head").T
         lse = logsumexp(z)
@@ -262,7 +274,7 @@ class Oracle:
             dh1 = dh + rmsnorm_bwd(dm, s["h1"], s["r2"], self.p(pre + "mlp_norm"))
             # attention sub-block: h1 = h_in + o Wo^T
             do = (dh1 @ self.p(pre + "wo")).reshape(n, H, hd)
-            dqh, dkh, dv = self.attention_bwd(do, s["qh"], s["K"], s["V"], s["P"], s["n_old"])
+            dqh, dkh, dv = self.attention_bwd(do, s["qh"], s["K"], s["V"], saved["pos"], s["pos_k"], s["n_old"])
             dqn = rope_bwd(dqh, cos, sin)
             dkn = rope_bwd(dkh, cos, sin)
             dq = rmsnorm_bwd(dqn, s["q"], s["rq"], self.p(pre + "q_norm"))
@@ -293,7 +305,7 @@ class Oracle:
             n = min(b, T - s0)
             x_in = tokens[s0:s0 + n]
             labels = tokens[s0 + 1:s0 + n + 1]
-            l_chunk, saved, new_cache = self.chunk_forward(W, cache, x_in, labels, s0)
+            l_chunk, saved, new_cache = self.chunk_forward(W, cache, x_in, labels, s0, consume=not return_trace)
             losses[s0:s0 + n] = l_chunk          # recorded before the update
             if return_trace:
                 trace.append({"W_before": [[w.copy() for w in ws] for ws in W],
