@@ -64,7 +64,9 @@ enum {
  *   the window covers at least one chunk); max_tokens >= 1.
  * Shapes outside the compiled kernels give TTT_EUNSUPPORTED: head_dim not in the
  * set above, head_dim > 64 with fp32, d_model > 8192, and in bf16 mode d_model
- * or d_ff not a multiple of 64.
+ * or d_ff not a multiple of 64, or an updated block's fast or static MLP weight
+ * that is not finite or not below 8192 in magnitude (their fp16 forward copies
+ * are stored scaled by a power of two chosen from the largest magnitude).
  */
 typedef struct {
   int32_t n_layers;     /* L */

@@ -62,11 +62,12 @@ hipError_t ce_reduce_launch(const float2 *part, int P, const float *zlab, const 
 // Rotary table: cs[p][i] = (cos, sin)(p * theta^(-2i/hd)) evaluated in fp64.
 hipError_t rope_table_launch(float2 *cs, long max_pos, int hd, double theta, hipStream_t st);
 
-// dst[r * ld_dst + c] = hi = (T) src[r * ld_src + c]; when lo is given also
-// lo[r * ld_lo + c] = (T) (src - hi), so that hi + lo carries the fp32 value to
-// about 16 (bf16) or 22 (fp16) significant bits.  dtype 2 writes fp16.
+// With x = scale * src[r * ld_src + c]: dst[r * ld_dst + c] = hi = (T) x; when lo
+// is given also lo[r * ld_lo + c] = (T) (x - hi), so that hi + lo carries x to
+// about 16 (bf16) or 22 (fp16) significant bits.  dtype 2 writes fp16; `scale`
+// (a power of two) keeps fp16's lo part out of the subnormal range.
 hipError_t convert_rows_launch(int dtype, const float *src, long ld_src, void *dst, long ld_dst, int rows, int cols,
-                               hipStream_t st, void *lo = nullptr, long ld_lo = 0);
+                               hipStream_t st, void *lo = nullptr, long ld_lo = 0, float scale = 1.f);
 // dst (T) = src (T) copies with row strides.
 hipError_t copy_rows_launch(int dtype, const void *src, long ld_src, void *dst, long ld_dst, int rows, int cols,
                             hipStream_t st);
@@ -77,9 +78,13 @@ hipError_t copy_rows_launch(int dtype, const void *src, long ld_src, void *dst, 
 enum { SRC_F32 = 0, SRC_WORK = 1, SRC_F16 = 2 };
 hipError_t transpose_launch(int dtype, int src_kind, const void *src, long lds, void *dst, long ldd, int R, int Rpad,
                             int C, hipStream_t st);
-// dst (fp16) = src (bf16), exactly for the weight magnitudes in use (|x| in the
-// fp16 normal range), with row strides.
-hipError_t bf16_to_f16_launch(const void *src, long lds, void *dst, long ldd, int rows, int cols, hipStream_t st);
+// dst (fp16) = scale * src (bf16), exact when the scaled value is in fp16's
+// normal range (scale a power of two), with row strides.
+hipError_t bf16_to_f16_launch(const void *src, long lds, void *dst, long ldd, int rows, int cols, hipStream_t st,
+                              float scale = 1.f);
+// *out = max(*out, bit pattern of max |x|) over a [rows][cols] block with row
+// stride ld (dtype 0 fp32, 1 bf16); *out must start at 0.  NaN counts as largest.
+hipError_t absmax_launch(int dtype, const void *x, long ld, int rows, int cols, unsigned *out, hipStream_t st);
 
 hipError_t set_int_launch(int *p, int v, hipStream_t st);
 hipError_t add_int_launch(int *p, int v, hipStream_t st);

@@ -320,11 +320,11 @@ __global__ void rope_table_kernel(float2 *cs, long max_pos, int hd, double theta
 
 template <typename T>
 __global__ void convert_rows_kernel(const float *src, long ld_src, T *dst, long ld_dst, T *lo, long ld_lo, int rows,
-                                    int cols) {
+                                    int cols, float scale) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long)rows * cols) return;
   const int r = idx / cols, c = idx % cols;
-  const float x = src[(long)r * ld_src + c];
+  const float x = src[(long)r * ld_src + c] * scale;
   const T hi = from_f<T>(x);
   dst[(long)r * ld_dst + c] = hi;
   if (lo) lo[(long)r * ld_lo + c] = from_f<T>(x - to_f(hi));
@@ -356,11 +356,25 @@ __global__ __launch_bounds__(256) void transpose_kernel(const S *src, long lds, 
   }
 }
 
-__global__ void bf16_to_f16_kernel(const bf16_t *src, long lds, f16_t *dst, long ldd, int rows, int cols) {
+__global__ void bf16_to_f16_kernel(const bf16_t *src, long lds, f16_t *dst, long ldd, int rows, int cols,
+                                   float scale) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long)rows * cols) return;
   const int r = idx / cols, c = idx % cols;
-  dst[(long)r * ldd + c] = from_f<f16_t>(to_f(src[(long)r * lds + c]));
+  dst[(long)r * ldd + c] = from_f<f16_t>(to_f(src[(long)r * lds + c]) * scale);
+}
+
+// *out = max(*out, bits of max |x|) over x[r * ld + c], r < rows, c < cols
+// (non-negative floats order like their bit patterns; a NaN compares highest).
+template <typename T>
+__global__ void absmax_kernel(const T *x, long ld, int rows, int cols, unsigned *out) {
+  float m = 0.f;
+  const long tot = (long)rows * cols;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < tot; i += (long)gridDim.x * 256) {
+    const float v = fabsf(to_f(x[(i / cols) * ld + i % cols]));
+    m = (v > m || v != v) ? v : m;
+  }
+  atomicMax(out, __float_as_uint(m));
 }
 
 __global__ void set_int_kernel(int *p, int v) { *p = v; }
@@ -507,17 +521,17 @@ hipError_t rope_table_launch(float2 *cs, long max_pos, int hd, double theta, hip
 }
 
 hipError_t convert_rows_launch(int dtype, const float *src, long ld_src, void *dst, long ld_dst, int rows, int cols,
-                               hipStream_t st, void *lo, long ld_lo) {
+                               hipStream_t st, void *lo, long ld_lo, float scale) {
   long tot = (long)rows * cols;
   if (tot <= 0) return hipSuccess;
   if (dtype == 2) {
     hipLaunchKernelGGL(convert_rows_kernel<f16_t>, dim3(blocks_for(tot)), dim3(256), 0, st, src, ld_src, (f16_t *)dst,
-                       ld_dst, (f16_t *)lo, ld_lo, rows, cols);
+                       ld_dst, (f16_t *)lo, ld_lo, rows, cols, scale);
     return hipGetLastError();
   }
 #define K_(T, ...)                                                                                               \
   hipLaunchKernelGGL(convert_rows_kernel<T>, dim3(blocks_for(tot)), dim3(256), 0, st, src, ld_src, (T *)dst, ld_dst, \
-                     (T *)lo, ld_lo, rows, cols)
+                     (T *)lo, ld_lo, rows, cols, scale)
   DT_DISPATCH(dtype, K_, 0);
 #undef K_
   return hipGetLastError();
@@ -556,11 +570,22 @@ hipError_t transpose_launch(int dtype, int src_kind, const void *src, long lds, 
   return hipGetLastError();
 }
 
-hipError_t bf16_to_f16_launch(const void *src, long lds, void *dst, long ldd, int rows, int cols, hipStream_t st) {
+hipError_t bf16_to_f16_launch(const void *src, long lds, void *dst, long ldd, int rows, int cols, hipStream_t st,
+                              float scale) {
   const long tot = (long)rows * cols;
   if (tot <= 0) return hipSuccess;
   hipLaunchKernelGGL(bf16_to_f16_kernel, dim3(blocks_for(tot)), dim3(256), 0, st, (const bf16_t *)src, lds,
-                     (f16_t *)dst, ldd, rows, cols);
+                     (f16_t *)dst, ldd, rows, cols, scale);
+  return hipGetLastError();
+}
+
+hipError_t absmax_launch(int dtype, const void *x, long ld, int rows, int cols, unsigned *out, hipStream_t st) {
+  const long tot = (long)rows * cols;
+  if (tot <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<long>((tot + 255) / 256, 1024);
+#define K_(T, ...) hipLaunchKernelGGL(absmax_kernel<T>, dim3(blocks), dim3(256), 0, st, (const T *)x, ld, rows, cols, out)
+  DT_DISPATCH(dtype, K_, 0);
+#undef K_
   return hipGetLastError();
 }
 

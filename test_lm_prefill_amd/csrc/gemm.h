@@ -13,8 +13,9 @@ enum GemmEpi {
   EPI_CE = 4,        // per-row partial (max, sum exp) over the tile's columns and the
                      // label logit -> part / zlab   (cross-entropy, first pass)
   EPI_DLOGITS = 5,   // C (T) = (exp(acc - lse[m]) - [n + col_off == label]) * alpha
-  EPI_SGD = 6,       // Cf (fp32 master) -= alpha * acc; C (T) = hi = round(Cf) and, when C2 is
-                     // set, C2 (T) = round(Cf - hi): the working copy as hi + lo (inner SGD)
+  EPI_SGD = 6,       // Cf (fp32 master) -= alpha * acc; C (T) = hi = round(c_scale * Cf) and,
+                     // when C2 is set, C2 (T) = round(c_scale * Cf - hi): the working copy as
+                     // hi + lo, scaled by c_scale (inner SGD)
 };
 
 struct GemmArgs {
@@ -44,6 +45,10 @@ struct GemmArgs {
   // 16-bit outputs (C, and C2 of EPI_SGD) are written as fp16 instead of bf16;
   // EPI_SWIGLU's C2 (pre-activations kept for the backward) stays bf16
   int c_f16;
+  // EPI_SWIGLU and EPI_ADD_F32 multiply the accumulator by acc_scale first (a
+  // power of two: B holds weights stored scaled by 1 / acc_scale); EPI_SGD
+  // writes its 16-bit copies scaled by c_scale.  Both are 1 when unused.
+  float acc_scale, c_scale;
   // split-K (internal)
   int ksplit;
   float *ws;

@@ -247,8 +247,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const GemmArgs g) {
         float h[4], gv[4], uv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          gv[r] = acc[i][j][r];
-          uv[r] = acc[i + 1][j][r];
+          gv[r] = acc[i][j][r] * g.acc_scale;
+          uv[r] = acc[i + 1][j][r] * g.acc_scale;
           h[r] = gv[r] / (1.f + __expf(-gv[r])) * uv[r];
         }
         store4<T>(Hm + (long)m * g.ldc + unit, h);
@@ -282,7 +282,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const GemmArgs g) {
       } else if constexpr (EPI == EPI_ADD_F32) {
         float4 *p = reinterpret_cast<float4 *>(g.Cf + (long)m * g.ldcf + n);
         float4 o = *p;
-        *p = make_float4(o.x + v[0], o.y + v[1], o.z + v[2], o.w + v[3]);
+        const float sc = g.acc_scale;
+        *p = make_float4(o.x + v[0] * sc, o.y + v[1] * sc, o.z + v[2] * sc, o.w + v[3] * sc);
       } else if constexpr (EPI == EPI_PARTIAL) {
         store4<float>(g.ws + ((long)blockIdx.z * g.M + m) * g.N + n, v);
       } else if constexpr (EPI == EPI_DLOGITS) {
@@ -298,11 +299,14 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const GemmArgs g) {
         float4 w = *pw;
         float nw[4] = {w.x - g.alpha * v[0], w.y - g.alpha * v[1], w.z - g.alpha * v[2], w.w - g.alpha * v[3]};
         *pw = make_float4(nw[0], nw[1], nw[2], nw[3]);
-        store4<T>(reinterpret_cast<T *>(g.C) + (long)m * g.ldc + n, nw);
+        float sw[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sw[r] = nw[r] * g.c_scale;
+        store4<T>(reinterpret_cast<T *>(g.C) + (long)m * g.ldc + n, sw);
         if (g.C2) {
           float lo[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) lo[r] = nw[r] - to_f(from_f<T>(nw[r]));
+          for (int r = 0; r < 4; ++r) lo[r] = sw[r] - to_f(from_f<T>(sw[r]));
           store4<T>(reinterpret_cast<T *>(g.C2) + (long)m * g.ldc2 + n, lo);
         }
       }
@@ -312,7 +316,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const GemmArgs g) {
 
 // out[m, n] (=|+=) sum_s ws[s, m, n], s in increasing order.
 template <typename T, int MODE>
-__global__ __launch_bounds__(256) void splitk_reduce(const float *ws, int S, int M, int N, void *out, long ld) {
+__global__ __launch_bounds__(256) void splitk_reduce(const float *ws, int S, int M, int N, void *out, long ld,
+                                                     float sc) {
   long idx = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
   long total = (long)M * N;
   if (idx >= total) return;
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float *ws, int S, int
   } else {
     float4 *p = reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + (long)m * ld + n);
     float4 o = *p;
-    *p = make_float4(o.x + v[0], o.y + v[1], o.z + v[2], o.w + v[3]);
+    *p = make_float4(o.x + v[0] * sc, o.y + v[1] * sc, o.z + v[2] * sc, o.w + v[3] * sc);
   }
 }
 
@@ -374,15 +379,15 @@ hipError_t reduce_launch(int epi, const GemmArgs &g, int S, hipStream_t st) {
   dim3 grid((unsigned)((total / 4 + 255) / 256));
   switch (epi) {
     case EPI_STORE:
-      hipLaunchKernelGGL((splitk_reduce<T, EPI_STORE>), grid, dim3(256), 0, st, g.ws, S, g.M, g.N, g.C, g.ldc);
+      hipLaunchKernelGGL((splitk_reduce<T, EPI_STORE>), grid, dim3(256), 0, st, g.ws, S, g.M, g.N, g.C, g.ldc, 1.f);
       break;
     case EPI_STORE_F32:
       hipLaunchKernelGGL((splitk_reduce<T, EPI_STORE_F32>), grid, dim3(256), 0, st, g.ws, S, g.M, g.N,
-                         (void *)g.Cf, g.ldcf);
+                         (void *)g.Cf, g.ldcf, 1.f);
       break;
     default:
       hipLaunchKernelGGL((splitk_reduce<T, EPI_ADD_F32>), grid, dim3(256), 0, st, g.ws, S, g.M, g.N,
-                         (void *)g.Cf, g.ldcf);
+                         (void *)g.Cf, g.ldcf, g.acc_scale);
       break;
   }
   return hipGetLastError();

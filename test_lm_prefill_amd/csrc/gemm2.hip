@@ -101,8 +101,8 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
         float hv[4], gv[4], uv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          gv[r] = acc[i][j][r];
-          uv[r] = acc[i + 1][j][r];
+          gv[r] = acc[i][j][r] * g.acc_scale;
+          uv[r] = acc[i + 1][j][r] * g.acc_scale;
           hv[r] = gv[r] / (1.f + __expf(-gv[r])) * uv[r];
         }
         store_c4(g, g.C, (long)m * g.ldc + unit, hv);
@@ -136,7 +136,8 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
       } else if constexpr (EPI == EPI_ADD_F32) {
         float4 *p = reinterpret_cast<float4 *>(g.Cf + (long)m * g.ldcf + n);
         float4 o = *p;
-        *p = make_float4(o.x + v[0], o.y + v[1], o.z + v[2], o.w + v[3]);
+        const float sc = g.acc_scale;
+        *p = make_float4(o.x + v[0] * sc, o.y + v[1] * sc, o.z + v[2] * sc, o.w + v[3] * sc);
       } else if constexpr (EPI == 100) {  // split-K partial
         store4<float>(g.ws + ((long)blockIdx.z * g.M + m) * g.N + n, v);
       } else if constexpr (EPI == EPI_DLOGITS) {
@@ -152,12 +153,15 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
         const float4 w = *pw;
         float nw[4] = {w.x - g.alpha * v[0], w.y - g.alpha * v[1], w.z - g.alpha * v[2], w.w - g.alpha * v[3]};
         *pw = make_float4(nw[0], nw[1], nw[2], nw[3]);
-        store_c4(g, g.C, (long)m * g.ldc + n, nw);
+        float sw[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sw[r] = nw[r] * g.c_scale;
+        store_c4(g, g.C, (long)m * g.ldc + n, sw);
         if (g.C2) {
           float lo[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            lo[r] = nw[r] - (g.c_f16 ? to_f(from_f<f16_t>(nw[r])) : to_f(from_f<bf16_t>(nw[r])));
+            lo[r] = sw[r] - (g.c_f16 ? to_f(from_f<f16_t>(sw[r])) : to_f(from_f<bf16_t>(sw[r])));
           store_c4(g, g.C2, (long)m * g.ldc2 + n, lo);
         }
       }

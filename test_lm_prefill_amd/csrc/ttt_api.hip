@@ -71,6 +71,11 @@ struct ttt_handle {
   ttt_config cfg;
   int dt = 0;
   size_t es = 4;
+  // bf16 mode: the forward copies of the updated blocks' MLP weights (fast hi | lo
+  // and the static down projection) are stored multiplied by this power of two,
+  // which keeps the fp16 lo part of small weights out of the subnormal range;
+  // the GEMMs that read them divide their accumulators by it.  1 in fp32 mode.
+  float wscale = 1.f;
   int L = 0, d = 0, H = 0, hd = 0, F = 0, V = 0, k = 0, b = 0, nu = 0, R = 0, Vs = 0, P = 0;
   std::vector<void *> allocs;
   std::vector<std::pair<void *, size_t>> zero_list;
@@ -148,6 +153,8 @@ GemmArgs gargs(const void *A, long lda, const void *B, long ldb, int M, int N, i
   g.N = N;
   g.K = K;
   g.alpha = 1.f;
+  g.acc_scale = 1.f;
+  g.c_scale = 1.f;
   return g;
 }
 
@@ -341,6 +348,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       g.C2 = S ? S->gu : nullptr;
       g.ldc2 = 4 * F;
       g.c_f16 = f16;
+      g.acc_scale = 1.f / h->wscale;
       gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, g, st, true);
       // static units [F, 2F)
       GemmArgs gs = gargs(m, d, off(lw.wgu, (size_t)4 * F * d * es), d, n, 2 * F, d);
@@ -355,6 +363,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       g2.a_kwrap = dt == 1 ? 2 * F : 0;
       g2.Cf = h->h;
       g2.ldcf = d;
+      g2.acc_scale = 1.f / h->wscale;
       gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st, true);
     }
     h->launches += lw.fast ? 5 : 4;
@@ -436,6 +445,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         g.C2 = dt == 1 ? off(lw.wd, (size_t)2 * F * es) : nullptr;  // lo columns [2F, 3F)
         g.ldc2 = 3 * F;
         g.c_f16 = f16;
+        g.c_scale = h->wscale;
         g.alpha = h->cfg.eta;
         gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st);
       }
@@ -468,6 +478,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         g.C2 = dt == 1 ? off(lw.wgu, (size_t)d * es) : nullptr;  // lo columns
         g.ldc2 = 2 * d;
         g.c_f16 = f16;
+        g.c_scale = h->wscale;
         g.alpha = h->cfg.eta;
         gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st);
       }
@@ -575,26 +586,24 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
   h->launches++;
 }
 
-// Copies W_init into the fp32 masters, the forward copies (hi | lo; fp16 in
-// bf16 mode) and the transposed working-dtype copies of the backward.
+// Copies W_init into the fp32 masters, the forward copies (hi | lo, fp16 and
+// scaled by wscale in bf16 mode) and the fast parts of the transposed
+// working-dtype copies of the backward (the static parts are set at creation).
 void reset_fast(ttt_handle *h, hipStream_t st) {
   const int d = h->d, F = h->F;
-  const int fdt = h->dt == 1 ? 2 : h->dt;            // forward copy type
-  const int fsrc = h->dt == 1 ? SRC_F16 : SRC_WORK;  // ... as a transpose source
+  const int fdt = h->dt == 1 ? 2 : h->dt;  // forward copy type
   for (int l = 0; l < h->L; ++l) {
     LayerBuf &lw = h->layers[l];
     if (!lw.fast) continue;
     HIPCHK(hipMemcpyAsync(h->m_gu[lw.u], h->i_gu[lw.u], (size_t)2 * F * d * 4, hipMemcpyDeviceToDevice, st));
     HIPCHK(hipMemcpyAsync(h->m_d[lw.u], h->i_d[lw.u], (size_t)d * F * 4, hipMemcpyDeviceToDevice, st));
-    HIPCHK(convert_rows_launch(fdt, h->i_gu[lw.u], d, lw.wgu, 2 * d, 2 * F, d, st, off(lw.wgu, (size_t)d * h->es),
-                               2 * d));
-    HIPCHK(convert_rows_launch(fdt, h->i_d[lw.u], F, lw.wd, 3 * F, d, F, st, off(lw.wd, (size_t)2 * F * h->es),
-                               3 * F));
-    // transposed working copies for the backward GEMMs: Wd_cat^T [2F][d], Wgu_cat^T [d][4F]
-    HIPCHK(transpose_launch(h->dt, fsrc, lw.wd, 3 * F, lw.wdT, d, d, d, 2 * F, st));  // fast hi, static
-    HIPCHK(transpose_launch(h->dt, fsrc, lw.wgu, 2 * d, lw.wguT, 4 * F, 2 * F, 2 * F, d, st));  // fast hi rows
-    HIPCHK(transpose_launch(h->dt, fsrc, off(lw.wgu, (size_t)4 * F * d * h->es), d, off(lw.wguT, (size_t)2 * F * h->es),
-                            4 * F, 2 * F, 2 * F, d, st));  // static rows
+    HIPCHK(convert_rows_launch(fdt, h->i_gu[lw.u], d, lw.wgu, 2 * d, 2 * F, d, st,
+                               h->dt == 1 ? off(lw.wgu, (size_t)d * h->es) : nullptr, 2 * d, h->wscale));
+    HIPCHK(convert_rows_launch(fdt, h->i_d[lw.u], F, lw.wd, 3 * F, d, F, st,
+                               h->dt == 1 ? off(lw.wd, (size_t)2 * F * h->es) : nullptr, 3 * F, h->wscale));
+    // Wd_cat^T [2F][d] rows [0, F) and Wgu_cat^T [d][4F] columns [0, 2F), from the masters
+    HIPCHK(transpose_launch(h->dt, SRC_F32, h->i_d[lw.u], F, lw.wdT, d, d, d, F, st));
+    HIPCHK(transpose_launch(h->dt, SRC_F32, h->i_gu[lw.u], d, lw.wguT, 4 * F, 2 * F, 2 * F, d, st));
   }
 }
 
@@ -732,6 +741,33 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
       lw.fwd16 = attn_fwd_f16_ok(h->dt, lw.sbound, h->hd);
       nplanes += 2 + (lw.bwd_attn ? (lw.fwd16 ? 3 : 2) : 0);
     }
+    if (h->dt == 1 && h->nu > 0) {
+      // largest |w| over the weights whose forward copies are stored scaled
+      unsigned *amax = (unsigned *)dalloc(h, 64, false);
+      HIPCHK(hipMemsetAsync(amax, 0, 4, st));
+      for (int u = 0; u < h->nu; ++u) {
+        HIPCHK(absmax_launch(0, w->fast_gate[u], d, F, d, amax, st));
+        HIPCHK(absmax_launch(0, w->fast_up[u], d, F, d, amax, st));
+        HIPCHK(absmax_launch(0, w->fast_down[u], F, d, F, amax, st));
+        HIPCHK(absmax_launch(1, w->w_down[L - h->nu + u], F, d, F, amax, st));
+      }
+      unsigned bits = 0;
+      HIPCHK(hipMemcpyAsync(&bits, amax, 4, hipMemcpyDeviceToHost, st));
+      HIPCHK(hipStreamSynchronize(st));
+      float mx;
+      std::memcpy(&mx, &bits, 4);
+      if (!(mx < 8192.f)) {
+        hipStreamSynchronize(st);
+        free_all(h);
+        delete h;
+        return fail(nullptr, TTT_EUNSUPPORTED,
+                    "bf16 mode needs finite MLP weights below 8192 in magnitude in the updated blocks");
+      }
+      // 2^s with max|w| * 2^s <= 4096 (16x headroom below fp16's largest value), s <= 12
+      int sh = 12;
+      while (sh > 0 && std::ldexp(mx, sh) > 4096.f) --sh;
+      h->wscale = std::ldexp(1.f, sh);
+    }
     h->ring_bytes = plane * nplanes;
     h->ring_base = dalloc(h, h->ring_bytes);
     size_t roff = 0;
@@ -778,6 +814,10 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
       if (lw.fast && h->nu > 0) {
         lw.wdT = dalloc(h, 2 * fd, false);
         lw.wguT = dalloc(h, 4 * fd, false);
+        // static parts of Wd_cat^T (rows [F, 2F)) and Wgu_cat^T (columns [2F, 4F))
+        HIPCHK(transpose_launch(h->dt, SRC_WORK, off(lw.wd, (size_t)F * es), 3 * F, off(lw.wdT, fd), d, d, d, F, st));
+        HIPCHK(transpose_launch(h->dt, SRC_WORK, off(lw.wgu, 4 * fd), d, off(lw.wguT, (size_t)2 * F * es), 4 * F,
+                                2 * F, 2 * F, d, st));
       }
       if (lw.bwd_attn) {
         lw.woT = dalloc(h, dd, false);
@@ -792,8 +832,9 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
         HIPCHK(bf16_to_f16_launch(lw.wo, d, lw.wo, d, 1, d * d, st));
         void *gus = lw.fast ? off(lw.wgu, 4 * fd) : lw.wgu;
         HIPCHK(bf16_to_f16_launch(gus, d, gus, d, 2 * F, d, st));
-        if (lw.fast)
-          HIPCHK(bf16_to_f16_launch(off(lw.wd, (size_t)F * es), 3 * F, off(lw.wd, (size_t)F * es), 3 * F, d, F, st));
+        if (lw.fast)  // static down columns share the fast ones' scale
+          HIPCHK(bf16_to_f16_launch(off(lw.wd, (size_t)F * es), 3 * F, off(lw.wd, (size_t)F * es), 3 * F, d, F, st,
+                                    h->wscale));
         else
           HIPCHK(bf16_to_f16_launch(lw.wd, F, lw.wd, F, d, F, st));
       }
