@@ -130,6 +130,71 @@ def gpu_bench(cfg, steps, warmup, profile=True):
     return ms_ttt, ms_swa, ktimes, mean_loss, tok_np
 
 
+def time_prefill(cfg, flags, steps, warmup):
+    """ms per prefill of cfg's own sequence with the given flags (fresh session)."""
+    import torch
+    from ttt_inputs import make_weights_torch, make_tokens
+    from test_lm_prefill_amd import Session
+    w = make_weights_torch(cfg, "cuda", seed=0)
+    tok = torch.from_numpy(make_tokens(cfg, seed=1)).cuda()
+    sess = Session(cfg, w, max_tokens=cfg.seq_len)
+    stream = torch.cuda.current_stream()
+    try:
+        for _ in range(warmup):
+            sess.prefill(tok, flags=flags, want_fast=False, check=False)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            sess.prefill(tok, flags=flags, want_fast=False, check=False)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+    finally:
+        sess.close()
+        del w, tok
+        torch.cuda.empty_cache()
+    log(f"[bench] {cfg.name} T={cfg.seq_len} k={cfg.window} n_u={cfg.n_update} flags={flags}: {ms:.1f} ms")
+    return ms
+
+
+def suite_full_attention(steps, warmup):
+    """Full-attention prefill baseline at the 2.7B shape: the window covers the whole
+    sequence (k >= T, a linear KV cache of T + b rows), no fast MLPs and no inner
+    updates, i.e. a plain causal Transformer of the same size; timed beside the
+    TTT-E2E prefill (k = 8K, inner updates) of the same T.  The notes quote a 2.7x
+    speed-up of TTT-E2E over full attention at 128K on one H100 (section 11.1)."""
+    from ttt_inputs import get
+    from test_lm_prefill_amd.ttt import TTT_NO_UPDATE
+    rows = []
+    for name in ("2.7b_8k", "2.7b_32k", "2.7b_128k"):
+        cfg = get(name)
+        T = cfg.seq_len
+        ms_ttt = time_prefill(cfg, 0, steps, warmup)
+        fa = cfg.with_(name=name + "_full_attention", window=-(-T // 64) * 64, n_update=0)
+        ms_fa = time_prefill(fa, TTT_NO_UPDATE, steps, warmup)
+        rows.append({"seq_len": T, "ttt_e2e_ms": round(ms_ttt, 1), "full_attention_ms": round(ms_fa, 1),
+                     "ttt_e2e_ms_per_1k": round(ms_ttt * 1024 / T, 3),
+                     "full_attention_ms_per_1k": round(ms_fa * 1024 / T, 3),
+                     "speedup_ttt_over_full": round(ms_fa / ms_ttt, 3)})
+    return {"suite": "full_attention_baseline", "shape": "2.7b", "rows": rows}
+
+
+def suite_sweep(steps, warmup):
+    """ms per 1K tokens of the TTT-E2E prefill at the 760M shape (T = 128K, b = 1K) over
+    the number of updated blocks n_u (k = 8K) and the window k (n_u = 6)."""
+    from ttt_inputs import get
+    base = get("760m")
+    rows = []
+    for nu, k in [(1, 8192), (3, 8192), (6, 8192), (12, 8192), (6, 2048), (6, 4096), (6, 16384)]:
+        cfg = base.with_(name=f"760m_nu{nu}_k{k}", n_update=nu, window=k)
+        ms = time_prefill(cfg, 0, steps, warmup)
+        rows.append({"n_update": nu, "window": k, "ms": round(ms, 1),
+                     "ms_per_1k": round(ms * 1024 / cfg.seq_len, 3)})
+    return {"suite": "n_update_and_window_sweep", "shape": "760m", "seq_len": base.seq_len, "rows": rows}
+
+
 def profile_pass(cfg):
     """For hardware-counter runs: one kernel of known traffic, then one prefill.
 
@@ -228,6 +293,9 @@ def main():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
                     help="run a calibration kernel and one prefill only (for counter runs)")
+    ap.add_argument("--suite", choices=["full_attention", "sweep"],
+                    help="instead of the benchmark line: the full-attention baseline at the 2.7B shape, "
+                         "or the n_update / window sweep at the 760M shape (one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: a TTT prefill sequence is a recurrence over chunks and "
@@ -237,6 +305,10 @@ def main():
     cfg = get(args.config)
     if args.profile_pass:
         profile_pass(cfg)
+        return
+    if args.suite:
+        fn = suite_full_attention if args.suite == "full_attention" else suite_sweep
+        print(json.dumps(fn(args.steps, args.warmup)), flush=True)
         return
     T = cfg.seq_len
     ms_ttt, ms_swa, kt, mean_loss, tok_np = gpu_bench(cfg, args.steps, args.warmup,

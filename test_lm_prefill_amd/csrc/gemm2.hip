@@ -275,8 +275,10 @@ DEVI void read_step_128(Frag<TI> (&fw)[2][4], Frag<TI> (&fx)[2][4], uint32_t w0,
 // the tiles of steps kt+1 and kt+2 are in flight.  Per step: wait for this
 // wave's loads of step kt, barrier, read the step's fragments, barrier (the
 // stage is free), stream step kt+2 into it, MFMAs.
-template <typename TI>
-__global__ __launch_bounds__(NT, 2) void gemm5_kernel(const GemmArgs g, int epi) {
+// EPI is a template parameter so that each epilogue is its own kernel symbol
+// (profiles then separate the GEMM classes).
+template <typename TI, int EPI>
+__global__ __launch_bounds__(NT, 2) void gemm5_kernel(const GemmArgs g) {
   using C = G2<128>;
   constexpr int SBYTES = C::SBYTES;
   constexpr int CPW = C::ROWS / 8 / 4;  // 1 KiB chunks per wave and stage
@@ -330,25 +332,40 @@ __global__ __launch_bounds__(NT, 2) void gemm5_kernel(const GemmArgs g, int epi)
 #pragma unroll
         for (int j = 0; j < 4; ++j) mma(acc[i][j], fw[ks][i], fx[ks][j]);
   }
-  switch (epi) {
-    case EPI_STORE: gemm2_epilogue<128, EPI_STORE>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
-    case EPI_STORE_F32: gemm2_epilogue<128, EPI_STORE_F32>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
-    case EPI_ADD_F32: gemm2_epilogue<128, EPI_ADD_F32>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
-    case EPI_SWIGLU: gemm2_epilogue<128, EPI_SWIGLU>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
-    case EPI_CE: gemm2_epilogue<128, EPI_CE>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
-    case EPI_DLOGITS: gemm2_epilogue<128, EPI_DLOGITS>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
-    case EPI_SGD: gemm2_epilogue<128, EPI_SGD>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
-    default: gemm2_epilogue<128, 100>(g, acc, m0, n0, tn, wm, wn, lr, lq); break;
-  }
+  gemm2_epilogue<128, EPI>(g, acc, m0, n0, tn, wm, wn, lr, lq);
 }
 
-template __global__ void gemm5_kernel<bf16_t>(const GemmArgs, int);
-template __global__ void gemm5_kernel<f16_t>(const GemmArgs, int);
+#define G5_INST(TI)                                                      \
+  template __global__ void gemm5_kernel<TI, EPI_STORE>(const GemmArgs);     \
+  template __global__ void gemm5_kernel<TI, EPI_STORE_F32>(const GemmArgs); \
+  template __global__ void gemm5_kernel<TI, EPI_ADD_F32>(const GemmArgs);   \
+  template __global__ void gemm5_kernel<TI, EPI_SWIGLU>(const GemmArgs);    \
+  template __global__ void gemm5_kernel<TI, EPI_CE>(const GemmArgs);        \
+  template __global__ void gemm5_kernel<TI, EPI_DLOGITS>(const GemmArgs);   \
+  template __global__ void gemm5_kernel<TI, EPI_SGD>(const GemmArgs);       \
+  template __global__ void gemm5_kernel<TI, 100>(const GemmArgs);
+G5_INST(bf16_t)
+G5_INST(f16_t)
+#undef G5_INST
+
+template <typename TI, int EPI> hipError_t launch5_e(const GemmArgs &g, hipStream_t st) {
+  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + 127) / 128);
+  hipLaunchKernelGGL((gemm5_kernel<TI, EPI>), dim3(tiles, 1, g.ksplit), dim3(NT), 0, st, g);
+  return hipGetLastError();
+}
 
 template <typename TI> hipError_t launch5(int epi, const GemmArgs &g, hipStream_t st) {
-  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + 127) / 128);
-  hipLaunchKernelGGL((gemm5_kernel<TI>), dim3(tiles, 1, g.ksplit), dim3(NT), 0, st, g, g.ksplit > 1 ? 100 : epi);
-  return hipGetLastError();
+  if (g.ksplit > 1) return launch5_e<TI, 100>(g, st);
+  switch (epi) {
+    case EPI_STORE: return launch5_e<TI, EPI_STORE>(g, st);
+    case EPI_STORE_F32: return launch5_e<TI, EPI_STORE_F32>(g, st);
+    case EPI_ADD_F32: return launch5_e<TI, EPI_ADD_F32>(g, st);
+    case EPI_SWIGLU: return launch5_e<TI, EPI_SWIGLU>(g, st);
+    case EPI_CE: return launch5_e<TI, EPI_CE>(g, st);
+    case EPI_DLOGITS: return launch5_e<TI, EPI_DLOGITS>(g, st);
+    case EPI_SGD: return launch5_e<TI, EPI_SGD>(g, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ttt_g2
