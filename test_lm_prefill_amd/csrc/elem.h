@@ -15,9 +15,10 @@ hipError_t rmsnorm_fwd_launch(int dtype, const float *x, const void *g, void *y,
                               int n, int d, float eps, hipStream_t st, bool y_f16 = false);
 
 // dh_out = dh_in + r * (g*dy) - x * r^3 * mean(x * g*dy)   (dh_in may be NULL or alias dh_out);
-// also writes dh_t, the same values in the working dtype.
+// also writes dh_t, the same values in the working dtype (fp16 when t_f16, bf16 mode only).
 hipError_t rmsnorm_bwd_launch(int dtype, const float *dy, const float *x, const float *r, const void *g,
-                              const float *dh_in, float *dh_out, void *dh_t, int n, int d, hipStream_t st);
+                              const float *dh_in, float *dh_out, void *dh_t, int n, int d, hipStream_t st,
+                              bool t_f16 = false);
 
 struct RopeArgs {
   const float *qkv;     // [n][3d] pre-norm q | k | v (fp32: the GEMM output is not rounded before the norm)
@@ -51,8 +52,9 @@ hipError_t attn_bwd_pre_launch(int dtype, const void *dO, const void *O, float *
 
 // SwiGLU backward over 16-row interleaved gate/up blocks.  GU [n][ld_gu],
 // dhmid [n][ld_h] (units), dGU [n][ld_gu]; `units` hidden units processed.
+// All three are fp16 when f16 (bf16 mode only), else the working dtype.
 hipError_t swiglu_bwd_launch(int dtype, const void *GU, const void *dhmid, void *dGU, int n, int units,
-                             long ld_gu, long ld_h, hipStream_t st);
+                             long ld_gu, long ld_h, hipStream_t st, bool f16 = false);
 
 // Combines per-row partials (max, sum exp) into lse[m] and
 // losses[*pos0 + m] = lse - zlab[m].
@@ -73,11 +75,12 @@ hipError_t copy_rows_launch(int dtype, const void *src, long ld_src, void *dst, 
                             hipStream_t st);
 
 // dst[c * ldd + r] = r < R ? src[r * lds + c] : 0 for r < Rpad, c < C.  The
-// destination has the working dtype; the source is fp32 (SRC_F32, always in
-// fp32 mode), the working dtype (SRC_WORK) or fp16 (SRC_F16, bf16 mode).
+// destination has the working dtype, or fp16 when dst_f16 (bf16 mode only);
+// the source is fp32 (SRC_F32, always in fp32 mode), the working dtype
+// (SRC_WORK) or fp16 (SRC_F16, bf16 mode).
 enum { SRC_F32 = 0, SRC_WORK = 1, SRC_F16 = 2 };
 hipError_t transpose_launch(int dtype, int src_kind, const void *src, long lds, void *dst, long ldd, int R, int Rpad,
-                            int C, hipStream_t st);
+                            int C, hipStream_t st, bool dst_f16 = false);
 // dst (fp16) = scale * src (bf16), exact when the scaled value is in fp16's
 // normal range (scale a power of two), with row strides.
 hipError_t bf16_to_f16_launch(const void *src, long lds, void *dst, long ldd, int rows, int cols, hipStream_t st,

@@ -71,9 +71,9 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float *x, const 
 
 // dx = r g dy - x r^3 mean(x g dy) (+ dh_in); written fp32 (dh_out) and in the
 // working dtype (dh_t, the next GEMM's operand).
-template <typename T, int NV>
+template <typename T, typename TY, int NV>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float *dy, const float *x, const float *r,
-                                                          const T *g, const float *dh_in, float *dh_out, T *dh_t,
+                                                          const T *g, const float *dh_in, float *dh_out, TY *dh_t,
                                                           int n, int d) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float *dy, const
         v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
       }
       store4<float>(dh_out + o + i, v);
-      store4<T>(dh_t + o + i, v);
+      store4<TY>(dh_t + o + i, v);
     }
   }
 }
@@ -441,15 +441,20 @@ hipError_t rmsnorm_fwd_launch(int dtype, const float *x, const void *g, void *y,
 }
 
 hipError_t rmsnorm_bwd_launch(int dtype, const float *dy, const float *x, const float *r, const void *g,
-                              const float *dh_in, float *dh_out, void *dh_t, int n, int d, hipStream_t st) {
+                              const float *dh_in, float *dh_out, void *dh_t, int n, int d, hipStream_t st,
+                              bool t_f16) {
   if (n <= 0) return hipSuccess;
+  if (t_f16 && dtype != 1) return hipErrorInvalidValue;
 #define CALL_(NV)                                                                                                  \
-  if (dtype == 1)                                                                                                  \
-    hipLaunchKernelGGL((rmsnorm_bwd_kernel<bf16_t, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, dy, x, r,      \
-                       (const bf16_t *)g, dh_in, dh_out, (bf16_t *)dh_t, n, d);                                    \
+  if (t_f16)                                                                                                       \
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<bf16_t, f16_t, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, dy, x,  \
+                       r, (const bf16_t *)g, dh_in, dh_out, (f16_t *)dh_t, n, d);                                  \
+  else if (dtype == 1)                                                                                             \
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<bf16_t, bf16_t, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, dy, x, \
+                       r, (const bf16_t *)g, dh_in, dh_out, (bf16_t *)dh_t, n, d);                                 \
   else                                                                                                             \
-    hipLaunchKernelGGL((rmsnorm_bwd_kernel<float, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, dy, x, r,       \
-                       (const float *)g, dh_in, dh_out, (float *)dh_t, n, d);
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<float, float, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, dy, x,   \
+                       r, (const float *)g, dh_in, dh_out, (float *)dh_t, n, d);
   NV_DISPATCH(d, CALL_)
 #undef CALL_
   return hipGetLastError();
@@ -496,9 +501,15 @@ hipError_t attn_bwd_pre_launch(int dtype, const void *dO, const void *O, float *
 }
 
 hipError_t swiglu_bwd_launch(int dtype, const void *GU, const void *dhmid, void *dGU, int n, int units, long ld_gu,
-                             long ld_h, hipStream_t st) {
+                             long ld_h, hipStream_t st, bool f16) {
   if (n <= 0) return hipSuccess;
   long tot = (long)n * (units / 4);
+  if (f16) {
+    if (dtype != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(swiglu_bwd_kernel<f16_t>, dim3(blocks_for(tot)), dim3(256), 0, st, (const f16_t *)GU,
+                       (const f16_t *)dhmid, (f16_t *)dGU, n, units, ld_gu, ld_h);
+    return hipGetLastError();
+  }
 #define K_(T, ...)                                                                                                  \
   hipLaunchKernelGGL(swiglu_bwd_kernel<T>, dim3(blocks_for(tot)), dim3(256), 0, st, (const T *)GU, (const T *)dhmid, \
                      (T *)dGU, n, units, ld_gu, ld_h)
@@ -550,9 +561,22 @@ hipError_t copy_rows_launch(int dtype, const void *src, long ld_src, void *dst, 
 }
 
 hipError_t transpose_launch(int dtype, int src_kind, const void *src, long lds, void *dst, long ldd, int R, int Rpad,
-                            int C, hipStream_t st) {
+                            int C, hipStream_t st, bool dst_f16) {
   if (Rpad <= 0 || C <= 0) return hipSuccess;
   dim3 grid((C + 63) / 64, (Rpad + 63) / 64);
+  if (dst_f16) {
+    if (dtype != 1) return hipErrorInvalidValue;
+    if (src_kind == SRC_F32)
+      hipLaunchKernelGGL((transpose_kernel<float, f16_t>), grid, dim3(256), 0, st, (const float *)src, lds,
+                         (f16_t *)dst, ldd, R, Rpad, C);
+    else if (src_kind == SRC_F16)
+      hipLaunchKernelGGL((transpose_kernel<f16_t, f16_t>), grid, dim3(256), 0, st, (const f16_t *)src, lds,
+                         (f16_t *)dst, ldd, R, Rpad, C);
+    else
+      hipLaunchKernelGGL((transpose_kernel<bf16_t, f16_t>), grid, dim3(256), 0, st, (const bf16_t *)src, lds,
+                         (f16_t *)dst, ldd, R, Rpad, C);
+    return hipGetLastError();
+  }
   if (dtype == 1) {
     if (src_kind == SRC_F32)
       hipLaunchKernelGGL((transpose_kernel<float, bf16_t>), grid, dim3(256), 0, st, (const float *)src, lds,

@@ -42,8 +42,8 @@ struct GemmArgs {
   // that multiply the same activations (a multiple of 64, or of 8 for the
   // generic kernel)
   int a_kwrap;
-  // 16-bit outputs (C, and C2 of EPI_SGD) are written as fp16 instead of bf16;
-  // EPI_SWIGLU's C2 (pre-activations kept for the backward) stays bf16
+  // 16-bit outputs (C and C2) are written as fp16 instead of bf16 (streaming
+  // kernel; the generic kernel writes its operand type)
   int c_f16;
   // EPI_SWIGLU and EPI_ADD_F32 multiply the accumulator by acc_scale first (a
   // power of two: B holds weights stored scaled by 1 / acc_scale); EPI_SGD

@@ -88,7 +88,7 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
     return;
   }
   if constexpr (EPI == EPI_SWIGLU) {
-    bf16_t *GU = reinterpret_cast<bf16_t *>(g.C2);
+    void *GU = g.C2;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int m = m0 + wm * 64 + j * 16 + lr;
@@ -107,8 +107,8 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
         }
         store_c4(g, g.C, (long)m * g.ldc + unit, hv);
         if (GU) {
-          store4<bf16_t>(GU + (long)m * g.ldc2 + nb + g4, gv);
-          store4<bf16_t>(GU + (long)m * g.ldc2 + nb + 16 + g4, uv);
+          store_c4(g, GU, (long)m * g.ldc2 + nb + g4, gv);
+          store_c4(g, GU, (long)m * g.ldc2 + nb + 16 + g4, uv);
         }
       }
     }

@@ -36,10 +36,10 @@ struct LayerBuf {
   void *attn_norm = nullptr, *wqkv = nullptr, *wo = nullptr, *q_norm = nullptr, *k_norm = nullptr,
        *mlp_norm = nullptr;
   // gate/up rows interleaved by 16.  Frozen layers: [2F][d].  Updated layers:
-  // fast rows [2F][2d] holding the bf16 working copy as hi | lo (hi = round(W),
-  // lo = round(W - hi), so hi + lo carries the fp32 master to ~16 bits and the
-  // small inner updates are not lost to bf16 rounding), then static rows
-  // [2F][d] at element offset 4Fd.
+  // fast rows [2F][2d] holding the forward working copy as hi | lo (in bf16
+  // mode fp16 of s*W with s = wscale: hi = round(sW), lo = round(sW - hi), so
+  // hi + lo carries the fp32 master to ~22 bits and the small inner updates are
+  // not lost to rounding), then static rows [2F][d] at element offset 4Fd.
   void *wgu = nullptr;
   // Frozen layers: [d][F].  Updated layers: [d][3F] = fast hi | static | fast lo.
   void *wd = nullptr;
@@ -51,7 +51,9 @@ struct LayerBuf {
   // ring planes: K, Vt in the attention forward's type; Kb (bf16 copy of K when the
   // forward is fp16), Kt, V in the working dtype for the backward
   void *K = nullptr, *Vt = nullptr, *Kb = nullptr, *Kt = nullptr, *V = nullptr;
-  // transposed working copies used by the backward GEMMs (k-contiguous operands)
+  // transposed working copies used by the backward GEMMs (k-contiguous
+  // operands); the first three are fp16 in bf16 mode (the MLP backward and the
+  // dO product take fp16 operands), wqkvT is bf16
   void *wdT = nullptr;    // [2F][d]  (fast units first), updated layers
   void *wguT = nullptr;   // [d][4F], updated layers
   void *woT = nullptr;    // [d][d], layers whose attention is back-propagated
@@ -76,6 +78,10 @@ struct ttt_handle {
   // which keeps the fp16 lo part of small weights out of the subnormal range;
   // the GEMMs that read them divide their accumulators by it.  1 in fp32 mode.
   float wscale = 1.f;
+  // bf16 mode: the backward carries the chunk loss times this power of two (so
+  // that its fp16 operands sit well inside fp16's normal range); the SGD step
+  // divides it out.  1 in fp32 mode.
+  float gscale = 1.f;
   int L = 0, d = 0, H = 0, hd = 0, F = 0, V = 0, k = 0, b = 0, nu = 0, R = 0, Vs = 0, P = 0;
   std::vector<void *> allocs;
   std::vector<std::pair<void *, size_t>> zero_list;
@@ -209,9 +215,10 @@ void prof_collect(ttt_handle *h, hipStream_t st) {
 }
 #define PROF(cls) Prof prof_(h, cls, st)
 
-// fwd: the operands are forward activations and weights, fp16 in bf16 mode
-void gemm(ttt_handle *h, int cls, bool akc, bool bkc, int epi, GemmArgs g, hipStream_t st, bool fwd = false) {
-  const int odt = (fwd && h->dt == 1) ? 2 : h->dt;
+// f16op: the operands are fp16 in bf16 mode (forward activations and weights,
+// and the MLP part of the backward)
+void gemm(ttt_handle *h, int cls, bool akc, bool bkc, int epi, GemmArgs g, hipStream_t st, bool f16op = false) {
+  const int odt = (f16op && h->dt == 1) ? 2 : h->dt;
   const int split = gemm_plan(odt, akc, bkc, epi, g, h->ws_elems);
   {
     Prof prof_(h, cls, st);
@@ -402,7 +409,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         g.rowi = h->tok + 1;
         g.pos0 = h->pos0;
         g.col_off = v0;
-        g.alpha = 1.f / (float)n;
+        g.alpha = h->gscale / (float)n;
         gemm(h, K_GEMM_DLOGITS, true, true, EPI_DLOGITS, g, st, true);  // logits recomputed as in the forward
       }
       {
@@ -415,7 +422,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
     }
     {
       PROF(K_RMSNORM_BWD);
-      HIPCHK(rmsnorm_bwd_launch(dt, h->dn, h->hf, h->rf, h->final_norm, nullptr, h->dh, h->dy, n, d, st));
+      HIPCHK(rmsnorm_bwd_launch(dt, h->dn, h->hf, h->rf, h->final_norm, nullptr, h->dh, h->dy, n, d, st, f16));
     }
     h->launches++;
     for (int l = L - 1; l >= L - h->nu; --l) {
@@ -428,12 +435,13 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         GemmArgs g = gargs(h->dy, d, lw.wdT, d, n, Fu, d);
         g.C = h->dhmid;
         g.ldc = 2 * F;
-        gemm(h, K_GEMM_DHMID, true, true, EPI_STORE, g, st);
+        g.c_f16 = f16;
+        gemm(h, K_GEMM_DHMID, true, true, EPI_STORE, g, st, true);
       }
       {
         PROF(K_TRANSPOSE);
-        HIPCHK(transpose_launch(dt, SRC_WORK, h->dy, d, h->dyT, h->b, n, np, d, st));
-        HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, S.hmid, 2 * F, h->hmidT, h->b, n, np, F, st));
+        HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, h->dy, d, h->dyT, h->b, n, np, d, st, f16));
+        HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, S.hmid, 2 * F, h->hmidT, h->b, n, np, F, st, f16));
       }
       // dWd_fast = dy^T hmid_fast over the chunk's tokens, SGD fused into the epilogue
       {
@@ -446,27 +454,27 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         g.ldc2 = 3 * F;
         g.c_f16 = f16;
         g.c_scale = h->wscale;
-        g.alpha = h->cfg.eta;
-        gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st);
+        g.alpha = h->cfg.eta / h->gscale;
+        gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st, true);
       }
       {
         PROF(K_TRANSPOSE);
-        HIPCHK(transpose_launch(dt, SRC_F32, h->m_d[lw.u], F, lw.wdT, d, d, d, F, st));
+        HIPCHK(transpose_launch(dt, SRC_F32, h->m_d[lw.u], F, lw.wdT, d, d, d, F, st, f16));
       }
       {
         PROF(K_SWIGLU_BWD);
-        HIPCHK(swiglu_bwd_launch(dt, S.gu, h->dhmid, h->dgu, n, Fu, 4 * F, 2 * F, st));
+        HIPCHK(swiglu_bwd_launch(dt, S.gu, h->dhmid, h->dgu, n, Fu, 4 * F, 2 * F, st, f16));
       }
       if (!last) {
         GemmArgs g = gargs(h->dgu, 4 * F, lw.wguT, 4 * F, n, d, 4 * F);
         g.Cf = h->dm;
         g.ldcf = d;
-        gemm(h, K_GEMM_DM, true, true, EPI_STORE_F32, g, st);
+        gemm(h, K_GEMM_DM, true, true, EPI_STORE_F32, g, st, true);
       }
       {
         PROF(K_TRANSPOSE);
-        HIPCHK(transpose_launch(dt, SRC_WORK, h->dgu, 4 * F, h->dguT, h->b, n, np, 2 * F, st));
-        HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, S.m, d, h->mT, h->b, n, np, d, st));
+        HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, h->dgu, 4 * F, h->dguT, h->b, n, np, 2 * F, st, f16));
+        HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, S.m, d, h->mT, h->b, n, np, d, st, f16));
       }
       // dW(gate|up)_fast = dGU_fast^T m, SGD fused
       {
@@ -479,25 +487,25 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
         g.ldc2 = 2 * d;
         g.c_f16 = f16;
         g.c_scale = h->wscale;
-        g.alpha = h->cfg.eta;
-        gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st);
+        g.alpha = h->cfg.eta / h->gscale;
+        gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st, true);
       }
       {
         PROF(K_TRANSPOSE);
-        HIPCHK(transpose_launch(dt, SRC_F32, h->m_gu[lw.u], d, lw.wguT, 4 * F, 2 * F, 2 * F, d, st));
+        HIPCHK(transpose_launch(dt, SRC_F32, h->m_gu[lw.u], d, lw.wguT, 4 * F, 2 * F, 2 * F, d, st, f16));
       }
       h->launches += 7;
       if (last) break;
       {
         PROF(K_RMSNORM_BWD);
-        HIPCHK(rmsnorm_bwd_launch(dt, h->dm, S.h1, S.r2, lw.mlp_norm, h->dh, h->dh, h->dy, n, d, st));
+        HIPCHK(rmsnorm_bwd_launch(dt, h->dm, S.h1, S.r2, lw.mlp_norm, h->dh, h->dh, h->dy, n, d, st, f16));
       }
       // attention sub-block backward
       {
         GemmArgs g = gargs(h->dy, d, lw.woT, d, n, d, d);
         g.C = h->dO;
         g.ldc = d;
-        gemm(h, K_GEMM_DO, true, true, EPI_STORE, g, st);
+        gemm(h, K_GEMM_DO, true, true, EPI_STORE, g, st, true);  // dO itself is bf16
       }
       {
         PROF(K_ATTN_BWD_PRE);
@@ -574,7 +582,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
       }
       {
         PROF(K_RMSNORM_BWD);
-        HIPCHK(rmsnorm_bwd_launch(dt, h->da, S.h_in, S.r1, lw.attn_norm, h->dh, h->dh, h->dy, n, d, st));
+        HIPCHK(rmsnorm_bwd_launch(dt, h->da, S.h_in, S.r1, lw.attn_norm, h->dh, h->dh, h->dy, n, d, st, f16));
       }
       h->launches += 6;
     }
@@ -602,8 +610,8 @@ void reset_fast(ttt_handle *h, hipStream_t st) {
     HIPCHK(convert_rows_launch(fdt, h->i_d[lw.u], F, lw.wd, 3 * F, d, F, st,
                                h->dt == 1 ? off(lw.wd, (size_t)2 * F * h->es) : nullptr, 3 * F, h->wscale));
     // Wd_cat^T [2F][d] rows [0, F) and Wgu_cat^T [d][4F] columns [0, 2F), from the masters
-    HIPCHK(transpose_launch(h->dt, SRC_F32, h->i_d[lw.u], F, lw.wdT, d, d, d, F, st));
-    HIPCHK(transpose_launch(h->dt, SRC_F32, h->i_gu[lw.u], d, lw.wguT, 4 * F, 2 * F, 2 * F, d, st));
+    HIPCHK(transpose_launch(h->dt, SRC_F32, h->i_d[lw.u], F, lw.wdT, d, d, d, F, st, h->dt == 1));
+    HIPCHK(transpose_launch(h->dt, SRC_F32, h->i_gu[lw.u], d, lw.wguT, 4 * F, 2 * F, 2 * F, d, st, h->dt == 1));
   }
 }
 
@@ -702,6 +710,7 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
   h->cfg = c;
   h->dt = c.dtype == TTT_BF16 ? 1 : 0;
   h->es = h->dt ? 2 : 4;
+  h->gscale = h->dt ? 4096.f : 1.f;
   h->L = c.n_layers;
   h->d = c.d_model;
   h->H = c.n_heads;
@@ -815,14 +824,15 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
         lw.wdT = dalloc(h, 2 * fd, false);
         lw.wguT = dalloc(h, 4 * fd, false);
         // static parts of Wd_cat^T (rows [F, 2F)) and Wgu_cat^T (columns [2F, 4F))
-        HIPCHK(transpose_launch(h->dt, SRC_WORK, off(lw.wd, (size_t)F * es), 3 * F, off(lw.wdT, fd), d, d, d, F, st));
+        HIPCHK(transpose_launch(h->dt, SRC_WORK, off(lw.wd, (size_t)F * es), 3 * F, off(lw.wdT, fd), d, d, d, F, st,
+                                h->dt == 1));
         HIPCHK(transpose_launch(h->dt, SRC_WORK, off(lw.wgu, 4 * fd), d, off(lw.wguT, (size_t)2 * F * es), 4 * F,
-                                2 * F, 2 * F, d, st));
+                                2 * F, 2 * F, d, st, h->dt == 1));
       }
       if (lw.bwd_attn) {
         lw.woT = dalloc(h, dd, false);
         lw.wqkvT = dalloc(h, 3 * dd, false);
-        HIPCHK(transpose_launch(h->dt, SRC_WORK, lw.wo, d, lw.woT, d, d, d, d, st));
+        HIPCHK(transpose_launch(h->dt, SRC_WORK, lw.wo, d, lw.woT, d, d, d, d, st, h->dt == 1));  // fp16 in bf16 mode
         HIPCHK(transpose_launch(h->dt, SRC_WORK, lw.wqkv, d, lw.wqkvT, 3 * d, 3 * d, 3 * d, d, st));
       }
       if (h->dt == 1) {

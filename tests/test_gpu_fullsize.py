@@ -83,12 +83,6 @@ def test_fullsize_fp32_whole_sequence_125m():
         torch.cuda.empty_cache()
 
 
-# bf16 activation rounding alone (reproduced on the CPU by rounding the oracle's
-# GEMM inputs to bf16) gives per-token loss deviations with a standard
-# deviation of about 4e-3 at the 125M shape and more at 760M, so the largest of
-# 1e4..3e4 tokens sits near or above 2e-2; expected to fail until the forward
-# activations carry more precision.
-@pytest.mark.xfail(strict=False, reason="bf16 activation rounding noise reaches the 2e-2 per-token bound")
 @pytest.mark.parametrize("name", NAMES)
 def test_fullsize_against_oracle_prefix(name):
     from test_lm_prefill_amd import Session
