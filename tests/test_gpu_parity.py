@@ -184,3 +184,38 @@ def test_qk_gains_score_bound(case):
     ol, of, _ = run_oracle(cfg, tok, weights_np=wn)
     dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, wn), f"gains-{case}")
     assert dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
+
+
+@pytest.mark.parametrize("dtype,n_update", [("bf16", 0), ("bf16", 2), ("fp32", 0)])
+def test_window_covers_sequence(dtype, n_update):
+    """Full causal attention: the window (and the ring, k + b rows) covers the
+    whole sequence, so no key is ever evicted.  n_update = 0 is the plain
+    Transformer timed as the full-attention baseline; with updates it is
+    TTT over full attention."""
+    T = 700
+    cfg = mid(64, dtype=dtype, T=T, k=768, b=128, n_update=n_update)
+    say(f"case: full window {dtype} n_update={n_update} T={T} k={cfg.window}")
+    tok = rand_tokens(T + 1, cfg.vocab, seed=200 + n_update)
+    sess, _ = gpu_session(cfg)
+    flags = TTT_NO_UPDATE if n_update == 0 else 0
+    gl, gf = run_gpu(sess, tok, flags=flags, want_fast=n_update > 0)
+    ol, of, w = run_oracle(cfg, tok)
+    dl, wr, dwr = compare(cfg, gl, gf if n_update else None, ol, of if n_update else None, fast_init(cfg, w),
+                          f"fullwin {dtype} nu={n_update}")
+    assert dl <= (1e-4 if dtype == "fp32" else 2e-2)
+    if n_update:
+        assert wr <= 1e-2 and dwr <= 5e-2
+
+
+@pytest.mark.parametrize("n_update,L", [(1, 3), (4, 4)])
+def test_n_update_extremes(n_update, L):
+    """One updated block, and every block updated (the first block's attention
+    is then back-propagated too only from blocks above it)."""
+    cfg = mid(64, T=600, L=L, n_update=n_update)
+    say(f"case: n_update={n_update} of L={L}")
+    tok = rand_tokens(cfg.seq_len + 1, cfg.vocab, seed=300 + n_update)
+    sess, _ = gpu_session(cfg)
+    gl, gf = run_gpu(sess, tok)
+    ol, of, w = run_oracle(cfg, tok)
+    dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, w), f"nu={n_update}/L={L}")
+    assert dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
