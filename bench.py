@@ -358,6 +358,11 @@ def main():
                      "mfma_util_pct": round(100 * swa_tf / (ms_swa_step / 1e3) / peak, 2)},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic (seeded Zipf+span-copy ids, seeded random-init weights)",
+        "precision": ({"weights": "bf16 values", "forward_operands": "fp16",
+                       "mlp_backward_operands": "fp16 (loss scaled by 2^12)",
+                       "attention_and_vocab_backward_operands": "bf16", "accumulate": "fp32",
+                       "fast_weight_master": "fp32", "residual_stream_and_losses": "fp32"}
+                      if cfg.dtype == "bf16" else {"all": "fp32"}),
         "config": {"workload": cfg.name, "n_layers": cfg.n_layers, "d_model": cfg.d_model, "n_heads": cfg.n_heads,
                    "d_ff": cfg.d_ff, "vocab": cfg.vocab, "seq_len": T, "window": cfg.window, "chunk": cfg.chunk,
                    "n_update": cfg.n_update, "eta": cfg.eta},
