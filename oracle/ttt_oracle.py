@@ -14,7 +14,11 @@ Algorithm 1, with Eq. (9) of section 5 and Eq. (3) of section 3):
   * take the gradient of the chunk's mean loss A_i(W) (Eq. 9) with respect to
     the fast weights only (step 3.4) and one SGD step W <- W - eta * grad
     (step 3.5, Eq. 9);
-  * keep only the attention state the window still needs (step 3.6).
+  * keep only the attention state the window still needs (step 3.6);
+  * after a prefill, generation with periodic updates (Algorithm 3): feed one
+    position at a time, take the next id from the prediction (or as given), and
+    once a chunk of b positions has all its targets, update W on that chunk as
+    Algorithm 1 does (``Oracle.decode``).
 
 Model (pre-norm Transformer with sliding-window attention and QK-norm; the
 jdon.com page, "架构极简" paragraph and the basic-recipe paragraph; the notes,
@@ -285,7 +289,8 @@ class Oracle:
         return grads
 
     # ---------------------------------------------------------------- Algorithm 1
-    def prefill(self, tokens, eta=None, no_update=False, W_init=None, return_trace=False, progress=None):
+    def prefill(self, tokens, eta=None, no_update=False, W_init=None, return_trace=False, progress=None,
+                return_cache=False):
         """Run Algorithm 1 on ids x_0..x_T; returns (losses[T], W_N[, trace]).
 
         Position p (0 <= p < T) predicts x_{p+1}; chunk i holds positions
@@ -316,9 +321,60 @@ class Oracle:
             cache = new_cache
             if progress is not None:
                 progress(s0, n)
+        if return_cache:
+            return losses, W, cache
         if return_trace:
             return losses, W, trace
         return losses, W
+
+    # ---------------------------------------------------------------- Algorithm 3
+    def decode(self, tokens, n_steps, forced=None, eta=None, no_update=False):
+        """Generation with periodic updates (the notes, section 7, Algorithm 3) after
+        Algorithm 1 on `tokens` = x_0..x_P (P scored positions).
+
+        Positions P, P+1, ... are fed one at a time with the current fast weights and
+        attention state; the id after each is forced[j] if given, else the argmax of
+        the prediction (lowest id among equal logits).  Decode chunks are
+        [P + i*b, P + (i+1)*b) (reading: counted from where the prefill stopped).
+        Once a chunk's last target is known, its mean loss under the weights that
+        predicted it, with the attention state of the chunk's start, is
+        back-propagated and one SGD step taken, exactly as for a prefill chunk,
+        before the next position is fed.
+
+        Returns (prefill losses [P], next ids [n_steps], step losses [n_steps],
+        top-2 logit margins [n_steps], W).
+        """
+        c = self.cfg
+        eta = c.eta if eta is None else eta
+        b = c.chunk
+        pre_losses, W, cache = self.prefill(tokens, eta=eta, no_update=no_update, return_cache=True)
+        seq = [int(x) for x in np.asarray(tokens)]
+        P = len(seq) - 1
+        chunk_cache = cache
+        s0 = P
+        ids = np.zeros(n_steps, dtype=np.int64)
+        step_losses = np.zeros(n_steps, dtype=self.dt)
+        margins = np.zeros(n_steps, dtype=self.dt)
+        for j in range(n_steps):
+            p = P + j
+            _, saved, cache = self.chunk_forward(W, cache, np.array([seq[p]]), np.array([0]), p)
+            z = saved["z"][0]
+            nxt = int(forced[j]) if forced is not None else int(np.argmax(z))
+            top2 = np.sort(z)[-2:]
+            margins[j] = top2[1] - top2[0]
+            step_losses[j] = saved["lse"][0] - z[nxt]
+            ids[j] = nxt
+            seq.append(nxt)
+            if p + 1 - s0 == b:
+                if not no_update and self.nu > 0:
+                    x_in = np.array(seq[s0:s0 + b])
+                    labels = np.array(seq[s0 + 1:s0 + b + 1])
+                    _, saved_c, cache = self.chunk_forward(W, chunk_cache, x_in, labels, s0)
+                    G = self.chunk_grad(W, saved_c)
+                    W = [[sgd_step(w, g, eta) for w, g in zip(ws, gs)] for ws, gs in zip(W, G)]
+                chunk_cache = cache
+                s0 += b
+        return pre_losses, ids, step_losses, margins, W
 
     def chunk_loss(self, W, cache, tokens, s0, n):
         """A_i(W): mean loss of the chunk at [s0, s0+n) with the state `cache` fixed."""

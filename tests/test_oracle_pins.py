@@ -356,3 +356,57 @@ def test_ragged_last_chunk_and_empty():
     assert len(l0) == 0
     for ws, u in zip(W0, range(cfg.n_update)):
         assert np.array_equal(ws[0], w[f"fast{u}.w_gate"].astype(np.float64))
+
+
+# ----------------------------------------------------------------------------- Pin 14
+def test_pin14_decode_eta0_is_greedy_generation():
+    """Algorithm 3 with the inner step size zero is plain greedy generation with the
+    frozen model: every generated id is the argmax of the next-token logits of the
+    whole sequence so far (an independent torch forward over the prefix), and every
+    step loss is that forward's cross-entropy of the generated id."""
+    cfg = micro(eta=0.0, window=12, chunk=8)
+    w = rand_gains(cfg, make_weights_np(cfg))
+    prompt = rand_tokens(17, cfg.vocab, seed=21)       # 16 scored positions
+    o = Oracle(cfg, w)
+    _, ids, step_losses, margins, _ = o.decode(prompt, 20)
+    fast = torch_ref.fast_tensors(torch_ref.fast_from_weights(cfg, w))
+    seq = list(prompt)
+    with torch.no_grad():
+        for j in range(20):
+            z = torch_ref.forward_losses(cfg, w, seq + [0], fast, mask="band", return_logits=True)[-1].numpy()
+            assert margins[j] > 1e-9
+            assert int(np.argmax(z)) == ids[j], j
+            lse = np.log(np.sum(np.exp(z - z.max()))) + z.max()
+            assert abs((lse - z[ids[j]]) - step_losses[j]) < 1e-10, j
+            seq.append(int(ids[j]))
+
+
+@pytest.mark.parametrize("greedy", [False, True])
+def test_pin15_decode_updates_follow_algorithm1(greedy):
+    """Algorithm 3's update after every b generated ids is Algorithm 1's chunk step
+    on the generated sequence: with the prompt a whole number of chunks, decoding
+    (forced or greedy) and then prefilling the prompt plus the generated ids give
+    the same fast weights and the same per-position losses; a shorter decode is a
+    prefix of a longer one."""
+    cfg = micro(eta=0.5, window=12, chunk=8)
+    w = rand_gains(cfg, make_weights_np(cfg))
+    prompt = rand_tokens(17, cfg.vocab, seed=22)
+    n = 24                                              # three decode chunks
+    forced = None if greedy else rand_tokens(n, cfg.vocab, seed=23)
+    o = Oracle(cfg, w)
+    pre, ids, step_losses, _, W = o.decode(prompt, n, forced=forced)
+    if forced is not None:
+        assert np.array_equal(ids, forced)
+    full = np.concatenate([prompt, ids]).astype(np.int64)
+    l_full, W_full = Oracle(cfg, w).prefill(full)
+    np.testing.assert_allclose(l_full[:16], pre, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l_full[16:], step_losses, rtol=0, atol=1e-10)
+    for a, b in zip([x for ws in W for x in ws], [x for ws in W_full for x in ws]):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    # the decode updates did something, and the first chunk's ids precede them
+    _, ids0, sl0, _, W0 = Oracle(cfg, w).decode(prompt, n, forced=forced, no_update=True)
+    assert np.max(np.abs(step_losses[8:] - sl0[8:])) > 1e-4
+    if greedy:
+        _, ids_pre, sl_pre, _, _ = Oracle(cfg, w).decode(prompt, 11)
+        assert np.array_equal(ids_pre, ids[:11])
+        np.testing.assert_allclose(sl_pre, step_losses[:11], rtol=0, atol=1e-12)

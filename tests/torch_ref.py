@@ -28,8 +28,9 @@ def rope_complex(x, pos, theta):
     return torch.cat([z.real, z.imag], dim=-1)
 
 
-def forward_losses(cfg, weights, tokens, fast, mask="band", wo_zero=False):
-    """Per-token losses of the whole sequence; `fast` is a list of [wg, wu, wd] tensors."""
+def forward_losses(cfg, weights, tokens, fast, mask="band", wo_zero=False, return_logits=False):
+    """Per-token losses of the whole sequence; `fast` is a list of [wg, wu, wd] tensors.
+    With return_logits, the logits [T, V] instead."""
     L, d, H, hd = cfg.n_layers, cfg.d_model, cfg.n_heads, cfg.head_dim
     eps = cfg.rms_eps
     tok = torch.as_tensor(np.asarray(tokens), dtype=torch.long)
@@ -67,6 +68,8 @@ def forward_losses(cfg, weights, tokens, fast, mask="band", wo_zero=False):
         h = h + y
     n = F.rms_norm(h, (d,), W["final_norm"], eps)
     z = F.linear(n, W["lm_head"])
+    if return_logits:
+        return z
     return F.cross_entropy(z, labels, reduction="none")
 
 
