@@ -144,8 +144,36 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
 ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float *d_losses,
                        float *const *d_fast_out, uint32_t flags, void *stream);
 
+/*
+ * Algorithm 3 of the notes (generation with periodic updates), continuing the
+ * sequence that the last ttt_prefill (given tokens), or ttt_decode, on this
+ * handle left: its fast weights, its window of keys/values and its length P
+ * (positions 0..P-1 processed; the id at position P, the prefill's last label,
+ * is known).
+ *   n_steps       positions fed, P + n_steps <= cfg.max_tokens.
+ *   d_forced      device int32 [n_steps] or NULL.  NULL: each next id is the
+ *                 argmax of the current prediction (greedy; lowest id among equal
+ *                 logits).  Otherwise id j is taken as the next token whatever the
+ *                 prediction (teacher forcing, for evaluation and tests).
+ *   d_tokens_out  device int32 [n_steps] out: the ids at positions P+1..P+n_steps.
+ *   d_losses_out  device float32 [n_steps] out: -ln p(next id | prefix) at each
+ *                 fed position, under the fast weights current at that position.
+ *   d_fast_out    as for ttt_prefill: the fast weights after the call, or NULL.
+ * Decode chunks are [P, P+b), [P+b, P+2b), ... counted from the length the
+ * prefill left.  Once every target of the open chunk is known (after the step
+ * that produces id s+b), the chunk's forward is run again and its mean loss
+ * back-propagated into the fast weights with one SGD step, exactly as a
+ * prefill chunk (no update with TTT_NO_UPDATE or n_update = 0); the next
+ * position then uses the new weights.  A partial chunk is kept open for the
+ * next call.  Returns after enqueueing; ttt_check_finite covers these losses
+ * too.  TTT_EINVAL when no prefill with tokens preceded it or the length
+ * would pass max_tokens.
+ */
+ttt_status ttt_decode(ttt_handle *h, int64_t n_steps, const int32_t *d_forced, int32_t *d_tokens_out,
+                      float *d_losses_out, float *const *d_fast_out, uint32_t flags, void *stream);
+
 /* Synchronises `stream` and returns TTT_ENONFINITE if any loss of the last
- * prefill on this handle was NaN or infinite, TTT_OK otherwise. */
+ * prefill or decode on this handle was NaN or infinite, TTT_OK otherwise. */
 ttt_status ttt_check_finite(ttt_handle *h, void *stream);
 
 /* Number of chunks and of kernel launches per chunk of the last prefill (host values). */

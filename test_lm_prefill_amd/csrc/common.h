@@ -148,6 +148,11 @@ DEVI float group4_max(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// min over the four lanes l, l^16, l^32, l^48
+DEVI int group4_min_int(int v) {
+  v = min(v, __shfl_xor(v, 16));
+  return min(v, __shfl_xor(v, 32));
+}
 DEVI float group4_sum(float v) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = __uint_as_float(r[0]) + __uint_as_float(r[1]);

@@ -61,6 +61,12 @@ hipError_t swiglu_bwd_launch(int dtype, const void *GU, const void *dhmid, void 
 hipError_t ce_reduce_launch(const float2 *part, int P, const float *zlab, const int *pos0, float *lse,
                             float *losses, int n, hipStream_t st);
 
+// Greedy choice for the last of n rows: over the per-tile partials (max, sum
+// exp) and their argmax columns, the largest logit (lowest id on ties) goes to
+// tok[*pos0 + n] and lse[n-1] - max to losses[*pos0 + n - 1].
+hipError_t decode_pick_launch(const float2 *part, const int *part_arg, int P, const float *lse, const int *pos0, int n,
+                              int *tok, float *losses, hipStream_t st);
+
 // Rotary table: cs[p][i] = (cos, sin)(p * theta^(-2i/hd)) evaluated in fp64.
 hipError_t rope_table_launch(float2 *cs, long max_pos, int hd, double theta, hipStream_t st);
 

@@ -388,6 +388,41 @@ __global__ void finite_check_kernel(const float *x, long n, int *flag) {
   if (bad) atomicOr(flag, 1);
 }
 
+// Greedy next token of the last position: the largest logit over the vocabulary
+// tiles' partials (lowest id on ties), written to tok[p + 1] with the loss
+// lse - max at losses[p], p = *pos0 + n - 1.
+__global__ __launch_bounds__(64) void decode_pick_kernel(const float2 *part, const int *part_arg, int P,
+                                                         const float *lse, const int *pos0, int n, int *tok,
+                                                         float *losses) {
+  const int lane = threadIdx.x;
+  const int row = n - 1;
+  float mx = -INFINITY;
+  int ai = 0x7fffffff;
+  for (int i = lane; i < P; i += 64) {
+    const float2 v = part[(long)row * P + i];
+    if (!(v.y > 0.f)) continue;  // tile half with no column
+    const int a = part_arg[(long)row * P + i];
+    if (v.x > mx || (v.x == mx && a < ai)) {
+      mx = v.x;
+      ai = a;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(mx, o);
+    const int a2 = __shfl_xor(ai, o);
+    if (m2 > mx || (m2 == mx && a2 < ai)) {
+      mx = m2;
+      ai = a2;
+    }
+  }
+  if (lane == 0) {
+    const int p = *pos0 + row;
+    tok[p + 1] = ai;
+    losses[p] = lse[row] - mx;
+  }
+}
+
 inline unsigned blocks_for(long n, int per = 256) { return (unsigned)((n + per - 1) / per); }
 
 }  // namespace
@@ -515,6 +550,13 @@ hipError_t swiglu_bwd_launch(int dtype, const void *GU, const void *dhmid, void 
                      (T *)dGU, n, units, ld_gu, ld_h)
   DT_DISPATCH(dtype, K_, 0);
 #undef K_
+  return hipGetLastError();
+}
+
+hipError_t decode_pick_launch(const float2 *part, const int *part_arg, int P, const float *lse, const int *pos0, int n,
+                              int *tok, float *losses, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_pick_kernel, dim3(1), dim3(64), 0, st, part, part_arg, P, lse, pos0, n, tok, losses);
   return hipGetLastError();
 }
 

@@ -35,6 +35,7 @@ struct GemmArgs {
   float2 *part;       // EPI_CE partials [M][part_ld]
   int part_ld;
   float *zlab;        // EPI_CE label logits [M]
+  int *part_arg;      // EPI_CE, optional: per-tile argmax column (+ col_off) beside each partial, lowest on ties
   float alpha;
   int col_off;
   // > 0: A is [M][a_kwrap] and its reduction index is taken modulo a_kwrap, so

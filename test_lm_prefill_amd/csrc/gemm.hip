@@ -216,6 +216,18 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const GemmArgs g) {
           if (n < g.N) mx = fmaxf(mx, acc[i][j][r]);
         }
       mx = group4_max(mx);
+      if (g.part_arg) {  // lowest column holding the tile's maximum (columns increase with i, r)
+        int ai = 0x7fffffff;
+#pragma unroll
+        for (int i = 3; i >= 0; --i)
+#pragma unroll
+          for (int r = 3; r >= 0; --r) {
+            const int n = n0 + wn * 64 + i * 16 + g4 + r;
+            if (n < g.N && acc[i][j][r] == mx) ai = n;
+          }
+        ai = group4_min_int(ai);
+        if (m < g.M && (lane >> 4) == 0) g.part_arg[(long)m * g.part_ld + tn * 2 + wn] = ai + g.col_off;
+      }
       float s = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)

@@ -71,6 +71,18 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
           if (n < g.N) mx = fmaxf(mx, acc[i][j][r]);
         }
       mx = group4_max(mx);
+      if (g.part_arg) {  // lowest column holding the tile's maximum (columns increase with i, r)
+        int ai = 0x7fffffff;
+#pragma unroll
+        for (int i = NI - 1; i >= 0; --i)
+#pragma unroll
+          for (int r = 3; r >= 0; --r) {
+            const int n = n0 + wn * WN + i * 16 + g4 + r;
+            if (n < g.N && acc[i][j][r] == mx) ai = n;
+          }
+        ai = group4_min_int(ai);
+        if (m < g.M && lq == 0) g.part_arg[(long)m * g.part_ld + tn * 2 + wn] = ai + g.col_off;
+      }
       float s = 0.f;
 #pragma unroll
       for (int i = 0; i < NI; ++i)

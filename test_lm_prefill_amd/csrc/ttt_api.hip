@@ -111,7 +111,15 @@ struct ttt_handle {
   float *attn_ws = nullptr;
   std::vector<Saved> saved;
   // graphs: [0] update, [1] no-update
-  hipGraphExec_t gexec[2] = {nullptr, nullptr};
+  // captured steps: full-chunk prefill with / without update, decode step greedy /
+  // forced, full-chunk recompute-and-update of a decoded chunk
+  hipGraphExec_t gexec[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  // continuation state for ttt_decode: positions processed, start of the open
+  // decode chunk, and whether a prefill has set them
+  int64_t len = 0, dstart = 0;
+  bool have_state = false;
+  float *rlosses = nullptr;  // [max_tokens] losses of recomputed decode chunks
+  int *part_arg = nullptr;   // [b][P] argmax columns beside the CE partials
   hipStream_t cap = nullptr;
   int64_t chunks_last = 0;
   int64_t launches = 0;
@@ -232,7 +240,14 @@ void gemm(ttt_handle *h, int cls, bool akc, bool bkc, int epi, GemmArgs g, hipSt
 }
 
 // --------------------------------------------------------------------------- the chunk step
-void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
+// What a step does besides the chunk forward (and, with update, its backward and SGD).
+enum ChunkMode {
+  MODE_PREFILL = 0,   // losses[pos] = loss of the stored label
+  MODE_GREEDY = 1,    // decode: also picks the argmax as the next token (tok[pos + n]) with its loss
+  MODE_RECOMPUTE = 2  // a decoded chunk run again for its update; losses go to rlosses
+};
+
+void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode = MODE_PREFILL) {
   const int d = h->d, F = h->F, L = h->L, dt = h->dt;
   const size_t es = h->es;
   const float eps = h->cfg.rms_eps;
@@ -388,13 +403,17 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st) {
     g.part = h->part;
     g.part_ld = h->P;
     g.zlab = h->zlab;
+    if (mode == MODE_GREEDY) g.part_arg = h->part_arg;
     gemm(h, K_GEMM_HEAD_CE, true, true, EPI_CE, g, st, true);
   }
   {
     PROF(K_CE_REDUCE);
-    HIPCHK(ce_reduce_launch(h->part, h->P, h->zlab, h->pos0, h->lse, h->losses, n, st));
+    HIPCHK(ce_reduce_launch(h->part, h->P, h->zlab, h->pos0, h->lse, mode == MODE_RECOMPUTE ? h->rlosses : h->losses,
+                            n, st));
+    if (mode == MODE_GREEDY)
+      HIPCHK(decode_pick_launch(h->part, h->part_arg, h->P, h->lse, h->pos0, n, h->tok, h->losses, st));
   }
-  h->launches += 2;
+  h->launches += mode == MODE_GREEDY ? 3 : 2;
 
   if (update && h->nu > 0) {
     const int np = (n + 63) / 64 * 64;  // token count padded for the weight-gradient GEMMs
@@ -629,7 +648,7 @@ ttt_status fail(ttt_handle *h, ttt_status s, const std::string &msg) {
 }
 
 void free_all(ttt_handle *h) {
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 5; ++i)
     if (h->gexec[i]) hipGraphExecDestroy(h->gexec[i]);
   if (h->cap) hipStreamDestroy(h->cap);
   for (void *p : h->allocs) hipFree(p);
@@ -666,6 +685,52 @@ float score_bound(ttt_handle *h, const void *gq, const void *gk, hipStream_t st)
   // 1% headroom for the bf16 rounding of the normalised rows
   const double b = 1.01 * mx(q) * mx(k) * std::sqrt((double)h->hd) * 1.4426950408889634;
   return (b > 0.0 && b <= ATTN_MAX_SBOUND) ? (float)b : 0.f;
+}
+
+// One step of n positions in the given mode: replayed from a captured graph when
+// graph replay is on and the step has its full size (b for chunks, 1 for decode
+// steps), else enqueued launch by launch.
+void run_step(ttt_handle *h, int n, bool update, int mode, bool use_graph, hipStream_t st) {
+  int gi = -1;
+  if (use_graph) {
+    if (mode == MODE_PREFILL && n == h->b) gi = update ? 0 : 1;
+    if (mode == MODE_GREEDY && n == 1 && !update) gi = 2;
+    if (mode == MODE_PREFILL && n == 1 && !update) gi = 3;
+    if (mode == MODE_RECOMPUTE && n == h->b && update) gi = 4;
+  }
+  if (gi < 0) {
+    enqueue_chunk(h, n, update, st, mode);
+    prof_collect(h, st);
+    return;
+  }
+  if (!h->gexec[gi]) {
+    hipGraph_t gr = nullptr;
+    HIPCHK(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
+    try {
+      enqueue_chunk(h, n, update, h->cap, mode);
+    } catch (...) {
+      hipStreamEndCapture(h->cap, &gr);
+      if (gr) hipGraphDestroy(gr);
+      throw;
+    }
+    HIPCHK(hipStreamEndCapture(h->cap, &gr));
+    hipError_t e = hipGraphInstantiate(&h->gexec[gi], gr, nullptr, nullptr, 0);
+    hipGraphDestroy(gr);
+    HIPCHK(e);
+  }
+  HIPCHK(hipGraphLaunch(h->gexec[gi], st));
+}
+
+void copy_fast_out(ttt_handle *h, float *const *d_fast_out, hipStream_t st) {
+  const int d = h->d, F = h->F;
+  const size_t blk = (size_t)16 * d * 4;
+  for (int u = 0; u < h->nu; ++u) {
+    HIPCHK(hipMemcpy2DAsync(d_fast_out[3 * u + 0], blk, h->m_gu[u], 2 * blk, blk, F / 16, hipMemcpyDeviceToDevice,
+                            st));
+    HIPCHK(hipMemcpy2DAsync(d_fast_out[3 * u + 1], blk, (char *)h->m_gu[u] + blk, 2 * blk, blk, F / 16,
+                            hipMemcpyDeviceToDevice, st));
+    HIPCHK(hipMemcpyAsync(d_fast_out[3 * u + 2], h->m_d[u], (size_t)d * F * 4, hipMemcpyDeviceToDevice, st));
+  }
 }
 
 }  // namespace
@@ -885,6 +950,8 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     h->zlab = (float *)dalloc(h, b * 4);
     h->lse = (float *)dalloc(h, b * 4);
     h->part = (float2 *)dalloc(h, (size_t)b * h->P * sizeof(float2));
+    h->part_arg = (int *)dalloc(h, (size_t)b * h->P * sizeof(int));
+    h->rlosses = (float *)dalloc(h, c.max_tokens * sizeof(float));
     if (h->nu > 0) {
       h->dz = dalloc(h, (size_t)b * h->Vs * es);
       h->dn = (float *)dalloc(h, bd * 4);
@@ -964,9 +1031,9 @@ ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float 
   const bool update = !(flags & TTT_NO_UPDATE) && h->nu > 0;
   const bool use_graph = !(flags & TTT_NO_GRAPH) && !h->prof;
   hipStream_t st = (hipStream_t)stream;
-  const int b = h->b, d = h->d, F = h->F;
+  const int b = h->b;
   try {
-    if (T > 0)
+    if (d_tokens)
       HIPCHK(hipMemcpyAsync(h->tok, d_tokens, (size_t)(T + 1) * sizeof(int), hipMemcpyDeviceToDevice, st));
     HIPCHK(set_int_launch(h->pos0, 0, st));
     HIPCHK(set_int_launch(h->flag, 0, st));
@@ -974,57 +1041,67 @@ ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float 
     reset_fast(h, st);
     const int64_t nfull = T / b;
     const int tail = (int)(T % b);
-    if (nfull > 0) {
-      hipGraphExec_t ex = nullptr;
-      if (use_graph) {
-        const int gi = update ? 0 : 1;
-        if (!h->gexec[gi]) {
-          // capture one full-chunk step on the private stream
-          hipGraph_t gr = nullptr;
-          HIPCHK(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
-          try {
-            enqueue_chunk(h, b, update, h->cap);
-          } catch (...) {
-            hipStreamEndCapture(h->cap, &gr);
-            if (gr) hipGraphDestroy(gr);
-            throw;
-          }
-          HIPCHK(hipStreamEndCapture(h->cap, &gr));
-          hipError_t e = hipGraphInstantiate(&h->gexec[gi], gr, nullptr, nullptr, 0);
-          hipGraphDestroy(gr);
-          HIPCHK(e);
-        }
-        ex = h->gexec[gi];
-      }
-      for (int64_t c = 0; c < nfull; ++c) {
-        if (ex) {
-          HIPCHK(hipGraphLaunch(ex, st));
-        } else {
-          enqueue_chunk(h, b, update, st);
-          prof_collect(h, st);
-        }
-      }
-    }
-    if (tail > 0) {
-      enqueue_chunk(h, tail, update, st);
-      prof_collect(h, st);
-    }
+    for (int64_t c = 0; c < nfull; ++c) run_step(h, b, update, MODE_PREFILL, use_graph, st);
+    if (tail > 0) run_step(h, tail, update, MODE_PREFILL, use_graph, st);
     if (T > 0) {
       HIPCHK(hipMemcpyAsync(d_losses, h->losses, (size_t)T * sizeof(float), hipMemcpyDeviceToDevice, st));
       HIPCHK(finite_check_launch(h->losses, T, h->flag, st));
     }
-    if (d_fast_out) {
-      const size_t blk = (size_t)16 * d * 4;
-      for (int u = 0; u < h->nu; ++u) {
-        HIPCHK(hipMemcpy2DAsync(d_fast_out[3 * u + 0], blk, h->m_gu[u], 2 * blk, blk, F / 16, hipMemcpyDeviceToDevice,
-                                st));
-        HIPCHK(hipMemcpy2DAsync(d_fast_out[3 * u + 1], blk, (char *)h->m_gu[u] + blk, 2 * blk, blk, F / 16,
-                                hipMemcpyDeviceToDevice, st));
-        HIPCHK(hipMemcpyAsync(d_fast_out[3 * u + 2], h->m_d[u], (size_t)d * F * 4, hipMemcpyDeviceToDevice, st));
-      }
-    }
+    if (d_fast_out) copy_fast_out(h, d_fast_out, st);
+    h->len = T;
+    h->dstart = T;
+    h->have_state = d_tokens != nullptr;  // the token at position T is known
     h->chunks_last = nfull + (tail > 0 ? 1 : 0);
   } catch (const HipFail &f) {
+    h->have_state = false;
+    return fail_hip(h, f);
+  }
+  return TTT_OK;
+}
+
+ttt_status ttt_decode(ttt_handle *h, int64_t n_steps, const int32_t *d_forced, int32_t *d_tokens_out,
+                      float *d_losses_out, float *const *d_fast_out, uint32_t flags, void *stream) {
+  if (!h) return fail(nullptr, TTT_EINVAL, "null handle");
+  if (!h->have_state) return fail(h, TTT_EINVAL, "no prefill state to continue (run ttt_prefill with tokens first)");
+  if (n_steps < 0 || h->len + n_steps > h->cfg.max_tokens)
+    return fail(h, TTT_EINVAL, "n_steps out of range: the sequence may not exceed max_tokens positions");
+  if (n_steps > 0 && (!d_tokens_out || !d_losses_out)) return fail(h, TTT_EINVAL, "null tokens_out or losses_out");
+  if (d_fast_out)
+    for (int i = 0; i < 3 * h->nu; ++i)
+      if (!d_fast_out[i]) return fail(h, TTT_EINVAL, "null entry in d_fast_out");
+  flags |= h->cfg.flags;
+  const bool update = !(flags & TTT_NO_UPDATE) && h->nu > 0;
+  const bool use_graph = !(flags & TTT_NO_GRAPH) && !h->prof;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t len0 = h->len;
+  try {
+    HIPCHK(set_int_launch(h->pos0, (int)len0, st));
+    if (d_forced && n_steps > 0)
+      HIPCHK(hipMemcpyAsync(h->tok + len0 + 1, d_forced, (size_t)n_steps * sizeof(int), hipMemcpyDeviceToDevice, st));
+    for (int64_t j = 0; j < n_steps; ++j) {
+      // position len: predict the token after it (the forced one's loss, or the argmax)
+      run_step(h, 1, false, d_forced ? MODE_PREFILL : MODE_GREEDY, use_graph, st);
+      h->len += 1;
+      if (h->len - h->dstart == h->b) {
+        // every target of the open chunk is known: its update (Algorithm 3 step 3)
+        // before the next position is fed
+        if (update) {
+          HIPCHK(set_int_launch(h->pos0, (int)h->dstart, st));
+          run_step(h, h->b, true, MODE_RECOMPUTE, use_graph, st);
+        }
+        h->dstart += h->b;
+      }
+    }
+    if (n_steps > 0) {
+      HIPCHK(hipMemcpyAsync(d_tokens_out, h->tok + len0 + 1, (size_t)n_steps * sizeof(int), hipMemcpyDeviceToDevice,
+                            st));
+      HIPCHK(hipMemcpyAsync(d_losses_out, h->losses + len0, (size_t)n_steps * sizeof(float), hipMemcpyDeviceToDevice,
+                            st));
+      HIPCHK(finite_check_launch(h->losses + len0, n_steps, h->flag, st));
+    }
+    if (d_fast_out) copy_fast_out(h, d_fast_out, st);
+  } catch (const HipFail &f) {
+    h->have_state = false;
     return fail_hip(h, f);
   }
   return TTT_OK;

@@ -15,7 +15,7 @@ TTT_OK, TTT_EINVAL, TTT_ENOMEM, TTT_EHIP, TTT_EUNSUPPORTED, TTT_ENONFINITE = 0, 
 TTT_FP32, TTT_BF16 = 0, 1
 TTT_NO_UPDATE, TTT_NO_GRAPH = 1, 2
 
-EXPORTED = ["ttt_create", "ttt_prefill", "ttt_check_finite", "ttt_get_stats", "ttt_set_kernel_timing",
+EXPORTED = ["ttt_create", "ttt_prefill", "ttt_decode", "ttt_check_finite", "ttt_get_stats", "ttt_set_kernel_timing",
             "ttt_kernel_class_count", "ttt_get_kernel_time", "ttt_last_error", "ttt_destroy"]
 
 
@@ -60,6 +60,9 @@ def lib():
         L.ttt_prefill.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, _PP,
                                   ctypes.c_uint32, ctypes.c_void_p]
         L.ttt_prefill.restype = ctypes.c_int
+        L.ttt_decode.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 _PP, ctypes.c_uint32, ctypes.c_void_p]
+        L.ttt_decode.restype = ctypes.c_int
         L.ttt_check_finite.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.ttt_check_finite.restype = ctypes.c_int
         L.ttt_get_stats.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
@@ -105,6 +108,16 @@ def ttt_prefill(handle, d_tokens, T, d_losses, d_fast_out=None, flags=0, stream=
     if d_fast_out is not None:
         fo, keep = _ptr_array(d_fast_out)
     st = lib().ttt_prefill(handle, d_tokens, T, d_losses, fo, flags, stream)
+    del keep
+    _check(st, handle)
+
+
+def ttt_decode(handle, n_steps, d_forced, d_tokens_out, d_losses_out, d_fast_out=None, flags=0, stream=None):
+    fo = None
+    keep = None
+    if d_fast_out is not None:
+        fo, keep = _ptr_array(d_fast_out)
+    st = lib().ttt_decode(handle, n_steps, d_forced, d_tokens_out, d_losses_out, fo, flags, stream)
     del keep
     _check(st, handle)
 
@@ -208,6 +221,37 @@ class Session:
         if check:
             ttt_check_finite(self.handle, stream)
         return losses, fast
+
+    def _fast_buffers(self, dev):
+        torch = self.torch
+        F, d = self.cfg.d_ff, self.cfg.d_model
+        fast = []
+        for _ in range(self.cfg.n_update):
+            fast += [torch.empty(F, d, dtype=torch.float32, device=dev),
+                     torch.empty(F, d, dtype=torch.float32, device=dev),
+                     torch.empty(d, F, dtype=torch.float32, device=dev)]
+        return fast
+
+    def decode(self, n_steps, forced=None, flags=0, want_fast=True, check=True):
+        """Continues the last prefill (Algorithm 3).  forced: int32 device tensor [n_steps]
+        of next ids, or None for greedy.  Returns (next ids [n_steps] int32, losses
+        [n_steps] fp32, fast tensors or None)."""
+        torch = self.torch
+        dev = torch.device("cuda", torch.cuda.current_device())
+        if forced is not None:
+            assert forced.dtype == torch.int32 and forced.is_cuda and forced.is_contiguous()
+            assert forced.numel() == n_steps
+        toks = torch.empty(max(n_steps, 0), dtype=torch.int32, device=dev)
+        losses = torch.empty(max(n_steps, 0), dtype=torch.float32, device=dev)
+        fast = self._fast_buffers(dev) if want_fast and self.cfg.n_update > 0 else None
+        ptrs = [t.data_ptr() for t in fast] if fast is not None else None
+        stream = torch.cuda.current_stream().cuda_stream
+        ttt_decode(self.handle, n_steps, forced.data_ptr() if forced is not None else None,
+                   toks.data_ptr() if n_steps > 0 else None, losses.data_ptr() if n_steps > 0 else None,
+                   ptrs, flags, stream)
+        if check:
+            ttt_check_finite(self.handle, stream)
+        return toks, losses, fast
 
     def stats(self):
         return ttt_get_stats(self.handle)
