@@ -195,6 +195,53 @@ def suite_sweep(steps, warmup):
     return {"suite": "n_update_and_window_sweep", "shape": "760m", "seq_len": base.seq_len, "rows": rows}
 
 
+def suite_decode(steps, warmup, n_decode=2048, prompt_cfg="2.7b_8k"):
+    """Algorithm 3 at the 2.7B shape: prefill an 8K prompt, then greedy-decode n_decode
+    ids one call per position, each bracketed by HIP events on the decode stream.
+    Steps whose call closes a decode chunk also run that chunk's update (the chunk
+    forward again, its backward and the SGD step): the stall at update boundaries."""
+    import torch
+    from ttt_inputs import get, make_weights_torch, make_tokens
+    from test_lm_prefill_amd import Session
+    cfg = get(prompt_cfg)
+    T = cfg.seq_len
+    w = make_weights_torch(cfg, "cuda", seed=0)
+    tok = torch.from_numpy(make_tokens(cfg, seed=1)).cuda()
+    sess = Session(cfg, w, max_tokens=T + n_decode)
+    stream = torch.cuda.current_stream()
+    try:
+        sess.prefill(tok, want_fast=False, check=False)
+        sess.decode(cfg.chunk + 8, want_fast=False, check=False)    # warm-up: captures both graphs
+        sess.prefill(tok, want_fast=False, check=False)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_decode)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for j in range(n_decode):
+            ev[j][0].record(stream)
+            sess.decode(1, want_fast=False, check=False)
+            ev[j][1].record(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in ev])
+        total = t0.elapsed_time(t1)
+    finally:
+        sess.close()
+        del w, tok
+        torch.cuda.empty_cache()
+    upd = np.arange(n_decode)[(np.arange(n_decode) + 1) % cfg.chunk == 0]
+    plain = np.setdiff1d(np.arange(n_decode), upd)
+    return {"suite": "decode_periodic_updates", "shape": "2.7b", "prompt": T, "decoded": n_decode,
+            "chunk": cfg.chunk, "mode": "greedy",
+            "ms_per_token_median": round(float(np.median(ms[plain])), 3),
+            "ms_per_token_p90": round(float(np.percentile(ms[plain], 90)), 3),
+            "update_step_ms_median": round(float(np.median(ms[upd])), 2) if len(upd) else None,
+            "stall_ms": round(float(np.median(ms[upd]) - np.median(ms[plain])), 2) if len(upd) else None,
+            "tokens_per_s_including_updates": round(n_decode / (total / 1e3), 1),
+            "total_ms": round(total, 1)}
+
+
 def profile_pass(cfg):
     """For hardware-counter runs: one kernel of known traffic, then one prefill.
 
@@ -293,9 +340,10 @@ def main():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
                     help="run a calibration kernel and one prefill only (for counter runs)")
-    ap.add_argument("--suite", choices=["full_attention", "sweep"],
+    ap.add_argument("--suite", choices=["full_attention", "sweep", "decode"],
                     help="instead of the benchmark line: the full-attention baseline at the 2.7B shape, "
-                         "or the n_update / window sweep at the 760M shape (one JSON line)")
+                         "the n_update / window sweep at the 760M shape, or decoding with periodic "
+                         "updates after an 8K prompt at the 2.7B shape (one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: a TTT prefill sequence is a recurrence over chunks and "
@@ -307,7 +355,7 @@ def main():
         profile_pass(cfg)
         return
     if args.suite:
-        fn = suite_full_attention if args.suite == "full_attention" else suite_sweep
+        fn = {"full_attention": suite_full_attention, "sweep": suite_sweep, "decode": suite_decode}[args.suite]
         print(json.dumps(fn(args.steps, args.warmup)), flush=True)
         return
     T = cfg.seq_len
