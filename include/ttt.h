@@ -84,6 +84,9 @@ typedef struct {
   int32_t dtype;        /* ttt_dtype of weights and activations */
   int64_t max_tokens;   /* largest T accepted by ttt_prefill; sizes the rotary table */
   uint32_t flags;       /* default flags OR-ed into every ttt_prefill call */
+  int32_t n_seq;        /* B: independent sequences per ttt_prefill (0 or 1: one; at most 256).
+                           Each has its own fast weights and window; they share the frozen
+                           weights, and every frozen-weight product runs once over all B chunks */
 } ttt_config;
 
 /*
@@ -124,16 +127,19 @@ typedef struct ttt_handle ttt_handle;
 ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream, ttt_handle **out);
 
 /*
- * Algorithm 1 of the notes on one sequence.
- *   d_tokens   device int32 [T+1]: ids x_0..x_T, each in [0, V).
+ * Algorithm 1 of the notes on each of the handle's B = n_seq sequences (each
+ * starts from W_init with its own fast weights and window; they advance chunk
+ * by chunk together, all of length T).
+ *   d_tokens   device int32 [B][T+1]: ids x_0..x_T of each sequence, each in [0, V).
  *   T          number of scored positions, 0 <= T <= cfg.max_tokens.  The last
  *              chunk may be short (T % b != 0); its update averages over its own size.
- *   d_losses   device float32 [T] out: d_losses[p] = -ln p(x_{p+1} | x_0..x_p)
- *              under the fast weights current at p's chunk, recorded before that
- *              chunk's update.
- *   d_fast_out host array of 3*n_u device float32 pointers, or NULL.  If given,
- *              receives W_N after all ceil(T/b) updates, in the order
- *              gate[F,d], up[F,d], down[d,F] for block L-n_u, then L-n_u+1, ...
+ *   d_losses   device float32 [B][T] out: d_losses[s][p] = -ln p(x_{p+1} | x_0..x_p)
+ *              of sequence s under its fast weights current at p's chunk,
+ *              recorded before that chunk's update.
+ *   d_fast_out host array of 3*n_u*B device float32 pointers, or NULL.  If given,
+ *              receives each sequence's W_N after all ceil(T/b) updates, in the
+ *              order gate[F,d], up[F,d], down[d,F] for block L-n_u, then
+ *              L-n_u+1, ..., sequence 0 first.
  *   flags      TTT_NO_UPDATE / TTT_NO_GRAPH, OR-ed with cfg.flags.
  *   stream     hipStream_t to enqueue on (NULL = default stream).
  * Starts from W_init and an empty ring every call.  Returns after enqueueing
@@ -167,7 +173,7 @@ ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float 
  * position then uses the new weights.  A partial chunk is kept open for the
  * next call.  Returns after enqueueing; ttt_check_finite covers these losses
  * too.  TTT_EINVAL when no prefill with tokens preceded it or the length
- * would pass max_tokens.
+ * would pass max_tokens; TTT_EUNSUPPORTED for a handle of more than one sequence.
  */
 ttt_status ttt_decode(ttt_handle *h, int64_t n_steps, const int32_t *d_forced, int32_t *d_tokens_out,
                       float *d_losses_out, float *const *d_fast_out, uint32_t flags, void *stream);

@@ -61,6 +61,14 @@ hipError_t swiglu_bwd_launch(int dtype, const void *GU, const void *dhmid, void 
 hipError_t ce_reduce_launch(const float2 *part, int P, const float *zlab, const int *pos0, float *lse,
                             float *losses, int n, hipStream_t st);
 
+// Batched chunk of B sequences, n positions each, row r = s * n + m at position
+// *pos0 + m of sequence s: ids[r] = tok[s * ld_tok + *pos0 + m], labs[r] = the
+// id after it; and losses[s * ld_loss + *pos0 + m] = closs[r].
+hipError_t gather_chunk_ids_launch(const int *tok, long ld_tok, const int *pos0, int n, int B, int *ids, int *labs,
+                                   hipStream_t st);
+hipError_t scatter_chunk_losses_launch(const float *closs, float *losses, long ld_loss, const int *pos0, int n, int B,
+                                       hipStream_t st);
+
 // Greedy choice for the last of n rows: over the per-tile partials (max, sum
 // exp) and their argmax columns, the largest logit (lowest id on ties) goes to
 // tok[*pos0 + n] and lse[n-1] - max to losses[*pos0 + n - 1].

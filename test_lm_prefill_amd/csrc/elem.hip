@@ -423,6 +423,24 @@ __global__ __launch_bounds__(64) void decode_pick_kernel(const float2 *part, con
   }
 }
 
+// Rows of a batched chunk: row r = s * n + m is position *pos0 + m of sequence s.
+__global__ void gather_chunk_ids_kernel(const int *tok, long ld_tok, const int *pos0, int n, int B, int *ids,
+                                        int *labs) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= B * n) return;
+  const int s = r / n, m = r % n;
+  const long i = (long)s * ld_tok + *pos0 + m;
+  ids[r] = tok[i];
+  labs[r] = tok[i + 1];
+}
+__global__ void scatter_chunk_losses_kernel(const float *closs, float *losses, long ld_loss, const int *pos0, int n,
+                                            int B) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= B * n) return;
+  const int s = r / n, m = r % n;
+  losses[(long)s * ld_loss + *pos0 + m] = closs[r];
+}
+
 inline unsigned blocks_for(long n, int per = 256) { return (unsigned)((n + per - 1) / per); }
 
 }  // namespace
@@ -550,6 +568,21 @@ hipError_t swiglu_bwd_launch(int dtype, const void *GU, const void *dhmid, void 
                      (T *)dGU, n, units, ld_gu, ld_h)
   DT_DISPATCH(dtype, K_, 0);
 #undef K_
+  return hipGetLastError();
+}
+
+hipError_t gather_chunk_ids_launch(const int *tok, long ld_tok, const int *pos0, int n, int B, int *ids, int *labs,
+                                   hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_chunk_ids_kernel, dim3(blocks_for((long)B * n)), dim3(256), 0, st, tok, ld_tok, pos0, n, B,
+                     ids, labs);
+  return hipGetLastError();
+}
+hipError_t scatter_chunk_losses_launch(const float *closs, float *losses, long ld_loss, const int *pos0, int n, int B,
+                                       hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_chunk_losses_kernel, dim3(blocks_for((long)B * n)), dim3(256), 0, st, closs, losses,
+                     ld_loss, pos0, n, B);
   return hipGetLastError();
 }
 

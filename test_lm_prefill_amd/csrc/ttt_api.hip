@@ -36,12 +36,14 @@ struct LayerBuf {
   void *attn_norm = nullptr, *wqkv = nullptr, *wo = nullptr, *q_norm = nullptr, *k_norm = nullptr,
        *mlp_norm = nullptr;
   // gate/up rows interleaved by 16.  Frozen layers: [2F][d].  Updated layers:
-  // fast rows [2F][2d] holding the forward working copy as hi | lo (in bf16
-  // mode fp16 of s*W with s = wscale: hi = round(sW), lo = round(sW - hi), so
-  // hi + lo carries the fp32 master to ~22 bits and the small inner updates are
-  // not lost to rounding), then static rows [2F][d] at element offset 4Fd.
-  void *wgu = nullptr;
-  // Frozen layers: [d][F].  Updated layers: [d][3F] = fast hi | static | fast lo.
+  // per sequence, fast rows [2F][2d] holding the forward working copy as hi | lo
+  // (in bf16 mode fp16 of s*W with s = wscale: hi = round(sW), lo = round(sW -
+  // hi), so hi + lo carries the fp32 master to ~22 bits and the small inner
+  // updates are not lost to rounding); the static rows [2F][d] in wgu_s.
+  void *wgu = nullptr, *wgu_s = nullptr;
+  // Frozen layers: [d][F].  Updated layers: per sequence [d][3F] = fast hi |
+  // static | fast lo (each sequence holds its own copy of the static columns, so
+  // that one product covers both MLPs).
   void *wd = nullptr;
   bool fast = false, bwd_attn = false;
   int u = -1;
@@ -78,6 +80,15 @@ struct ttt_handle {
   // which keeps the fp16 lo part of small weights out of the subnormal range;
   // the GEMMs that read them divide their accumulators by it.  1 in fp32 mode.
   float wscale = 1.f;
+  // independent sequences per call; each has its own fast weights (and their
+  // copies) and ring; the frozen weights and the chunk scratch rows are shared
+  int B = 1;
+  size_t ring_sbytes = 0;                          // ring bytes of one sequence
+  size_t fgu_sb = 0, fd_sb = 0, fdT_sb = 0, fguT_sb = 0;  // per-sequence strides of the fast copies (bytes)
+  long ld_tok = 0;                                 // ids per sequence in tok (max_tokens + 1)
+  int *ids = nullptr, *labs = nullptr;             // [B*b] the chunk's ids and labels
+  int *zero = nullptr;                             // a device 0 (offset for gathered rows)
+  float *closs = nullptr;                          // [B*b] the chunk's losses before the scatter
   // bf16 mode: the backward carries the chunk loss times this power of two (so
   // that its fp16 operands sit well inside fp16's normal range); the SGD step
   // divides it out.  1 in fp32 mode.
@@ -248,17 +259,21 @@ enum ChunkMode {
 };
 
 void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode = MODE_PREFILL) {
-  const int d = h->d, F = h->F, L = h->L, dt = h->dt;
+  const int d = h->d, F = h->F, L = h->L, dt = h->dt, B = h->B, H = h->H, hd = h->hd, b = h->b;
+  const int Bn = B * n;  // rows of the batched chunk: sequence s owns rows [s*n, (s+1)*n)
   const size_t es = h->es;
   const float eps = h->cfg.rms_eps;
   const bool f16 = dt == 1;  // bf16 mode: forward activations and weights are fp16
+  // byte offset of sequence s's rows in a [Bn][cols] buffer of element size esz
+  auto rows = [n](int s, long cols, size_t esz) { return (size_t)s * n * cols * esz; };
   h->launches = 0;
 
   {
     PROF(K_EMBED);
-    HIPCHK(embed_launch(dt, h->tok_emb, h->tok, h->pos0, h->h, n, d, st));
+    HIPCHK(gather_chunk_ids_launch(h->tok, h->ld_tok, h->pos0, n, B, h->ids, h->labs, st));
+    HIPCHK(embed_launch(dt, h->tok_emb, h->ids, h->zero, h->h, Bn, d, st));
   }
-  h->launches++;
+  h->launches += 2;
   for (int l = 0; l < L; ++l) {
     LayerBuf &lw = h->layers[l];
     Saved *S = (lw.fast && update) ? &h->saved[lw.u] : nullptr;
@@ -266,80 +281,83 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
     // --- attention sub-block
     {
       PROF(K_RMSNORM);
-      HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.attn_norm, h->a, sb ? S->r1 : nullptr, sb ? S->h_in : nullptr, n, d, eps,
+      HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.attn_norm, h->a, sb ? S->r1 : nullptr, sb ? S->h_in : nullptr, Bn, d, eps,
                                 st, f16));
     }
-    float *qkv = sb ? S->qkv : h->qkv;  // fp32: q, k, v are normalised / cached without a bf16 rounding first
+    float *qkv = sb ? S->qkv : h->qkv;  // fp32: q, k, v are normalised / cached without a 16-bit rounding first
     {
-      GemmArgs g = gargs(h->a, d, lw.wqkv, d, n, 3 * d, d);
+      GemmArgs g = gargs(h->a, d, lw.wqkv, d, Bn, 3 * d, d);
       g.Cf = qkv;
       g.ldcf = 3 * d;
       gemm(h, K_GEMM_QKV, true, true, EPI_STORE_F32, g, st, true);
     }
     void *qh = sb ? S->qh : h->qh;
-    {
-      RopeArgs ra;
-      memset(&ra, 0, sizeof(ra));
-      ra.qkv = qkv;
-      ra.gq = lw.q_norm;
-      ra.gk = lw.k_norm;
-      ra.cs = h->rope;
-      ra.pos0 = h->pos0;
-      ra.n = n;
-      ra.d = d;
-      ra.H = h->H;
-      ra.hd = h->hd;
-      ra.R = h->R;
-      ra.eps = eps;
-      ra.qh = qh;
-      ra.qhb = (sb && lw.fwd16) ? S->qhb : nullptr;
-      ra.qht = sb ? S->qht : nullptr;
-      ra.K = lw.K;
-      ra.Vt = lw.Vt;
-      ra.Kb = lw.bwd_attn ? lw.Kb : nullptr;
-      ra.Kt = lw.bwd_attn ? lw.Kt : nullptr;
-      ra.V = lw.bwd_attn ? lw.V : nullptr;
-      ra.fwd_f16 = lw.fwd16;
-      ra.ldt = h->b;
+    void *o = sb ? S->o : h->o;
+    float *lse2 = sb ? S->lse2 : h->lse2;
+    for (int s = 0; s < B; ++s) {  // per sequence: its ring and its positions
+      const size_t rs = s * h->ring_sbytes;
       {
+        RopeArgs ra;
+        memset(&ra, 0, sizeof(ra));
+        ra.qkv = (const float *)off(qkv, rows(s, 3 * d, 4));
+        ra.gq = lw.q_norm;
+        ra.gk = lw.k_norm;
+        ra.cs = h->rope;
+        ra.pos0 = h->pos0;
+        ra.n = n;
+        ra.d = d;
+        ra.H = H;
+        ra.hd = hd;
+        ra.R = h->R;
+        ra.eps = eps;
+        ra.qh = off(qh, rows(s, d, es));
+        ra.qhb = (sb && lw.fwd16) ? off(S->qhb, rows(s, d, es)) : nullptr;
+        ra.qht = sb ? off(S->qht, (size_t)s * b * d * es) : nullptr;
+        ra.K = off(lw.K, rs);
+        ra.Vt = off(lw.Vt, rs);
+        ra.Kb = lw.bwd_attn && lw.Kb ? off(lw.Kb, rs) : nullptr;
+        ra.Kt = lw.bwd_attn ? off(lw.Kt, rs) : nullptr;
+        ra.V = lw.bwd_attn ? off(lw.V, rs) : nullptr;
+        ra.fwd_f16 = lw.fwd16;
+        ra.ldt = b;
         PROF(K_ROPE);
         HIPCHK(qk_rope_fwd_launch(dt, ra, st));
       }
-    }
-    void *o = sb ? S->o : h->o;
-    {
-      AttnArgs aa;
-      memset(&aa, 0, sizeof(aa));
-      aa.q = qh;
-      aa.K = lw.K;
-      aa.Vt = lw.Vt;
-      aa.o = o;
-      aa.lse2 = sb ? S->lse2 : h->lse2;
-      aa.n = n;
-      aa.d = d;
-      aa.H = h->H;
-      aa.R = h->R;
-      aa.window = h->k;
-      aa.ldl = h->b;
-      aa.ldt = h->b;
-      aa.pos0 = h->pos0;
-      aa.scale = 1.f / sqrtf((float)h->hd);
-      aa.nsplit = lw.fsplit;
-      aa.sbound = lw.sbound;
-      aa.fwd_f16 = lw.fwd16;
-      aa.o_f16 = f16;
-      aa.ws = h->attn_ws;
       {
-        PROF(K_ATTN_FWD);
-        HIPCHK(attn_fwd_launch(dt, h->hd, aa, st));
+        AttnArgs aa;
+        memset(&aa, 0, sizeof(aa));
+        aa.q = off(qh, rows(s, d, es));
+        aa.K = off(lw.K, rs);
+        aa.Vt = off(lw.Vt, rs);
+        aa.o = off(o, rows(s, d, es));
+        aa.lse2 = lse2 + (size_t)s * H * b;
+        aa.n = n;
+        aa.d = d;
+        aa.H = H;
+        aa.R = h->R;
+        aa.window = h->k;
+        aa.ldl = b;
+        aa.ldt = b;
+        aa.pos0 = h->pos0;
+        aa.scale = 1.f / sqrtf((float)hd);
+        aa.nsplit = lw.fsplit;
+        aa.sbound = lw.sbound;
+        aa.fwd_f16 = lw.fwd16;
+        aa.o_f16 = f16;
+        aa.ws = h->attn_ws;
+        {
+          PROF(K_ATTN_FWD);
+          HIPCHK(attn_fwd_launch(dt, hd, aa, st));
+        }
+        if (aa.nsplit > 1) {
+          PROF(K_ATTN_MERGE);
+          HIPCHK(attn_merge_launch(dt, hd, false, aa, st));
+        }
       }
-      if (aa.nsplit > 1) {
-        PROF(K_ATTN_MERGE);
-        HIPCHK(attn_merge_launch(dt, h->hd, false, aa, st));
-      }
+      h->launches += lw.fsplit > 1 ? 3 : 2;
     }
     {
-      GemmArgs g = gargs(o, d, lw.wo, d, n, d, d);
+      GemmArgs g = gargs(o, d, lw.wo, d, Bn, d, d);
       g.Cf = h->h;
       g.ldcf = d;
       gemm(h, K_GEMM_O, true, true, EPI_ADD_F32, g, st, true);
@@ -348,58 +366,63 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
     void *m = S ? S->m : h->m;
     {
       PROF(K_RMSNORM);
-      HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.mlp_norm, m, S ? S->r2 : nullptr, S ? S->h1 : nullptr, n, d, eps, st, f16));
+      HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.mlp_norm, m, S ? S->r2 : nullptr, S ? S->h1 : nullptr, Bn, d, eps, st, f16));
     }
     void *hm = S ? S->hmid : h->hmid;  // hidden units: F (frozen) or 2F = fast then static
     if (!lw.fast) {
-      GemmArgs g = gargs(m, d, lw.wgu, d, n, 2 * F, d);
+      GemmArgs g = gargs(m, d, lw.wgu, d, Bn, 2 * F, d);
       g.C = hm;
       g.ldc = F;
       g.c_f16 = f16;
       gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, g, st, true);
-      GemmArgs g2 = gargs(hm, F, lw.wd, F, n, d, F);
+      GemmArgs g2 = gargs(hm, F, lw.wd, F, Bn, d, F);
       g2.Cf = h->h;
       g2.ldcf = d;
       gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st, true);
+      h->launches += 4;
     } else {
-      // fast units [0, F): bf16 runs the reduction over [m | m] x [hi | lo]
-      GemmArgs g = gargs(m, d, lw.wgu, 2 * d, n, 2 * F, dt == 1 ? 2 * d : d);
-      g.a_kwrap = dt == 1 ? d : 0;
-      g.C = hm;
-      g.ldc = 2 * F;
-      g.C2 = S ? S->gu : nullptr;
-      g.ldc2 = 4 * F;
-      g.c_f16 = f16;
-      g.acc_scale = 1.f / h->wscale;
-      gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, g, st, true);
-      // static units [F, 2F)
-      GemmArgs gs = gargs(m, d, off(lw.wgu, (size_t)4 * F * d * es), d, n, 2 * F, d);
+      // static units [F, 2F), all sequences at once
+      GemmArgs gs = gargs(m, d, lw.wgu_s, d, Bn, 2 * F, d);
       gs.C = off(hm, (size_t)F * es);
       gs.ldc = 2 * F;
       gs.C2 = S ? off(S->gu, (size_t)2 * F * es) : nullptr;
       gs.ldc2 = 4 * F;
       gs.c_f16 = f16;
       gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, gs, st, true);
-      // down: [fast | static | fast] units x [hi | static | lo] columns (bf16)
-      GemmArgs g2 = gargs(hm, 2 * F, lw.wd, 3 * F, n, d, dt == 1 ? 3 * F : 2 * F);
-      g2.a_kwrap = dt == 1 ? 2 * F : 0;
-      g2.Cf = h->h;
-      g2.ldcf = d;
-      g2.acc_scale = 1.f / h->wscale;
-      gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st, true);
+      for (int s = 0; s < B; ++s) {
+        void *wgu = off(lw.wgu, s * h->fgu_sb);
+        void *wd = off(lw.wd, s * h->fd_sb);
+        // fast units [0, F): bf16 runs the reduction over [m | m] x [hi | lo]
+        GemmArgs g = gargs(off(m, rows(s, d, es)), d, wgu, 2 * d, n, 2 * F, dt == 1 ? 2 * d : d);
+        g.a_kwrap = dt == 1 ? d : 0;
+        g.C = off(hm, rows(s, 2 * F, es));
+        g.ldc = 2 * F;
+        g.C2 = S ? off(S->gu, rows(s, 4 * F, es)) : nullptr;
+        g.ldc2 = 4 * F;
+        g.c_f16 = f16;
+        g.acc_scale = 1.f / h->wscale;
+        gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, g, st, true);
+        // down: [fast | static | fast] units x [hi | static | lo] columns (bf16 mode)
+        GemmArgs g2 = gargs(off(hm, rows(s, 2 * F, es)), 2 * F, wd, 3 * F, n, d, dt == 1 ? 3 * F : 2 * F);
+        g2.a_kwrap = dt == 1 ? 2 * F : 0;
+        g2.Cf = h->h + (size_t)s * n * d;
+        g2.ldcf = d;
+        g2.acc_scale = 1.f / h->wscale;
+        gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st, true);
+      }
+      h->launches += 2 + 2 * B;
     }
-    h->launches += lw.fast ? 5 : 4;
   }
   // --- head: final norm, LM head + cross-entropy (losses written before any update)
   {
     PROF(K_RMSNORM);
-    HIPCHK(rmsnorm_fwd_launch(dt, h->h, h->final_norm, h->nf, update ? h->rf : nullptr, update ? h->hf : nullptr, n, d,
+    HIPCHK(rmsnorm_fwd_launch(dt, h->h, h->final_norm, h->nf, update ? h->rf : nullptr, update ? h->hf : nullptr, Bn, d,
                               eps, st, f16));
   }
   {
-    GemmArgs g = gargs(h->nf, d, h->lm_head, d, n, h->V, d);
-    g.rowi = h->tok + 1;
-    g.pos0 = h->pos0;
+    GemmArgs g = gargs(h->nf, d, h->lm_head, d, Bn, h->V, d);
+    g.rowi = h->labs;  // label of row r = labs[*zero + r]
+    g.pos0 = h->zero;
     g.part = h->part;
     g.part_ld = h->P;
     g.zlab = h->zlab;
@@ -408,40 +431,41 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
   }
   {
     PROF(K_CE_REDUCE);
-    HIPCHK(ce_reduce_launch(h->part, h->P, h->zlab, h->pos0, h->lse, mode == MODE_RECOMPUTE ? h->rlosses : h->losses,
-                            n, st));
-    if (mode == MODE_GREEDY)
+    HIPCHK(ce_reduce_launch(h->part, h->P, h->zlab, h->zero, h->lse, h->closs, Bn, st));
+    HIPCHK(scatter_chunk_losses_launch(h->closs, mode == MODE_RECOMPUTE ? h->rlosses : h->losses, h->cfg.max_tokens,
+                                       h->pos0, n, B, st));
+    if (mode == MODE_GREEDY)  // one sequence
       HIPCHK(decode_pick_launch(h->part, h->part_arg, h->P, h->lse, h->pos0, n, h->tok, h->losses, st));
   }
-  h->launches += mode == MODE_GREEDY ? 3 : 2;
+  h->launches += mode == MODE_GREEDY ? 4 : 3;
 
   if (update && h->nu > 0) {
     const int np = (n + 63) / 64 * 64;  // token count padded for the weight-gradient GEMMs
-    // --- dlogits (softmax - onehot)/n, streamed over vocab slabs, and dn = dz W_lm
-    for (int v0 = 0, s = 0; v0 < h->V; v0 += h->Vs, ++s) {
+    // --- dlogits (softmax - onehot) * 2^s / n, streamed over vocab slabs, and dn = dz W_lm
+    for (int v0 = 0, sl = 0; v0 < h->V; v0 += h->Vs, ++sl) {
       const int vs = std::min(h->Vs, h->V - v0);
       {
-        GemmArgs g = gargs(h->nf, d, off(h->lm_head, (size_t)v0 * d * es), d, n, vs, d);
+        GemmArgs g = gargs(h->nf, d, off(h->lm_head, (size_t)v0 * d * es), d, Bn, vs, d);
         g.C = h->dz;
         g.ldc = h->Vs;
         g.rowf = h->lse;
-        g.rowi = h->tok + 1;
-        g.pos0 = h->pos0;
+        g.rowi = h->labs;
+        g.pos0 = h->zero;
         g.col_off = v0;
         g.alpha = h->gscale / (float)n;
         gemm(h, K_GEMM_DLOGITS, true, true, EPI_DLOGITS, g, st, true);  // logits recomputed as in the forward
       }
       {
         // B[n = model dim][k = vocab] from the transposed head [d][V]
-        GemmArgs g = gargs(h->dz, h->Vs, off(h->lm_headT, (size_t)v0 * es), h->V, n, d, vs);
+        GemmArgs g = gargs(h->dz, h->Vs, off(h->lm_headT, (size_t)v0 * es), h->V, Bn, d, vs);
         g.Cf = h->dn;
         g.ldcf = d;
-        gemm(h, K_GEMM_DN, true, true, s == 0 ? EPI_STORE_F32 : EPI_ADD_F32, g, st);
+        gemm(h, K_GEMM_DN, true, true, sl == 0 ? EPI_STORE_F32 : EPI_ADD_F32, g, st);
       }
     }
     {
       PROF(K_RMSNORM_BWD);
-      HIPCHK(rmsnorm_bwd_launch(dt, h->dn, h->hf, h->rf, h->final_norm, nullptr, h->dh, h->dy, n, d, st, f16));
+      HIPCHK(rmsnorm_bwd_launch(dt, h->dn, h->hf, h->rf, h->final_norm, nullptr, h->dh, h->dy, Bn, d, st, f16));
     }
     h->launches++;
     for (int l = L - 1; l >= L - h->nu; --l) {
@@ -449,161 +473,181 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
       Saved &S = h->saved[lw.u];
       const bool last = (l == L - h->nu);
       const int Fu = last ? F : 2 * F;  // hidden units whose gradient is needed
-      // dhmid = dy Wd_cat[:, :Fu]  (B from the transposed [2F][d] copy)
-      {
-        GemmArgs g = gargs(h->dy, d, lw.wdT, d, n, Fu, d);
-        g.C = h->dhmid;
-        g.ldc = 2 * F;
-        g.c_f16 = f16;
-        gemm(h, K_GEMM_DHMID, true, true, EPI_STORE, g, st, true);
-      }
-      {
-        PROF(K_TRANSPOSE);
-        HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, h->dy, d, h->dyT, h->b, n, np, d, st, f16));
-        HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, S.hmid, 2 * F, h->hmidT, h->b, n, np, F, st, f16));
-      }
-      // dWd_fast = dy^T hmid_fast over the chunk's tokens, SGD fused into the epilogue
-      {
-        GemmArgs g = gargs(h->dyT, h->b, h->hmidT, h->b, d, F, np);
-        g.Cf = h->m_d[lw.u];
-        g.ldcf = F;
-        g.C = lw.wd;  // hi columns [0, F)
-        g.ldc = 3 * F;
-        g.C2 = dt == 1 ? off(lw.wd, (size_t)2 * F * es) : nullptr;  // lo columns [2F, 3F)
-        g.ldc2 = 3 * F;
-        g.c_f16 = f16;
-        g.c_scale = h->wscale;
-        g.alpha = h->cfg.eta / h->gscale;
-        gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st, true);
-      }
-      {
-        PROF(K_TRANSPOSE);
-        HIPCHK(transpose_launch(dt, SRC_F32, h->m_d[lw.u], F, lw.wdT, d, d, d, F, st, f16));
+      for (int s = 0; s < B; ++s) {
+        void *wdT = off(lw.wdT, s * h->fdT_sb);
+        void *wd = off(lw.wd, s * h->fd_sb);
+        float *md = h->m_d[lw.u] + (size_t)s * d * F;
+        // dhmid = dy Wd_cat[:, :Fu]  (B from the transposed [2F][d] copy)
+        {
+          GemmArgs g = gargs(off(h->dy, rows(s, d, es)), d, wdT, d, n, Fu, d);
+          g.C = off(h->dhmid, rows(s, 2 * F, es));
+          g.ldc = 2 * F;
+          g.c_f16 = f16;
+          gemm(h, K_GEMM_DHMID, true, true, EPI_STORE, g, st, true);
+        }
+        {
+          PROF(K_TRANSPOSE);
+          HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, off(h->dy, rows(s, d, es)), d, h->dyT, b, n, np, d, st,
+                                  f16));
+          HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, off(S.hmid, rows(s, 2 * F, es)), 2 * F, h->hmidT, b,
+                                  n, np, F, st, f16));
+        }
+        // dWd_fast = dy^T hmid_fast over the chunk's tokens, SGD fused into the epilogue
+        {
+          GemmArgs g = gargs(h->dyT, b, h->hmidT, b, d, F, np);
+          g.Cf = md;
+          g.ldcf = F;
+          g.C = wd;  // hi columns [0, F)
+          g.ldc = 3 * F;
+          g.C2 = dt == 1 ? off(wd, (size_t)2 * F * es) : nullptr;  // lo columns [2F, 3F)
+          g.ldc2 = 3 * F;
+          g.c_f16 = f16;
+          g.c_scale = h->wscale;
+          g.alpha = h->cfg.eta / h->gscale;
+          gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st, true);
+        }
+        {
+          PROF(K_TRANSPOSE);
+          HIPCHK(transpose_launch(dt, SRC_F32, md, F, wdT, d, d, d, F, st, f16));
+        }
+        h->launches += 5;
       }
       {
         PROF(K_SWIGLU_BWD);
-        HIPCHK(swiglu_bwd_launch(dt, S.gu, h->dhmid, h->dgu, n, Fu, 4 * F, 2 * F, st, f16));
+        HIPCHK(swiglu_bwd_launch(dt, S.gu, h->dhmid, h->dgu, Bn, Fu, 4 * F, 2 * F, st, f16));
       }
-      if (!last) {
-        GemmArgs g = gargs(h->dgu, 4 * F, lw.wguT, 4 * F, n, d, 4 * F);
-        g.Cf = h->dm;
-        g.ldcf = d;
-        gemm(h, K_GEMM_DM, true, true, EPI_STORE_F32, g, st, true);
+      h->launches++;
+      for (int s = 0; s < B; ++s) {
+        void *wguT = off(lw.wguT, s * h->fguT_sb);
+        void *wgu = off(lw.wgu, s * h->fgu_sb);
+        float *mgu = h->m_gu[lw.u] + (size_t)s * 2 * F * d;
+        if (!last) {
+          GemmArgs g = gargs(off(h->dgu, rows(s, 4 * F, es)), 4 * F, wguT, 4 * F, n, d, 4 * F);
+          g.Cf = h->dm + (size_t)s * n * d;
+          g.ldcf = d;
+          gemm(h, K_GEMM_DM, true, true, EPI_STORE_F32, g, st, true);
+        }
+        {
+          PROF(K_TRANSPOSE);
+          HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, off(h->dgu, rows(s, 4 * F, es)), 4 * F, h->dguT, b, n,
+                                  np, 2 * F, st, f16));
+          HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, off(S.m, rows(s, d, es)), d, h->mT, b, n, np, d, st,
+                                  f16));
+        }
+        // dW(gate|up)_fast = dGU_fast^T m, SGD fused
+        {
+          GemmArgs g = gargs(h->dguT, b, h->mT, b, 2 * F, d, np);
+          g.Cf = mgu;
+          g.ldcf = d;
+          g.C = wgu;  // hi columns of the fast rows
+          g.ldc = 2 * d;
+          g.C2 = dt == 1 ? off(wgu, (size_t)d * es) : nullptr;  // lo columns
+          g.ldc2 = 2 * d;
+          g.c_f16 = f16;
+          g.c_scale = h->wscale;
+          g.alpha = h->cfg.eta / h->gscale;
+          gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st, true);
+        }
+        {
+          PROF(K_TRANSPOSE);
+          HIPCHK(transpose_launch(dt, SRC_F32, mgu, d, wguT, 4 * F, 2 * F, 2 * F, d, st, f16));
+        }
+        h->launches += last ? 4 : 5;
       }
-      {
-        PROF(K_TRANSPOSE);
-        HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, h->dgu, 4 * F, h->dguT, h->b, n, np, 2 * F, st, f16));
-        HIPCHK(transpose_launch(dt, f16 ? SRC_F16 : SRC_WORK, S.m, d, h->mT, h->b, n, np, d, st, f16));
-      }
-      // dW(gate|up)_fast = dGU_fast^T m, SGD fused
-      {
-        GemmArgs g = gargs(h->dguT, h->b, h->mT, h->b, 2 * F, d, np);
-        g.Cf = h->m_gu[lw.u];
-        g.ldcf = d;
-        g.C = lw.wgu;  // hi columns of the fast rows
-        g.ldc = 2 * d;
-        g.C2 = dt == 1 ? off(lw.wgu, (size_t)d * es) : nullptr;  // lo columns
-        g.ldc2 = 2 * d;
-        g.c_f16 = f16;
-        g.c_scale = h->wscale;
-        g.alpha = h->cfg.eta / h->gscale;
-        gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st, true);
-      }
-      {
-        PROF(K_TRANSPOSE);
-        HIPCHK(transpose_launch(dt, SRC_F32, h->m_gu[lw.u], d, lw.wguT, 4 * F, 2 * F, 2 * F, d, st, f16));
-      }
-      h->launches += 7;
       if (last) break;
       {
         PROF(K_RMSNORM_BWD);
-        HIPCHK(rmsnorm_bwd_launch(dt, h->dm, S.h1, S.r2, lw.mlp_norm, h->dh, h->dh, h->dy, n, d, st, f16));
+        HIPCHK(rmsnorm_bwd_launch(dt, h->dm, S.h1, S.r2, lw.mlp_norm, h->dh, h->dh, h->dy, Bn, d, st, f16));
       }
       // attention sub-block backward
       {
-        GemmArgs g = gargs(h->dy, d, lw.woT, d, n, d, d);
+        GemmArgs g = gargs(h->dy, d, lw.woT, d, Bn, d, d);
         g.C = h->dO;
         g.ldc = d;
         gemm(h, K_GEMM_DO, true, true, EPI_STORE, g, st, true);  // dO itself is bf16
       }
-      {
-        PROF(K_ATTN_BWD_PRE);
-        HIPCHK(attn_bwd_pre_launch(dt, h->dO, S.o, h->Dq, h->dOt, n, d, h->H, h->hd, h->b, h->b, st, f16));
-      }
-      {
-        AttnArgs aa;
-        memset(&aa, 0, sizeof(aa));
-        aa.q = lw.fwd16 ? S.qhb : S.qh;  // working-dtype copies for the backward
-        aa.qt = S.qht;
-        aa.dout = h->dO;
-        aa.doutt = h->dOt;
-        aa.K = lw.fwd16 ? lw.Kb : lw.K;
-        aa.Vt = lw.Vt;
-        aa.Kt = lw.Kt;
-        aa.V = lw.V;
-        aa.lse2 = S.lse2;
-        aa.Dq = h->Dq;
-        aa.dq = h->dq;
-        aa.dk = h->dk;
-        aa.dv = h->dv;
-        aa.n = n;
-        aa.d = d;
-        aa.H = h->H;
-        aa.R = h->R;
-        aa.window = h->k;
-        aa.ldl = h->b;
-        aa.ldt = h->b;
-        aa.pos0 = h->pos0;
-        aa.scale = 1.f / sqrtf((float)h->hd);
-        aa.nsplit = h->attn_split;
-        aa.ws = h->attn_ws;
+      h->launches += 2;
+      for (int s = 0; s < B; ++s) {
+        const size_t rs = s * h->ring_sbytes;
+        void *dO = off(h->dO, rows(s, d, es));
         {
-          PROF(K_ATTN_BWD_DQ);
-          HIPCHK(attn_bwd_dq_launch(dt, h->hd, aa, st));
-        }
-        if (aa.nsplit > 1) {
-          PROF(K_ATTN_MERGE);
-          HIPCHK(attn_merge_launch(dt, h->hd, true, aa, st));
+          PROF(K_ATTN_BWD_PRE);
+          HIPCHK(attn_bwd_pre_launch(dt, dO, off(S.o, rows(s, d, es)), h->Dq, h->dOt, n, d, H, hd, b, b, st, f16));
         }
         {
-          PROF(K_ATTN_BWD_DKDV);
-          HIPCHK(attn_bwd_dkdv_launch(dt, h->hd, aa, st));
+          AttnArgs aa;
+          memset(&aa, 0, sizeof(aa));
+          aa.q = off(lw.fwd16 ? S.qhb : S.qh, rows(s, d, es));  // working-dtype copies for the backward
+          aa.qt = off(S.qht, (size_t)s * b * d * es);
+          aa.dout = dO;
+          aa.doutt = h->dOt;
+          aa.K = off(lw.fwd16 ? lw.Kb : lw.K, rs);
+          aa.Vt = off(lw.Vt, rs);
+          aa.Kt = off(lw.Kt, rs);
+          aa.V = off(lw.V, rs);
+          aa.lse2 = S.lse2 + (size_t)s * H * b;
+          aa.Dq = h->Dq;
+          aa.dq = h->dq + (size_t)s * n * d;
+          aa.dk = h->dk + (size_t)s * n * d;
+          aa.dv = h->dv + (size_t)s * n * d;
+          aa.n = n;
+          aa.d = d;
+          aa.H = H;
+          aa.R = h->R;
+          aa.window = h->k;
+          aa.ldl = b;
+          aa.ldt = b;
+          aa.pos0 = h->pos0;
+          aa.scale = 1.f / sqrtf((float)hd);
+          aa.nsplit = h->attn_split;
+          aa.ws = h->attn_ws;
+          {
+            PROF(K_ATTN_BWD_DQ);
+            HIPCHK(attn_bwd_dq_launch(dt, hd, aa, st));
+          }
+          if (aa.nsplit > 1) {
+            PROF(K_ATTN_MERGE);
+            HIPCHK(attn_merge_launch(dt, hd, true, aa, st));
+          }
+          {
+            PROF(K_ATTN_BWD_DKDV);
+            HIPCHK(attn_bwd_dkdv_launch(dt, hd, aa, st));
+          }
         }
-      }
-      {
-        RopeArgs ra;
-        memset(&ra, 0, sizeof(ra));
-        ra.qkv = S.qkv;
-        ra.gq = lw.q_norm;
-        ra.gk = lw.k_norm;
-        ra.cs = h->rope;
-        ra.pos0 = h->pos0;
-        ra.n = n;
-        ra.d = d;
-        ra.H = h->H;
-        ra.hd = h->hd;
-        ra.R = h->R;
-        ra.eps = eps;
-        ra.dqh = h->dq;
-        ra.dkh = h->dk;
-        ra.dv = h->dv;
-        ra.dqkv = h->dqkv;
         {
+          RopeArgs ra;
+          memset(&ra, 0, sizeof(ra));
+          ra.qkv = S.qkv + (size_t)s * n * 3 * d;
+          ra.gq = lw.q_norm;
+          ra.gk = lw.k_norm;
+          ra.cs = h->rope;
+          ra.pos0 = h->pos0;
+          ra.n = n;
+          ra.d = d;
+          ra.H = H;
+          ra.hd = hd;
+          ra.R = h->R;
+          ra.eps = eps;
+          ra.dqh = h->dq + (size_t)s * n * d;
+          ra.dkh = h->dk + (size_t)s * n * d;
+          ra.dv = h->dv + (size_t)s * n * d;
+          ra.dqkv = off(h->dqkv, rows(s, 3 * d, es));
           PROF(K_ROPE_BWD);
           HIPCHK(qk_rope_bwd_launch(dt, ra, st));
         }
+        h->launches += h->attn_split > 1 ? 5 : 4;
       }
       {
-        GemmArgs g = gargs(h->dqkv, 3 * d, lw.wqkvT, 3 * d, n, d, 3 * d);
+        GemmArgs g = gargs(h->dqkv, 3 * d, lw.wqkvT, 3 * d, Bn, d, 3 * d);
         g.Cf = h->da;
         g.ldcf = d;
         gemm(h, K_GEMM_DA, true, true, EPI_STORE_F32, g, st);
       }
       {
         PROF(K_RMSNORM_BWD);
-        HIPCHK(rmsnorm_bwd_launch(dt, h->da, S.h_in, S.r1, lw.attn_norm, h->dh, h->dh, h->dy, n, d, st, f16));
+        HIPCHK(rmsnorm_bwd_launch(dt, h->da, S.h_in, S.r1, lw.attn_norm, h->dh, h->dh, h->dy, Bn, d, st, f16));
       }
-      h->launches += 6;
+      h->launches += 2;
     }
   }
   {
@@ -613,8 +657,8 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
   h->launches++;
 }
 
-// Copies W_init into the fp32 masters, the forward copies (hi | lo, fp16 and
-// scaled by wscale in bf16 mode) and the fast parts of the transposed
+// Copies W_init into every sequence's fp32 masters, forward copies (hi | lo,
+// fp16 and scaled by wscale in bf16 mode) and the fast parts of the transposed
 // working-dtype copies of the backward (the static parts are set at creation).
 void reset_fast(ttt_handle *h, hipStream_t st) {
   const int d = h->d, F = h->F;
@@ -622,15 +666,21 @@ void reset_fast(ttt_handle *h, hipStream_t st) {
   for (int l = 0; l < h->L; ++l) {
     LayerBuf &lw = h->layers[l];
     if (!lw.fast) continue;
-    HIPCHK(hipMemcpyAsync(h->m_gu[lw.u], h->i_gu[lw.u], (size_t)2 * F * d * 4, hipMemcpyDeviceToDevice, st));
-    HIPCHK(hipMemcpyAsync(h->m_d[lw.u], h->i_d[lw.u], (size_t)d * F * 4, hipMemcpyDeviceToDevice, st));
-    HIPCHK(convert_rows_launch(fdt, h->i_gu[lw.u], d, lw.wgu, 2 * d, 2 * F, d, st,
-                               h->dt == 1 ? off(lw.wgu, (size_t)d * h->es) : nullptr, 2 * d, h->wscale));
-    HIPCHK(convert_rows_launch(fdt, h->i_d[lw.u], F, lw.wd, 3 * F, d, F, st,
-                               h->dt == 1 ? off(lw.wd, (size_t)2 * F * h->es) : nullptr, 3 * F, h->wscale));
-    // Wd_cat^T [2F][d] rows [0, F) and Wgu_cat^T [d][4F] columns [0, 2F), from the masters
-    HIPCHK(transpose_launch(h->dt, SRC_F32, h->i_d[lw.u], F, lw.wdT, d, d, d, F, st, h->dt == 1));
-    HIPCHK(transpose_launch(h->dt, SRC_F32, h->i_gu[lw.u], d, lw.wguT, 4 * F, 2 * F, 2 * F, d, st, h->dt == 1));
+    for (int s = 0; s < h->B; ++s) {
+      float *mgu = h->m_gu[lw.u] + (size_t)s * 2 * F * d, *md = h->m_d[lw.u] + (size_t)s * d * F;
+      void *wgu = off(lw.wgu, s * h->fgu_sb), *wd = off(lw.wd, s * h->fd_sb);
+      HIPCHK(hipMemcpyAsync(mgu, h->i_gu[lw.u], (size_t)2 * F * d * 4, hipMemcpyDeviceToDevice, st));
+      HIPCHK(hipMemcpyAsync(md, h->i_d[lw.u], (size_t)d * F * 4, hipMemcpyDeviceToDevice, st));
+      HIPCHK(convert_rows_launch(fdt, h->i_gu[lw.u], d, wgu, 2 * d, 2 * F, d, st,
+                                 h->dt == 1 ? off(wgu, (size_t)d * h->es) : nullptr, 2 * d, h->wscale));
+      HIPCHK(convert_rows_launch(fdt, h->i_d[lw.u], F, wd, 3 * F, d, F, st,
+                                 h->dt == 1 ? off(wd, (size_t)2 * F * h->es) : nullptr, 3 * F, h->wscale));
+      // Wd_cat^T [2F][d] rows [0, F) and Wgu_cat^T [d][4F] columns [0, 2F), from the masters
+      HIPCHK(transpose_launch(h->dt, SRC_F32, h->i_d[lw.u], F, off(lw.wdT, s * h->fdT_sb), d, d, d, F, st,
+                              h->dt == 1));
+      HIPCHK(transpose_launch(h->dt, SRC_F32, h->i_gu[lw.u], d, off(lw.wguT, s * h->fguT_sb), 4 * F, 2 * F, 2 * F, d,
+                              st, h->dt == 1));
+    }
   }
 }
 
@@ -724,13 +774,14 @@ void run_step(ttt_handle *h, int n, bool update, int mode, bool use_graph, hipSt
 void copy_fast_out(ttt_handle *h, float *const *d_fast_out, hipStream_t st) {
   const int d = h->d, F = h->F;
   const size_t blk = (size_t)16 * d * 4;
-  for (int u = 0; u < h->nu; ++u) {
-    HIPCHK(hipMemcpy2DAsync(d_fast_out[3 * u + 0], blk, h->m_gu[u], 2 * blk, blk, F / 16, hipMemcpyDeviceToDevice,
-                            st));
-    HIPCHK(hipMemcpy2DAsync(d_fast_out[3 * u + 1], blk, (char *)h->m_gu[u] + blk, 2 * blk, blk, F / 16,
-                            hipMemcpyDeviceToDevice, st));
-    HIPCHK(hipMemcpyAsync(d_fast_out[3 * u + 2], h->m_d[u], (size_t)d * F * 4, hipMemcpyDeviceToDevice, st));
-  }
+  for (int s = 0; s < h->B; ++s)
+    for (int u = 0; u < h->nu; ++u) {
+      float *const *o = d_fast_out + 3 * (s * h->nu + u);
+      const float *mgu = h->m_gu[u] + (size_t)s * 2 * F * d, *md = h->m_d[u] + (size_t)s * d * F;
+      HIPCHK(hipMemcpy2DAsync(o[0], blk, mgu, 2 * blk, blk, F / 16, hipMemcpyDeviceToDevice, st));
+      HIPCHK(hipMemcpy2DAsync(o[1], blk, (const char *)mgu + blk, 2 * blk, blk, F / 16, hipMemcpyDeviceToDevice, st));
+      HIPCHK(hipMemcpyAsync(o[2], md, (size_t)d * F * 4, hipMemcpyDeviceToDevice, st));
+    }
 }
 
 }  // namespace
@@ -744,6 +795,7 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
   const ttt_config c = *cfg;
   if (c.n_layers < 1 || c.n_update < 0 || c.n_update > c.n_layers)
     return fail(nullptr, TTT_EINVAL, "n_layers >= 1 and 0 <= n_update <= n_layers required");
+  if (c.n_seq < 0 || c.n_seq > 256) return fail(nullptr, TTT_EINVAL, "n_seq must be in [0, 256] (0 means 1)");
   if (c.n_heads < 1 || c.d_model != c.n_heads * c.head_dim) return fail(nullptr, TTT_EINVAL, "d_model != n_heads * head_dim");
   if (c.d_model % 16 || c.d_ff % 16 || c.vocab % 16 || c.d_model <= 0 || c.d_ff <= 0 || c.vocab <= 0)
     return fail(nullptr, TTT_EINVAL, "d_model, d_ff and vocab must be positive multiples of 16");
@@ -786,6 +838,8 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
   h->b = c.chunk;
   h->nu = c.n_update;
   h->R = c.window + c.chunk;  // positions s-k+1 .. s+b-1 must coexist; multiple of 64
+  h->B = c.n_seq > 0 ? c.n_seq : 1;
+  h->ld_tok = c.max_tokens + 1;
   h->Vs = std::min(h->V, 16384);
   h->P = 2 * ((h->V + 127) / 128);
   hipStream_t st = (hipStream_t)stream;
@@ -842,7 +896,8 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
       while (sh > 0 && std::ldexp(mx, sh) > 4096.f) --sh;
       h->wscale = std::ldexp(1.f, sh);
     }
-    h->ring_bytes = plane * nplanes;
+    h->ring_sbytes = plane * nplanes;
+    h->ring_bytes = h->ring_sbytes * h->B;  // sequence s's planes at s * ring_sbytes
     h->ring_base = dalloc(h, h->ring_bytes);
     size_t roff = 0;
     for (int l = 0; l < L; ++l) {
@@ -872,27 +927,35 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
         HIPCHK(hipMemcpyAsync(lw.wd, w->w_down[l], fd, hipMemcpyDeviceToDevice, st));
       } else {
         const int u = lw.u;
-        lw.wgu = dalloc(h, 6 * fd, false);
-        pack_gu(w->w_gate[l], w->w_up[l], off(lw.wgu, 4 * fd), F, d, es, st);  // static rows after fast hi|lo
-        lw.wd = dalloc(h, 3 * fd, false);
-        HIPCHK(hipMemcpy2DAsync(off(lw.wd, (size_t)F * es), 3 * F * es, w->w_down[l], F * es, F * es, d,
-                                hipMemcpyDeviceToDevice, st));
+        h->fgu_sb = 4 * fd;
+        h->fd_sb = 3 * fd;
+        h->fdT_sb = 2 * fd;
+        h->fguT_sb = 4 * fd;
+        lw.wgu = dalloc(h, h->B * h->fgu_sb, false);  // fast hi | lo rows per sequence (written by reset_fast)
+        lw.wgu_s = dalloc(h, 2 * fd, false);
+        pack_gu(w->w_gate[l], w->w_up[l], lw.wgu_s, F, d, es, st);
+        lw.wd = dalloc(h, h->B * h->fd_sb, false);
+        for (int sq = 0; sq < h->B; ++sq)
+          HIPCHK(hipMemcpy2DAsync(off(lw.wd, sq * h->fd_sb + (size_t)F * es), 3 * F * es, w->w_down[l], F * es, F * es,
+                                  d, hipMemcpyDeviceToDevice, st));
         const size_t f32fd = (size_t)F * d * 4;
-        h->m_gu[u] = (float *)dalloc(h, 2 * f32fd);
-        h->m_d[u] = (float *)dalloc(h, f32fd);
+        h->m_gu[u] = (float *)dalloc(h, h->B * 2 * f32fd);
+        h->m_d[u] = (float *)dalloc(h, h->B * f32fd);
         h->i_gu[u] = (float *)dalloc(h, 2 * f32fd, false);
         h->i_d[u] = (float *)dalloc(h, f32fd, false);
         pack_gu(w->fast_gate[u], w->fast_up[u], h->i_gu[u], F, d, 4, st);
         HIPCHK(hipMemcpyAsync(h->i_d[u], w->fast_down[u], f32fd, hipMemcpyDeviceToDevice, st));
       }
       if (lw.fast && h->nu > 0) {
-        lw.wdT = dalloc(h, 2 * fd, false);
-        lw.wguT = dalloc(h, 4 * fd, false);
-        // static parts of Wd_cat^T (rows [F, 2F)) and Wgu_cat^T (columns [2F, 4F))
-        HIPCHK(transpose_launch(h->dt, SRC_WORK, off(lw.wd, (size_t)F * es), 3 * F, off(lw.wdT, fd), d, d, d, F, st,
-                                h->dt == 1));
-        HIPCHK(transpose_launch(h->dt, SRC_WORK, off(lw.wgu, 4 * fd), d, off(lw.wguT, (size_t)2 * F * es), 4 * F,
-                                2 * F, 2 * F, d, st, h->dt == 1));
+        lw.wdT = dalloc(h, h->B * h->fdT_sb, false);
+        lw.wguT = dalloc(h, h->B * h->fguT_sb, false);
+        // static parts of each sequence's Wd_cat^T (rows [F, 2F)) and Wgu_cat^T (columns [2F, 4F))
+        for (int sq = 0; sq < h->B; ++sq) {
+          HIPCHK(transpose_launch(h->dt, SRC_WORK, off(lw.wd, (size_t)F * es), 3 * F, off(lw.wdT, sq * h->fdT_sb + fd), d,
+                                  d, d, F, st, h->dt == 1));
+          HIPCHK(transpose_launch(h->dt, SRC_WORK, lw.wgu_s, d, off(lw.wguT, sq * h->fguT_sb + (size_t)2 * F * es),
+                                  4 * F, 2 * F, 2 * F, d, st, h->dt == 1));
+        }
       }
       if (lw.bwd_attn) {
         lw.woT = dalloc(h, dd, false);
@@ -905,11 +968,13 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
         // (the fast hi | lo rows and columns are written by reset_fast)
         HIPCHK(bf16_to_f16_launch(lw.wqkv, 3 * d, lw.wqkv, 3 * d, 1, 3 * d * d, st));
         HIPCHK(bf16_to_f16_launch(lw.wo, d, lw.wo, d, 1, d * d, st));
-        void *gus = lw.fast ? off(lw.wgu, 4 * fd) : lw.wgu;
+        void *gus = lw.fast ? lw.wgu_s : lw.wgu;
         HIPCHK(bf16_to_f16_launch(gus, d, gus, d, 2 * F, d, st));
         if (lw.fast)  // static down columns share the fast ones' scale
-          HIPCHK(bf16_to_f16_launch(off(lw.wd, (size_t)F * es), 3 * F, off(lw.wd, (size_t)F * es), 3 * F, d, F, st,
-                                    h->wscale));
+          for (int sq = 0; sq < h->B; ++sq) {
+            void *sc = off(lw.wd, sq * h->fd_sb + (size_t)F * es);
+            HIPCHK(bf16_to_f16_launch(sc, 3 * F, sc, 3 * F, d, F, st, h->wscale));
+          }
         else
           HIPCHK(bf16_to_f16_launch(lw.wd, F, lw.wd, F, d, F, st));
       }
@@ -929,60 +994,66 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
       }
     }
     // ---- state and chunk scratch
-    const size_t bd = (size_t)b * d;
-    h->tok = (int *)dalloc(h, (c.max_tokens + 1) * sizeof(int));
-    h->losses = (float *)dalloc(h, c.max_tokens * sizeof(float));
+    const size_t bd = (size_t)b * d;        // one sequence's chunk
+    const int Bb = h->B * b;                 // rows of a batched chunk
+    const size_t Bbd = (size_t)Bb * d;
+    h->tok = (int *)dalloc(h, h->B * h->ld_tok * sizeof(int));
+    h->losses = (float *)dalloc(h, h->B * c.max_tokens * sizeof(float));
+    h->ids = (int *)dalloc(h, Bb * sizeof(int));
+    h->labs = (int *)dalloc(h, Bb * sizeof(int));
+    h->zero = (int *)dalloc(h, 64);
+    h->closs = (float *)dalloc(h, Bb * sizeof(float));
     h->pos0 = (int *)dalloc(h, 64);
     h->flag = (int *)dalloc(h, 64);
     h->rope = (float2 *)dalloc(h, (size_t)c.max_tokens * (h->hd / 2) * sizeof(float2), false);
     HIPCHK(rope_table_launch(h->rope, c.max_tokens, h->hd, (double)c.rope_theta, st));
-    h->h = (float *)dalloc(h, bd * 4);
-    h->lse2 = (float *)dalloc(h, (size_t)h->H * b * 4);
-    h->a = dalloc(h, bd * es);
-    h->qkv = (float *)dalloc(h, 3 * bd * 4);
-    h->qh = dalloc(h, bd * es);
-    h->o = dalloc(h, bd * es);
-    h->m = dalloc(h, bd * es);
-    h->hmid = dalloc(h, (size_t)b * (h->nu > 0 ? 2 * F : F) * es);
-    h->nf = dalloc(h, bd * es);
-    h->hf = (float *)dalloc(h, bd * 4);
-    h->rf = (float *)dalloc(h, b * 4);
-    h->zlab = (float *)dalloc(h, b * 4);
-    h->lse = (float *)dalloc(h, b * 4);
-    h->part = (float2 *)dalloc(h, (size_t)b * h->P * sizeof(float2));
-    h->part_arg = (int *)dalloc(h, (size_t)b * h->P * sizeof(int));
+    h->h = (float *)dalloc(h, Bbd * 4);
+    h->lse2 = (float *)dalloc(h, (size_t)h->H * Bb * 4);
+    h->a = dalloc(h, Bbd * es);
+    h->qkv = (float *)dalloc(h, 3 * Bbd * 4);
+    h->qh = dalloc(h, Bbd * es);
+    h->o = dalloc(h, Bbd * es);
+    h->m = dalloc(h, Bbd * es);
+    h->hmid = dalloc(h, (size_t)Bb * (h->nu > 0 ? 2 * F : F) * es);
+    h->nf = dalloc(h, Bbd * es);
+    h->hf = (float *)dalloc(h, Bbd * 4);
+    h->rf = (float *)dalloc(h, Bb * 4);
+    h->zlab = (float *)dalloc(h, Bb * 4);
+    h->lse = (float *)dalloc(h, Bb * 4);
+    h->part = (float2 *)dalloc(h, (size_t)Bb * h->P * sizeof(float2));
+    h->part_arg = (int *)dalloc(h, (size_t)Bb * h->P * sizeof(int));
     h->rlosses = (float *)dalloc(h, c.max_tokens * sizeof(float));
     if (h->nu > 0) {
-      h->dz = dalloc(h, (size_t)b * h->Vs * es);
-      h->dn = (float *)dalloc(h, bd * 4);
-      h->dh = (float *)dalloc(h, bd * 4);
-      h->dy = dalloc(h, bd * es);
-      h->dhmid = dalloc(h, (size_t)b * 2 * F * es);
-      h->dgu = dalloc(h, (size_t)b * 4 * F * es);
-      h->dm = (float *)dalloc(h, bd * 4);
-      h->dO = dalloc(h, bd * es);
-      h->dOt = dalloc(h, bd * es);
-      h->Dq = (float *)dalloc(h, (size_t)h->H * b * 4);
-      h->dq = (float *)dalloc(h, bd * 4);
-      h->dk = (float *)dalloc(h, bd * 4);
-      h->dv = (float *)dalloc(h, bd * 4);
-      h->dqkv = dalloc(h, 3 * bd * es);
-      h->da = (float *)dalloc(h, bd * 4);
+      h->dz = dalloc(h, (size_t)Bb * h->Vs * es);
+      h->dn = (float *)dalloc(h, Bbd * 4);
+      h->dh = (float *)dalloc(h, Bbd * 4);
+      h->dy = dalloc(h, Bbd * es);
+      h->dhmid = dalloc(h, (size_t)Bb * 2 * F * es);
+      h->dgu = dalloc(h, (size_t)Bb * 4 * F * es);
+      h->dm = (float *)dalloc(h, Bbd * 4);
+      h->dO = dalloc(h, Bbd * es);
+      h->dOt = dalloc(h, bd * es);                       // one sequence at a time
+      h->Dq = (float *)dalloc(h, (size_t)h->H * b * 4);  // one sequence at a time
+      h->dq = (float *)dalloc(h, Bbd * 4);
+      h->dk = (float *)dalloc(h, Bbd * 4);
+      h->dv = (float *)dalloc(h, Bbd * 4);
+      h->dqkv = dalloc(h, 3 * Bbd * es);
+      h->da = (float *)dalloc(h, Bbd * 4);
       for (int u = 0; u < h->nu; ++u) {
         Saved &S = h->saved[u];
-        S.h_in = (float *)dalloc(h, bd * 4);
-        S.r1 = (float *)dalloc(h, b * 4);
-        S.lse2 = (float *)dalloc(h, (size_t)h->H * b * 4);
-        S.h1 = (float *)dalloc(h, bd * 4);
-        S.r2 = (float *)dalloc(h, b * 4);
-        S.qkv = (float *)dalloc(h, 3 * bd * 4);
-        S.qh = dalloc(h, bd * es);
-        if (h->layers[h->L - h->nu + u].fwd16) S.qhb = dalloc(h, bd * es);
-        S.qht = dalloc(h, bd * es);
-        S.o = dalloc(h, bd * es);
-        S.m = dalloc(h, bd * es);
-        S.gu = dalloc(h, (size_t)b * 4 * F * es);
-        S.hmid = dalloc(h, (size_t)b * 2 * F * es);
+        S.h_in = (float *)dalloc(h, Bbd * 4);
+        S.r1 = (float *)dalloc(h, Bb * 4);
+        S.lse2 = (float *)dalloc(h, (size_t)h->H * Bb * 4);
+        S.h1 = (float *)dalloc(h, Bbd * 4);
+        S.r2 = (float *)dalloc(h, Bb * 4);
+        S.qkv = (float *)dalloc(h, 3 * Bbd * 4);
+        S.qh = dalloc(h, Bbd * es);
+        if (h->layers[h->L - h->nu + u].fwd16) S.qhb = dalloc(h, Bbd * es);
+        S.qht = dalloc(h, Bbd * es);
+        S.o = dalloc(h, Bbd * es);
+        S.m = dalloc(h, Bbd * es);
+        S.gu = dalloc(h, (size_t)Bb * 4 * F * es);
+        S.hmid = dalloc(h, (size_t)Bb * 2 * F * es);
       }
     }
     h->attn_split = attn_pick_split(b, h->H, h->k, b);
@@ -1025,7 +1096,7 @@ ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float 
   if (T < 0 || T > h->cfg.max_tokens) return fail(h, TTT_EINVAL, "T out of range [0, max_tokens]");
   if (T > 0 && (!d_tokens || !d_losses)) return fail(h, TTT_EINVAL, "null tokens or losses");
   if (d_fast_out)
-    for (int i = 0; i < 3 * h->nu; ++i)
+    for (int i = 0; i < 3 * h->nu * h->B; ++i)
       if (!d_fast_out[i]) return fail(h, TTT_EINVAL, "null entry in d_fast_out");
   flags |= h->cfg.flags;
   const bool update = !(flags & TTT_NO_UPDATE) && h->nu > 0;
@@ -1034,7 +1105,8 @@ ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float 
   const int b = h->b;
   try {
     if (d_tokens)
-      HIPCHK(hipMemcpyAsync(h->tok, d_tokens, (size_t)(T + 1) * sizeof(int), hipMemcpyDeviceToDevice, st));
+      HIPCHK(hipMemcpy2DAsync(h->tok, h->ld_tok * sizeof(int), d_tokens, (size_t)(T + 1) * sizeof(int),
+                              (size_t)(T + 1) * sizeof(int), h->B, hipMemcpyDeviceToDevice, st));
     HIPCHK(set_int_launch(h->pos0, 0, st));
     HIPCHK(set_int_launch(h->flag, 0, st));
     HIPCHK(zero_launch(h->ring_base, h->ring_bytes, st));
@@ -1044,8 +1116,11 @@ ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float 
     for (int64_t c = 0; c < nfull; ++c) run_step(h, b, update, MODE_PREFILL, use_graph, st);
     if (tail > 0) run_step(h, tail, update, MODE_PREFILL, use_graph, st);
     if (T > 0) {
-      HIPCHK(hipMemcpyAsync(d_losses, h->losses, (size_t)T * sizeof(float), hipMemcpyDeviceToDevice, st));
-      HIPCHK(finite_check_launch(h->losses, T, h->flag, st));
+      const size_t ldl = (size_t)h->cfg.max_tokens * sizeof(float);
+      HIPCHK(hipMemcpy2DAsync(d_losses, (size_t)T * sizeof(float), h->losses, ldl, (size_t)T * sizeof(float), h->B,
+                              hipMemcpyDeviceToDevice, st));
+      for (int s = 0; s < h->B; ++s)
+        HIPCHK(finite_check_launch(h->losses + (size_t)s * h->cfg.max_tokens, T, h->flag, st));
     }
     if (d_fast_out) copy_fast_out(h, d_fast_out, st);
     h->len = T;
@@ -1062,6 +1137,7 @@ ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float 
 ttt_status ttt_decode(ttt_handle *h, int64_t n_steps, const int32_t *d_forced, int32_t *d_tokens_out,
                       float *d_losses_out, float *const *d_fast_out, uint32_t flags, void *stream) {
   if (!h) return fail(nullptr, TTT_EINVAL, "null handle");
+  if (h->B != 1) return fail(h, TTT_EUNSUPPORTED, "ttt_decode continues a single sequence (n_seq = 1)");
   if (!h->have_state) return fail(h, TTT_EINVAL, "no prefill state to continue (run ttt_prefill with tokens first)");
   if (n_steps < 0 || h->len + n_steps > h->cfg.max_tokens)
     return fail(h, TTT_EINVAL, "n_steps out of range: the sequence may not exceed max_tokens positions");

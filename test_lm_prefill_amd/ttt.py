@@ -24,7 +24,8 @@ class ttt_config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("chunk", ctypes.c_int32), ("n_update", ctypes.c_int32),
                 ("eta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
-                ("dtype", ctypes.c_int32), ("max_tokens", ctypes.c_int64), ("flags", ctypes.c_uint32)]
+                ("dtype", ctypes.c_int32), ("max_tokens", ctypes.c_int64), ("flags", ctypes.c_uint32),
+                ("n_seq", ctypes.c_int32)]
 
 
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -161,7 +162,7 @@ class Session:
     """Holds one handle built from a dict of device tensors named as in the
     workload generators (tok_emb, lm_head, final_norm, l{i}.wq, ..., fast{u}.w_gate, ...)."""
 
-    def __init__(self, cfg, weights, max_tokens=None, flags=0):
+    def __init__(self, cfg, weights, max_tokens=None, flags=0, n_seq=1):
         import torch
         self.torch = torch
         self.cfg = cfg
@@ -173,6 +174,8 @@ class Session:
         c.dtype = TTT_BF16 if cfg.dtype == "bf16" else TTT_FP32
         c.max_tokens = int(max_tokens if max_tokens is not None else cfg.seq_len)
         c.flags = flags
+        c.n_seq = int(n_seq)
+        self.n_seq = max(1, int(n_seq))
         self.c = c
         L, nu = cfg.n_layers, cfg.n_update
         w = ttt_weights()
@@ -200,26 +203,28 @@ class Session:
         self.handle = ttt_create(c, w, stream)
 
     def prefill(self, tokens, flags=0, want_fast=True, check=True):
-        """tokens: int32 device tensor [T+1].  Returns (losses [T] fp32, list of fast tensors or None)."""
+        """tokens: int32 device tensor [T+1] (one sequence) or [B, T+1] (B = n_seq).
+        Returns (losses [T] or [B, T] fp32, fast tensors or None: a flat list of 3*n_u
+        for one sequence, a list of B such lists otherwise)."""
         torch = self.torch
         assert tokens.dtype == torch.int32 and tokens.is_cuda and tokens.is_contiguous()
-        T = tokens.numel() - 1
+        batched = tokens.dim() == 2
+        B = tokens.shape[0] if batched else 1
+        assert B == self.n_seq, "the token batch must hold n_seq sequences"
+        T = tokens.shape[-1] - 1
         dev = tokens.device
-        losses = torch.empty(max(T, 0), dtype=torch.float32, device=dev)
+        losses = torch.empty((B, max(T, 0)) if batched else (max(T, 0),), dtype=torch.float32, device=dev)
         fast = None
         ptrs = None
         if want_fast and self.cfg.n_update > 0:
-            F, d = self.cfg.d_ff, self.cfg.d_model
-            fast = []
-            for _ in range(self.cfg.n_update):
-                fast += [torch.empty(F, d, dtype=torch.float32, device=dev),
-                         torch.empty(F, d, dtype=torch.float32, device=dev),
-                         torch.empty(d, F, dtype=torch.float32, device=dev)]
-            ptrs = [t.data_ptr() for t in fast]
+            fast = [self._fast_buffers(dev) for _ in range(B)]
+            ptrs = [t.data_ptr() for fs in fast for t in fs]
         stream = torch.cuda.current_stream().cuda_stream
         ttt_prefill(self.handle, tokens.data_ptr(), T, losses.data_ptr() if T > 0 else None, ptrs, flags, stream)
         if check:
             ttt_check_finite(self.handle, stream)
+        if fast is not None and not batched:
+            fast = fast[0]
         return losses, fast
 
     def _fast_buffers(self, dev):
