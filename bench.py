@@ -130,14 +130,18 @@ def gpu_bench(cfg, steps, warmup, profile=True):
     return ms_ttt, ms_swa, ktimes, mean_loss, tok_np
 
 
-def time_prefill(cfg, flags, steps, warmup):
-    """ms per prefill of cfg's own sequence with the given flags (fresh session)."""
+def time_prefill(cfg, flags, steps, warmup, n_seq=1):
+    """ms per prefill of cfg's own sequence with the given flags (fresh session); with
+    n_seq > 1, of a batch of n_seq sequences (the workload's stream and n_seq-1 more seeds)."""
     import torch
     from ttt_inputs import make_weights_torch, make_tokens
     from test_lm_prefill_amd import Session
     w = make_weights_torch(cfg, "cuda", seed=0)
-    tok = torch.from_numpy(make_tokens(cfg, seed=1)).cuda()
-    sess = Session(cfg, w, max_tokens=cfg.seq_len)
+    if n_seq == 1:
+        tok = torch.from_numpy(make_tokens(cfg, seed=1)).cuda()
+    else:
+        tok = torch.from_numpy(np.stack([make_tokens(cfg, seed=1 + i) for i in range(n_seq)])).cuda()
+    sess = Session(cfg, w, max_tokens=cfg.seq_len, n_seq=n_seq)
     stream = torch.cuda.current_stream()
     try:
         for _ in range(warmup):
@@ -155,7 +159,7 @@ def time_prefill(cfg, flags, steps, warmup):
         sess.close()
         del w, tok
         torch.cuda.empty_cache()
-    log(f"[bench] {cfg.name} T={cfg.seq_len} k={cfg.window} n_u={cfg.n_update} flags={flags}: {ms:.1f} ms")
+    log(f"[bench] {cfg.name} B={n_seq} T={cfg.seq_len} k={cfg.window} n_u={cfg.n_update} flags={flags}: {ms:.1f} ms")
     return ms
 
 
@@ -193,6 +197,24 @@ def suite_sweep(steps, warmup):
         rows.append({"n_update": nu, "window": k, "ms": round(ms, 1),
                      "ms_per_1k": round(ms * 1024 / cfg.seq_len, 3)})
     return {"suite": "n_update_and_window_sweep", "shape": "760m", "seq_len": base.seq_len, "rows": rows}
+
+
+def suite_batch(steps, warmup):
+    """Batched independent sequences at the 2.7B shape with 131072 tokens per call
+    (B = 131072 / T sequences of T tokens, each with its own fast weights and window),
+    against the same T one sequence per call."""
+    from ttt_inputs import get
+    rows = []
+    for name, B in (("2.7b_8k", 16), ("2.7b_32k", 4)):
+        cfg = get(name)
+        T = cfg.seq_len
+        ms1 = time_prefill(cfg, 0, steps, warmup)
+        msb = time_prefill(cfg, 0, steps, warmup, n_seq=B)
+        rows.append({"seq_len": T, "n_seq": B, "one_seq_ms": round(ms1, 1),
+                     "one_seq_tokens_per_s": round(T / (ms1 / 1e3), 1), "batch_ms": round(msb, 1),
+                     "batch_tokens_per_s": round(B * T / (msb / 1e3), 1),
+                     "speedup": round(B * ms1 / msb, 3)})
+    return {"suite": "batched_sequences", "shape": "2.7b", "tokens_per_batch": 131072, "rows": rows}
 
 
 def suite_decode(steps, warmup, n_decode=2048, prompt_cfg="2.7b_8k"):
@@ -340,10 +362,11 @@ def main():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
                     help="run a calibration kernel and one prefill only (for counter runs)")
-    ap.add_argument("--suite", choices=["full_attention", "sweep", "decode"],
+    ap.add_argument("--suite", choices=["full_attention", "sweep", "decode", "batch"],
                     help="instead of the benchmark line: the full-attention baseline at the 2.7B shape, "
                          "the n_update / window sweep at the 760M shape, or decoding with periodic "
-                         "updates after an 8K prompt at the 2.7B shape (one JSON line)")
+                         "updates after an 8K prompt at the 2.7B shape, or batched sequences at 131072 "
+                         "tokens per call at the 2.7B shape (one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: a TTT prefill sequence is a recurrence over chunks and "
@@ -355,7 +378,8 @@ def main():
         profile_pass(cfg)
         return
     if args.suite:
-        fn = {"full_attention": suite_full_attention, "sweep": suite_sweep, "decode": suite_decode}[args.suite]
+        fn = {"full_attention": suite_full_attention, "sweep": suite_sweep, "decode": suite_decode,
+              "batch": suite_batch}[args.suite]
         print(json.dumps(fn(args.steps, args.warmup)), flush=True)
         return
     T = cfg.seq_len
