@@ -442,6 +442,24 @@ template <int HD> struct F2Issue {
   }
 };
 
+// acc + the sum of the eight 16-bit values of a fragment (v_dot2 against (1, 1)).
+DEVI float sum_pairs(const Frag<f16_t> &f, float acc) {
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  const h2_t one = {(_Float16)1.f, (_Float16)1.f};
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, f.v.x), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, f.v.y), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, f.v.z), one, acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, f.v.w), one, acc, false);
+}
+DEVI float sum_pairs(const Frag<bf16_t> &f, float acc) {
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  const b2_t one = {(__bf16)1.f, (__bf16)1.f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, f.v.x), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, f.v.y), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, f.v.z), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, f.v.w), one, acc, false);
+}
+
 template <int HD, typename TF> struct F2State {
   using C = F2<HD>;
   Frag<TF> qf[4][C::NC];
@@ -501,9 +519,10 @@ DEVI void fwd2_range(F2State<HD, TF> &st, const F2Issue<HD> &is, char *stage, in
             e = (j > p || j <= p - a.window) ? 0.f : e;
           }
           x[4 * ks + r] = e;
-          st.lsum[qs] += e;
         }
       pack_frag(pf[qs], x);
+      // row sum from the packed 16-bit p (the values the PV product uses), two per dot2
+      st.lsum[qs] = sum_pairs(pf[qs], st.lsum[qs]);
     }
 #pragma unroll
     for (int hs = 0; hs < C::NH; ++hs)
