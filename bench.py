@@ -76,6 +76,42 @@ def algorithmic_flops(cfg, T, update=True):
     return f
 
 
+def algorithmic_bytes(cfg, T, update=True):
+    """Per-class HBM bytes of one prefill for the bandwidth-bound kernels: what each kernel
+    must read and write given the stored layouts (fp32 residual stream and projections,
+    16-bit activations, fp32 master fast weights), counted once; no re-reads, padding or
+    cache effects.  Attention merges and split-K reductions depend on the split chosen per
+    launch and are not listed.  `update_in_gemm_dw_sgd` is the SGD step fused into the
+    weight-gradient GEMM's epilogue (read and write the fp32 master, write the 16-bit copy)."""
+    L, d, F, V, nu, H = cfg.n_layers, cfg.d_model, cfg.d_ff, cfg.vocab, cfg.n_update, cfg.n_heads
+    a = 2 if cfg.dtype == "bf16" else 4          # activation / working-copy element size
+    hilo = 2 if cfg.dtype == "bf16" else 1       # 16-bit forward copy is hi + lo
+    nb = max(nu - 1, 0)                          # blocks whose attention is back-propagated
+    P = 2 * ((V + 127) // 128)                   # CE partials per row
+    n_chunks = (T + cfg.chunk - 1) // cfg.chunk
+    # rmsnorm: read fp32 row, write the normalised row; the saved inputs of back-propagated norms
+    rms = (2 * L + 1) * (4 + a) * d + ((nb + nu + 1) * 4 * d if update and nu > 0 else 0)
+    # QK-norm + RoPE: read fp32 q, k, v; write q and the ring's K and V^T; the backward's
+    # copies (V, K^T, 16-bit K) of back-propagated blocks, and with the update q copies
+    rope = L * (12 + 3 * a) * d + nb * 3 * a * d + (nb * 2 * a * d if update else 0)
+    b = {"embed": T * (a + 4) * d, "rmsnorm": T * rms, "qknorm_rope_ring": T * rope,
+         "ce_reduce": T * (8 * P + 12)}
+    if update and nu > 0:
+        b.update({
+            # final norm (dy, x, out fp32 + 16-bit) and two norms per back-propagated block (+ dh_in)
+            "rmsnorm_bwd": T * ((12 + a) * d + 2 * nb * (16 + a) * d),
+            # gate/up pre-activations and dhmid in, dgate/dup out (2F units above the lowest block)
+            "swiglu_bwd": T * 5 * a * (nb * 2 * F + F),
+            "qknorm_rope_bwd": T * nb * (24 + 3 * a) * d,
+            "attn_bwd_pre": T * nb * (3 * a * d + 4 * H),
+            # activations dy, hmid, dgu, m (read + write) per token; the refreshed transposed
+            # weight copies (fp32 master in, 16-bit out) per chunk
+            "transpose": nu * (T * 2 * a * (2 * d + 3 * F) + n_chunks * 3 * d * F * (4 + a)),
+            "update_in_gemm_dw_sgd": n_chunks * nu * 3 * d * F * (8 + hilo * a),
+        })
+    return b
+
+
 def gpu_bench(cfg, steps, warmup, profile=True):
     import torch
     from ttt_inputs import make_weights_torch, make_tokens
@@ -395,6 +431,7 @@ def main():
 
     roof = None
     kernels = {}
+    hbm = algorithmic_bytes(cfg, T, update=True)
     if kt:
         tot_prof = sum(v[0] for v in kt.values())
         for nm, (ms, n) in sorted(kt.items(), key=lambda x: -x[1][0]):
@@ -404,6 +441,13 @@ def main():
             if nm in flops and ms > 0:
                 ent["tflops"] = round(flops[nm] / 1e12 / (ms / 1e3), 1)
                 ent["mfma_frac"] = round(flops[nm] / 1e12 / (ms / 1e3) / peak, 4)
+            ub = hbm.get("update_in_gemm_dw_sgd") if nm == "gemm_dw_sgd" else None
+            if (nm in hbm or ub) and ms > 0:
+                by = ub if ub else hbm[nm]
+                key = "update_" if ub else ""
+                ent[key + "gbytes"] = round(by / 1e9, 3)
+                ent[key + "gbps"] = round(by / 1e9 / (ms / 1e3), 1)
+                ent[key + "hbm_frac"] = round(by / 1e9 / (ms / 1e3) / PEAK_HBM_GBS, 4)
             kernels[nm] = ent
         dom = max((nm for nm in kernels if nm in flops), key=lambda nm: kernels[nm]["ms"])
         ms_d, n_d = kt[dom]

@@ -36,28 +36,37 @@ __global__ __launch_bounds__(256) void embed_kernel(const T *E, const int *tok, 
 }
 
 // ----------------------------------------------------------------- RMSNorm
-// One wave per row; the row stays in registers (NV float4 per lane, d <= 256 NV)
-// so x (and dy) are read from HBM once.  Four rows per 256-thread block.
+// One 256-thread block per row; the row stays in registers (NV float4 per thread,
+// d <= 1024 NV) so x (and dy) are read from HBM once.  A block per row (rather than a
+// wave) keeps four times as many loads in flight, which a chunk of ~1K rows needs to
+// approach the HBM rate.
+DEVI float block_sum4(float v, float *red) {
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 template <typename T, typename TY, int NV>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float *x, const T *g, TY *y, float *r_out,
                                                           float *x_copy, int n, int d, float eps) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= n) return;
+  __shared__ float red[4];
+  const int row = blockIdx.x;
   const long o = (long)row * d;
   float4 v[NV];
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    const int i = (k * 64 + lane) * 4;
+    const int i = (k * 256 + threadIdx.x) * 4;
     v[k] = i < d ? *reinterpret_cast<const float4 *>(x + o + i) : make_float4(0.f, 0.f, 0.f, 0.f);
     ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
   }
-  ss = wave_sum(ss);
+  ss = block_sum4(ss, red);
   const float r = 1.f / sqrtf(ss / (float)d + eps);
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    const int i = (k * 64 + lane) * 4;
+    const int i = (k * 256 + threadIdx.x) * 4;
     if (i < d) {
       float gv[4];
       load4<T>(g + i, gv);
@@ -66,7 +75,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float *x, const 
       if (x_copy) *reinterpret_cast<float4 *>(x_copy + o + i) = v[k];
     }
   }
-  if (r_out && lane == 0) r_out[row] = r;
+  if (r_out && threadIdx.x == 0) r_out[row] = r;
 }
 
 // dx = r g dy - x r^3 mean(x g dy) (+ dh_in); written fp32 (dh_out) and in the
@@ -75,15 +84,14 @@ template <typename T, typename TY, int NV>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float *dy, const float *x, const float *r,
                                                           const T *g, const float *dh_in, float *dh_out, TY *dh_t,
                                                           int n, int d) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= n) return;
+  __shared__ float red[4];
+  const int row = blockIdx.x;
   const long o = (long)row * d;
   float4 xa[NV], gy[NV];
   float dot = 0.f;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    const int i = (k * 64 + lane) * 4;
+    const int i = (k * 256 + threadIdx.x) * 4;
     if (i < d) {
       xa[k] = *reinterpret_cast<const float4 *>(x + o + i);
       const float4 b = *reinterpret_cast<const float4 *>(dy + o + i);
@@ -96,12 +104,12 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float *dy, const
     }
     dot += xa[k].x * gy[k].x + xa[k].y * gy[k].y + xa[k].z * gy[k].z + xa[k].w * gy[k].w;
   }
-  dot = wave_sum(dot);
+  dot = block_sum4(dot, red);
   const float rr = r[row];
   const float c = rr * rr * rr * dot / (float)d;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    const int i = (k * 64 + lane) * 4;
+    const int i = (k * 256 + threadIdx.x) * 4;
     if (i < d) {
       float v[4] = {rr * gy[k].x - xa[k].x * c, rr * gy[k].y - xa[k].y * c, rr * gy[k].z - xa[k].z * c,
                     rr * gy[k].w - xa[k].w * c};
@@ -131,17 +139,25 @@ __global__ __launch_bounds__(256) void qk_rope_fwd_kernel(const RopeArgs a) {
   const bool act = lane < half;
   const float gqi = act ? to_f(gq[lane]) : 0.f, gqj = act ? to_f(gq[lane + half]) : 0.f;
   const float gki = act ? to_f(gk[lane]) : 0.f, gkj = act ? to_f(gk[lane + half]) : 0.f;
+  // all loads of the wave's 8 tokens are issued first (one memory round trip, not eight)
+  float ld[8][6];
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt) {
+    const int t = t0 + wave * 8 + tt;
+    const long base = (long)t * 3 * a.d + h * hd;
+    const bool ok = act && t < a.n;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      ld[tt][2 * c] = ok ? qkv[base + c * a.d + lane] : 0.f;
+      ld[tt][2 * c + 1] = ok ? qkv[base + c * a.d + lane + half] : 0.f;
+    }
+  }
+#pragma unroll
   for (int tt = 0; tt < 8; ++tt) {
     const int tl = wave * 8 + tt, t = t0 + tl;
     if (t >= a.n) break;
     const int p = pos0 + t;
-    const long base = (long)t * 3 * a.d + h * hd;
-    float qi = 0, qj = 0, ki = 0, kj = 0, vi = 0, vj = 0;
-    if (act) {
-      qi = qkv[base + lane]; qj = qkv[base + lane + half];
-      ki = qkv[base + a.d + lane]; kj = qkv[base + a.d + lane + half];
-      vi = qkv[base + 2 * a.d + lane]; vj = qkv[base + 2 * a.d + lane + half];
-    }
+    const float qi = ld[tt][0], qj = ld[tt][1], ki = ld[tt][2], kj = ld[tt][3], vi = ld[tt][4], vj = ld[tt][5];
     const float sq = wave_sum(qi * qi + qj * qj), sk = wave_sum(ki * ki + kj * kj);
     const float rq = 1.f / sqrtf(sq / (float)hd + a.eps), rk = 1.f / sqrtf(sk / (float)hd + a.eps);
     if (act) {
@@ -356,6 +372,55 @@ __global__ __launch_bounds__(256) void transpose_kernel(const S *src, long lds, 
   }
 }
 
+// The same with 4-element vectors: each thread loads 4 consecutive columns of 4 rows
+// and stores 4 consecutive rows of 4 columns (needs lds, ldd multiples of 4 and
+// 4-element-aligned bases; partial vectors at the edges go element by element).
+template <typename T> struct V4;
+template <> struct V4<float> { typedef float4 t; };
+template <> struct V4<f16_t> { typedef uint2 t; };
+template <> struct V4<bf16_t> { typedef uint2 t; };
+template <typename T> DEVI void put4(T *p, const float *v) { store4<T>(p, v); }
+
+template <typename S, typename D>
+__global__ __launch_bounds__(256) void transpose4_kernel(const S *src, long lds, D *dst, long ldd, int R, int Rpad,
+                                                         int C) {
+  __shared__ float tile[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int q = (threadIdx.x & 15) * 4, w = threadIdx.x >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rl = w + 16 * i, r = r0 + rl, c = c0 + q;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (r < R) {
+      if (c + 3 < C) {
+        load4<S>(src + (long)r * lds + c, v);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (c + j < C) v[j] = to_f(src[(long)r * lds + c + j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tile[rl][q + j] = v[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int cl = w + 16 * i, c = c0 + cl, r = r0 + q;
+    if (c >= C) continue;
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = tile[q + j][cl];
+    if (r + 3 < Rpad) {
+      put4<D>(dst + (long)c * ldd + r, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (r + j < Rpad) dst[(long)c * ldd + r + j] = from_f<D>(v[j]);
+    }
+  }
+}
+
 __global__ void bf16_to_f16_kernel(const bf16_t *src, long lds, f16_t *dst, long ldd, int rows, int cols,
                                    float scale) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
@@ -463,15 +528,13 @@ hipError_t embed_launch(int dtype, const void *E, const int *tok, const int *pos
   return hipGetLastError();
 }
 
-// Row width classes (float4 per lane): d <= 256 NV.
+// Row width classes (float4 per thread of a 256-thread block): d <= 1024 NV.
 #define NV_DISPATCH(d, CALL)                   \
-  if ((d) <= 256) { CALL(1); }                 \
-  else if ((d) <= 512) { CALL(2); }            \
-  else if ((d) <= 1024) { CALL(4); }           \
-  else if ((d) <= 2048) { CALL(8); }           \
-  else if ((d) <= 3072) { CALL(12); }          \
-  else if ((d) <= 4096) { CALL(16); }          \
-  else if ((d) <= 8192) { CALL(32); }          \
+  if ((d) <= 1024) { CALL(1); }                \
+  else if ((d) <= 2048) { CALL(2); }           \
+  else if ((d) <= 3072) { CALL(3); }           \
+  else if ((d) <= 4096) { CALL(4); }           \
+  else if ((d) <= 8192) { CALL(8); }           \
   else return hipErrorInvalidValue;
 
 hipError_t rmsnorm_fwd_launch(int dtype, const float *x, const void *g, void *y, float *r_out, float *x_copy, int n,
@@ -480,13 +543,13 @@ hipError_t rmsnorm_fwd_launch(int dtype, const float *x, const void *g, void *y,
   if (n <= 0) return hipSuccess;
 #define CALL_(NV)                                                                                                  \
   if (dtype == 1 && y_f16)                                                                                         \
-    hipLaunchKernelGGL((rmsnorm_fwd_kernel<bf16_t, f16_t, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, x,      \
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<bf16_t, f16_t, NV>), dim3(n), dim3(256), 0, st, x,      \
                        (const bf16_t *)g, (f16_t *)y, r_out, x_copy, n, d, eps);                                   \
   else if (dtype == 1)                                                                                             \
-    hipLaunchKernelGGL((rmsnorm_fwd_kernel<bf16_t, bf16_t, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, x,     \
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<bf16_t, bf16_t, NV>), dim3(n), dim3(256), 0, st, x,     \
                        (const bf16_t *)g, (bf16_t *)y, r_out, x_copy, n, d, eps);                                  \
   else                                                                                                             \
-    hipLaunchKernelGGL((rmsnorm_fwd_kernel<float, float, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, x,       \
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<float, float, NV>), dim3(n), dim3(256), 0, st, x,       \
                        (const float *)g, (float *)y, r_out, x_copy, n, d, eps);
   NV_DISPATCH(d, CALL_)
 #undef CALL_
@@ -500,13 +563,13 @@ hipError_t rmsnorm_bwd_launch(int dtype, const float *dy, const float *x, const 
   if (t_f16 && dtype != 1) return hipErrorInvalidValue;
 #define CALL_(NV)                                                                                                  \
   if (t_f16)                                                                                                       \
-    hipLaunchKernelGGL((rmsnorm_bwd_kernel<bf16_t, f16_t, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, dy, x,  \
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<bf16_t, f16_t, NV>), dim3(n), dim3(256), 0, st, dy, x,  \
                        r, (const bf16_t *)g, dh_in, dh_out, (f16_t *)dh_t, n, d);                                  \
   else if (dtype == 1)                                                                                             \
-    hipLaunchKernelGGL((rmsnorm_bwd_kernel<bf16_t, bf16_t, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, dy, x, \
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<bf16_t, bf16_t, NV>), dim3(n), dim3(256), 0, st, dy, x, \
                        r, (const bf16_t *)g, dh_in, dh_out, (bf16_t *)dh_t, n, d);                                 \
   else                                                                                                             \
-    hipLaunchKernelGGL((rmsnorm_bwd_kernel<float, float, NV>), dim3(blocks_for(n, 4)), dim3(256), 0, st, dy, x,   \
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<float, float, NV>), dim3(n), dim3(256), 0, st, dy, x,   \
                        r, (const float *)g, dh_in, dh_out, (float *)dh_t, n, d);
   NV_DISPATCH(d, CALL_)
 #undef CALL_
@@ -596,7 +659,7 @@ hipError_t decode_pick_launch(const float2 *part, const int *part_arg, int P, co
 hipError_t ce_reduce_launch(const float2 *part, int P, const float *zlab, const int *pos0, float *lse, float *losses,
                             int n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ce_reduce_kernel, dim3(blocks_for(n, 4)), dim3(256), 0, st, part, P, zlab, pos0, lse, losses, n);
+  hipLaunchKernelGGL(ce_reduce_kernel, dim3(n), dim3(256), 0, st, part, P, zlab, pos0, lse, losses, n);
   return hipGetLastError();
 }
 
@@ -635,36 +698,43 @@ hipError_t copy_rows_launch(int dtype, const void *src, long ld_src, void *dst, 
   return hipGetLastError();
 }
 
+template <typename S, typename D>
+static void launch_transpose(bool vec, dim3 grid, const void *src, long lds, void *dst, long ldd, int R, int Rpad,
+                             int C, hipStream_t st) {
+  if (vec)
+    hipLaunchKernelGGL((transpose4_kernel<S, D>), grid, dim3(256), 0, st, (const S *)src, lds, (D *)dst, ldd, R,
+                       Rpad, C);
+  else
+    hipLaunchKernelGGL((transpose_kernel<S, D>), grid, dim3(256), 0, st, (const S *)src, lds, (D *)dst, ldd, R,
+                       Rpad, C);
+}
+
 hipError_t transpose_launch(int dtype, int src_kind, const void *src, long lds, void *dst, long ldd, int R, int Rpad,
                             int C, hipStream_t st, bool dst_f16) {
   if (Rpad <= 0 || C <= 0) return hipSuccess;
   dim3 grid((C + 63) / 64, (Rpad + 63) / 64);
+  const size_t ssz = (src_kind == SRC_F32 || dtype == 0) ? 4 : 2, dsz = (dst_f16 || dtype == 1) ? 2 : 4;
+  // 4-element vectors need row strides that keep every vector aligned
+  const bool vec = lds % 4 == 0 && ldd % 4 == 0 && (uintptr_t)src % (4 * ssz) == 0 && (uintptr_t)dst % (4 * dsz) == 0;
   if (dst_f16) {
     if (dtype != 1) return hipErrorInvalidValue;
     if (src_kind == SRC_F32)
-      hipLaunchKernelGGL((transpose_kernel<float, f16_t>), grid, dim3(256), 0, st, (const float *)src, lds,
-                         (f16_t *)dst, ldd, R, Rpad, C);
+      launch_transpose<float, f16_t>(vec, grid, src, lds, dst, ldd, R, Rpad, C, st);
     else if (src_kind == SRC_F16)
-      hipLaunchKernelGGL((transpose_kernel<f16_t, f16_t>), grid, dim3(256), 0, st, (const f16_t *)src, lds,
-                         (f16_t *)dst, ldd, R, Rpad, C);
+      launch_transpose<f16_t, f16_t>(vec, grid, src, lds, dst, ldd, R, Rpad, C, st);
     else
-      hipLaunchKernelGGL((transpose_kernel<bf16_t, f16_t>), grid, dim3(256), 0, st, (const bf16_t *)src, lds,
-                         (f16_t *)dst, ldd, R, Rpad, C);
+      launch_transpose<bf16_t, f16_t>(vec, grid, src, lds, dst, ldd, R, Rpad, C, st);
     return hipGetLastError();
   }
   if (dtype == 1) {
     if (src_kind == SRC_F32)
-      hipLaunchKernelGGL((transpose_kernel<float, bf16_t>), grid, dim3(256), 0, st, (const float *)src, lds,
-                         (bf16_t *)dst, ldd, R, Rpad, C);
+      launch_transpose<float, bf16_t>(vec, grid, src, lds, dst, ldd, R, Rpad, C, st);
     else if (src_kind == SRC_F16)
-      hipLaunchKernelGGL((transpose_kernel<f16_t, bf16_t>), grid, dim3(256), 0, st, (const f16_t *)src, lds,
-                         (bf16_t *)dst, ldd, R, Rpad, C);
+      launch_transpose<f16_t, bf16_t>(vec, grid, src, lds, dst, ldd, R, Rpad, C, st);
     else
-      hipLaunchKernelGGL((transpose_kernel<bf16_t, bf16_t>), grid, dim3(256), 0, st, (const bf16_t *)src, lds,
-                         (bf16_t *)dst, ldd, R, Rpad, C);
+      launch_transpose<bf16_t, bf16_t>(vec, grid, src, lds, dst, ldd, R, Rpad, C, st);
   } else {
-    hipLaunchKernelGGL((transpose_kernel<float, float>), grid, dim3(256), 0, st, (const float *)src, lds,
-                       (float *)dst, ldd, R, Rpad, C);
+    launch_transpose<float, float>(vec, grid, src, lds, dst, ldd, R, Rpad, C, st);
   }
   return hipGetLastError();
 }
