@@ -47,6 +47,20 @@ template <typename T, int ROWS, int COLSP> struct TileIO {
       v[i] = x;
     }
   }
+  // All ROWS rows valid and cols a multiple of VE: columns at or past cols read as zero
+  // through a select, with no per-lane branches (a divergent branch around a load
+  // makes the compiler wait for every earlier load at the join).
+  DEVI void load_rows(const T *g, long gld, int cols, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * NT;
+      const int r = idx / VPR, c = (idx % VPR) * VE;
+      const bool ok = (idx < TOT) && (c < cols);
+      const long o = ok ? (long)r * gld + c : 0;
+      const uint4 x = *reinterpret_cast<const uint4 *>(g + o);
+      v[i] = ok ? x : make_uint4(0, 0, 0, 0);
+    }
+  }
   DEVI void store(T *sm, int sld, int tid) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -1048,7 +1062,7 @@ __global__ __launch_bounds__(NT) void attn_bwd_dq_kernel(const AttnArgs a) {
 // grid (ceil(n/64), H); 4 waves x 16 chunk keys; loops over the chunk's
 // queries at or after the key tile (all inside the window since b <= k).
 template <typename T, int HD>
-__global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const AttnArgs a) {
   constexpr int HDP = Dims<HD>::HDP, NC = Dims<HD>::NC, NH = Dims<HD>::NH;
   constexpr int LDK = HDP + pad_el<T>(), LDV = 64 + pad_el<T>();
   __shared__ __align__(16) T smQ[64 * LDK];
@@ -1059,7 +1073,18 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(const AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4, g4 = lg * 4;
-  const int h = blockIdx.y, k_lo = blockIdx.x * 64;
+  // Work-groups go to the 8 XCDs round-robin by linear index; remap so that each XCD
+  // gets whole heads: the key tiles of one head then re-read that head's query-side
+  // tiles (q, dO and their transposes) from one L2 instead of eight.
+  int h, k_lo;
+  {
+    const int gx = gridDim.x, total = gx * gridDim.y;
+    const int i = blockIdx.x + gx * blockIdx.y;
+    const int q8 = total / 8, rem = total % 8, x = i % 8;
+    const int m = x * q8 + min(x, rem) + i / 8;
+    k_lo = (m % gx) * 64;
+    h = m / gx;
+  }
   const int pos0 = *a.pos0;
   const int kw = k_lo + wave * 16;
   const int key = kw + lr;  // this lane's key (chunk-relative)
@@ -1093,25 +1118,43 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(const AttnArgs a) {
     dV[hs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int qt = k_lo; qt < a.n; qt += 64) {
-    {
-      TileIO<T, 64, HDP> io;
-      io.load(Q + (long)qt * a.d + h * HD, a.d, a.n - qt, HD, tid);
-      io.store(smQ, LDK, tid);
-      io.load(dO + (long)qt * a.d + h * HD, a.d, a.n - qt, HD, tid);
-      io.store(smdO, LDK, tid);
-      TileIO<T, HD, 64> io2;
-      io2.load(Qt + qt, a.ldt, HD, a.n - qt, tid);
-      io2.store(smQt, LDV, tid);
-      io2.load(dOt + qt, a.ldt, HD, a.n - qt, tid);
-      io2.store(smdOt, LDV, tid);
-      if (tid < 64) {
-        const int q = qt + tid;
-        smL[tid] = q < a.n ? a.lse2[(long)h * a.ldl + q] : 0.f;
-        smD[tid] = q < a.n ? a.Dq[(long)h * a.ldl + q] : 0.f;
-      }
+  // The next query tile is loaded into registers while the current one is multiplied
+  // from LDS (one tile of global-load latency per block instead of one per tile).
+  TileIO<T, 64, HDP> ioq, iod;
+  TileIO<T, HD, 64> ioqt, iodt;
+  float nl = 0.f, nd = 0.f;
+  auto fetch = [&](int qt) {
+    if (qt + 64 <= a.n) {  // whole tile inside the chunk
+      ioq.load_rows(Q + (long)qt * a.d + h * HD, a.d, HD, tid);
+      iod.load_rows(dO + (long)qt * a.d + h * HD, a.d, HD, tid);
+      ioqt.load_rows(Qt + qt, a.ldt, 64, tid);
+      iodt.load_rows(dOt + qt, a.ldt, 64, tid);
+    } else {
+      ioq.load(Q + (long)qt * a.d + h * HD, a.d, a.n - qt, HD, tid);
+      iod.load(dO + (long)qt * a.d + h * HD, a.d, a.n - qt, HD, tid);
+      ioqt.load(Qt + qt, a.ldt, HD, a.n - qt, tid);
+      iodt.load(dOt + qt, a.ldt, HD, a.n - qt, tid);
     }
-    __syncthreads();
+    if (tid < 64) {
+      const int q = qt + tid;
+      nl = q < a.n ? a.lse2[(long)h * a.ldl + q] : 0.f;
+      nd = q < a.n ? a.Dq[(long)h * a.ldl + q] : 0.f;
+    }
+  };
+  if (k_lo < a.n) fetch(k_lo);
+  for (int qt = k_lo; qt < a.n; qt += 64) {
+    ioq.store(smQ, LDK, tid);
+    iod.store(smdO, LDK, tid);
+    ioqt.store(smQt, LDV, tid);
+    iodt.store(smdOt, LDV, tid);
+    if (tid < 64) {
+      smL[tid] = nl;
+      smD[tid] = nd;
+    }
+    asm volatile("" ::: "memory");
+    lds_barrier();  // LDS only: the prefetch of the next tile stays in flight
+    asm volatile("" ::: "memory");
+    if (qt + 64 < a.n) fetch(qt + 64);
     f32x4_v S[4], dP[4];
 #pragma unroll
     for (int qs = 0; qs < 4; ++qs) {
@@ -1161,7 +1204,9 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(const AttnArgs a) {
         mma(dK[hs], aq, sf);
       }
     }
-    __syncthreads();
+    asm volatile("" ::: "memory");
+    lds_barrier();  // LDS only: the prefetch of the next tile stays in flight
+    asm volatile("" ::: "memory");
   }
 
   if (key < a.n) {
