@@ -50,8 +50,11 @@ DEVI void store_c4(const GemmArgs &g, void *base, long off, const float *v) {
     store4<bf16_t>(reinterpret_cast<bf16_t *>(base) + off, v);
 }
 
-template <int BN, int EPI, typename Acc>
-DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, int wm, int wn, int lr, int lq) {
+// PRE: the fp32 master values of EPI_SGD were loaded ahead into `pre` (same [i][j]
+// indexing as acc).
+template <int BN, int EPI, bool PRE = false, typename Acc>
+DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, int wm, int wn, int lr, int lq,
+                         const float4 (&pre)[4][4]) {
   constexpr int NI = G2<BN>::NI, WN = G2<BN>::WN;
   // ------------------------------------------------------------- epilogues
   // lane holds C[m][n .. n+3] for m = m0 + wm*64 + 16 j + lr, n = n0 + wn*WN + 16 i + 4 lq
@@ -162,7 +165,11 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
         store_c4(g, g.C, (long)m * g.ldc + n, d);
       } else if constexpr (EPI == EPI_SGD) {
         float4 *pw = reinterpret_cast<float4 *>(g.Cf + (long)m * g.ldcf + n);
-        const float4 w = *pw;
+        float4 w;
+        if constexpr (PRE)
+          w = pre[i][j];
+        else
+          w = *pw;
         float nw[4] = {w.x - g.alpha * v[0], w.y - g.alpha * v[1], w.z - g.alpha * v[2], w.w - g.alpha * v[3]};
         *pw = make_float4(nw[0], nw[1], nw[2], nw[3]);
         float sw[4];
@@ -326,17 +333,39 @@ __global__ __launch_bounds__(NT, 2) void gemm5_kernel(const GemmArgs g) {
   const uint32_t smb = (uint32_t)(uintptr_t)(lds_void *)sm;
   if (nk > 0) is.run(0, 0);
   if (nk > 1) is.run(1, SBYTES);
+  // SGD: the fp32 master values this lane updates are loaded while the last steps run,
+  // issued after the last tile load so that the waits on tile loads do not cover them
+  // (vector-memory loads complete in issue order).
+  constexpr bool PRE = EPI == EPI_SGD;
+  constexpr int NPRE = PRE ? 16 : 0;
+  float4 pre[4][4];
+  // through a buffer descriptor: every lane issues all 16 loads (offsets outside the matrix
+  // read zero), so the wave's count of outstanding loads is the same on every tile
+  const __amdgpu_buffer_rsrc_t rcf = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)g.Cf, (short)0, PRE ? (uint32_t)(((long)(g.M - 1) * g.ldcf + g.N) * 4) : 0u, RSRC_W3);
+#define GEMM5_PREFETCH                                                                                       \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i) _Pragma("unroll") for (int j = 0; j < 4; ++j) {              \
+    const int m = m0 + wm * 64 + j * 16 + lr, n = n0 + wn * 64 + i * 16 + lq * 4;                              \
+    const uint32_t o = (m < g.M && n < g.N) ? (uint32_t)(((long)m * g.ldcf + n) * 4) : OOB;                   \
+    pre[i][j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rcf, o, 0, 0));              \
+  }
+
+  if (PRE && nk <= 2) { GEMM5_PREFETCH }  // no tile load is issued inside the loop
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk)
-      wait_vm<CPW>();
-    else
-      wait_vm<0>();
+    // outstanding, oldest first: tile loads of steps kt and kt+1, then (from step nk-2 on)
+    // the master values
+    if (kt + 1 < nk) {
+      if (PRE && nk > 2 && kt == nk - 2) wait_vm<CPW + NPRE>(); else wait_vm<CPW>();
+    } else {
+      if (PRE) wait_vm<NPRE>(); else wait_vm<0>();
+    }
     __builtin_amdgcn_s_barrier();
     const uint32_t so = smb + (kt & 1) * SBYTES;
     Frag<TI> fw[2][4], fx[2][4];
     read_step_128<TI>(fw, fx, so + aw0, so + aw1, so + ax0, so + ax1);
     __builtin_amdgcn_s_barrier();
     if (kt + 2 < nk) is.run(kt + 2, (kt & 1) * SBYTES);
+    if (PRE && kt + 2 == nk - 1) { GEMM5_PREFETCH }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -344,7 +373,8 @@ __global__ __launch_bounds__(NT, 2) void gemm5_kernel(const GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) mma(acc[i][j], fw[ks][i], fx[ks][j]);
   }
-  gemm2_epilogue<128, EPI>(g, acc, m0, n0, tn, wm, wn, lr, lq);
+  gemm2_epilogue<128, EPI, PRE>(g, acc, m0, n0, tn, wm, wn, lr, lq, pre);
+#undef GEMM5_PREFETCH
 }
 
 #define G5_INST(TI)                                                      \
