@@ -82,7 +82,8 @@ def algorithmic_bytes(cfg, T, update=True):
     16-bit activations, fp32 master fast weights), counted once; no re-reads, padding or
     cache effects.  Attention merges and split-K reductions depend on the split chosen per
     launch and are not listed.  `update_in_gemm_dw_sgd` is the SGD step fused into the
-    weight-gradient GEMM's epilogue (read and write the fp32 master, write the 16-bit copy)."""
+    weight-gradient GEMM's epilogue (read and write the fp32 master, write the 16-bit
+    forward copy and the transposed copy the backward reads)."""
     L, d, F, V, nu, H = cfg.n_layers, cfg.d_model, cfg.d_ff, cfg.vocab, cfg.n_update, cfg.n_heads
     a = 2 if cfg.dtype == "bf16" else 4          # activation / working-copy element size
     hilo = 2 if cfg.dtype == "bf16" else 1       # 16-bit forward copy is hi + lo
@@ -104,10 +105,11 @@ def algorithmic_bytes(cfg, T, update=True):
             "swiglu_bwd": T * 5 * a * (nb * 2 * F + F),
             "qknorm_rope_bwd": T * nb * (24 + 3 * a) * d,
             "attn_bwd_pre": T * nb * (3 * a * d + 4 * H),
-            # activations dy, hmid, dgu, m (read + write) per token; the refreshed transposed
-            # weight copies (fp32 master in, 16-bit out) per chunk
-            "transpose": nu * (T * 2 * a * (2 * d + 3 * F) + n_chunks * 3 * d * F * (4 + a)),
-            "update_in_gemm_dw_sgd": n_chunks * nu * 3 * d * F * (8 + hilo * a),
+            # activations dy, hmid, dgu, m (read + write) per token
+            "transpose": nu * T * 2 * a * (2 * d + 3 * F),
+            # fp32 master read + write, the forward copy (hi | lo) and the backward's
+            # transposed copy, written by the weight-gradient GEMM's epilogue
+            "update_in_gemm_dw_sgd": n_chunks * nu * 3 * d * F * (8 + hilo * a + a),
         })
     return b
 

@@ -15,7 +15,8 @@ enum GemmEpi {
   EPI_DLOGITS = 5,   // C (T) = (exp(acc - lse[m]) - [n + col_off == label]) * alpha
   EPI_SGD = 6,       // Cf (fp32 master) -= alpha * acc; C (T) = hi = round(c_scale * Cf) and,
                      // when C2 is set, C2 (T) = round(c_scale * Cf - hi): the working copy as
-                     // hi + lo, scaled by c_scale (inner SGD)
+                     // hi + lo, scaled by c_scale (inner SGD); when CT is set, also
+                     // CT[n][m] = round(Cf[m][n]) (the transposed working copy)
 };
 
 struct GemmArgs {
@@ -50,6 +51,11 @@ struct GemmArgs {
   // power of two: B holds weights stored scaled by 1 / acc_scale); EPI_SGD
   // writes its 16-bit copies scaled by c_scale.  Both are 1 when unused.
   float acc_scale, c_scale;
+  // EPI_SGD, optional: the updated fp32 values also written transposed and unscaled,
+  // CT[n * ldct + m], in the 16-bit output type (the streaming kernel) or the operand
+  // type (the generic kernel)
+  void *CT;
+  long ldct;
   // split-K (internal)
   int ksplit;
   float *ws;

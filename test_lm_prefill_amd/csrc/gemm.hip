@@ -321,6 +321,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const GemmArgs g) {
           for (int r = 0; r < 4; ++r) lo[r] = sw[r] - to_f(from_f<T>(sw[r]));
           store4<T>(reinterpret_cast<T *>(g.C2) + (long)m * g.ldc2 + n, lo);
         }
+        if (g.CT) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) reinterpret_cast<T *>(g.CT)[(long)(n + r) * g.ldct + m] = from_f<T>(nw[r]);
+        }
       }
     }
   }

@@ -52,9 +52,11 @@ DEVI void store_c4(const GemmArgs &g, void *base, long off, const float *v) {
 
 // PRE: the fp32 master values of EPI_SGD were loaded ahead into `pre` (same [i][j]
 // indexing as acc).
+// ct_lds: 8 KiB of LDS private to this wave (EPI_SGD with CT), where the updated
+// 64 x 64 tile is transposed so that CT is written in 16-byte rows.
 template <int BN, int EPI, bool PRE = false, typename Acc>
 DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, int wm, int wn, int lr, int lq,
-                         const float4 (&pre)[4][4]) {
+                         const float4 (&pre)[4][4], uint16_t *ct_lds = nullptr) {
   constexpr int NI = G2<BN>::NI, WN = G2<BN>::WN;
   // ------------------------------------------------------------- epilogues
   // lane holds C[m][n .. n+3] for m = m0 + wm*64 + 16 j + lr, n = n0 + wn*WN + 16 i + 4 lq
@@ -182,6 +184,30 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
           for (int r = 0; r < 4; ++r)
             lo[r] = sw[r] - (g.c_f16 ? to_f(from_f<f16_t>(sw[r])) : to_f(from_f<bf16_t>(sw[r])));
           store_c4(g, g.C2, (long)m * g.ldc2 + n, lo);
+        }
+        if (ct_lds) {  // [n][m] within the wave's 64 x 64 tile
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            ct_lds[(i * 16 + g4 + r) * 64 + j * 16 + lr] =
+                g.c_f16 ? from_f<f16_t>(nw[r]).x : from_f<bf16_t>(nw[r]);
+        }
+      }
+    }
+  }
+  if constexpr (EPI == EPI_SGD) {
+    if (ct_lds) {
+      // rows of 8 consecutive m: 8 lanes cover one n row of the tile (128 bytes)
+      const int lane = lr + 16 * lq, mb = m0 + wm * 64, nb = n0 + wn * WN;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int idx = lane + 64 * c, nl = idx >> 3, ml = (idx & 7) * 8;
+        const int n = nb + nl, m = mb + ml;
+        if (n >= g.N || m >= g.M) continue;
+        uint16_t *dst = reinterpret_cast<uint16_t *>(g.CT) + (long)n * g.ldct + m;
+        if (m + 7 < g.M) {
+          *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(ct_lds + nl * 64 + ml);
+        } else {
+          for (int e = 0; e < 8 && m + e < g.M; ++e) dst[e] = ct_lds[nl * 64 + ml + e];
         }
       }
     }
@@ -373,7 +399,10 @@ __global__ __launch_bounds__(NT, 2) void gemm5_kernel(const GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) mma(acc[i][j], fw[ks][i], fx[ks][j]);
   }
-  gemm2_epilogue<128, EPI, PRE>(g, acc, m0, n0, tn, wm, wn, lr, lq, pre);
+  uint16_t *ct_lds = nullptr;
+  if (PRE && g.CT)  // the stage not read by the last step is free once every wave passed its barrier
+    ct_lds = reinterpret_cast<uint16_t *>(sm + (nk & 1) * SBYTES + wave * 8192);
+  gemm2_epilogue<128, EPI, PRE>(g, acc, m0, n0, tn, wm, wn, lr, lq, pre, ct_lds);
 #undef GEMM5_PREFETCH
 }
 

@@ -504,13 +504,11 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
           g.c_f16 = f16;
           g.c_scale = h->wscale;
           g.alpha = h->cfg.eta / h->gscale;
+          g.CT = wdT;  // the backward's transposed copy [F][d] of the fast rows, refreshed in place
+          g.ldct = d;
           gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st, true);
         }
-        {
-          PROF(K_TRANSPOSE);
-          HIPCHK(transpose_launch(dt, SRC_F32, md, F, wdT, d, d, d, F, st, f16));
-        }
-        h->launches += 5;
+        h->launches += 4;
       }
       {
         PROF(K_SWIGLU_BWD);
@@ -546,13 +544,11 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
           g.c_f16 = f16;
           g.c_scale = h->wscale;
           g.alpha = h->cfg.eta / h->gscale;
+          g.CT = wguT;  // transposed copy [d][4F], fast columns [0, 2F)
+          g.ldct = 4 * F;
           gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st, true);
         }
-        {
-          PROF(K_TRANSPOSE);
-          HIPCHK(transpose_launch(dt, SRC_F32, mgu, d, wguT, 4 * F, 2 * F, 2 * F, d, st, f16));
-        }
-        h->launches += last ? 4 : 5;
+        h->launches += last ? 3 : 4;
       }
       if (last) break;
       {
