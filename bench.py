@@ -80,8 +80,9 @@ def algorithmic_bytes(cfg, T, update=True):
     """Per-class HBM bytes of one prefill for the bandwidth-bound kernels: what each kernel
     must read and write given the stored layouts (fp32 residual stream and projections,
     16-bit activations, fp32 master fast weights), counted once; no re-reads, padding or
-    cache effects.  Attention merges and split-K reductions depend on the split chosen per
-    launch and are not listed.  `update_in_gemm_dw_sgd` is the SGD step fused into the
+    cache effects.  The forward residual products' split-K partials are counted where they
+    are reduced (in the RMSNorm that follows each product, with the planner's split); the
+    backward's split-K reductions and the attention merges are not listed.  `update_in_gemm_dw_sgd` is the SGD step fused into the
     weight-gradient GEMM's epilogue (read and write the fp32 master, write the 16-bit
     forward copy and the transposed copy the backward reads)."""
     L, d, F, V, nu, H = cfg.n_layers, cfg.d_model, cfg.d_ff, cfg.vocab, cfg.n_update, cfg.n_heads
@@ -90,8 +91,26 @@ def algorithmic_bytes(cfg, T, update=True):
     nb = max(nu - 1, 0)                          # blocks whose attention is back-propagated
     P = 2 * ((V + 127) // 128)                   # CE partials per row
     n_chunks = (T + cfg.chunk - 1) // cfg.chunk
-    # rmsnorm: read fp32 row, write the normalised row; the saved inputs of back-propagated norms
-    rms = (2 * L + 1) * (4 + a) * d + ((nb + nu + 1) * 4 * d if update and nu > 0 else 0)
+    # rmsnorm: read fp32 row, write the normalised row; the saved inputs of back-propagated norms;
+    # the norms after the O and down products also apply those products' split-K partials
+    # (read each fp32 partial, write the updated residual row)
+    def split_k(M, N, K):  # the GEMM planner's choice for a residual product (128 x 128 tiles)
+        tiles = -(-M // 128) * -(-N // 128)
+        if tiles >= 256:
+            return 1
+        sp = min(-(-400 // tiles), K // 512, 4)
+        if sp < 2:
+            return 1
+        per = -(-(-(-K // sp)) // 64) * 64
+        return -(-K // per)
+    b_rows = cfg.chunk
+    sp_o = split_k(b_rows, d, d)
+    sp_dn = split_k(b_rows, d, F)
+    sp_df = split_k(b_rows, d, (3 if a == 2 else 2) * F)
+    red = L * (sp_o * 4 + 4) * d if sp_o > 1 else 0
+    red += (L - nu) * (sp_dn * 4 + 4) * d if sp_dn > 1 else 0
+    red += nu * (sp_df * 4 + 4) * d if sp_df > 1 else 0
+    rms = (2 * L + 1) * (4 + a) * d + ((nb + nu + 1) * 4 * d if update and nu > 0 else 0) + red
     # QK-norm + RoPE: read fp32 q, k, v; write q and the ring's K and V^T; the backward's
     # copies (V, K^T, 16-bit K) of back-propagated blocks, and with the update q copies
     rope = L * (12 + 3 * a) * d + nb * 3 * a * d + (nb * 2 * a * d if update else 0)

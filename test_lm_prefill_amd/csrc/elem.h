@@ -10,9 +10,17 @@ hipError_t embed_launch(int dtype, const void *E, const int *tok, const int *pos
 
 // y = x * r * g, r = (mean(x^2) + eps)^-1/2 per row; optional r_out [n] and x_copy [n, d].
 // g has the working dtype; y too, or fp16 when y_f16 (bf16 mode's forward GEMM operand).
-// d <= 8192.
-hipError_t rmsnorm_fwd_launch(int dtype, const float *x, const void *g, void *y, float *r_out, float *x_copy,
-                              int n, int d, float eps, hipStream_t st, bool y_f16 = false);
+// d <= 8192.  With red.ws set, x is first updated in place by a split-K residual
+// product: x += red.sc * (ws[0] + ws[1] + ... + ws[red.split - 1]) with ws[s] the
+// fp32 partial [n, d] at red.ws + s * n * d, summed in that order (the reduction a
+// separate split-K reduce would apply), and the updated x is normalised.
+struct ResidualPartials {
+  const float *ws = nullptr;
+  int split = 0;
+  float sc = 1.f;
+};
+hipError_t rmsnorm_fwd_launch(int dtype, float *x, const void *g, void *y, float *r_out, float *x_copy, int n, int d,
+                              float eps, hipStream_t st, bool y_f16 = false, ResidualPartials red = {});
 
 // dh_out = dh_in + r * (g*dy) - x * r^3 * mean(x * g*dy)   (dh_in may be NULL or alias dh_out);
 // also writes dh_t, the same values in the working dtype (fp16 when t_f16, bf16 mode only).

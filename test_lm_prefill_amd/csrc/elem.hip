@@ -49,8 +49,8 @@ DEVI float block_sum4(float v, float *red) {
 }
 
 template <typename T, typename TY, int NV>
-__global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float *x, const T *g, TY *y, float *r_out,
-                                                          float *x_copy, int n, int d, float eps) {
+__global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(float *x, const T *g, TY *y, float *r_out, float *x_copy,
+                                                          int n, int d, float eps, ResidualPartials rp) {
   __shared__ float red[4];
   const int row = blockIdx.x;
   const long o = (long)row * d;
@@ -60,6 +60,17 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float *x, const 
   for (int k = 0; k < NV; ++k) {
     const int i = (k * 256 + threadIdx.x) * 4;
     v[k] = i < d ? *reinterpret_cast<const float4 *>(x + o + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (rp.ws && i < d) {  // pending split-K residual product, summed in split order
+      const long st = (long)n * d;
+      float4 acc = *reinterpret_cast<const float4 *>(rp.ws + o + i);
+      for (int s = 1; s < rp.split; ++s) {
+        const float4 p = *reinterpret_cast<const float4 *>(rp.ws + s * st + o + i);
+        acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+      }
+      v[k] = make_float4(v[k].x + acc.x * rp.sc, v[k].y + acc.y * rp.sc, v[k].z + acc.z * rp.sc,
+                         v[k].w + acc.w * rp.sc);
+      *reinterpret_cast<float4 *>(x + o + i) = v[k];
+    }
     ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
   }
   ss = block_sum4(ss, red);
@@ -537,20 +548,20 @@ hipError_t embed_launch(int dtype, const void *E, const int *tok, const int *pos
   else if ((d) <= 8192) { CALL(8); }           \
   else return hipErrorInvalidValue;
 
-hipError_t rmsnorm_fwd_launch(int dtype, const float *x, const void *g, void *y, float *r_out, float *x_copy, int n,
-                              int d, float eps, hipStream_t st, bool y_f16) {
+hipError_t rmsnorm_fwd_launch(int dtype, float *x, const void *g, void *y, float *r_out, float *x_copy, int n, int d,
+                              float eps, hipStream_t st, bool y_f16, ResidualPartials red) {
   if (y_f16 && dtype != 1) return hipErrorInvalidValue;
   if (n <= 0) return hipSuccess;
 #define CALL_(NV)                                                                                                  \
   if (dtype == 1 && y_f16)                                                                                         \
     hipLaunchKernelGGL((rmsnorm_fwd_kernel<bf16_t, f16_t, NV>), dim3(n), dim3(256), 0, st, x,      \
-                       (const bf16_t *)g, (f16_t *)y, r_out, x_copy, n, d, eps);                                   \
+                       (const bf16_t *)g, (f16_t *)y, r_out, x_copy, n, d, eps, red);                                   \
   else if (dtype == 1)                                                                                             \
     hipLaunchKernelGGL((rmsnorm_fwd_kernel<bf16_t, bf16_t, NV>), dim3(n), dim3(256), 0, st, x,     \
-                       (const bf16_t *)g, (bf16_t *)y, r_out, x_copy, n, d, eps);                                  \
+                       (const bf16_t *)g, (bf16_t *)y, r_out, x_copy, n, d, eps, red);                                  \
   else                                                                                                             \
     hipLaunchKernelGGL((rmsnorm_fwd_kernel<float, float, NV>), dim3(n), dim3(256), 0, st, x,       \
-                       (const float *)g, (float *)y, r_out, x_copy, n, d, eps);
+                       (const float *)g, (float *)y, r_out, x_copy, n, d, eps, red);
   NV_DISPATCH(d, CALL_)
 #undef CALL_
   return hipGetLastError();

@@ -250,6 +250,27 @@ void gemm(ttt_handle *h, int cls, bool akc, bool bkc, int epi, GemmArgs g, hipSt
   h->launches += split > 1 ? 2 : 1;
 }
 
+// A residual product h += A B^T (EPI_ADD_F32, 16-bit operands) whose split-K reduction
+// is left to the RMSNorm that reads h next: returns the pending fp32 partials, or an
+// empty descriptor when the product was not split (then h is already updated).  The
+// partials live in h->ws until the next GEMM, so the norm must come first.
+ResidualPartials gemm_residual(ttt_handle *h, int cls, GemmArgs g, hipStream_t st) {
+  const int odt = h->dt == 1 ? 2 : h->dt;
+  const int split = gemm_plan(odt, true, true, EPI_ADD_F32, g, h->ws_elems);
+  {
+    Prof prof_(h, cls, st);
+    HIPCHK(gemm_main_launch(odt, true, true, EPI_ADD_F32, g, h->ws, split, st));
+  }
+  h->launches += 1;
+  ResidualPartials r;
+  if (split > 1) {
+    r.ws = h->ws;
+    r.split = split;
+    r.sc = g.acc_scale;
+  }
+  return r;
+}
+
 // --------------------------------------------------------------------------- the chunk step
 // What a step does besides the chunk forward (and, with update, its backward and SGD).
 enum ChunkMode {
@@ -267,6 +288,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
   // byte offset of sequence s's rows in a [Bn][cols] buffer of element size esz
   auto rows = [n](int s, long cols, size_t esz) { return (size_t)s * n * cols * esz; };
   h->launches = 0;
+  ResidualPartials pend;  // split-K partials of the last residual product, reduced by the next RMSNorm
 
   {
     PROF(K_EMBED);
@@ -282,7 +304,8 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
     {
       PROF(K_RMSNORM);
       HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.attn_norm, h->a, sb ? S->r1 : nullptr, sb ? S->h_in : nullptr, Bn, d, eps,
-                                st, f16));
+                                st, f16, pend));
+      pend = ResidualPartials();
     }
     float *qkv = sb ? S->qkv : h->qkv;  // fp32: q, k, v are normalised / cached without a 16-bit rounding first
     {
@@ -360,13 +383,15 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
       GemmArgs g = gargs(o, d, lw.wo, d, Bn, d, d);
       g.Cf = h->h;
       g.ldcf = d;
-      gemm(h, K_GEMM_O, true, true, EPI_ADD_F32, g, st, true);
+      pend = gemm_residual(h, K_GEMM_O, g, st);
     }
     // --- MLP sub-block (fast + static summed on one norm for updated blocks)
     void *m = S ? S->m : h->m;
     {
       PROF(K_RMSNORM);
-      HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.mlp_norm, m, S ? S->r2 : nullptr, S ? S->h1 : nullptr, Bn, d, eps, st, f16));
+      HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.mlp_norm, m, S ? S->r2 : nullptr, S ? S->h1 : nullptr, Bn, d, eps, st, f16,
+                                pend));
+      pend = ResidualPartials();
     }
     void *hm = S ? S->hmid : h->hmid;  // hidden units: F (frozen) or 2F = fast then static
     if (!lw.fast) {
@@ -378,7 +403,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
       GemmArgs g2 = gargs(hm, F, lw.wd, F, Bn, d, F);
       g2.Cf = h->h;
       g2.ldcf = d;
-      gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st, true);
+      pend = gemm_residual(h, K_GEMM_DOWN, g2, st);
       h->launches += 4;
     } else {
       // static units [F, 2F), all sequences at once
@@ -408,7 +433,10 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
         g2.Cf = h->h + (size_t)s * n * d;
         g2.ldcf = d;
         g2.acc_scale = 1.f / h->wscale;
-        gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st, true);
+        if (B == 1)
+          pend = gemm_residual(h, K_GEMM_DOWN, g2, st);
+        else
+          gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st, true);
       }
       h->launches += 2 + 2 * B;
     }
@@ -417,7 +445,8 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
   {
     PROF(K_RMSNORM);
     HIPCHK(rmsnorm_fwd_launch(dt, h->h, h->final_norm, h->nf, update ? h->rf : nullptr, update ? h->hf : nullptr, Bn, d,
-                              eps, st, f16));
+                              eps, st, f16, pend));
+    pend = ResidualPartials();
   }
   {
     GemmArgs g = gargs(h->nf, d, h->lm_head, d, Bn, h->V, d);
