@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libttt.so")
-SOURCES = ["gemm.hip", "gemm2.hip", "attn.hip", "elem.hip", "ttt_api.hip"]
+SOURCES = ["gemm.hip", "gemm2.hip", "gemv.hip", "attn.hip", "elem.hip", "ttt_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -333,6 +333,9 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const AttnArgs a) {
 }
 
 // out[q, h, :] = sum_s 2^(lse_s - lse) O_s[q, h, :],  lse = log2 sum_s 2^lse_s  (fixed order in s).
+// nsplit <= MERGE_MAX.  The loads of all splits are issued before they are combined (a thread
+// otherwise waits for one partial after the other, which dominates when there are few rows).
+constexpr int MERGE_MAX = 32;
 template <typename T>
 __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(const AttnArgs a, int hd) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
@@ -340,15 +343,34 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(const AttnArgs a, i
   if (idx >= (long)a.n * dq4) return;
   const int q = idx / dq4, col = (idx % dq4) * 4, h = col / hd;
   const float *L = a.ws + (long)a.nsplit * a.n * a.d;
+  float ls[MERGE_MAX];
+#pragma unroll
+  for (int s = 0; s < MERGE_MAX; ++s) {
+    const int sc = min(s, a.nsplit - 1);
+    const float x = L[((long)sc * a.H + h) * a.ldl + q];
+    ls[s] = s < a.nsplit ? x : -INFINITY;
+  }
   float mx = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) mx = fmaxf(mx, L[((long)s * a.H + h) * a.ldl + q]);
+#pragma unroll
+  for (int s = 0; s < MERGE_MAX; ++s) mx = fmaxf(mx, ls[s]);
   float den = 0.f, v[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float ls = L[((long)s * a.H + h) * a.ldl + q];
-    const float w = (ls == -INFINITY) ? 0.f : exp2f(ls - mx);
-    den += w;
-    const float4 o = *reinterpret_cast<const float4 *>(a.ws + ((long)s * a.n + q) * a.d + col);
-    v[0] += w * o.x; v[1] += w * o.y; v[2] += w * o.z; v[3] += w * o.w;
+#pragma unroll
+  for (int g = 0; g < MERGE_MAX / 8; ++g) {
+    if (8 * g >= a.nsplit) break;
+    float4 o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sc = min(8 * g + u, a.nsplit - 1);
+      o[u] = *reinterpret_cast<const float4 *>(a.ws + ((long)sc * a.n + q) * a.d + col);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (8 * g + u >= a.nsplit) break;
+      const float l = ls[8 * g + u];
+      const float w = (l == -INFINITY) ? 0.f : exp2f(l - mx);
+      den += w;
+      v[0] += w * o[u].x; v[1] += w * o[u].y; v[2] += w * o[u].z; v[3] += w * o[u].w;
+    }
   }
   const float inv = 1.f / den;
   v[0] *= inv; v[1] *= inv; v[2] *= inv; v[3] *= inv;
@@ -1365,6 +1387,7 @@ hipError_t attn_bwd_dq_launch(int dtype, int hd, const AttnArgs &a, hipStream_t 
 }
 hipError_t attn_merge_launch(int dtype, int hd, bool dq, const AttnArgs &a, hipStream_t st) {
   if (a.n <= 0 || a.nsplit <= 1) return hipSuccess;
+  if (a.nsplit > MERGE_MAX) return hipErrorInvalidValue;
   const long tot = (long)a.n * a.d / 4;
   const dim3 grid((unsigned)((tot + 255) / 256));
   if (dq)

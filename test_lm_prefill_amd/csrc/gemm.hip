@@ -414,6 +414,9 @@ hipError_t reduce_launch(int epi, const GemmArgs &g, int S, hipStream_t st) {
 size_t gemm_ws_elems(int M, int N) { return (size_t)8 * M * N; }
 
 hipError_t gemm_dma_launch(bool f16, int epi, const GemmArgs &g, hipStream_t st);
+// few-row products (gemv.hip): M <= 4, 16-bit k-contiguous operands, fp32 / SwiGLU / CE epilogues
+bool gemv_ok(int dtype, bool a_kc, bool b_kc, int epi, const GemmArgs &g);
+hipError_t gemv_launch(bool f16, int epi, const GemmArgs &g, hipStream_t st);
 
 static bool use_dma(int dtype, bool a_kc, bool b_kc, const GemmArgs &g) {
   return (dtype == 1 || dtype == 2) && a_kc && b_kc && g.K % 64 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
@@ -423,6 +426,7 @@ static bool use_dma(int dtype, bool a_kc, bool b_kc, const GemmArgs &g) {
 int gemm_plan(int dtype, bool a_kc, bool b_kc, int epi, const GemmArgs &g, size_t ws_elems, int force_split) {
   const bool dma = use_dma(dtype, a_kc, b_kc, g);
   int split = 1;
+  if (force_split <= 0 && gemv_ok(dtype, a_kc, b_kc, epi, g)) return 1;
   if (epi == EPI_STORE || epi == EPI_STORE_F32 || epi == EPI_ADD_F32) {
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
     if (force_split > 0) {
@@ -454,6 +458,7 @@ hipError_t gemm_main_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g
   g.ws = ws;
   // the wrapped activation operand must be k-contiguous, whole 16-byte vectors
   if (g.a_kwrap < 0 || (g.a_kwrap > 0 && (!a_kc || g.a_kwrap % 8 != 0))) return hipErrorInvalidValue;
+  if (split <= 1 && gemv_ok(dtype, a_kc, b_kc, epi, g)) return gemv_launch(dtype == 2, epi, g, st);
   if (use_dma(dtype, a_kc, b_kc, g)) return gemm_dma_launch(dtype == 2, epi, g, st);
   if (dtype == 2 || g.c_f16) return hipErrorInvalidValue;
   return dtype == 1 ? dispatch_layout<bf16_t>(a_kc, b_kc, epi, g, st, split)

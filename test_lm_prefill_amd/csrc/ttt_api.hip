@@ -119,6 +119,7 @@ struct ttt_handle {
   float *ws = nullptr;
   size_t ws_elems = 0;
   int attn_split = 1;
+  int dec_split = 1;   // key-range split of the forward for chunks of at most 16 rows (decode steps)
   float *attn_ws = nullptr;
   std::vector<Saved> saved;
   // graphs: [0] update, [1] no-update
@@ -363,7 +364,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
         aa.ldt = b;
         aa.pos0 = h->pos0;
         aa.scale = 1.f / sqrtf((float)hd);
-        aa.nsplit = lw.fsplit;
+        aa.nsplit = n <= 16 ? std::max(lw.fsplit, h->dec_split) : lw.fsplit;
         aa.sbound = lw.sbound;
         aa.fwd_f16 = lw.fwd16;
         aa.o_f16 = f16;
@@ -377,7 +378,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
           HIPCHK(attn_merge_launch(dt, hd, false, aa, st));
         }
       }
-      h->launches += lw.fsplit > 1 ? 3 : 2;
+      h->launches += (n <= 16 ? std::max(lw.fsplit, h->dec_split) : lw.fsplit) > 1 ? 3 : 2;
     }
     {
       GemmArgs g = gargs(o, d, lw.wo, d, Bn, d, d);
@@ -1086,6 +1087,13 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
       int smax = h->attn_split;
       for (const LayerBuf &lw : h->layers) smax = std::max(smax, lw.fsplit);
       h->attn_ws = (float *)dalloc(h, attn_ws_floats(smax, b, d, h->H, b) * 4);
+      // a decode step has one query per head: split its window into up to 32 ranges of at
+      // least 8 key tiles each (a work-group streams its tiles one after another)
+      int ds = 32;
+      while (ds > 1 && ((h->k + b) / 32 < 8 * ds ||
+                        attn_ws_floats(ds, 16, d, h->H, b) > attn_ws_floats(smax, b, d, h->H, b)))
+        ds /= 2;
+      h->dec_split = ds;
     }
     if (h->nu > 0) {
       h->lm_headT = dalloc(h, (size_t)V * d * es, false);
