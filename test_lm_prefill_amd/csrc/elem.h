@@ -72,6 +72,11 @@ hipError_t ce_reduce_launch(const float2 *part, int P, const float *zlab, const 
 // Batched chunk of B sequences, n positions each, row r = s * n + m at position
 // *pos0 + m of sequence s: ids[r] = tok[s * ld_tok + *pos0 + m], labs[r] = the
 // id after it; and losses[s * ld_loss + *pos0 + m] = closs[r].
+// dst[s n + t][:] = src[s (*src_n) + (*pos0 mod G) + t][:] for s < B, t < n (fp32 rows of d,
+// d % 4 == 0): a chunk's residual rows from the frozen-prefix pass of its group (groups start
+// at multiples of G; that pass ran *src_n rows per sequence).
+hipError_t lead_rows_launch(const float *src, const int *src_n, int G, const int *pos0, float *dst, int n, int d,
+                            int B, hipStream_t st);
 hipError_t gather_chunk_ids_launch(const int *tok, long ld_tok, const int *pos0, int n, int B, int *ids, int *labs,
                                    hipStream_t st);
 hipError_t scatter_chunk_losses_launch(const float *closs, float *losses, long ld_loss, const int *pos0, int n, int B,

@@ -500,6 +500,15 @@ __global__ __launch_bounds__(64) void decode_pick_kernel(const float2 *part, con
 }
 
 // Rows of a batched chunk: row r = s * n + m is position *pos0 + m of sequence s.
+__global__ void lead_rows_kernel(const float4 *src, const int *src_n, int G, const int *pos0, float4 *dst, int n,
+                                 int d4, int B) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)B * n * d4) return;
+  const int c = idx % d4;
+  const long r = idx / d4;
+  const int s = r / n, t = r % n;
+  dst[r * d4 + c] = src[((long)s * *src_n + *pos0 % G + t) * d4 + c];
+}
 __global__ void gather_chunk_ids_kernel(const int *tok, long ld_tok, const int *pos0, int n, int B, int *ids,
                                         int *labs) {
   const int r = blockIdx.x * 256 + threadIdx.x;
@@ -650,6 +659,14 @@ hipError_t gather_chunk_ids_launch(const int *tok, long ld_tok, const int *pos0,
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(gather_chunk_ids_kernel, dim3(blocks_for((long)B * n)), dim3(256), 0, st, tok, ld_tok, pos0, n, B,
                      ids, labs);
+  return hipGetLastError();
+}
+hipError_t lead_rows_launch(const float *src, const int *src_n, int G, const int *pos0, float *dst, int n, int d,
+                            int B, hipStream_t st) {
+  if (n <= 0 || d % 4 != 0) return n <= 0 ? hipSuccess : hipErrorInvalidValue;
+  const long tot = (long)B * n * (d / 4);
+  hipLaunchKernelGGL(lead_rows_kernel, dim3(blocks_for(tot)), dim3(256), 0, st, (const float4 *)src, src_n, G, pos0,
+                     (float4 *)dst, n, d / 4, B);
   return hipGetLastError();
 }
 hipError_t scatter_chunk_losses_launch(const float *closs, float *losses, long ld_loss, const int *pos0, int n, int B,

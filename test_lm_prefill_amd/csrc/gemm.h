@@ -75,9 +75,10 @@ size_t gemm_ws_elems(int M, int N);
 
 // The same work in two launches, for callers that time them separately:
 // gemm_plan returns the K split gemm_launch would use; gemm_main_launch runs
-// the GEMM (partials to ws when split > 1); gemm_reduce_launch applies the
-// epilogue to the fixed-order sum of the partials.
+// the GEMM (partials to ws when split > 1; allow_gemv = false keeps products of a
+// few rows on the tiled kernel); gemm_reduce_launch applies the epilogue to the
+// fixed-order sum of the partials.
 int gemm_plan(int dtype, bool a_kc, bool b_kc, int epi, const GemmArgs &g, size_t ws_elems, int force_split = 0);
 hipError_t gemm_main_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, float *ws, int split,
-                            hipStream_t st);
+                            hipStream_t st, bool allow_gemv = true);
 hipError_t gemm_reduce_launch(int dtype, int epi, GemmArgs g, float *ws, int split, hipStream_t st);

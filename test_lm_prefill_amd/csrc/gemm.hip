@@ -453,12 +453,12 @@ int gemm_plan(int dtype, bool a_kc, bool b_kc, int epi, const GemmArgs &g, size_
 }
 
 hipError_t gemm_main_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, float *ws, int split,
-                            hipStream_t st) {
+                            hipStream_t st, bool allow_gemv) {
   g.ksplit = split;
   g.ws = ws;
   // the wrapped activation operand must be k-contiguous, whole 16-byte vectors
   if (g.a_kwrap < 0 || (g.a_kwrap > 0 && (!a_kc || g.a_kwrap % 8 != 0))) return hipErrorInvalidValue;
-  if (split <= 1 && gemv_ok(dtype, a_kc, b_kc, epi, g)) return gemv_launch(dtype == 2, epi, g, st);
+  if (allow_gemv && split <= 1 && gemv_ok(dtype, a_kc, b_kc, epi, g)) return gemv_launch(dtype == 2, epi, g, st);
   if (use_dma(dtype, a_kc, b_kc, g)) return gemm_dma_launch(dtype == 2, epi, g, st);
   if (dtype == 2 || g.c_f16) return hipErrorInvalidValue;
   return dtype == 1 ? dispatch_layout<bf16_t>(a_kc, b_kc, epi, g, st, split)

@@ -49,6 +49,7 @@ struct LayerBuf {
   int u = -1;
   float sbound = 0.f;  // bound of the scaled scores (log2 units) for the bounded forward, 0 = none
   int fsplit = 1;      // key-range split of the forward
+  int R = 0;           // ring rows: k + b, or k + G for the frozen prefix run in groups of G tokens
   bool fwd16 = false;  // attention forward operands (q, ring K and V^T) are fp16
   // ring planes: K, Vt in the attention forward's type; Kb (bf16 copy of K when the
   // forward is fp16), Kt, V in the working dtype for the backward
@@ -120,12 +121,19 @@ struct ttt_handle {
   size_t ws_elems = 0;
   int attn_split = 1;
   int dec_split = 1;   // key-range split of the forward for chunks of at most 16 rows (decode steps)
+  // Frozen prefix: blocks 0 .. Lf-1 carry no fast weights, so a prefill runs them over groups
+  // of G tokens (a multiple of b) ahead of the chunk loop; their output residual rows wait in
+  // h_lead [B][G][d].  G = 0: no grouping (every chunk step runs all blocks).
+  int G = 0, Lf = 0;
+  float *h_lead = nullptr;
+  int *lead_n = nullptr;  // device: rows per sequence of the last frozen-prefix pass (G, or fewer at the end)
   float *attn_ws = nullptr;
   std::vector<Saved> saved;
   // graphs: [0] update, [1] no-update
   // captured steps: full-chunk prefill with / without update, decode step greedy /
   // forced, full-chunk recompute-and-update of a decoded chunk
-  hipGraphExec_t gexec[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  // [5]: the frozen prefix over a full group of G tokens
+  hipGraphExec_t gexec[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   // continuation state for ttt_decode: positions processed, start of the open
   // decode chunk, and whether a prefill has set them
   int64_t len = 0, dstart = 0;
@@ -237,12 +245,15 @@ void prof_collect(ttt_handle *h, hipStream_t st) {
 
 // f16op: the operands are fp16 in bf16 mode (forward activations and weights,
 // and the MLP part of the backward)
-void gemm(ttt_handle *h, int cls, bool akc, bool bkc, int epi, GemmArgs g, hipStream_t st, bool f16op = false) {
+// whole: one tiled product with no K split (each output element then depends only on its
+// own row and column, whatever the row count; used for the frozen prefix)
+void gemm(ttt_handle *h, int cls, bool akc, bool bkc, int epi, GemmArgs g, hipStream_t st, bool f16op = false,
+          bool whole = false) {
   const int odt = (f16op && h->dt == 1) ? 2 : h->dt;
-  const int split = gemm_plan(odt, akc, bkc, epi, g, h->ws_elems);
+  const int split = whole ? 1 : gemm_plan(odt, akc, bkc, epi, g, h->ws_elems);
   {
     Prof prof_(h, cls, st);
-    HIPCHK(gemm_main_launch(odt, akc, bkc, epi, g, h->ws, split, st));
+    HIPCHK(gemm_main_launch(odt, akc, bkc, epi, g, h->ws, split, st, !whole));
   }
   if (split > 1) {
     Prof prof_(h, K_SPLITK_REDUCE, st);
@@ -280,7 +291,11 @@ enum ChunkMode {
   MODE_RECOMPUTE = 2  // a decoded chunk run again for its update; losses go to rlosses
 };
 
-void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode = MODE_PREFILL) {
+// lb > 0: blocks below lb were run ahead by the frozen-prefix pass (lead); the chunk's
+// residual rows are taken from h_lead.  lead: run only the frozen prefix over n rows per
+// sequence (a group), into h_lead, with no head, backward or position advance.
+void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode = MODE_PREFILL, int lb = 0,
+                   bool lead = false) {
   const int d = h->d, F = h->F, L = h->L, dt = h->dt, B = h->B, H = h->H, hd = h->hd, b = h->b;
   const int Bn = B * n;  // rows of the batched chunk: sequence s owns rows [s*n, (s+1)*n)
   const size_t es = h->es;
@@ -290,21 +305,34 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
   auto rows = [n](int s, long cols, size_t esz) { return (size_t)s * n * cols * esz; };
   h->launches = 0;
   ResidualPartials pend;  // split-K partials of the last residual product, reduced by the next RMSNorm
+  float *const hres = lead ? h->h_lead : h->h;  // the residual stream of this pass
+  const int ldr = lead ? h->G : b;              // rows per sequence of the per-row statistics buffers
+  const int le = lead ? h->Lf : L;
 
   {
     PROF(K_EMBED);
     HIPCHK(gather_chunk_ids_launch(h->tok, h->ld_tok, h->pos0, n, B, h->ids, h->labs, st));
-    HIPCHK(embed_launch(dt, h->tok_emb, h->ids, h->zero, h->h, Bn, d, st));
+    if (lead) HIPCHK(set_int_launch(h->lead_n, n, st));
+    if (lb == 0)
+      HIPCHK(embed_launch(dt, h->tok_emb, h->ids, h->zero, hres, Bn, d, st));
+    else
+      HIPCHK(lead_rows_launch(h->h_lead, h->lead_n, h->G, h->pos0, h->h, n, d, B, st));
   }
   h->launches += 2;
-  for (int l = 0; l < L; ++l) {
+  for (int l = lb; l < le; ++l) {
     LayerBuf &lw = h->layers[l];
+    // blocks below Lf: unsplit products and one key range per head, so that a token's
+    // result does not depend on how many rows share the pass (a group or a chunk)
+    // (decode steps of one or a few rows keep the few-row products: nothing compares them
+    // with a prefill bit for bit; a lead pass always runs whole, so no split-K partials are
+    // left pending when it returns)
+    const bool frozen_whole = h->G > 0 && l < h->Lf && (lead || n > 16);
     Saved *S = (lw.fast && update) ? &h->saved[lw.u] : nullptr;
     const bool sb = S && lw.bwd_attn;  // attention of this block is back-propagated
     // --- attention sub-block
     {
       PROF(K_RMSNORM);
-      HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.attn_norm, h->a, sb ? S->r1 : nullptr, sb ? S->h_in : nullptr, Bn, d, eps,
+      HIPCHK(rmsnorm_fwd_launch(dt, hres, lw.attn_norm, h->a, sb ? S->r1 : nullptr, sb ? S->h_in : nullptr, Bn, d, eps,
                                 st, f16, pend));
       pend = ResidualPartials();
     }
@@ -313,7 +341,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
       GemmArgs g = gargs(h->a, d, lw.wqkv, d, Bn, 3 * d, d);
       g.Cf = qkv;
       g.ldcf = 3 * d;
-      gemm(h, K_GEMM_QKV, true, true, EPI_STORE_F32, g, st, true);
+      gemm(h, K_GEMM_QKV, true, true, EPI_STORE_F32, g, st, true, frozen_whole);
     }
     void *qh = sb ? S->qh : h->qh;
     void *o = sb ? S->o : h->o;
@@ -332,7 +360,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
         ra.d = d;
         ra.H = H;
         ra.hd = hd;
-        ra.R = h->R;
+        ra.R = lw.R;
         ra.eps = eps;
         ra.qh = off(qh, rows(s, d, es));
         ra.qhb = (sb && lw.fwd16) ? off(S->qhb, rows(s, d, es)) : nullptr;
@@ -354,17 +382,17 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
         aa.K = off(lw.K, rs);
         aa.Vt = off(lw.Vt, rs);
         aa.o = off(o, rows(s, d, es));
-        aa.lse2 = lse2 + (size_t)s * H * b;
+        aa.lse2 = lse2 + (size_t)s * H * ldr;
         aa.n = n;
         aa.d = d;
         aa.H = H;
-        aa.R = h->R;
+        aa.R = lw.R;
         aa.window = h->k;
-        aa.ldl = b;
+        aa.ldl = ldr;
         aa.ldt = b;
         aa.pos0 = h->pos0;
         aa.scale = 1.f / sqrtf((float)hd);
-        aa.nsplit = n <= 16 ? std::max(lw.fsplit, h->dec_split) : lw.fsplit;
+        aa.nsplit = frozen_whole ? 1 : n <= 16 ? std::max(lw.fsplit, h->dec_split) : lw.fsplit;
         aa.sbound = lw.sbound;
         aa.fwd_f16 = lw.fwd16;
         aa.o_f16 = f16;
@@ -378,19 +406,22 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
           HIPCHK(attn_merge_launch(dt, hd, false, aa, st));
         }
       }
-      h->launches += (n <= 16 ? std::max(lw.fsplit, h->dec_split) : lw.fsplit) > 1 ? 3 : 2;
+      h->launches += 3;
     }
     {
       GemmArgs g = gargs(o, d, lw.wo, d, Bn, d, d);
-      g.Cf = h->h;
+      g.Cf = hres;
       g.ldcf = d;
-      pend = gemm_residual(h, K_GEMM_O, g, st);
+      if (frozen_whole)
+        gemm(h, K_GEMM_O, true, true, EPI_ADD_F32, g, st, true, true);
+      else
+        pend = gemm_residual(h, K_GEMM_O, g, st);
     }
     // --- MLP sub-block (fast + static summed on one norm for updated blocks)
     void *m = S ? S->m : h->m;
     {
       PROF(K_RMSNORM);
-      HIPCHK(rmsnorm_fwd_launch(dt, h->h, lw.mlp_norm, m, S ? S->r2 : nullptr, S ? S->h1 : nullptr, Bn, d, eps, st, f16,
+      HIPCHK(rmsnorm_fwd_launch(dt, hres, lw.mlp_norm, m, S ? S->r2 : nullptr, S ? S->h1 : nullptr, Bn, d, eps, st, f16,
                                 pend));
       pend = ResidualPartials();
     }
@@ -400,11 +431,14 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
       g.C = hm;
       g.ldc = F;
       g.c_f16 = f16;
-      gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, g, st, true);
+      gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, g, st, true, frozen_whole);
       GemmArgs g2 = gargs(hm, F, lw.wd, F, Bn, d, F);
-      g2.Cf = h->h;
+      g2.Cf = hres;
       g2.ldcf = d;
-      pend = gemm_residual(h, K_GEMM_DOWN, g2, st);
+      if (frozen_whole)
+        gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st, true, true);
+      else
+        pend = gemm_residual(h, K_GEMM_DOWN, g2, st);
       h->launches += 4;
     } else {
       // static units [F, 2F), all sequences at once
@@ -442,6 +476,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
       h->launches += 2 + 2 * B;
     }
   }
+  if (lead) return;  // the frozen prefix of a group: its residual rows stay in h_lead
   // --- head: final norm, LM head + cross-entropy (losses written before any update)
   {
     PROF(K_RMSNORM);
@@ -619,7 +654,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
           aa.n = n;
           aa.d = d;
           aa.H = H;
-          aa.R = h->R;
+          aa.R = lw.R;
           aa.window = h->k;
           aa.ldl = b;
           aa.ldt = b;
@@ -652,7 +687,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
           ra.d = d;
           ra.H = H;
           ra.hd = hd;
-          ra.R = h->R;
+          ra.R = lw.R;
           ra.eps = eps;
           ra.dqh = h->dq + (size_t)s * n * d;
           ra.dkh = h->dk + (size_t)s * n * d;
@@ -724,7 +759,7 @@ ttt_status fail(ttt_handle *h, ttt_status s, const std::string &msg) {
 }
 
 void free_all(ttt_handle *h) {
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 6; ++i)
     if (h->gexec[i]) hipGraphExecDestroy(h->gexec[i]);
   if (h->cap) hipStreamDestroy(h->cap);
   for (void *p : h->allocs) hipFree(p);
@@ -766,16 +801,25 @@ float score_bound(ttt_handle *h, const void *gq, const void *gk, hipStream_t st)
 // One step of n positions in the given mode: replayed from a captured graph when
 // graph replay is on and the step has its full size (b for chunks, 1 for decode
 // steps), else enqueued launch by launch.
-void run_step(ttt_handle *h, int n, bool update, int mode, bool use_graph, hipStream_t st) {
+// lead: the frozen prefix of a group of n tokens.  grouped: a prefill chunk whose frozen
+// prefix the lead pass has run (the graphs of full prefill chunks are only used this way
+// when the handle groups).
+void run_step(ttt_handle *h, int n, bool update, int mode, bool use_graph, hipStream_t st, bool lead = false,
+              bool grouped = false) {
   int gi = -1;
   if (use_graph) {
-    if (mode == MODE_PREFILL && n == h->b) gi = update ? 0 : 1;
-    if (mode == MODE_GREEDY && n == 1 && !update) gi = 2;
-    if (mode == MODE_PREFILL && n == 1 && !update) gi = 3;
-    if (mode == MODE_RECOMPUTE && n == h->b && update) gi = 4;
+    if (lead) {
+      if (n == h->G) gi = 5;
+    } else {
+      if (mode == MODE_PREFILL && n == h->b && grouped == (h->G > 0)) gi = update ? 0 : 1;
+      if (mode == MODE_GREEDY && n == 1 && !update) gi = 2;
+      if (mode == MODE_PREFILL && n == 1 && !update) gi = 3;
+      if (mode == MODE_RECOMPUTE && n == h->b && update) gi = 4;
+    }
   }
+  const int lb = grouped ? h->Lf : 0;
   if (gi < 0) {
-    enqueue_chunk(h, n, update, st, mode);
+    enqueue_chunk(h, n, update, st, mode, lb, lead);
     prof_collect(h, st);
     return;
   }
@@ -783,7 +827,7 @@ void run_step(ttt_handle *h, int n, bool update, int mode, bool use_graph, hipSt
     hipGraph_t gr = nullptr;
     HIPCHK(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
     try {
-      enqueue_chunk(h, n, update, h->cap, mode);
+      enqueue_chunk(h, n, update, h->cap, mode, lb, lead);
     } catch (...) {
       hipStreamEndCapture(h->cap, &gr);
       if (gr) hipGraphDestroy(gr);
@@ -865,6 +909,15 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
   h->nu = c.n_update;
   h->R = c.window + c.chunk;  // positions s-k+1 .. s+b-1 must coexist; multiple of 64
   h->B = c.n_seq > 0 ? c.n_seq : 1;
+  // frozen-prefix groups: about 8192 rows per pass (B sequences of G tokens), never
+  // longer than the longest sequence
+  h->Lf = c.n_layers - c.n_update;
+  {
+    const int gc = std::max(1, 8192 / (h->B * c.chunk));
+    const long gmax = (c.max_tokens + c.chunk - 1) / c.chunk * (long)c.chunk;
+    h->G = (int)std::min<long>((long)gc * c.chunk, gmax);
+    if (h->Lf == 0 || h->G <= c.chunk) h->G = 0;
+  }
   h->ld_tok = c.max_tokens + 1;
   h->Vs = std::min(h->V, 16384);
   h->P = 2 * ((h->V + 127) / 128);
@@ -885,15 +938,15 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     h->i_gu.resize(h->nu);
     h->i_d.resize(h->nu);
     h->saved.resize(h->nu);
-    const size_t plane = (size_t)h->H * h->R * h->hd * es;
-    int nplanes = 0;
+    size_t ring_sb = 0;  // one sequence's ring planes, all layers
     for (int l = 0; l < L; ++l) {
       LayerBuf &lw = h->layers[l];
       lw.fast = l >= L - h->nu;
       lw.bwd_attn = l > L - h->nu;
       lw.sbound = score_bound(h, w->q_norm[l], w->k_norm[l], st);
       lw.fwd16 = attn_fwd_f16_ok(h->dt, lw.sbound, h->hd);
-      nplanes += 2 + (lw.bwd_attn ? (lw.fwd16 ? 3 : 2) : 0);
+      lw.R = (h->G > 0 && l < h->Lf) ? c.window + h->G : h->R;
+      ring_sb += (size_t)h->H * lw.R * h->hd * es * (2 + (lw.bwd_attn ? (lw.fwd16 ? 3 : 2) : 0));
     }
     if (h->dt == 1 && h->nu > 0) {
       // largest |w| over the weights whose forward copies are stored scaled
@@ -922,7 +975,7 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
       while (sh > 0 && std::ldexp(mx, sh) > 4096.f) --sh;
       h->wscale = std::ldexp(1.f, sh);
     }
-    h->ring_sbytes = plane * nplanes;
+    h->ring_sbytes = ring_sb;
     h->ring_bytes = h->ring_sbytes * h->B;  // sequence s's planes at s * ring_sbytes
     h->ring_base = dalloc(h, h->ring_bytes);
     size_t roff = 0;
@@ -1004,6 +1057,7 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
         else
           HIPCHK(bf16_to_f16_launch(lw.wd, F, lw.wd, F, d, F, st));
       }
+      const size_t plane = (size_t)h->H * lw.R * h->hd * es;
       lw.K = off(h->ring_base, roff);
       roff += plane;
       lw.Vt = off(h->ring_base, roff);
@@ -1023,10 +1077,12 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     const size_t bd = (size_t)b * d;        // one sequence's chunk
     const int Bb = h->B * b;                 // rows of a batched chunk
     const size_t Bbd = (size_t)Bb * d;
+    const int Br = h->B * std::max(b, h->G);  // rows of the forward scratch: a chunk or a frozen-prefix group
+    const size_t Brd = (size_t)Br * d;
     h->tok = (int *)dalloc(h, h->B * h->ld_tok * sizeof(int));
     h->losses = (float *)dalloc(h, h->B * c.max_tokens * sizeof(float));
-    h->ids = (int *)dalloc(h, Bb * sizeof(int));
-    h->labs = (int *)dalloc(h, Bb * sizeof(int));
+    h->ids = (int *)dalloc(h, Br * sizeof(int));
+    h->labs = (int *)dalloc(h, Br * sizeof(int));
     h->zero = (int *)dalloc(h, 64);
     h->closs = (float *)dalloc(h, Bb * sizeof(float));
     h->pos0 = (int *)dalloc(h, 64);
@@ -1034,13 +1090,17 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     h->rope = (float2 *)dalloc(h, (size_t)c.max_tokens * (h->hd / 2) * sizeof(float2), false);
     HIPCHK(rope_table_launch(h->rope, c.max_tokens, h->hd, (double)c.rope_theta, st));
     h->h = (float *)dalloc(h, Bbd * 4);
-    h->lse2 = (float *)dalloc(h, (size_t)h->H * Bb * 4);
-    h->a = dalloc(h, Bbd * es);
-    h->qkv = (float *)dalloc(h, 3 * Bbd * 4);
-    h->qh = dalloc(h, Bbd * es);
-    h->o = dalloc(h, Bbd * es);
-    h->m = dalloc(h, Bbd * es);
-    h->hmid = dalloc(h, (size_t)Bb * (h->nu > 0 ? 2 * F : F) * es);
+    if (h->G > 0) {
+      h->h_lead = (float *)dalloc(h, (size_t)h->B * h->G * d * 4);
+      h->lead_n = (int *)dalloc(h, 64);
+    }
+    h->lse2 = (float *)dalloc(h, (size_t)h->H * Br * 4);
+    h->a = dalloc(h, Brd * es);
+    h->qkv = (float *)dalloc(h, 3 * Brd * 4);
+    h->qh = dalloc(h, Brd * es);
+    h->o = dalloc(h, Brd * es);
+    h->m = dalloc(h, Brd * es);
+    h->hmid = dalloc(h, (size_t)Br * (h->nu > 0 ? 2 * F : F) * es);
     h->nf = dalloc(h, Bbd * es);
     h->hf = (float *)dalloc(h, Bbd * 4);
     h->rf = (float *)dalloc(h, Bb * 4);
@@ -1146,8 +1206,17 @@ ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float 
     reset_fast(h, st);
     const int64_t nfull = T / b;
     const int tail = (int)(T % b);
-    for (int64_t c = 0; c < nfull; ++c) run_step(h, b, update, MODE_PREFILL, use_graph, st);
-    if (tail > 0) run_step(h, tail, update, MODE_PREFILL, use_graph, st);
+    if (h->G > 0) {
+      // the frozen prefix of each group of G tokens, then the group's chunks from block Lf
+      for (int64_t g0 = 0; g0 < T; g0 += h->G) {
+        const int gn = (int)std::min<int64_t>(h->G, T - g0);
+        run_step(h, gn, false, MODE_PREFILL, use_graph, st, true);
+        for (int c0 = 0; c0 < gn; c0 += b) run_step(h, std::min(b, gn - c0), update, MODE_PREFILL, use_graph, st, false, true);
+      }
+    } else {
+      for (int64_t c = 0; c < nfull; ++c) run_step(h, b, update, MODE_PREFILL, use_graph, st);
+      if (tail > 0) run_step(h, tail, update, MODE_PREFILL, use_graph, st);
+    }
     if (T > 0) {
       const size_t ldl = (size_t)h->cfg.max_tokens * sizeof(float);
       HIPCHK(hipMemcpy2DAsync(d_losses, (size_t)T * sizeof(float), h->losses, ldl, (size_t)T * sizeof(float), h->B,
