@@ -333,8 +333,16 @@ __global__ __launch_bounds__(NT, 2) void gemm5_kernel(const GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int mt = (g.M + BM - 1) / BM, ntl = (g.N + 127) / 128;
+  // Each XCD takes a contiguous run of the tile order; the order walks bands of
+  // GM row tiles across all columns (rows fastest), so the 64 work-groups an XCD
+  // runs at once share about 8 activation and 8 weight tiles in its L2 instead of
+  // one weight tile and 64 activation tiles.  With mt <= GM it is plain
+  // row-fastest order.
+  constexpr int GM = 8;
   const int tile = remap_tile2(blockIdx.x, mt * ntl);
-  const int tm = tile % mt, tn = tile / mt;
+  const int band = tile / (GM * ntl), in_band = tile % (GM * ntl);
+  const int bm = min(GM, mt - band * GM);
+  const int tm = band * GM + in_band % bm, tn = in_band / bm;
   const int m0 = tm * BM, n0 = tn * 128;
   int kbeg = 0, kend = g.K;
   if (g.ksplit > 1) {
