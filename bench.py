@@ -104,17 +104,24 @@ def algorithmic_bytes(cfg, T, update=True):
         per = -(-(-(-K // sp)) // 64) * 64
         return -(-K // per)
     b_rows = cfg.chunk
+    # the frozen blocks below the updated ones run ahead over groups of about 8192 tokens
+    # (the library's rule for one sequence) with unsplit products; their outputs are then
+    # copied into each chunk's residual rows (fp32 read + write, timed with the embedding)
+    gc = max(1, 8192 // cfg.chunk)
+    G = min(gc * cfg.chunk, n_chunks * cfg.chunk)
+    grouped = (L - nu) > 0 and G > cfg.chunk
     sp_o = split_k(b_rows, d, d)
     sp_dn = split_k(b_rows, d, F)
     sp_df = split_k(b_rows, d, (3 if a == 2 else 2) * F)
-    red = L * (sp_o * 4 + 4) * d if sp_o > 1 else 0
-    red += (L - nu) * (sp_dn * 4 + 4) * d if sp_dn > 1 else 0
+    n_o = nu if grouped else L                   # layers whose O product is split by rows of a chunk
+    red = n_o * (sp_o * 4 + 4) * d if sp_o > 1 else 0
+    red += (L - nu) * (sp_dn * 4 + 4) * d if sp_dn > 1 and not grouped else 0
     red += nu * (sp_df * 4 + 4) * d if sp_df > 1 else 0
     rms = (2 * L + 1) * (4 + a) * d + ((nb + nu + 1) * 4 * d if update and nu > 0 else 0) + red
     # QK-norm + RoPE: read fp32 q, k, v; write q and the ring's K and V^T; the backward's
     # copies (V, K^T, 16-bit K) of back-propagated blocks, and with the update q copies
     rope = L * (12 + 3 * a) * d + nb * 3 * a * d + (nb * 2 * a * d if update else 0)
-    b = {"embed": T * (a + 4) * d, "rmsnorm": T * rms, "qknorm_rope_ring": T * rope,
+    b = {"embed": T * (a + 4) * d + (T * 8 * d if grouped else 0), "rmsnorm": T * rms, "qknorm_rope_ring": T * rope,
          "ce_reduce": T * (8 * P + 12)}
     if update and nu > 0:
         b.update({
