@@ -219,3 +219,30 @@ def test_n_update_extremes(n_update, L):
     ol, of, w = run_oracle(cfg, tok)
     dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, w), f"nu={n_update}/L={L}")
     assert dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
+
+
+@pytest.mark.parametrize("dtype,hd,T", [("fp32", 16, 2 * 8192 + 300), ("bf16", 64, 8192 + 300)])
+def test_frozen_prefix_over_several_groups(dtype, hd, T):
+    # T spans several groups of 8192 tokens (the last one ragged), so the blocks below the
+    # updated ones run ahead over each group and the chunks pick their rows from it
+    cfg = mid(hd, dtype=dtype, T=T, L=3, n_update=2, V=512, k=256, b=256)
+    say(f"case: frozen prefix over groups {dtype} hd={hd} T={T} L=3 n_u=2 b=256")
+    tok = rand_tokens(T + 1, cfg.vocab, seed=21)
+    sess, w = gpu_session(cfg)
+    gl, gf = run_gpu(sess, tok)
+    ol, of, wn = run_oracle(cfg, tok)
+    dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, wn), f"groups {dtype}")
+    if dtype == "fp32":
+        assert dl <= 1e-4 and wr <= 1e-5 and dwr <= 1e-3
+    else:
+        assert dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
+    # the number of rows of the group a position falls in does not change its result:
+    # shorter runs (one group of fewer rows; a second group of three chunks) reproduce the
+    # long run's losses bit for bit.  A ragged last chunk of a few rows may take other
+    # kernels in the updated blocks, so only the positions before it are compared there.
+    b = cfg.chunk
+    for n, m in [(20 * b + 17, 20 * b + 17), (8192 + 3 * b, 8192 + 3 * b), (8192 + 3 * b + 5, 8192 + 3 * b)]:
+        if n < T:
+            l_p, _ = run_gpu(sess, tok[:n + 1])
+            bad = np.nonzero(l_p[:m] != gl[:m])[0]
+            assert bad.size == 0, (n, bad[:5])
