@@ -130,6 +130,8 @@ def algorithmic_bytes(cfg, T, update=True):
             # gate/up pre-activations and dhmid in, dgate/dup out (2F units above the lowest block)
             "swiglu_bwd": T * 5 * a * (nb * 2 * F + F),
             "qknorm_rope_bwd": T * nb * (24 + 3 * a) * d,
+            # cross-entropy gradient from the fp32 logits the LM-head GEMM kept: read z, write dz
+            "gemm_dlogits": T * V * (4 + a),
             "attn_bwd_pre": T * nb * (3 * a * d + 4 * H),
             # activations dy, hmid, dgu, m (read + write) per token
             "transpose": nu * T * 2 * a * (2 * d + 3 * F),

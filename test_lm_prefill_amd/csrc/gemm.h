@@ -11,7 +11,8 @@ enum GemmEpi {
   EPI_SWIGLU = 3,    // C (T)[m, unit] = silu(gate) * up over 16-row interleaved gate/up
                      // blocks of B; C2 (T, optional) = raw gate/up pre-activations
   EPI_CE = 4,        // per-row partial (max, sum exp) over the tile's columns and the
-                     // label logit -> part / zlab   (cross-entropy, first pass)
+                     // label logit -> part / zlab   (cross-entropy, first pass); when Cf is
+                     // set, also Cf (fp32) = acc, the logits
   EPI_DLOGITS = 5,   // C (T) = (exp(acc - lse[m]) - [n + col_off == label]) * alpha
   EPI_SGD = 6,       // Cf (fp32 master) -= alpha * acc; C (T) = hi = round(c_scale * Cf) and,
                      // when C2 is set, C2 (T) = round(c_scale * Cf - hi): the working copy as

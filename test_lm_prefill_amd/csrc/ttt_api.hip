@@ -126,7 +126,8 @@ struct ttt_handle {
   // h_lead [B][G][d].  G = 0: no grouping (every chunk step runs all blocks).
   int G = 0, Lf = 0;
   float *h_lead = nullptr;
-  int *lead_n = nullptr;  // device: rows per sequence of the last frozen-prefix pass (G, or fewer at the end)
+  int *lead_n = nullptr;
+  float *zlog = nullptr;  // [B b][V] fp32 logits of the chunk, kept by the LM-head GEMM for the backward  // device: rows per sequence of the last frozen-prefix pass (G, or fewer at the end)
   float *attn_ws = nullptr;
   std::vector<Saved> saved;
   // graphs: [0] update, [1] no-update
@@ -492,7 +493,12 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
     g.part_ld = h->P;
     g.zlab = h->zlab;
     if (mode == MODE_GREEDY) g.part_arg = h->part_arg;
-    gemm(h, K_GEMM_HEAD_CE, true, true, EPI_CE, g, st, true);
+    const bool keep = update && h->nu > 0;  // keep the fp32 logits for the backward
+    if (keep) {
+      g.Cf = h->zlog;
+      g.ldcf = h->V;
+    }
+    gemm(h, K_GEMM_HEAD_CE, true, true, EPI_CE, g, st, true, keep);
   }
   {
     PROF(K_CE_REDUCE);
@@ -510,15 +516,10 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
     for (int v0 = 0, sl = 0; v0 < h->V; v0 += h->Vs, ++sl) {
       const int vs = std::min(h->Vs, h->V - v0);
       {
-        GemmArgs g = gargs(h->nf, d, off(h->lm_head, (size_t)v0 * d * es), d, Bn, vs, d);
-        g.C = h->dz;
-        g.ldc = h->Vs;
-        g.rowf = h->lse;
-        g.rowi = h->labs;
-        g.pos0 = h->zero;
-        g.col_off = v0;
-        g.alpha = h->gscale / (float)n;
-        gemm(h, K_GEMM_DLOGITS, true, true, EPI_DLOGITS, g, st, true);  // logits recomputed as in the forward
+        PROF(K_GEMM_DLOGITS);
+        HIPCHK(dlogits_launch(dt, h->zlog + v0, h->V, h->lse, h->labs, h->zero, v0, h->gscale / (float)n, h->dz,
+                              h->Vs, Bn, vs, st));
+        h->launches++;
       }
       {
         // B[n = model dim][k = vocab] from the transposed head [d][V]
@@ -1111,6 +1112,7 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     h->rlosses = (float *)dalloc(h, c.max_tokens * sizeof(float));
     if (h->nu > 0) {
       h->dz = dalloc(h, (size_t)Bb * h->Vs * es);
+      h->zlog = (float *)dalloc(h, (size_t)Bb * h->V * 4);
       h->dn = (float *)dalloc(h, Bbd * 4);
       h->dh = (float *)dalloc(h, Bbd * 4);
       h->dy = dalloc(h, Bbd * es);
