@@ -65,6 +65,30 @@ def test_batch_each_sequence_matches_oracle(dtype, hd, T, B):
         assert dwr <= (1e-3 if dtype == "fp32" else 5e-2)
 
 
+def test_batch_over_several_groups():
+    # two sequences of 4796 tokens in 256-token chunks: the frozen-prefix pass takes groups of
+    # 4096 tokens per sequence (8192 rows over both), so each sequence spans a whole group and a
+    # ragged one, and every chunk picks its rows from its own sequence's part of the group
+    from oracle.ttt_oracle import Oracle
+    from test_lm_prefill_amd import Session
+    T, B = 4096 + 700, 2
+    cfg = cfg_b(dtype="fp32", hd=64, T=T, b=256, V=512)
+    say(f"case: batch over groups fp32 T={T} B={B} b=256")
+    w = make_weights_torch(cfg, "cuda")
+    wn = make_weights_np(cfg)
+    tok = batch_tokens(B, T + 1, cfg.vocab, seed=91)
+    sess = Session(cfg, w, max_tokens=T, n_seq=B)
+    gl, gf = _run(sess, tok)
+    sess.close()
+    for s in range(B):
+        ol, W = Oracle(cfg, wn).prefill(tok[s])
+        of = [x for ws in W for x in ws]
+        dl, wr, dwr = compare(cfg, gl[s], gf[s], ol, of, fast_init(cfg, wn), f"batch groups seq {s}")
+        assert dl <= 1e-4
+        assert wr <= 1e-5
+        assert dwr <= 1e-3
+
+
 def test_batch_invariants():
     from test_lm_prefill_amd import Session
     cfg = cfg_b(T=520)
