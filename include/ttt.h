@@ -43,7 +43,8 @@ typedef enum {
   TTT_ENOMEM = -2,        /* device allocation failed */
   TTT_EHIP = -3,          /* a HIP runtime call failed (text in ttt_last_error) */
   TTT_EUNSUPPORTED = -4,  /* shape not supported by the compiled kernels (e.g. head_dim) */
-  TTT_ENONFINITE = -5     /* a recorded loss was NaN or infinite (checked after the prefill) */
+  TTT_ENONFINITE = -5     /* a recorded loss or an updated fast weight was NaN or infinite
+                             (checked after the prefill, see ttt_check_finite) */
 } ttt_status;
 
 typedef enum { TTT_FP32 = 0, TTT_BF16 = 1 } ttt_dtype;
@@ -182,12 +183,20 @@ ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float 
 ttt_status ttt_decode(ttt_handle *h, int64_t n_steps, const int32_t *d_forced, int32_t *d_tokens_out,
                       float *d_losses_out, float *const *d_fast_out, uint32_t flags, void *stream);
 
-/* Synchronises `stream` and returns TTT_ENONFINITE if any loss of the last
- * prefill or decode on this handle was NaN or infinite, TTT_OK otherwise. */
+/* Synchronises `stream` and returns TTT_ENONFINITE if, in the last prefill or
+ * decode on this handle, any recorded loss was NaN or infinite or any fast
+ * weight after its inner updates was (Algorithm 1 steps 3.3-3.5: the fp32
+ * master copies hold W_0 - eta * the sum of every step's gradient, so a
+ * non-finite gradient of any chunk leaves a non-finite weight behind; they are
+ * checked after the last update), TTT_OK otherwise.  The kernels finish
+ * normally either way; only the status reports the condition. */
 ttt_status ttt_check_finite(ttt_handle *h, void *stream);
 
-/* Number of chunks and of kernel launches per chunk of the last prefill (host values). */
-ttt_status ttt_get_stats(const ttt_handle *h, int64_t *chunks_last, int64_t *launches_per_chunk);
+/* Host values of the last prefill: its duration in ms between events recorded on
+ * its stream at the start and at the end of ttt_prefill's work (waits for the
+ * end event; 0 before any prefill), the number of chunks and the kernel launches
+ * of one chunk step.  Each out pointer may be NULL. */
+ttt_status ttt_get_stats(ttt_handle *h, double *ms_last, int64_t *chunks_last, int64_t *launches_per_chunk);
 
 /*
  * Kernel timing (diagnostics).  While enabled, ttt_prefill launches kernel by

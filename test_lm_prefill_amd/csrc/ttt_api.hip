@@ -144,6 +144,9 @@ struct ttt_handle {
   hipStream_t cap = nullptr;
   int64_t chunks_last = 0;
   int64_t launches = 0;
+  // events on the caller's stream at the start and the end of the last prefill
+  hipEvent_t ev_pf[2] = {nullptr, nullptr};
+  bool ev_pf_set = false;
   // kernel-class timing (diagnostics)
   bool prof = false;
   std::vector<hipEvent_t> ev;
@@ -746,6 +749,17 @@ void reset_fast(ttt_handle *h, hipStream_t st) {
   }
 }
 
+// flag |= 1 if any fp32 master fast weight of any sequence is NaN or infinite: the
+// masters are W_0 - eta * (sum of every update so far), so a non-finite gradient in
+// any chunk leaves a non-finite entry behind.
+void check_masters(ttt_handle *h, hipStream_t st) {
+  const long gu = (long)h->B * 2 * h->F * h->d, dd = (long)h->B * h->d * h->F;
+  for (int u = 0; u < h->nu; ++u) {
+    HIPCHK(finite_check_launch(h->m_gu[u], gu, h->flag, st));
+    HIPCHK(finite_check_launch(h->m_d[u], dd, h->flag, st));
+  }
+}
+
 ttt_status fail_hip(ttt_handle *h, const HipFail &f) {
   char buf[512];
   snprintf(buf, sizeof(buf), "HIP error %d (%s) in %s", (int)f.e, hipGetErrorString(f.e), f.what);
@@ -763,6 +777,8 @@ void free_all(ttt_handle *h) {
   for (int i = 0; i < 6; ++i)
     if (h->gexec[i]) hipGraphExecDestroy(h->gexec[i]);
   if (h->cap) hipStreamDestroy(h->cap);
+  for (int i = 0; i < 2; ++i)
+    if (h->ev_pf[i]) hipEventDestroy(h->ev_pf[i]);
   for (void *p : h->allocs) hipFree(p);
   h->allocs.clear();
 }
@@ -1174,6 +1190,8 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     for (auto &z : h->zero_list) HIPCHK(hipMemsetAsync(z.first, 0, z.second, st));
     HIPCHK(hipStreamSynchronize(st));
     HIPCHK(hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking));
+    HIPCHK(hipEventCreate(&h->ev_pf[0]));
+    HIPCHK(hipEventCreate(&h->ev_pf[1]));
   } catch (const HipFail &f) {
     ttt_status s = fail_hip(h, f);
     hipStreamSynchronize(st);
@@ -1199,6 +1217,8 @@ ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float 
   hipStream_t st = (hipStream_t)stream;
   const int b = h->b;
   try {
+    h->ev_pf_set = false;
+    HIPCHK(hipEventRecord(h->ev_pf[0], st));
     if (d_tokens)
       HIPCHK(hipMemcpy2DAsync(h->tok, h->ld_tok * sizeof(int), d_tokens, (size_t)(T + 1) * sizeof(int),
                               (size_t)(T + 1) * sizeof(int), h->B, hipMemcpyDeviceToDevice, st));
@@ -1226,7 +1246,10 @@ ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float 
       for (int s = 0; s < h->B; ++s)
         HIPCHK(finite_check_launch(h->losses + (size_t)s * h->cfg.max_tokens, T, h->flag, st));
     }
+    if (update && T > 0) check_masters(h, st);
     if (d_fast_out) copy_fast_out(h, d_fast_out, st);
+    HIPCHK(hipEventRecord(h->ev_pf[1], st));
+    h->ev_pf_set = true;
     h->len = T;
     h->dstart = T;
     h->have_state = d_tokens != nullptr;  // the token at position T is known
@@ -1279,6 +1302,7 @@ ttt_status ttt_decode(ttt_handle *h, int64_t n_steps, const int32_t *d_forced, i
                             st));
       HIPCHK(finite_check_launch(h->losses + len0, n_steps, h->flag, st));
     }
+    if (update && h->dstart > len0) check_masters(h, st);
     if (d_fast_out) copy_fast_out(h, d_fast_out, st);
   } catch (const HipFail &f) {
     h->have_state = false;
@@ -1293,13 +1317,23 @@ ttt_status ttt_check_finite(ttt_handle *h, void *stream) {
   hipError_t e = hipMemcpyAsync(&flag, h->flag, sizeof(int), hipMemcpyDeviceToHost, (hipStream_t)stream);
   if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(h, HipFail{e, "ttt_check_finite"});
-  return flag ? fail(h, TTT_ENONFINITE, "non-finite loss recorded") : TTT_OK;
+  return flag ? fail(h, TTT_ENONFINITE, "non-finite loss or fast weight") : TTT_OK;
 }
 
-ttt_status ttt_get_stats(const ttt_handle *h, int64_t *chunks_last, int64_t *launches_per_chunk) {
-  if (!h) return TTT_EINVAL;
+ttt_status ttt_get_stats(ttt_handle *h, double *ms_last, int64_t *chunks_last, int64_t *launches_per_chunk) {
+  if (!h) return fail(nullptr, TTT_EINVAL, "null handle");
   if (chunks_last) *chunks_last = h->chunks_last;
   if (launches_per_chunk) *launches_per_chunk = h->launches;
+  if (ms_last) {
+    *ms_last = 0.0;
+    if (h->ev_pf_set) {
+      float ms = 0.f;
+      hipError_t e = hipEventSynchronize(h->ev_pf[1]);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, h->ev_pf[0], h->ev_pf[1]);
+      if (e != hipSuccess) return fail_hip(h, HipFail{e, "ttt_get_stats"});
+      *ms_last = ms;
+    }
+  }
   return TTT_OK;
 }
 

@@ -66,7 +66,8 @@ def lib():
         L.ttt_decode.restype = ctypes.c_int
         L.ttt_check_finite.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.ttt_check_finite.restype = ctypes.c_int
-        L.ttt_get_stats.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+        L.ttt_get_stats.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
+                                    ctypes.POINTER(ctypes.c_int64)]
         L.ttt_get_stats.restype = ctypes.c_int
         L.ttt_set_kernel_timing.argtypes = [ctypes.c_void_p, ctypes.c_int]
         L.ttt_set_kernel_timing.restype = ctypes.c_int
@@ -128,9 +129,10 @@ def ttt_check_finite(handle, stream=None):
 
 
 def ttt_get_stats(handle):
-    a, b = ctypes.c_int64(), ctypes.c_int64()
-    _check(lib().ttt_get_stats(handle, ctypes.byref(a), ctypes.byref(b)), handle)
-    return a.value, b.value
+    """Returns (ms of the last prefill, its chunks, kernel launches per chunk step)."""
+    ms, a, b = ctypes.c_double(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().ttt_get_stats(handle, ctypes.byref(ms), ctypes.byref(a), ctypes.byref(b)), handle)
+    return ms.value, a.value, b.value
 
 
 def ttt_set_kernel_timing(handle, enable):

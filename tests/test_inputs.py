@@ -61,3 +61,18 @@ def test_markov_tokens_deterministic():
     b = make_tokens(cfg, seed=1)
     assert len(a) == cfg.seq_len + 1 and np.array_equal(a, b)
     assert a.max() < 256
+
+
+def test_random_gains_distinct_and_bf16_exact():
+    from ttt_inputs import TTTConfig, random_gains, round_bf16_np
+    cfg = TTTConfig("g", 3, 256, 4, 64, 512, 1024, 600, 256, 128, 2, 0.5, "bf16")
+    g = random_gains(cfg, 1, qk_range=(0.8, 1.05))
+    assert len(g) == 3 * 4 + 1
+    vals = [tuple(v[:4]) for v in g.values()]
+    assert len(set(vals)) == len(vals)
+    for k, v in g.items():
+        lo, hi = (0.8, 1.05) if k.endswith(("q_norm", "k_norm")) else (0.5, 1.5)
+        assert lo - 1e-2 <= v.min() and v.max() <= hi + 1e-2 and np.std(v) > 0.05 * (hi - lo)
+        assert np.array_equal(v, round_bf16_np(v))
+    g2 = random_gains(cfg, 1, qk_range=(0.8, 1.05))
+    assert all(np.array_equal(g[k], g2[k]) for k in g)

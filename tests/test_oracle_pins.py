@@ -76,6 +76,53 @@ def test_pin1_finite_differences(n_u, chunk_idx):
     assert rel < 1e-6, rel
 
 
+def test_pin1_ragged_last_chunk_finite_differences():
+    """A short last chunk (T = 29, b = 8: the last chunk has n = 5 positions): the
+    update's gradient is that of the mean loss over the chunk's own n positions
+    (notes section 5, Eq. 9 averages over the chunk's targets; the pages leave a
+    partial chunk open, and the plain reading is the mean over the targets it has).
+    Central differences of numpy's mean over the n losses, with the window state of
+    the earlier chunks held fixed, against the oracle's hand-written gradient; an
+    oracle that divided by b instead of n would be off by n/b."""
+    cfg = micro(n_update=2, seq_len=29)
+    w = rand_gains(cfg, make_weights_np(cfg, seed=23))
+    tok = rand_tokens(cfg.seq_len + 1, cfg.vocab, seed=24)
+    orc = Oracle(cfg, w)
+    _, _, trace = orc.prefill(tok, return_trace=True)
+    tr = trace[-1]
+    W, cache, s0, n = tr["W_before"], tr["cache"], tr["s0"], tr["n"]
+    assert n == 5 and s0 == 24 and len(cache[-1]["pos"]) > 0
+    _, saved, _ = orc.chunk_forward(W, cache, tok[s0:s0 + n], tok[s0 + 1:s0 + n + 1], s0)
+    G = orc.chunk_grad(W, saved)
+
+    def mean_loss():
+        l_chunk, _, _ = orc.chunk_forward(W, cache, tok[s0:s0 + n], tok[s0 + 1:s0 + n + 1], s0)
+        return float(np.mean(l_chunk))
+
+    h = 1e-5
+    num, ana = [], []
+    for u in range(cfg.n_update):
+        for t in range(3):
+            flat = W[u][t].reshape(-1)
+            for j in range(flat.size):
+                old = flat[j]
+                flat[j] = old + h
+                fp = mean_loss()
+                flat[j] = old - h
+                fm = mean_loss()
+                flat[j] = old
+                num.append((fp - fm) / (2 * h))
+                ana.append(G[u][t].reshape(-1)[j])
+    num, ana = np.array(num), np.array(ana)
+    rel = np.linalg.norm(num - ana) / np.linalg.norm(ana)
+    assert rel < 1e-6, rel
+    # the update the prefill applied is eta times that gradient
+    _, WN = orc.prefill(tok)
+    for ws, w0, g in zip(WN, W, G):
+        for x, y, gg in zip(ws, w0, g):
+            np.testing.assert_allclose(x, y - cfg.eta * gg, rtol=0, atol=1e-14)
+
+
 # ----------------------------------------------------------------------------- Pin 2 / 3
 def _static_losses_torch(cfg, w, tok, mask):
     fast = torch_ref.fast_tensors(torch_ref.fast_from_weights(cfg, w))
@@ -202,6 +249,32 @@ def test_pin6_one_chunk_matches_autograd(hd, d, k):
         for t in range(3):
             w1_ref = fast[u][t].detach().numpy() - cfg.eta * fast[u][t].grad.numpy()
             dw_ref = w1_ref - fast[u][t].detach().numpy()
+            dw = W1[u][t] - fast[u][t].detach().numpy()
+            num += np.sum((dw - dw_ref) ** 2)
+            den += np.sum(dw_ref ** 2)
+    assert math.sqrt(num / den) < 1e-9
+
+
+@pytest.mark.parametrize("T,b", [(100, 128), (77, 256)])
+def test_pin6_partial_single_chunk_matches_autograd(T, b):
+    """One chunk shorter than b (T not a multiple of 64): W_1 = W_0 - eta * grad of
+    the mean over its T losses, with grad from torch autograd of torch's mean over
+    the T cross-entropies (notes section 5, Eq. 9; reading: a partial chunk is
+    averaged over its own positions)."""
+    hd, d = 64, 256
+    cfg = TTTConfig("pin6r", 3, d, d // hd, hd, 704, 1024, T, 64, b, 2, 0.05, "fp32", init_std=0.05)
+    w = rand_gains(cfg, make_weights_np(cfg, seed=26))
+    tok = rand_tokens(T + 1, cfg.vocab, seed=27)
+    losses, W1 = Oracle(cfg, w).prefill(tok)
+    fast = torch_ref.fast_tensors(torch_ref.fast_from_weights(cfg, w), requires_grad=True)
+    ref = torch_ref.forward_losses(cfg, w, tok, fast, mask="band")
+    assert ref.shape[0] == T
+    assert np.max(np.abs(losses - ref.detach().numpy())) < 1e-10
+    ref.mean().backward()
+    num = den = 0.0
+    for u in range(cfg.n_update):
+        for t in range(3):
+            dw_ref = -cfg.eta * fast[u][t].grad.numpy()
             dw = W1[u][t] - fast[u][t].detach().numpy()
             num += np.sum((dw - dw_ref) ** 2)
             den += np.sum(dw_ref ** 2)

@@ -131,30 +131,51 @@ def tensor_specs(cfg):
     return specs
 
 
-def make_weights_np(cfg, seed=0, names=None):
-    """All weights as float32 numpy arrays (bf16-valued for bf16 workloads)."""
+def random_gains(cfg, seed, norm_range=(0.5, 1.5), qk_range=None):
+    """Non-unit norm gains for tests: each gain vector (block norms, final norm, QK-norm)
+    drawn uniform in its range from its own PCG64 stream seeded by (seed, position in
+    tensor_specs), rounded to bf16 so that bf16 and fp32 workloads hold the same values.
+    qk_range (default: norm_range) applies to q_norm and k_norm."""
+    qk_range = norm_range if qk_range is None else qk_range
+    out = {}
+    for i, (name, _, shape, kind) in enumerate(tensor_specs(cfg)):
+        if kind != "gain":
+            continue
+        lo, hi = qk_range if name.endswith(("q_norm", "k_norm")) else norm_range
+        g = np.random.Generator(np.random.PCG64([seed, i])).uniform(lo, hi, shape).astype(np.float32)
+        out[name] = round_bf16_np(g)
+    return out
+
+
+def make_weights_np(cfg, seed=0, names=None, gains=None):
+    """All weights as float32 numpy arrays (bf16-valued for bf16 workloads).  gains:
+    None for unit norm gains, or a dict from random_gains replacing them."""
     bf16 = cfg.dtype == "bf16"
     out = {}
     for name, tid, shape, kind in tensor_specs(cfg):
         if names is not None and name not in names:
             continue
         if kind == "gain":
-            out[name] = np.ones(shape, dtype=np.float32)
+            out[name] = gains[name].copy() if gains is not None else np.ones(shape, dtype=np.float32)
         else:
             out[name] = draw_np(seed, tid, shape, cfg.init_std, bf16)
     return out
 
 
-def make_weights_torch(cfg, device, seed=0):
+def make_weights_torch(cfg, device, seed=0, gains=None):
     """Weights as torch tensors on `device`: the working dtype for frozen tensors,
-    float32 (bf16-valued in bf16 workloads) for the fast-weight initial values."""
+    float32 (bf16-valued in bf16 workloads) for the fast-weight initial values.
+    gains as for make_weights_np."""
     import torch
     bf16 = cfg.dtype == "bf16"
     wdt = torch.bfloat16 if bf16 else torch.float32
     out = {}
     for name, tid, shape, kind in tensor_specs(cfg):
         if kind == "gain":
-            out[name] = torch.ones(shape, dtype=wdt, device=device)
+            if gains is not None:
+                out[name] = torch.from_numpy(gains[name]).to(device=device, dtype=wdt)
+            else:
+                out[name] = torch.ones(shape, dtype=wdt, device=device)
         elif kind == "fast":
             out[name] = draw_torch(seed, tid, shape, cfg.init_std, bf16, device).to(torch.float32)
         else:
