@@ -156,6 +156,30 @@ ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float 
                        float *const *d_fast_out, uint32_t flags, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): ttt_prefill with the
+ * same arguments, results and errors, except that
+ *   - the partial results of split-K products and of key-range-split attention
+ *     go to a static device array of the library (160 MiB per device, held from
+ *     the library's load until the process ends: 96 MiB for the product
+ *     partials, 64 MiB for the attention partials) instead of the handle's
+ *     workspaces; TTT_EUNSUPPORTED, with nothing enqueued, when the handle's
+ *     shapes need more (the 2.7B workload needs 80 and 41 MiB);
+ *   - every kernel is launched one by one on `stream` (no HIP graph is captured
+ *     or instantiated) and no event is recorded, so the call allocates nothing
+ *     and ttt_get_stats reports no duration for it (0 ms);
+ *   - TTT_EINVAL when kernel timing is on or the current device is not the
+ *     handle's.
+ * The handle's own state (created by ttt_create) is used as by ttt_prefill.
+ * Every call on a device shares that device's array: calls that overlap in
+ * time on one device (on different streams, or from several threads) race and
+ * give undefined results.  The HIP runtime may load the kernels' code on their
+ * first launch; a caller that must not see that does one ttt_prefill first.
+ */
+ttt_status ttt_prefill_noalloc(ttt_handle *h, const int32_t *d_tokens, int64_t T, float *d_losses,
+                               float *const *d_fast_out, uint32_t flags, void *stream);
+
+/*
  * Algorithm 3 of the notes (generation with periodic updates), continuing the
  * sequence that the last ttt_prefill (given tokens), or ttt_decode, on this
  * handle left: its fast weights, its window of keys/values and its length P

@@ -20,6 +20,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -28,9 +29,27 @@
 #include "elem.h"
 #include "gemm.h"
 
+// ----------------------------------------------------------------------------
+// Static scratch for ttt_prefill_noalloc: the partial results of split-K products
+// (first SCRATCH_GEMM_FLOATS floats) and of key-range-split attention (the rest)
+// live in this array instead of the handle's workspaces.  Each device holds its own
+// copy from the library's load until the process ends.  In host code `scratch`
+// names a host-side stand-in, never the device memory: its device address is taken
+// once per device with hipGetSymbolAddress (scratch_setup) and only that address
+// is passed to kernels.
+constexpr size_t SCRATCH_BYTES = (size_t)160 << 20;
+constexpr size_t SCRATCH_GEMM_FLOATS = (size_t)24 << 20;  // 96 MiB of split-K partials
+constexpr size_t SCRATCH_ATTN_FLOATS = SCRATCH_BYTES / 4 - SCRATCH_GEMM_FLOATS;  // 64 MiB
+static __device__ __align__(256) float scratch[SCRATCH_BYTES / 4];
+
 namespace {
 
 thread_local std::string g_thread_err;
+
+// device address of `scratch` per device (nullptr until set up), guarded by g_scratch_mu
+constexpr int SCRATCH_MAX_DEV = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[SCRATCH_MAX_DEV] = {};
 
 struct LayerBuf {
   void *attn_norm = nullptr, *wqkv = nullptr, *wo = nullptr, *q_norm = nullptr, *k_norm = nullptr,
@@ -129,6 +148,10 @@ struct ttt_handle {
   int *lead_n = nullptr;
   float *zlog = nullptr;  // [B b][V] fp32 logits of the chunk, kept by the LM-head GEMM for the backward  // device: rows per sequence of the last frozen-prefix pass (G, or fewer at the end)
   float *attn_ws = nullptr;
+  size_t attn_ws_n = 0;      // floats of attn_ws
+  int dev = 0;               // device the handle lives on
+  float *scratch = nullptr;  // this device's static scratch (device address), or nullptr
+  std::string scratch_err;   // why it is unavailable
   std::vector<Saved> saved;
   // graphs: [0] update, [1] no-update
   // captured steps: full-chunk prefill with / without update, decode step greedy /
@@ -773,6 +796,31 @@ ttt_status fail(ttt_handle *h, ttt_status s, const std::string &msg) {
   return s;
 }
 
+// Once per device, with that device current: the device address of the static
+// scratch, cleared to zeros (finite start values for partials that masked lanes
+// read before a split overwrites them).  Failures are kept in h->scratch_err; only
+// ttt_prefill_noalloc needs the scratch.
+void scratch_setup(ttt_handle *h, hipStream_t st) {
+  if (h->dev < 0 || h->dev >= SCRATCH_MAX_DEV) {
+    h->scratch_err = "device index beyond the static scratch table";
+    return;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[h->dev]) {
+    void *p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e == hipSuccess && !p) e = hipErrorInvalidSymbol;
+    if (e == hipSuccess) e = zero_launch(p, SCRATCH_BYTES, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+      h->scratch_err = std::string("static scratch set-up failed: ") + hipGetErrorString(e);
+      return;
+    }
+    g_scratch_ptr[h->dev] = reinterpret_cast<float *>(p);
+  }
+  h->scratch = g_scratch_ptr[h->dev];
+}
+
 void free_all(ttt_handle *h) {
   for (int i = 0; i < 6; ++i)
     if (h->gexec[i]) hipGraphExecDestroy(h->gexec[i]);
@@ -1164,7 +1212,8 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     {
       int smax = h->attn_split;
       for (const LayerBuf &lw : h->layers) smax = std::max(smax, lw.fsplit);
-      h->attn_ws = (float *)dalloc(h, attn_ws_floats(smax, b, d, h->H, b) * 4);
+      h->attn_ws_n = attn_ws_floats(smax, b, d, h->H, b);
+      h->attn_ws = (float *)dalloc(h, h->attn_ws_n * 4);
       // a decode step has one query per head: split its window into up to 32 ranges of at
       // least 8 key tiles each (a work-group streams its tiles one after another)
       int ds = 32;
@@ -1192,6 +1241,8 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     HIPCHK(hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking));
     HIPCHK(hipEventCreate(&h->ev_pf[0]));
     HIPCHK(hipEventCreate(&h->ev_pf[1]));
+    HIPCHK(hipGetDevice(&h->dev));
+    scratch_setup(h, st);
   } catch (const HipFail &f) {
     ttt_status s = fail_hip(h, f);
     hipStreamSynchronize(st);
@@ -1203,22 +1254,52 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
   return TTT_OK;
 }
 
-ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float *d_losses, float *const *d_fast_out,
-                       uint32_t flags, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Algorithm 1 over every sequence of the handle.  noalloc: the split-K and attention
+// partials go to this device's static scratch, every kernel is launched one by one
+// (no graph is captured or instantiated) and no event is recorded, so the call
+// allocates nothing; the results are the same bits as the graph-replayed call.
+ttt_status prefill_impl(ttt_handle *h, const int32_t *d_tokens, int64_t T, float *d_losses,
+                        float *const *d_fast_out, uint32_t flags, void *stream, bool noalloc) {
   if (!h) return fail(nullptr, TTT_EINVAL, "null handle");
   if (T < 0 || T > h->cfg.max_tokens) return fail(h, TTT_EINVAL, "T out of range [0, max_tokens]");
   if (T > 0 && (!d_tokens || !d_losses)) return fail(h, TTT_EINVAL, "null tokens or losses");
   if (d_fast_out)
     for (int i = 0; i < 3 * h->nu * h->B; ++i)
       if (!d_fast_out[i]) return fail(h, TTT_EINVAL, "null entry in d_fast_out");
+  float *ws_keep = h->ws, *attn_keep = h->attn_ws;
+  if (noalloc) {
+    if (h->prof) return fail(h, TTT_EINVAL, "kernel timing is on (it creates events); disable it first");
+    if (!h->scratch) return fail(h, TTT_EHIP, "static scratch unavailable: " + h->scratch_err);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != h->dev)
+      return fail(h, TTT_EINVAL, "the current device is not the handle's device");
+    // every split-K plan keeps its partials within ws_elems floats; the attention
+    // splits within attn_ws_n
+    if (h->ws_elems > SCRATCH_GEMM_FLOATS || h->attn_ws_n > SCRATCH_ATTN_FLOATS) {
+      char buf[256];
+      snprintf(buf, sizeof(buf),
+               "shape needs %zu MiB of split-K and %zu MiB of attention partials; the static scratch holds "
+               "%zu and %zu MiB",
+               (h->ws_elems * 4) >> 20, (h->attn_ws_n * 4) >> 20, (SCRATCH_GEMM_FLOATS * 4) >> 20,
+               (SCRATCH_ATTN_FLOATS * 4) >> 20);
+      return fail(h, TTT_EUNSUPPORTED, buf);
+    }
+    h->ws = h->scratch;
+    h->attn_ws = h->scratch + SCRATCH_GEMM_FLOATS;
+  }
   flags |= h->cfg.flags;
   const bool update = !(flags & TTT_NO_UPDATE) && h->nu > 0;
-  const bool use_graph = !(flags & TTT_NO_GRAPH) && !h->prof;
+  const bool use_graph = !(flags & TTT_NO_GRAPH) && !h->prof && !noalloc;
   hipStream_t st = (hipStream_t)stream;
   const int b = h->b;
+  ttt_status ret = TTT_OK;
   try {
     h->ev_pf_set = false;
-    HIPCHK(hipEventRecord(h->ev_pf[0], st));
+    if (!noalloc) HIPCHK(hipEventRecord(h->ev_pf[0], st));
     if (d_tokens)
       HIPCHK(hipMemcpy2DAsync(h->tok, h->ld_tok * sizeof(int), d_tokens, (size_t)(T + 1) * sizeof(int),
                               (size_t)(T + 1) * sizeof(int), h->B, hipMemcpyDeviceToDevice, st));
@@ -1248,17 +1329,35 @@ ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float 
     }
     if (update && T > 0) check_masters(h, st);
     if (d_fast_out) copy_fast_out(h, d_fast_out, st);
-    HIPCHK(hipEventRecord(h->ev_pf[1], st));
-    h->ev_pf_set = true;
+    if (!noalloc) {
+      HIPCHK(hipEventRecord(h->ev_pf[1], st));
+      h->ev_pf_set = true;
+    }
     h->len = T;
     h->dstart = T;
     h->have_state = d_tokens != nullptr;  // the token at position T is known
     h->chunks_last = nfull + (tail > 0 ? 1 : 0);
   } catch (const HipFail &f) {
     h->have_state = false;
-    return fail_hip(h, f);
+    ret = fail_hip(h, f);
   }
-  return TTT_OK;
+  h->ws = ws_keep;
+  h->attn_ws = attn_keep;
+  return ret;
+}
+
+}  // namespace
+
+extern "C" {
+
+ttt_status ttt_prefill(ttt_handle *h, const int32_t *d_tokens, int64_t T, float *d_losses, float *const *d_fast_out,
+                       uint32_t flags, void *stream) {
+  return prefill_impl(h, d_tokens, T, d_losses, d_fast_out, flags, stream, false);
+}
+
+ttt_status ttt_prefill_noalloc(ttt_handle *h, const int32_t *d_tokens, int64_t T, float *d_losses,
+                               float *const *d_fast_out, uint32_t flags, void *stream) {
+  return prefill_impl(h, d_tokens, T, d_losses, d_fast_out, flags, stream, true);
 }
 
 ttt_status ttt_decode(ttt_handle *h, int64_t n_steps, const int32_t *d_forced, int32_t *d_tokens_out,

@@ -15,7 +15,7 @@ TTT_OK, TTT_EINVAL, TTT_ENOMEM, TTT_EHIP, TTT_EUNSUPPORTED, TTT_ENONFINITE = 0, 
 TTT_FP32, TTT_BF16 = 0, 1
 TTT_NO_UPDATE, TTT_NO_GRAPH = 1, 2
 
-EXPORTED = ["ttt_create", "ttt_prefill", "ttt_decode", "ttt_check_finite", "ttt_get_stats", "ttt_set_kernel_timing",
+EXPORTED = ["ttt_create", "ttt_prefill", "ttt_prefill_noalloc", "ttt_decode", "ttt_check_finite", "ttt_get_stats", "ttt_set_kernel_timing",
             "ttt_kernel_class_count", "ttt_get_kernel_time", "ttt_last_error", "ttt_destroy"]
 
 
@@ -61,6 +61,8 @@ def lib():
         L.ttt_prefill.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, _PP,
                                   ctypes.c_uint32, ctypes.c_void_p]
         L.ttt_prefill.restype = ctypes.c_int
+        L.ttt_prefill_noalloc.argtypes = L.ttt_prefill.argtypes
+        L.ttt_prefill_noalloc.restype = ctypes.c_int
         L.ttt_decode.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                  _PP, ctypes.c_uint32, ctypes.c_void_p]
         L.ttt_decode.restype = ctypes.c_int
@@ -110,6 +112,16 @@ def ttt_prefill(handle, d_tokens, T, d_losses, d_fast_out=None, flags=0, stream=
     if d_fast_out is not None:
         fo, keep = _ptr_array(d_fast_out)
     st = lib().ttt_prefill(handle, d_tokens, T, d_losses, fo, flags, stream)
+    del keep
+    _check(st, handle)
+
+
+def ttt_prefill_noalloc(handle, d_tokens, T, d_losses, d_fast_out=None, flags=0, stream=None):
+    fo = None
+    keep = None
+    if d_fast_out is not None:
+        fo, keep = _ptr_array(d_fast_out)
+    st = lib().ttt_prefill_noalloc(handle, d_tokens, T, d_losses, fo, flags, stream)
     del keep
     _check(st, handle)
 
