@@ -76,6 +76,15 @@ def algorithmic_flops(cfg, T, update=True):
     return f
 
 
+def recompute_flops(cfg, T, update=True):
+    """FLOPs the path spends again on purpose and that are not algorithmic: the head
+    backward computes each vocabulary slab's logits a second time (2 d V per token)
+    instead of keeping the [b, V] logits of the forward."""
+    if not update or cfg.n_update == 0:
+        return {}
+    return {"gemm_dlogits": 2 * cfg.d_model * cfg.vocab * T}
+
+
 def algorithmic_bytes(cfg, T, update=True):
     """Per-class HBM bytes of one prefill for the bandwidth-bound kernels: what each kernel
     must read and write given the stored layouts (fp32 residual stream and projections,
@@ -130,8 +139,6 @@ def algorithmic_bytes(cfg, T, update=True):
             # gate/up pre-activations and dhmid in, dgate/dup out (2F units above the lowest block)
             "swiglu_bwd": T * 5 * a * (nb * 2 * F + F),
             "qknorm_rope_bwd": T * nb * (24 + 3 * a) * d,
-            # cross-entropy gradient from the fp32 logits the LM-head GEMM kept: read z, write dz
-            "gemm_dlogits": T * V * (4 + a),
             "attn_bwd_pre": T * nb * (3 * a * d + 4 * H),
             # activations dy, hmid, dgu, m (read + write) per token
             "transpose": nu * T * 2 * a * (2 * d + 3 * F),
@@ -462,6 +469,7 @@ def main():
     roof = None
     kernels = {}
     hbm = algorithmic_bytes(cfg, T, update=True)
+    rflops = recompute_flops(cfg, T, update=True)
     if kt:
         tot_prof = sum(v[0] for v in kt.values())
         for nm, (ms, n) in sorted(kt.items(), key=lambda x: -x[1][0]):
@@ -471,6 +479,8 @@ def main():
             if nm in flops and ms > 0:
                 ent["tflops"] = round(flops[nm] / 1e12 / (ms / 1e3), 1)
                 ent["mfma_frac"] = round(flops[nm] / 1e12 / (ms / 1e3) / peak, 4)
+            if nm in rflops and ms > 0:  # recomputation: its rate, outside the utilisation numerator
+                ent["recompute_tflops"] = round(rflops[nm] / 1e12 / (ms / 1e3), 1)
             ub = hbm.get("update_in_gemm_dw_sgd") if nm == "gemm_dw_sgd" else None
             if (nm in hbm or ub) and ms > 0:
                 by = ub if ub else hbm[nm]

@@ -122,8 +122,10 @@ typedef struct ttt_handle ttt_handle;
  * Creates a handle on the current HIP device: validates cfg, allocates the
  * bounded state (per-layer key/value rings of k+b rows, or k+G rows for the
  * blocks below the updated ones, which run ahead over groups of G tokens;
- * activations of one chunk and of one group; the chunk's fp32 logits when
- * n_update > 0; fp32 master fast weights) and copies/repacks the weights.
+ * activations of one chunk and of one group; the cross-entropy gradient of
+ * one vocabulary slab when n_update > 0 - no logits are kept, the backward
+ * computes each slab's again; fp32 master fast weights) and copies/repacks
+ * the weights.
  * G is about 8192 tokens over all sequences, at most max_tokens rounded up to
  * a chunk, and 0 (no group pass) when that is not more than one chunk.
  * `stream` is a hipStream_t (NULL = default stream); the call synchronises it

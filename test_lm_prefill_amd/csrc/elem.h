@@ -121,10 +121,3 @@ hipError_t add_int_launch(int *p, int v, hipStream_t st);
 hipError_t zero_launch(void *p, size_t bytes, hipStream_t st);
 // flag |= 1 if any of x[0..n) is not finite.
 hipError_t finite_check_launch(const float *x, long n, int *flag, hipStream_t st);
-
-// dz[m][c] = (exp(z[m][c] - lse[m]) - [c + col_off == label of m]) * alpha for m < M, c < N
-// (N % 4 == 0): the cross-entropy gradient of one vocabulary slab from the fp32 logits z
-// (row stride ldz) the forward kept, label of m = labels[*pos0 + m]; dz has row stride ldc
-// and is written as fp32 (dtype 0) or bf16 (dtype 1).
-hipError_t dlogits_launch(int dtype, const float *z, long ldz, const float *lse, const int *labels, const int *pos0,
-                          int col_off, float alpha, void *dz, long ldc, int M, int N, hipStream_t st);

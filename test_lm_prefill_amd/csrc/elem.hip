@@ -807,36 +807,3 @@ hipError_t finite_check_launch(const float *x, long n, int *flag, hipStream_t st
   hipLaunchKernelGGL(finite_check_kernel, dim3(blocks), dim3(256), 0, st, x, n, flag);
   return hipGetLastError();
 }
-
-template <typename T>
-__global__ void dlogits_kernel(const float *z, long ldz, const float *lse, const int *labels, const int *pos0,
-                               int col_off, float alpha, T *dz, long ldc, int M, int N4) {
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long)M * N4) return;
-  const int m = idx / N4, c = (idx % N4) * 4;
-  const int lab = labels[*pos0 + m];
-  const float l = lse[m];
-  const float4 v = *reinterpret_cast<const float4 *>(z + (long)m * ldz + c);
-  const float x[4] = {v.x, v.y, v.z, v.w};
-  float d[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float p = __expf(x[r] - l);
-    d[r] = (p - ((c + r + col_off == lab) ? 1.f : 0.f)) * alpha;
-  }
-  store4<T>(dz + (long)m * ldc + c, d);
-}
-
-hipError_t dlogits_launch(int dtype, const float *z, long ldz, const float *lse, const int *labels, const int *pos0,
-                          int col_off, float alpha, void *dz, long ldc, int M, int N, hipStream_t st) {
-  if (M <= 0 || N <= 0) return hipSuccess;
-  if (N % 4 != 0 || ldz % 4 != 0 || ldc % 4 != 0) return hipErrorInvalidValue;
-  const long tot = (long)M * (N / 4);
-  if (dtype == 0)
-    hipLaunchKernelGGL(dlogits_kernel<float>, dim3(blocks_for(tot)), dim3(256), 0, st, z, ldz, lse, labels, pos0,
-                       col_off, alpha, (float *)dz, ldc, M, N / 4);
-  else
-    hipLaunchKernelGGL(dlogits_kernel<bf16_t>, dim3(blocks_for(tot)), dim3(256), 0, st, z, ldz, lse, labels, pos0,
-                       col_off, alpha, (bf16_t *)dz, ldc, M, N / 4);
-  return hipGetLastError();
-}

@@ -207,16 +207,6 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const GemmArgs g) {
     for (int j = 0; j < 4; ++j) {
       const int m = m0 + wm * 64 + j * 16 + lr;
       const int lab = (m < g.M) ? g.rowi[lab_base + m] : -1;
-      if (g.Cf && m < g.M) {  // the fp32 logits, kept for the backward
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = n0 + wn * 64 + i * 16 + g4;
-          if (n < g.N) {
-            const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-            store4<float>(g.Cf + (long)m * g.ldcf + n, v);
-          }
-        }
-      }
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i)

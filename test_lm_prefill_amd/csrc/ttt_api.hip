@@ -145,8 +145,7 @@ struct ttt_handle {
   // h_lead [B][G][d].  G = 0: no grouping (every chunk step runs all blocks).
   int G = 0, Lf = 0;
   float *h_lead = nullptr;
-  int *lead_n = nullptr;
-  float *zlog = nullptr;  // [B b][V] fp32 logits of the chunk, kept by the LM-head GEMM for the backward  // device: rows per sequence of the last frozen-prefix pass (G, or fewer at the end)
+  int *lead_n = nullptr;  // device: rows per sequence of the last frozen-prefix pass (G, or fewer at the end)
   float *attn_ws = nullptr;
   size_t attn_ws_n = 0;      // floats of attn_ws
   int dev = 0;               // device the handle lives on
@@ -519,12 +518,10 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
     g.part_ld = h->P;
     g.zlab = h->zlab;
     if (mode == MODE_GREEDY) g.part_arg = h->part_arg;
-    const bool keep = update && h->nu > 0;  // keep the fp32 logits for the backward
-    if (keep) {
-      g.Cf = h->zlog;
-      g.ldcf = h->V;
-    }
-    gemm(h, K_GEMM_HEAD_CE, true, true, EPI_CE, g, st, true, keep);
+    // with an update the backward computes these logits again slab by slab with the tiled
+    // kernel: the forward takes the same kernel (never the few-row one), so both see the
+    // same values
+    gemm(h, K_GEMM_HEAD_CE, true, true, EPI_CE, g, st, true, update && h->nu > 0);
   }
   {
     PROF(K_CE_REDUCE);
@@ -538,14 +535,23 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
 
   if (update && h->nu > 0) {
     const int np = (n + 63) / 64 * 64;  // token count padded for the weight-gradient GEMMs
-    // --- dlogits (softmax - onehot) * 2^s / n, streamed over vocab slabs, and dn = dz W_lm
+    // --- dlogits (softmax - onehot) * 2^s / n, streamed over vocab slabs, and dn = dz W_lm.
+    // No logits are kept from the forward: each slab's logits are computed again by the
+    // LM-head product (the forward's kernel and reduction order, so the same values) and
+    // turned into the gradient in its epilogue with the saved log-sum-exp; only the
+    // slab's [B b, Vs] gradient goes to memory before the dn product reads it.
     for (int v0 = 0, sl = 0; v0 < h->V; v0 += h->Vs, ++sl) {
       const int vs = std::min(h->Vs, h->V - v0);
       {
-        PROF(K_GEMM_DLOGITS);
-        HIPCHK(dlogits_launch(dt, h->zlog + v0, h->V, h->lse, h->labs, h->zero, v0, h->gscale / (float)n, h->dz,
-                              h->Vs, Bn, vs, st));
-        h->launches++;
+        GemmArgs g = gargs(h->nf, d, off(h->lm_head, (size_t)v0 * d * es), d, Bn, vs, d);
+        g.C = h->dz;
+        g.ldc = h->Vs;
+        g.rowf = h->lse;
+        g.rowi = h->labs;  // label of row r = labs[*zero + r]
+        g.pos0 = h->zero;
+        g.col_off = v0;
+        g.alpha = h->gscale / (float)n;
+        gemm(h, K_GEMM_DLOGITS, true, true, EPI_DLOGITS, g, st, true);  // dz in the working dtype
       }
       {
         // B[n = model dim][k = vocab] from the transposed head [d][V]
@@ -984,7 +990,8 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     if (h->Lf == 0 || h->G <= c.chunk) h->G = 0;
   }
   h->ld_tok = c.max_tokens + 1;
-  h->Vs = std::min(h->V, 16384);
+  // vocabulary slab of the head backward: its [B b, Vs] gradient is about 32 MiB or less
+  h->Vs = std::min(h->V, std::max(1024, (16384 * 1024 / std::max(1, h->B * c.chunk)) / 128 * 128));
   h->P = 2 * ((h->V + 127) / 128);
   hipStream_t st = (hipStream_t)stream;
   const int d = h->d, F = h->F, b = h->b, L = h->L, V = h->V;
@@ -1176,7 +1183,6 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     h->rlosses = (float *)dalloc(h, c.max_tokens * sizeof(float));
     if (h->nu > 0) {
       h->dz = dalloc(h, (size_t)Bb * h->Vs * es);
-      h->zlog = (float *)dalloc(h, (size_t)Bb * h->V * 4);
       h->dn = (float *)dalloc(h, Bbd * 4);
       h->dh = (float *)dalloc(h, Bbd * 4);
       h->dy = dalloc(h, Bbd * es);
