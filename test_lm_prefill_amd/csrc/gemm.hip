@@ -414,6 +414,7 @@ hipError_t reduce_launch(int epi, const GemmArgs &g, int S, hipStream_t st) {
 size_t gemm_ws_elems(int M, int N) { return (size_t)8 * M * N; }
 
 hipError_t gemm_dma_launch(bool f16, int epi, const GemmArgs &g, hipStream_t st);
+hipError_t gemm_dma256_launch(bool f16, int epi, const GemmArgs &g, hipStream_t st);
 // few-row products (gemv.hip): M <= 4, 16-bit k-contiguous operands, fp32 / SwiGLU / CE epilogues
 bool gemv_ok(int dtype, bool a_kc, bool b_kc, int epi, const GemmArgs &g);
 hipError_t gemv_launch(bool f16, int epi, const GemmArgs &g, hipStream_t st);
@@ -459,7 +460,14 @@ hipError_t gemm_main_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g
   // the wrapped activation operand must be k-contiguous, whole 16-byte vectors
   if (g.a_kwrap < 0 || (g.a_kwrap > 0 && (!a_kc || g.a_kwrap % 8 != 0))) return hipErrorInvalidValue;
   if (allow_gemv && split <= 1 && gemv_ok(dtype, a_kc, b_kc, epi, g)) return gemv_launch(dtype == 2, epi, g, st);
-  if (use_dma(dtype, a_kc, b_kc, g)) return gemm_dma_launch(dtype == 2, epi, g, st);
+  if (use_dma(dtype, a_kc, b_kc, g)) {
+    // the 256 x 256 tile (one work-group per CU) when it has enough tiles to fill the
+    // GPU; both kernels sum every output in the same order, so the choice never changes
+    // a result bit
+    const long t256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
+    if (split <= 1 && epi != EPI_SGD && t256 >= 200) return gemm_dma256_launch(dtype == 2, epi, g, st);
+    return gemm_dma_launch(dtype == 2, epi, g, st);
+  }
   if (dtype == 2 || g.c_f16) return hipErrorInvalidValue;
   return dtype == 1 ? dispatch_layout<bf16_t>(a_kc, b_kc, epi, g, st, split)
                     : dispatch_layout<float>(a_kc, b_kc, epi, g, st, split);

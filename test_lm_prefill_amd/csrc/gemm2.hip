@@ -16,6 +16,8 @@
 // returns as zeros.  Two LDS stages: while one k-step is multiplied from
 // registers the next two are in flight; each thread waits on its own
 // vector-memory counter for the oldest, then a barrier publishes it.
+#include <type_traits>
+
 #include "common.h"
 #include "gemm.h"
 
@@ -447,6 +449,261 @@ template <typename TI> hipError_t launch5(int epi, const GemmArgs &g, hipStream_
   return hipErrorInvalidValue;
 }
 
+
+// ====================================================================== 256 x 256 tile
+// Work-group tile 256 (weight rows) x 256 (tokens) x 64 (k), 512 threads = 8 waves in a
+// 2 x 4 grid (weight halves x token quarters), one work-group per CU and two waves per
+// SIMD; each wave owns 128 x 64 outputs, 32 accumulator tiles of 16x16 held in AGPRs.
+// Per FLOP this tile moves half the L2 -> LDS bytes of the 128 x 128 tile; while one
+// wave of a SIMD waits (for a barrier, its loads or its LDS reads) the other issues
+// MFMAs.
+//
+// LDS: two stages (one per k-step in flight), each split into two 32 KiB halves, one
+// per 32-deep half of the step: 512 rows x 64 bytes (weight rows 0..255, token rows
+// 256..511), 16-byte chunk c of row r stored at chunk position c ^ ((r >> 1) & 2).
+// gfx950's LDS has 64 banks of 4 bytes and serves a ds_read_b128 in four passes of 16
+// lanes (measured: lanes l < 32 whose 4-lane group index l / 4 has even bit parity form
+// one pass, odd parity another, likewise for l >= 32); with this swizzle the 16 lanes of
+// every pass of a fragment read (16 rows, one chunk per 16 lanes) hit 16 distinct 16-byte
+// bank groups.  buffer_load ... lds fills a half with 4 loads per thread (1 KiB = 16 rows).
+//
+// Schedule of k-step t (first-half fragments of t already in registers F0):
+//   barrier S (this thread waited for its loads of (t, half 1)), then
+//   A: 32 MFMAs from F0; interleaved, one instruction between MFMAs: the 12 reads of
+//      (t, half 1) into F1, then the 4 loads of (t+2, half 0) into the half region
+//      (t, half 0), free since barrier S;
+//   barrier M (loads of (t+1, half 0) waited for), then
+//   B: 32 MFMAs from F1 with the reads of (t+1, half 0) into F0 and the loads of
+//      (t+2, half 1) into the region (t, half 1), free since barrier M.
+// A half's data is requested one and a half k-steps before it is read.  The whole loop
+// is one asm statement: the accumulators stay in their AGPRs (tied "+a"; the register
+// allocator moves values tied across several statements between registers), the
+// fragment registers are its outputs, and every LDS read is waited for inside it.
+namespace g8 {
+constexpr int NT8 = 512;
+constexpr int TW = 256, TX = 256, ROWS = TW + TX, HBYTES = ROWS * 64, SBYTES = 2 * HBYTES;
+constexpr int LPH = HBYTES / 16 / NT8;  // loads per thread and half-step (4)
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+#define G8_MF(t, F, i, j) "v_mfma_f32_16x16x32_" t " %[c" #i #j "], %[" #F "w" #i "], %[" #F "x" #j "], %[c" #i #j "]\n"
+#define G8_MF4(t, F, i) G8_MF(t, F, i, 0) G8_MF(t, F, i, 1) G8_MF(t, F, i, 2) G8_MF(t, F, i, 3)
+#define G8_R(N, wx, i, P, o) "ds_read_b128 %[" #N #wx #i "], %[" #P "] offset:" #o "\n"
+#define G8_M0(c, MB) "s_add_u32 m0, %[" #MB "], " #c "*1024\n"
+#define G8_BL(c) "buffer_load_dwordx4 %[vo" #c "], %[rsrc], %[soff] offen lds\n"
+#define G8_ADV "s_add_u32 %[soff], %[soff], 64\n s_cmp_ge_u32 %[soff], %[wrap]\n s_cselect_b32 %[tmp], %[wrap], 0\n" \
+               "s_sub_u32 %[soff], %[soff], %[tmp]\n"
+#define G8_LDH(MB) G8_M0(0, MB) "s_nop 0\n" G8_BL(0) G8_M0(1, MB) "s_nop 0\n" G8_BL(1) G8_M0(2, MB) "s_nop 0\n"   \
+  G8_BL(2) G8_M0(3, MB) "s_nop 0\n" G8_BL(3) G8_ADV
+// the 4 MFMAs of weight fragment i with one other instruction (or none) after each of the first three
+#define G8_ROW(t, F, i, s0, s1, s2) G8_MF(t, F, i, 0) s0 G8_MF(t, F, i, 1) s1 G8_MF(t, F, i, 2) s2 G8_MF(t, F, i, 3)
+// half-step: 32 MFMAs of F; the next half's 12 reads into N during the first four rows,
+// with LD the 4 loads of half region MB during rows 4..7
+#define G8_HALF_X(t, F, N, PW, PX, L0, L1, L2, L3, B0, B1, B2, B3, ADV)                                    \
+  G8_ROW(t, F, 0, G8_R(N, w, 0, PW, 0), G8_R(N, x, 0, PX, 0), G8_R(N, w, 1, PW, 1024))                      \
+  G8_ROW(t, F, 1, G8_R(N, x, 1, PX, 1024), G8_R(N, w, 2, PW, 2048), G8_R(N, x, 2, PX, 2048))                \
+  G8_ROW(t, F, 2, G8_R(N, w, 3, PW, 3072), G8_R(N, x, 3, PX, 3072), G8_R(N, w, 4, PW, 4096))                \
+  G8_ROW(t, F, 3, G8_R(N, w, 5, PW, 5120), G8_R(N, w, 6, PW, 6144), G8_R(N, w, 7, PW, 7168))                \
+  G8_ROW(t, F, 4, L0, B0, "") G8_ROW(t, F, 5, L1, B1, "") G8_ROW(t, F, 6, L2, B2, "") G8_ROW(t, F, 7, L3, B3, "") \
+  ADV "s_waitcnt lgkmcnt(0)\n"
+#define G8_HALF_RD(t, F, N, PW, PX) G8_HALF_X(t, F, N, PW, PX, "", "", "", "", "", "", "", "", "")
+#define G8_HALF_RD_LD(t, F, N, PW, PX, MB)                                                                  \
+  G8_HALF_X(t, F, N, PW, PX, G8_M0(0, MB), G8_M0(1, MB), G8_M0(2, MB), G8_M0(3, MB), G8_BL(0), G8_BL(1),    \
+            G8_BL(2), G8_BL(3), G8_ADV)
+#define G8_HALF(t, F) G8_MF4(t, F, 0) G8_MF4(t, F, 1) G8_MF4(t, F, 2) G8_MF4(t, F, 3) \
+                      G8_MF4(t, F, 4) G8_MF4(t, F, 5) G8_MF4(t, F, 6) G8_MF4(t, F, 7)
+#define G8_RD_ALL(N, PW, PX) G8_R(N, w, 0, PW, 0) G8_R(N, w, 1, PW, 1024) G8_R(N, w, 2, PW, 2048)          \
+  G8_R(N, w, 3, PW, 3072) G8_R(N, w, 4, PW, 4096) G8_R(N, w, 5, PW, 5120) G8_R(N, w, 6, PW, 6144)          \
+  G8_R(N, w, 7, PW, 7168) G8_R(N, x, 0, PX, 0) G8_R(N, x, 1, PX, 1024) G8_R(N, x, 2, PX, 2048)             \
+  G8_R(N, x, 3, PX, 3072) "s_waitcnt lgkmcnt(0)\n"
+#define G8_IF(D) "s_add_u32 %[tmp], %[t], " #D "\n s_cmp_lt_u32 %[tmp], %[nk]\n"
+// per half region 4 loads per thread: the wait counts below are 8 (two halves) and 4
+#define G8_LOOP(t)                                                                                       \
+  G8_LDH(m00) G8_LDH(m01)                                                                                \
+  "s_cmp_lt_u32 1, %[nk]\n s_cbranch_scc0 .Lg8one%=\n" G8_LDH(m10) G8_LDH(m11)                          \
+  "s_waitcnt vmcnt(8)\n s_branch .Lg8pro%=\n"                                                          \
+  ".Lg8one%=:\n s_waitcnt vmcnt(0)\n"                                                                  \
+  ".Lg8pro%=:\n s_barrier\n" G8_RD_ALL(f0, a00, x00) "s_nop 4\n s_mov_b32 %[t], 0\n"                   \
+  ".Lg8top%=:\n" G8_IF(1) "s_cbranch_scc0 .Lg8sa0%=\n s_waitcnt vmcnt(8)\n s_branch .Lg8sb0%=\n"       \
+  ".Lg8sa0%=:\n s_waitcnt vmcnt(0)\n .Lg8sb0%=:\n s_barrier\n"                                         \
+  G8_IF(2) "s_cbranch_scc0 .Lg8a0n%=\n" G8_HALF_RD_LD(t, f0, f1, a01, x01, m00) "s_branch .Lg8a0d%=\n"  \
+  ".Lg8a0n%=:\n" G8_HALF_RD(t, f0, f1, a01, x01) ".Lg8a0d%=:\n"                                        \
+  G8_IF(1) "s_cbranch_scc0 .Lg8last%=\n"                                                               \
+  G8_IF(2) "s_cbranch_scc0 .Lg8ma0%=\n s_waitcnt vmcnt(8)\n s_branch .Lg8mb0%=\n"                      \
+  ".Lg8ma0%=:\n s_waitcnt vmcnt(4)\n .Lg8mb0%=:\n s_barrier\n"                                         \
+  G8_IF(2) "s_cbranch_scc0 .Lg8b0n%=\n" G8_HALF_RD_LD(t, f1, f0, a10, x10, m01) "s_branch .Lg8b0d%=\n"  \
+  ".Lg8b0n%=:\n" G8_HALF_RD(t, f1, f0, a10, x10) ".Lg8b0d%=:\n"                                        \
+  G8_IF(2) "s_cbranch_scc0 .Lg8sa1%=\n s_waitcnt vmcnt(8)\n s_branch .Lg8sb1%=\n"                      \
+  ".Lg8sa1%=:\n s_waitcnt vmcnt(0)\n .Lg8sb1%=:\n s_barrier\n"                                         \
+  G8_IF(3) "s_cbranch_scc0 .Lg8a1n%=\n" G8_HALF_RD_LD(t, f0, f1, a11, x11, m10) "s_branch .Lg8a1d%=\n"  \
+  ".Lg8a1n%=:\n" G8_HALF_RD(t, f0, f1, a11, x11) ".Lg8a1d%=:\n"                                        \
+  G8_IF(2) "s_cbranch_scc0 .Lg8last%=\n"                                                               \
+  G8_IF(3) "s_cbranch_scc0 .Lg8ma1%=\n s_waitcnt vmcnt(8)\n s_branch .Lg8mb1%=\n"                      \
+  ".Lg8ma1%=:\n s_waitcnt vmcnt(4)\n .Lg8mb1%=:\n s_barrier\n"                                         \
+  G8_IF(3) "s_cbranch_scc0 .Lg8b1n%=\n" G8_HALF_RD_LD(t, f1, f0, a00, x00, m11) "s_branch .Lg8b1d%=\n"  \
+  ".Lg8b1n%=:\n" G8_HALF_RD(t, f1, f0, a00, x00) ".Lg8b1d%=:\n"                                        \
+  "s_add_u32 %[t], %[t], 2\n s_branch .Lg8top%=\n"                                                     \
+  ".Lg8last%=:\n" G8_HALF(t, f1) "s_nop 15\n s_nop 15\n s_nop 15\n"
+
+#define G8_C4(i) [c##i##0] "+a"(acc[i][0]), [c##i##1] "+a"(acc[i][1]), [c##i##2] "+a"(acc[i][2]), [c##i##3] "+a"(acc[i][3])
+#define G8_W8(n, v) [n##0] "=&v"(v[0]), [n##1] "=&v"(v[1]), [n##2] "=&v"(v[2]), [n##3] "=&v"(v[3]), \
+  [n##4] "=&v"(v[4]), [n##5] "=&v"(v[5]), [n##6] "=&v"(v[6]), [n##7] "=&v"(v[7])
+#define G8_X4(n, v) [n##0] "=&v"(v[0]), [n##1] "=&v"(v[1]), [n##2] "=&v"(v[2]), [n##3] "=&v"(v[3])
+#define G8_OUTS G8_C4(0), G8_C4(1), G8_C4(2), G8_C4(3), G8_C4(4), G8_C4(5), G8_C4(6), G8_C4(7), \
+  G8_W8(f0w, f0w), G8_X4(f0x, f0x), G8_W8(f1w, f1w), G8_X4(f1x, f1x), [t] "=&s"(st), [tmp] "=&s"(stmp), \
+  [soff] "+s"(soff)
+#define G8_INS [vo0] "v"(vo[0]), [vo1] "v"(vo[1]), [vo2] "v"(vo[2]), [vo3] "v"(vo[3]),                           \
+  [a00] "v"(aw[0][0]), [a01] "v"(aw[0][1]), [a10] "v"(aw[1][0]), [a11] "v"(aw[1][1]),                          \
+  [x00] "v"(ax[0][0]), [x01] "v"(ax[0][1]), [x10] "v"(ax[1][0]), [x11] "v"(ax[1][1]),                          \
+  [m00] "s"(mb[0][0]), [m01] "s"(mb[0][1]), [m10] "s"(mb[1][0]), [m11] "s"(mb[1][1]),                          \
+  [rsrc] "s"(rsrc), [wrap] "s"(wrap), [nk] "s"(nk)
+
+template <typename TI>
+DEVI void main_loop(f32x4_v (&acc)[8][4], const uint32_t (&vo)[LPH], const uint32_t (&aw)[2][2],
+                    const uint32_t (&ax)[2][2], const uint32_t (&mb)[2][2], v4i rsrc, uint32_t soff, uint32_t wrap,
+                    uint32_t nk) {
+  v4i f0w[8], f0x[4], f1w[8], f1x[4];
+  uint32_t st, stmp;
+  if constexpr (std::is_same<TI, f16_t>::value)
+    asm volatile(G8_LOOP("f16") : G8_OUTS : G8_INS : "memory", "m0", "scc");
+  else
+    asm volatile(G8_LOOP("bf16") : G8_OUTS : G8_INS : "memory", "m0", "scc");
+}
+#undef G8_MF
+#undef G8_MF4
+#undef G8_R
+#undef G8_M0
+#undef G8_BL
+#undef G8_ADV
+#undef G8_LDH
+#undef G8_ROW
+#undef G8_HALF_X
+#undef G8_HALF_RD
+#undef G8_HALF_RD_LD
+#undef G8_HALF
+#undef G8_RD_ALL
+#undef G8_IF
+#undef G8_LOOP
+#undef G8_C4
+#undef G8_W8
+#undef G8_X4
+#undef G8_OUTS
+#undef G8_INS
+}  // namespace g8
+
+template <typename TI, int EPI>
+__global__ __launch_bounds__(g8::NT8, 1) void gemm8_kernel(const GemmArgs g) {
+  using namespace g8;
+  __shared__ __align__(1024) char sm[2 * SBYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave >> 2, wm = wave & 3;  // weight half, token quarter
+  const int mt = (g.M + TX - 1) / TX, ntl = (g.N + TW - 1) / TW;
+  constexpr int GM = 8;
+  const int tile = remap_tile2(blockIdx.x, mt * ntl);
+  const int band = tile / (GM * ntl), in_band = tile % (GM * ntl);
+  const int bm = min(GM, mt - band * GM);
+  const int tm = band * GM + in_band % bm, tn = in_band / bm;
+  const int m0 = tm * TX, n0 = tn * TW;
+  int kbeg = 0, kend = g.K;
+  if (g.ksplit > 1) {
+    const int per = ((g.K + g.ksplit - 1) / g.ksplit + BK - 1) / BK * BK;
+    kbeg = blockIdx.z * per;
+    kend = min(g.K, kbeg + per);
+  }
+  const int nk = (kend - kbeg + BK - 1) / BK;
+  // waves 0-3 stream weight rows, waves 4-7 token rows; load c of a half covers rows
+  // 16 (wave LPH + c) .. +15, lane l row + l / 4, chunk position l % 4
+  const bool tok = wave >= 4;
+  uint32_t vo[LPH];
+#pragma unroll
+  for (int c = 0; c < LPH; ++c) {
+    const int row = (wave * LPH + c) * 16 + (lane >> 2);
+    const int kc = (lane & 3) ^ ((row >> 1) & 2);
+    if (!tok) {
+      const int gr = n0 + row;
+      vo[c] = gr < g.N ? (uint32_t)(((long)gr * g.ldb + kc * 8) * 2) : OOB;
+    } else {
+      const int gr = m0 + row - TW;
+      vo[c] = gr < g.M ? (uint32_t)(((long)gr * g.lda + kc * 8) * 2) : OOB;
+    }
+  }
+  v4i rsrc;
+  uint32_t soff, wrap;
+  {
+    const void *base = tok ? g.A : g.B;
+    const int ka = g.a_kwrap > 0 ? g.a_kwrap : g.K;
+    const uint32_t bytes = tok ? (uint32_t)(((long)(g.M - 1) * g.lda + ka) * 2)
+                               : (uint32_t)(((long)(g.N - 1) * g.ldb + g.K) * 2);
+    const uint64_t ad = (uint64_t)(uintptr_t)base;
+    rsrc = v4i{(int)(uint32_t)ad, (int)(uint32_t)(ad >> 32), (int)bytes, RSRC_W3};
+    const bool wr = tok && g.a_kwrap > 0;
+    wrap = wr ? (uint32_t)g.a_kwrap * 2 : 0x7fffffffu;
+    soff = (uint32_t)(wr ? kbeg % g.a_kwrap : kbeg) * 2;
+  }
+  const uint32_t smb = (uint32_t)(uintptr_t)(lds_void *)sm;
+  f32x4_v acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  const int lr = lane & 15, lq = lane >> 4;
+  const uint32_t cs = (uint32_t)((lq ^ ((lr >> 1) & 2)) << 4);
+  uint32_t aw[2][2], ax[2][2], mb[2][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t base = smb + s * SBYTES + h * HBYTES;
+      aw[s][h] = base + (wn * 128 + lr) * 64 + cs;
+      ax[s][h] = base + (TW + wm * 64 + lr) * 64 + cs;
+      mb[s][h] = (uint32_t)__builtin_amdgcn_readfirstlane(base + wave * LPH * 1024);
+    }
+  if (nk > 0)
+    main_loop<TI>(acc, vo, aw, ax, mb, rsrc, (uint32_t)__builtin_amdgcn_readfirstlane(soff),
+                  (uint32_t)__builtin_amdgcn_readfirstlane(wrap), (uint32_t)__builtin_amdgcn_readfirstlane(nk));
+  float4 pre[4][4];
+#pragma unroll
+  for (int qn = 0; qn < 2; ++qn) {
+    f32x4_v q[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q[i][j] = acc[qn * 4 + i][j];
+    const int mq = m0 + wm * 64, nq = n0 + wn * 128 + qn * 64;
+    gemm2_epilogue<128, EPI, false>(g, q, mq, nq / 128 * 128, nq / 128, 0, (nq / 64) & 1, lr, lq, pre);
+  }
+}
+
+#define G8_INST(TI)                                                      \
+  template __global__ void gemm8_kernel<TI, EPI_STORE>(const GemmArgs);     \
+  template __global__ void gemm8_kernel<TI, EPI_STORE_F32>(const GemmArgs); \
+  template __global__ void gemm8_kernel<TI, EPI_ADD_F32>(const GemmArgs);   \
+  template __global__ void gemm8_kernel<TI, EPI_SWIGLU>(const GemmArgs);    \
+  template __global__ void gemm8_kernel<TI, EPI_CE>(const GemmArgs);        \
+  template __global__ void gemm8_kernel<TI, EPI_DLOGITS>(const GemmArgs);   \
+  template __global__ void gemm8_kernel<TI, 100>(const GemmArgs);
+G8_INST(bf16_t)
+G8_INST(f16_t)
+#undef G8_INST
+
+template <typename TI, int EPI> hipError_t launch8_e(const GemmArgs &g, hipStream_t st) {
+  const int tiles = ((g.M + g8::TX - 1) / g8::TX) * ((g.N + g8::TW - 1) / g8::TW);
+  hipLaunchKernelGGL((gemm8_kernel<TI, EPI>), dim3(tiles, 1, g.ksplit), dim3(g8::NT8), 0, st, g);
+  return hipGetLastError();
+}
+template <typename TI> hipError_t launch8(int epi, const GemmArgs &g, hipStream_t st) {
+  if (g.ksplit > 1) return launch8_e<TI, 100>(g, st);
+  switch (epi) {
+    case EPI_STORE: return launch8_e<TI, EPI_STORE>(g, st);
+    case EPI_STORE_F32: return launch8_e<TI, EPI_STORE_F32>(g, st);
+    case EPI_ADD_F32: return launch8_e<TI, EPI_ADD_F32>(g, st);
+    case EPI_SWIGLU: return launch8_e<TI, EPI_SWIGLU>(g, st);
+    case EPI_CE: return launch8_e<TI, EPI_CE>(g, st);
+    case EPI_DLOGITS: return launch8_e<TI, EPI_DLOGITS>(g, st);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace ttt_g2
 using namespace ttt_g2;
 
@@ -455,4 +712,9 @@ using namespace ttt_g2;
 // fixed order).
 hipError_t gemm_dma_launch(bool f16, int epi, const GemmArgs &g, hipStream_t st) {
   return f16 ? launch5<f16_t>(epi, g, st) : launch5<bf16_t>(epi, g, st);
+}
+
+// The 256 x 256 tile (same operand conditions as gemm_dma_launch; no EPI_SGD).
+hipError_t gemm_dma256_launch(bool f16, int epi, const GemmArgs &g, hipStream_t st) {
+  return f16 ? launch8<f16_t>(epi, g, st) : launch8<bf16_t>(epi, g, st);
 }
