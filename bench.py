@@ -103,15 +103,22 @@ def algorithmic_bytes(cfg, T, update=True):
     # rmsnorm: read fp32 row, write the normalised row; the saved inputs of back-propagated norms;
     # the norms after the O and down products also apply those products' split-K partials
     # (read each fp32 partial, write the updated residual row)
-    def split_k(M, N, K):  # the GEMM planner's choice for a residual product (128 x 128 tiles)
+    def split_k(M, N, K):  # the GEMM planner's split for a residual product (16-bit operands)
+        def rnd(sp):
+            if sp < 2:
+                return 1
+            per = -(-(-(-K // sp)) // 64) * 64
+            return -(-K // per)
+        t256 = -(-M // 256) * -(-N // 256)
+        if t256 >= 200:
+            return 1
+        s256 = min(-(-240 // t256), K // 1024, 8)
+        if s256 >= 4:
+            return rnd(s256)
         tiles = -(-M // 128) * -(-N // 128)
         if tiles >= 256:
             return 1
-        sp = min(-(-400 // tiles), K // 512, 4)
-        if sp < 2:
-            return 1
-        per = -(-(-(-K // sp)) // 64) * 64
-        return -(-K // per)
+        return rnd(min(-(-400 // tiles), K // 512, 4))
     b_rows = cfg.chunk
     # the frozen blocks below the updated ones run ahead over groups of about 8192 tokens
     # (the library's rule for one sequence) with unsplit products; their outputs are then

@@ -73,12 +73,20 @@ hipError_t gemm_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, flo
 // Number of fp32 partial entries the launcher may need for an M x N output.
 size_t gemm_ws_elems(int M, int N);
 
+// How a product runs: the K split (fp32 partials in a workspace when > 1) and, for
+// 16-bit k-contiguous operands, whether the 256 x 256 tile (wide) or the 128 x 128 tile
+// computes it.  Both tiles sum every output element in the same order.
+struct GemmPlan {
+  int split = 1;
+  bool wide = false;
+};
+
 // The same work in two launches, for callers that time them separately:
-// gemm_plan returns the K split gemm_launch would use; gemm_main_launch runs
-// the GEMM (partials to ws when split > 1; allow_gemv = false keeps products of a
-// few rows on the tiled kernel); gemm_reduce_launch applies the epilogue to the
-// fixed-order sum of the partials.
-int gemm_plan(int dtype, bool a_kc, bool b_kc, int epi, const GemmArgs &g, size_t ws_elems, int force_split = 0);
-hipError_t gemm_main_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, float *ws, int split,
+// gemm_plan returns the plan gemm_launch would use; gemm_main_launch runs the GEMM
+// (partials to ws when split > 1; allow_gemv = false keeps products of a few rows on
+// the tiled kernels); gemm_reduce_launch applies the epilogue to the fixed-order sum of
+// the partials.
+GemmPlan gemm_plan(int dtype, bool a_kc, bool b_kc, int epi, const GemmArgs &g, size_t ws_elems, int force_split = 0);
+hipError_t gemm_main_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, float *ws, GemmPlan plan,
                             hipStream_t st, bool allow_gemv = true);
 hipError_t gemm_reduce_launch(int dtype, int epi, GemmArgs g, float *ws, int split, hipStream_t st);

@@ -424,48 +424,63 @@ static bool use_dma(int dtype, bool a_kc, bool b_kc, const GemmArgs &g) {
          g.a_kwrap % 64 == 0;
 }
 
-int gemm_plan(int dtype, bool a_kc, bool b_kc, int epi, const GemmArgs &g, size_t ws_elems, int force_split) {
+// Each split must own at least one 64-deep step.
+static int round_split(int split, int K) {
+  if (split < 2) return 1;
+  const int per = ((K + split - 1) / split + BK - 1) / BK * BK;
+  return (K + per - 1) / per;
+}
+
+GemmPlan gemm_plan(int dtype, bool a_kc, bool b_kc, int epi, const GemmArgs &g, size_t ws_elems, int force_split) {
   const bool dma = use_dma(dtype, a_kc, b_kc, g);
-  int split = 1;
-  if (force_split <= 0 && gemv_ok(dtype, a_kc, b_kc, epi, g)) return 1;
+  GemmPlan p;
+  if (force_split <= 0 && gemv_ok(dtype, a_kc, b_kc, epi, g)) return p;
+  const long t256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
+  // the 256 x 256 tile (one work-group per CU) when it has enough tiles to fill the GPU
+  if (dma && force_split <= 0 && epi != EPI_SGD && t256 >= 200) {
+    p.wide = true;
+    return p;
+  }
   if (epi == EPI_STORE || epi == EPI_STORE_F32 || epi == EPI_ADD_F32) {
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+    int split = 1;
     if (force_split > 0) {
       split = force_split;
     } else if (dma) {
-      // split only when the tiles leave CUs idle: aim for ~400 work-groups,
-      // each split at least eight 64-deep steps (the fp32 partial traffic of a
-      // split costs about as much as a short K range saves)
+      // few tiles: split K.  The 256 x 256 tile takes about 240 work-groups (one per CU)
+      // when every split keeps at least 16 steps and there are at least 4 splits;
+      // otherwise the 128 x 128 tile aims for ~400 work-groups (two per CU), each split at
+      // least eight steps (the fp32 partial traffic of a split costs about as much as a
+      // short K range saves)
+      const int s256 = std::min<long>(std::min<long>((240 + t256 - 1) / t256, g.K / (16 * BK)), 8);
+      if (s256 >= 4 && (size_t)s256 * g.M * g.N <= ws_elems) {
+        p.split = round_split(s256, g.K);
+        p.wide = true;
+        return p;
+      }
       if (tiles < 256) split = std::min(std::min((400 + tiles - 1) / tiles, g.K / (8 * BK)), 4);
     } else if (tiles < 256 && g.K >= 4 * BK) {
       split = (2 * 256 + tiles - 1) / tiles;
       split = min(split, g.K / (2 * BK));
       split = min(split, 8);
     }
-    if (split < 2) split = 1;
-    if (split > 1) {
-      // each split must own at least one BK step
-      int per = ((g.K + split - 1) / split + BK - 1) / BK * BK;
-      split = (g.K + per - 1) / per;
-    }
+    split = round_split(split, g.K);
     if (split > 1 && (size_t)split * g.M * g.N > ws_elems) split = 1;
+    p.split = split;
   }
-  return split;
+  return p;
 }
 
-hipError_t gemm_main_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, float *ws, int split,
+hipError_t gemm_main_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, float *ws, GemmPlan plan,
                             hipStream_t st, bool allow_gemv) {
+  const int split = plan.split;
   g.ksplit = split;
   g.ws = ws;
   // the wrapped activation operand must be k-contiguous, whole 16-byte vectors
   if (g.a_kwrap < 0 || (g.a_kwrap > 0 && (!a_kc || g.a_kwrap % 8 != 0))) return hipErrorInvalidValue;
   if (allow_gemv && split <= 1 && gemv_ok(dtype, a_kc, b_kc, epi, g)) return gemv_launch(dtype == 2, epi, g, st);
   if (use_dma(dtype, a_kc, b_kc, g)) {
-    // the 256 x 256 tile (one work-group per CU) when it has enough tiles to fill the
-    // GPU; both kernels sum every output in the same order, so the choice never changes
-    // a result bit
-    const long t256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
-    if (split <= 1 && epi != EPI_SGD && t256 >= 200) return gemm_dma256_launch(dtype == 2, epi, g, st);
+    if (plan.wide && epi != EPI_SGD) return gemm_dma256_launch(dtype == 2, epi, g, st);
     return gemm_dma_launch(dtype == 2, epi, g, st);
   }
   if (dtype == 2 || g.c_f16) return hipErrorInvalidValue;
@@ -482,8 +497,8 @@ hipError_t gemm_reduce_launch(int dtype, int epi, GemmArgs g, float *ws, int spl
 
 hipError_t gemm_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, float *ws, size_t ws_elems,
                        hipStream_t st, int force_split) {
-  const int split = gemm_plan(dtype, a_kc, b_kc, epi, g, ws_elems, force_split);
-  hipError_t e = gemm_main_launch(dtype, a_kc, b_kc, epi, g, ws, split, st);
+  const GemmPlan plan = gemm_plan(dtype, a_kc, b_kc, epi, g, ws_elems, force_split);
+  hipError_t e = gemm_main_launch(dtype, a_kc, b_kc, epi, g, ws, plan, st);
   if (e != hipSuccess) return e;
-  return gemm_reduce_launch(dtype, epi, g, ws, split, st);
+  return gemm_reduce_launch(dtype, epi, g, ws, plan.split, st);
 }

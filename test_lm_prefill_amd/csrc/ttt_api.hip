@@ -276,10 +276,12 @@ void prof_collect(ttt_handle *h, hipStream_t st) {
 void gemm(ttt_handle *h, int cls, bool akc, bool bkc, int epi, GemmArgs g, hipStream_t st, bool f16op = false,
           bool whole = false) {
   const int odt = (f16op && h->dt == 1) ? 2 : h->dt;
-  const int split = whole ? 1 : gemm_plan(odt, akc, bkc, epi, g, h->ws_elems);
+  GemmPlan plan = gemm_plan(odt, akc, bkc, epi, g, h->ws_elems);
+  if (whole) plan.split = 1;  // the wide / narrow choice never changes a result bit
+  const int split = plan.split;
   {
     Prof prof_(h, cls, st);
-    HIPCHK(gemm_main_launch(odt, akc, bkc, epi, g, h->ws, split, st, !whole));
+    HIPCHK(gemm_main_launch(odt, akc, bkc, epi, g, h->ws, plan, st, !whole));
   }
   if (split > 1) {
     Prof prof_(h, K_SPLITK_REDUCE, st);
@@ -294,10 +296,11 @@ void gemm(ttt_handle *h, int cls, bool akc, bool bkc, int epi, GemmArgs g, hipSt
 // partials live in h->ws until the next GEMM, so the norm must come first.
 ResidualPartials gemm_residual(ttt_handle *h, int cls, GemmArgs g, hipStream_t st) {
   const int odt = h->dt == 1 ? 2 : h->dt;
-  const int split = gemm_plan(odt, true, true, EPI_ADD_F32, g, h->ws_elems);
+  const GemmPlan plan = gemm_plan(odt, true, true, EPI_ADD_F32, g, h->ws_elems);
+  const int split = plan.split;
   {
     Prof prof_(h, cls, st);
-    HIPCHK(gemm_main_launch(odt, true, true, EPI_ADD_F32, g, h->ws, split, st));
+    HIPCHK(gemm_main_launch(odt, true, true, EPI_ADD_F32, g, h->ws, plan, st));
   }
   h->launches += 1;
   ResidualPartials r;
