@@ -1242,6 +1242,355 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const AttnArgs a) 
   }
 }
 
+// ================================================================ dK, dV, 16-bit, streamed
+// Gradients of the chunk's own keys and values (cached keys are constants):
+//   dV[j] = sum_q P[q][j] dO[q],   dK[j] = scale * sum_q dS[q][j] q^[q],
+//   P = 2^(s log2e scale - lse2[q]),   dS = P (dP - D[q]),   dP = dO v^T,
+// over the chunk queries q >= j (all inside the window, since the window covers a chunk).
+//
+// Work: a work-group owns a pair of 64-key blocks (j, nkb-1-j), whose query tiles
+// number nqt-j and j+1 (nqt = nkb tiles of 64 queries), so every work-group has nqt+1
+// tiles (the middle block of an odd nkb alone); grid (ceil(nkb/2), H), remapped so that
+// the work-groups of one head share an XCD and its L2 for the query-side tiles.
+// 8 waves, two per SIMD: wave = (key slice kw of 16 keys) x (query half qh of the
+// tile); each keeps its keys' K and V fragments in registers and accumulates dK, dV
+// over its query half.  At the end of a key block the qh = 1 waves pass their sums to the
+// qh = 0 waves through LDS, which add theirs and store (a fixed order).
+//
+// Per query tile of 64, one LDS stage holds (streamed by buffer_load ... lds three
+// stages deep: tile it+2 streams while tile it is computed):
+//   Q, dO   [64 rows][KCH chunks of 16 bytes] (head dims, zero past hd), chunk c of row r
+//           at c ^ sq(r);
+//   Q^T, dO^T [hd rows][8 chunks] (8 queries per chunk), chunk c of row d at c ^ ((d>>1)&7);
+//   lse2, D [64] each (in a 1 KiB slot).
+// Score rows are taken in the order 8 (i/4) + 4 qs + i%4 of the half (i = MFMA row), so
+// each lane ends up with 8 consecutive queries of one key: exactly one 16-byte fragment
+// of Q^T or dO^T for the dK / dV products.  The swizzles put the 16 lanes of every
+// ds_read_b128 pass on 16 distinct 16-byte bank groups (measured pass grouping: lanes
+// < 32 whose 4-lane group index has even bit parity form one pass, odd another, likewise
+// for lanes >= 32).  A tile's reads are three asm statements that wait for their own
+// reads (other stages' loads are still in flight then).
+template <int HD> struct K2 {
+  static constexpr int NC = (HD + 31) / 32;   // 32-deep steps over the head dims
+  static constexpr int KCH = 4 * NC;          // chunks per padded Q / dO row
+  static constexpr int RC = HD / 8;           // chunks holding data
+  static constexpr int NH = HD / 16;          // 16-row tiles over the head dims
+  static constexpr int QB = 64 * KCH * 16;    // bytes of a Q (or dO) tile
+  static constexpr int TB = HD * 128;         // bytes of a Q^T (or dO^T) tile
+  static constexpr int LOFF = 2 * QB + 2 * TB, DOFF = LOFF + 1024;
+  static constexpr int SB = DOFF + 1024;      // bytes of a stage
+  static constexpr int INS = SB / 1024;       // 1 KiB direct-to-LDS loads per stage
+  static constexpr int IPW = (INS + 7) / 8;   // per wave (the last ones repeat the last load)
+  static constexpr int QI = QB / 1024, TI = TB / 1024;
+  static_assert(2 * NH * 4 * 64 * 16 <= SB, "a stage holds the dK / dV hand-over of the 4 key slices");
+};
+template <int HD> DEVI int k2sq(int r) {
+  return (((r >> 3) & 1) << 1) | ((K2<HD>::KCH == 8) ? (((r >> 1) & 1) << 2) : 0);
+}
+typedef int k2v4 __attribute__((ext_vector_type(4)));
+
+// ---- a tile's fragment reads, each statement waiting for its own reads
+#define K2R(o, a, off) "ds_read_b128 %[" #o "], %[" #a "] offset:%[" #off "]\n"
+// Q (offset 0) and dO (offset QB) fragments [qs][c] at addresses a_qs_c
+template <int HD>
+DEVI void k2_rd_qd(k2v4 (&q)[2][K2<HD>::NC], k2v4 (&d)[2][K2<HD>::NC], const uint32_t (&ad)[2][K2<HD>::NC]) {
+  constexpr int NC = K2<HD>::NC, QB = K2<HD>::QB;
+  if constexpr (NC == 1) {
+    asm volatile(K2R(q0, a0, z) K2R(q1, a1, z) K2R(d0, a0, qb) K2R(d1, a1, qb) "s_waitcnt lgkmcnt(0)"
+                 : [q0] "=&v"(q[0][0]), [q1] "=&v"(q[1][0]), [d0] "=&v"(d[0][0]), [d1] "=&v"(d[1][0])
+                 : [a0] "v"(ad[0][0]), [a1] "v"(ad[1][0]), [z] "i"(0), [qb] "i"(QB) : "memory");
+  } else if constexpr (NC == 2) {
+    asm volatile(K2R(q00, a00, z) K2R(q01, a01, z) K2R(q10, a10, z) K2R(q11, a11, z)
+                 K2R(d00, a00, qb) K2R(d01, a01, qb) K2R(d10, a10, qb) K2R(d11, a11, qb) "s_waitcnt lgkmcnt(0)"
+                 : [q00] "=&v"(q[0][0]), [q01] "=&v"(q[0][1]), [q10] "=&v"(q[1][0]), [q11] "=&v"(q[1][1]),
+                   [d00] "=&v"(d[0][0]), [d01] "=&v"(d[0][1]), [d10] "=&v"(d[1][0]), [d11] "=&v"(d[1][1])
+                 : [a00] "v"(ad[0][0]), [a01] "v"(ad[0][1]), [a10] "v"(ad[1][0]), [a11] "v"(ad[1][1]), [z] "i"(0),
+                   [qb] "i"(QB)
+                 : "memory");
+  } else {
+    static_assert(NC == 3, "head dims up to 96");
+    asm volatile(K2R(q00, a00, z) K2R(q01, a01, z) K2R(q02, a02, z) K2R(q10, a10, z) K2R(q11, a11, z)
+                 K2R(q12, a12, z) K2R(d00, a00, qb) K2R(d01, a01, qb) K2R(d02, a02, qb) K2R(d10, a10, qb)
+                 K2R(d11, a11, qb) K2R(d12, a12, qb) "s_waitcnt lgkmcnt(0)"
+                 : [q00] "=&v"(q[0][0]), [q01] "=&v"(q[0][1]), [q02] "=&v"(q[0][2]), [q10] "=&v"(q[1][0]),
+                   [q11] "=&v"(q[1][1]), [q12] "=&v"(q[1][2]), [d00] "=&v"(d[0][0]), [d01] "=&v"(d[0][1]),
+                   [d02] "=&v"(d[0][2]), [d10] "=&v"(d[1][0]), [d11] "=&v"(d[1][1]), [d12] "=&v"(d[1][2])
+                 : [a00] "v"(ad[0][0]), [a01] "v"(ad[0][1]), [a02] "v"(ad[0][2]), [a10] "v"(ad[1][0]),
+                   [a11] "v"(ad[1][1]), [a12] "v"(ad[1][2]), [z] "i"(0), [qb] "i"(QB)
+                 : "memory");
+  }
+}
+// Q^T (offset 2048 hs) and dO^T (offset TB + 2048 hs) fragments from address a
+#define K2T(hs) K2R(t##hs, a, ot##hs) K2R(o##hs, a, oo##hs)
+#define K2TO(hs) [t##hs] "=&v"(t[hs]), [o##hs] "=&v"(o[hs])
+#define K2TI(hs) [ot##hs] "i"(2048 * hs), [oo##hs] "i"(TB + 2048 * hs)
+template <int HD> DEVI void k2_rd_t(k2v4 (&t)[K2<HD>::NH], k2v4 (&o)[K2<HD>::NH], uint32_t a) {
+  constexpr int NH = K2<HD>::NH, TB = K2<HD>::TB;
+  if constexpr (NH == 1) {
+    asm volatile(K2T(0) "s_waitcnt lgkmcnt(0)" : K2TO(0) : [a] "v"(a), K2TI(0) : "memory");
+  } else if constexpr (NH == 2) {
+    asm volatile(K2T(0) K2T(1) "s_waitcnt lgkmcnt(0)" : K2TO(0), K2TO(1) : [a] "v"(a), K2TI(0), K2TI(1) : "memory");
+  } else if constexpr (NH == 4) {
+    asm volatile(K2T(0) K2T(1) K2T(2) K2T(3) "s_waitcnt lgkmcnt(0)"
+                 : K2TO(0), K2TO(1), K2TO(2), K2TO(3)
+                 : [a] "v"(a), K2TI(0), K2TI(1), K2TI(2), K2TI(3) : "memory");
+  } else if constexpr (NH == 5) {
+    asm volatile(K2T(0) K2T(1) K2T(2) K2T(3) K2T(4) "s_waitcnt lgkmcnt(0)"
+                 : K2TO(0), K2TO(1), K2TO(2), K2TO(3), K2TO(4)
+                 : [a] "v"(a), K2TI(0), K2TI(1), K2TI(2), K2TI(3), K2TI(4) : "memory");
+  } else {
+    static_assert(NH == 6, "head dims 16, 32, 64, 80, 96");
+    asm volatile(K2T(0) K2T(1) K2T(2) K2T(3) K2T(4) K2T(5) "s_waitcnt lgkmcnt(0)"
+                 : K2TO(0), K2TO(1), K2TO(2), K2TO(3), K2TO(4), K2TO(5)
+                 : [a] "v"(a), K2TI(0), K2TI(1), K2TI(2), K2TI(3), K2TI(4), K2TI(5) : "memory");
+  }
+}
+// lse2 and D of the lane's 8 queries from address a
+template <int HD> DEVI void k2_rd_ld(k2v4 (&l)[2], k2v4 (&d)[2], uint32_t a) {
+  asm volatile(K2R(l0, a, o0) K2R(l1, a, o1) K2R(d0, a, o2) K2R(d1, a, o3) "s_waitcnt lgkmcnt(0)"
+               : [l0] "=&v"(l[0]), [l1] "=&v"(l[1]), [d0] "=&v"(d[0]), [d1] "=&v"(d[1])
+               : [a] "v"(a), [o0] "i"(K2<HD>::LOFF), [o1] "i"(K2<HD>::LOFF + 16), [o2] "i"(K2<HD>::DOFF),
+                 [o3] "i"(K2<HD>::DOFF + 16)
+               : "memory");
+}
+#undef K2R
+#undef K2T
+#undef K2TO
+#undef K2TI
+
+template <int HD>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv2_kernel(const AttnArgs a) {
+  using C = K2<HD>;
+  constexpr int NC = C::NC, KCH = C::KCH, NH = C::NH, STG = 3;
+  __shared__ __align__(1024) char sm[STG * C::SB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave & 3, qh = wave >> 2;
+  const int lr = lane & 15, lg = lane >> 4, g4 = lg * 4;
+  int pr, h;
+  {
+    const int gx = gridDim.x, total = gx * gridDim.y;
+    const int i = blockIdx.x + gx * blockIdx.y;
+    const int q8 = total / 8, rem = total % 8, x = i % 8;
+    const int m = x * q8 + min(x, rem) + i / 8;
+    pr = m % gx;
+    h = m / gx;
+  }
+  const int n = a.n, nkb = (n + 63) / 64;
+  const int kb1 = pr, kb2 = nkb - 1 - pr;
+  const int nq1 = nkb - kb1, nq2 = kb2 != kb1 ? nkb - kb2 : 0;
+  const int total_it = nq1 + nq2;
+  const int pos0 = *a.pos0;
+  const uint32_t smb = (uint32_t)(uintptr_t)(lds_void *)sm;
+
+  // ---- this wave's loads of a stage: load c covers stage bytes [1024 j, 1024 j + 1024)
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)a.q, (short)0, (uint32_t)n * a.d * 2, BUF_RSRC_W3);
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc((void *)a.dout, (short)0, (uint32_t)n * a.d * 2, BUF_RSRC_W3);
+  const __amdgpu_buffer_rsrc_t rqt = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.qt, (short)0, (uint32_t)a.H * HD * a.ldt * 2, BUF_RSRC_W3);
+  const __amdgpu_buffer_rsrc_t rdt = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)a.doutt, (short)0, (uint32_t)a.H * HD * a.ldt * 2, BUF_RSRC_W3);
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc((void *)a.lse2, (short)0, (uint32_t)a.H * a.ldl * 4, BUF_RSRC_W3);
+  const __amdgpu_buffer_rsrc_t rD = __builtin_amdgcn_make_buffer_rsrc((void *)a.Dq, (short)0, (uint32_t)a.H * a.ldl * 4, BUF_RSRC_W3);
+  int srow[C::IPW], sch[C::IPW];  // per load: tile row and global chunk of this lane
+#pragma unroll
+  for (int c = 0; c < C::IPW; ++c) {
+    const int j = min(wave * C::IPW + c, C::INS - 1);
+    if (j < 2 * C::QI) {
+      const int sl = (j % C::QI) * 64 + lane;
+      srow[c] = sl / KCH;
+      sch[c] = (sl % KCH) ^ k2sq<HD>(srow[c]);
+    } else if (j < 2 * C::QI + 2 * C::TI) {
+      const int sl = ((j - 2 * C::QI) % C::TI) * 64 + lane;
+      srow[c] = sl / 8;
+      sch[c] = (sl % 8) ^ ((srow[c] >> 1) & 7);
+    } else {
+      srow[c] = 0;
+      sch[c] = lane;
+    }
+  }
+  // streams the tile of 64 queries starting at qt into stage st (branches uniform per wave)
+  auto issue = [=](int st, int qt) {
+#pragma unroll
+    for (int c = 0; c < C::IPW; ++c) {
+      const int j = min(wave * C::IPW + c, C::INS - 1);
+      lds_void *dst = (lds_void *)(sm + st * C::SB + j * 1024);
+      if (j < 2 * C::QI) {
+        const int row = srow[c], cc = sch[c];
+        const uint32_t o = (cc < C::RC && qt + row < n) ? (uint32_t)(((qt + row) * a.d + h * HD + cc * 8) * 2) : BUF_OOB;
+        if (j < C::QI)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, dst, 16, o, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, dst, 16, o, 0, 0, 0);
+      } else if (j < 2 * C::QI + 2 * C::TI) {
+        const int row = srow[c], cc = sch[c];
+        const uint32_t o = qt + 8 * cc < n ? (uint32_t)(((h * HD + row) * a.ldt + qt + 8 * cc) * 2) : BUF_OOB;
+        if (j < 2 * C::QI + C::TI)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rqt, dst, 16, o, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rdt, dst, 16, o, 0, 0, 0);
+      } else {
+        const uint32_t o = (lane < 16 && qt + 4 * lane < n) ? (uint32_t)((h * a.ldl + qt + 4 * lane) * 4) : BUF_OOB;
+        if (j == C::INS - 2)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, dst, 16, o, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, dst, 16, o, 0, 0, 0);
+      }
+    }
+  };
+  auto qt_of = [&](int it) { return 64 * (it < nq1 ? kb1 + it : kb2 + it - nq1); };
+
+  // ---- per-lane read offsets within a stage
+  uint32_t aq[2][NC], at, al;
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const int row = 32 * qh + 8 * (lr >> 2) + 4 * qs + (lr & 3);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) aq[qs][c] = row * KCH * 16 + (((4 * c + lg) ^ k2sq<HD>(row)) << 4);
+  }
+  at = 2 * C::QB + lr * 128 + (((4 * qh + lg) ^ ((lr >> 1) & 7)) << 4);  // row hs*16+lr at + 2048 hs
+  al = (32 * qh + 8 * lg) * 4;  // this lane's 8 queries in the lse2 / D slots
+
+  const float sl2 = a.scale * LOG2E_F;
+  for (int s = 0; s < 2; ++s)
+    if (s < total_it) issue(s, qt_of(s));
+  // the K and V fragments of both key blocks' keys, loaded once up front: a load left in
+  // flight across the loop would make every iteration wait for the tile loads behind it
+  Frag<bf16_t> kf[NC], vf[NC], kf2[NC], vf2[NC];
+  {
+    auto load_kv = [&](Frag<bf16_t>(&kk)[NC], Frag<bf16_t>(&vv)[NC], int kbl) {
+      const int ky = kbl * 64 + kw * 16 + lr;
+      const long slot = (pos0 + ky) % a.R;
+      const bf16_t *kr = reinterpret_cast<const bf16_t *>(a.K) + ((long)h * a.R + slot) * HD;
+      const bf16_t *vr = reinterpret_cast<const bf16_t *>(a.V) + ((long)h * a.R + slot) * HD;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int col = c * 32 + lg * 8;
+        if (ky < n && col < HD) {
+          load_frag(kk[c], kr + col);
+          load_frag(vv[c], vr + col);
+        } else {
+          zero_frag(kk[c]);
+          zero_frag(vv[c]);
+        }
+      }
+    };
+    load_kv(kf, vf, kb1);
+    load_kv(kf2, vf2, kb2);
+    wait_vm<0>();
+  }
+  f32x4_v dK[NH], dV[NH];
+  int key = 0, kb = -1, qt0 = 0;
+  for (int it = 0; it < total_it; ++it) {
+    const int st = it % STG;
+    const int kbi = it < nq1 ? kb1 : kb2;
+    const int qt = qt_of(it);
+    // tile it landed for this thread: the loads of tile it+1 may stay in flight
+    if (it + 1 < total_it)
+      wait_vm<C::IPW>();
+    else
+      wait_vm<0>();
+    __builtin_amdgcn_s_barrier();  // every wave's loads of tile it landed; stage (it+2) % 3 is free
+    if (it + 2 < total_it) issue((it + 2) % STG, qt_of(it + 2));
+    if (kbi != kb) {  // a new key block: its keys' fragments, zeroed sums
+      if (kb >= 0) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          kf[c] = kf2[c];
+          vf[c] = vf2[c];
+        }
+      }
+      kb = kbi;
+      qt0 = qt;
+      key = kb * 64 + kw * 16 + lr;
+#pragma unroll
+      for (int hs = 0; hs < NH; ++hs) {
+        dK[hs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+        dV[hs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    const uint32_t sb = smb + st * C::SB;
+    k2v4 fq[2][NC], fd[2][NC], ft[NH], fo[NH], lv[2], dv[2];
+    {
+      uint32_t ad[2][NC];
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) ad[qs][c] = sb + aq[qs][c];
+      k2_rd_qd<HD>(fq, fd, ad);
+    }
+    // S = Q K^T, dP = dO V^T for this wave's 32 queries x 16 keys
+    f32x4_v S[2], P[2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      S[qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      P[qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        Frag<bf16_t> x, y;
+        x.v = __builtin_bit_cast(uint4, fq[qs][c]);
+        y.v = __builtin_bit_cast(uint4, fd[qs][c]);
+        mma(S[qs], x, kf[c]);
+        mma(P[qs], y, vf[c]);
+      }
+    }
+    k2_rd_t<HD>(ft, fo, sb + at);
+    k2_rd_ld<HD>(lv, dv, sb + al);
+    // lane: queries qt + 32 qh + 8 lg + (4 qs + r), key `key`
+    Frag<bf16_t> pf, sf;
+    {
+      const bool diag = qt == qt0;  // the key block's own tile: queries before a key are masked
+      float x[8], y[8];
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int k = 4 * qs + r, q = qt + 32 * qh + 8 * lg + k;
+          const bool ok = (q < n) && (key < n) && (!diag || q >= key);
+          const float L = __int_as_float(lv[qs][r]), D = __int_as_float(dv[qs][r]);
+          const float pv = fast_exp2(__builtin_fmaf(S[qs][r], sl2, -L));
+          x[k] = ok ? pv : 0.f;
+          y[k] = ok ? pv * (P[qs][r] - D) : 0.f;
+        }
+      pack_frag(pf, x);
+      pack_frag(sf, y);
+    }
+    // dV += dO^T P, dK += Q^T dS over the 32 queries
+#pragma unroll
+    for (int hs = 0; hs < NH; ++hs) {
+      Frag<bf16_t> x, y;
+      x.v = __builtin_bit_cast(uint4, fo[hs]);
+      y.v = __builtin_bit_cast(uint4, ft[hs]);
+      mma(dV[hs], x, pf);
+      mma(dK[hs], y, sf);
+    }
+    const bool last = (it + 1 == total_it) || (it + 1 == nq1);
+    if (last) {
+      // the key block is done: the qh = 1 waves hand their sums to the qh = 0 waves
+      // through this stage, which every wave has finished reading (the next load into
+      // it is issued after the next iteration's barrier)
+      lds_barrier();
+      f32x4_v *red = reinterpret_cast<f32x4_v *>(sm + st * C::SB) + kw * 64 + lane;
+      if (qh == 1) {
+#pragma unroll
+        for (int hs = 0; hs < NH; ++hs) {
+          red[(2 * hs) * 256] = dK[hs];
+          red[(2 * hs + 1) * 256] = dV[hs];
+        }
+      }
+      lds_barrier();
+      if (qh == 0 && key < n) {
+        float *pk = a.dk + (long)key * a.d + h * HD + g4, *pv = a.dv + (long)key * a.d + h * HD + g4;
+#pragma unroll
+        for (int hs = 0; hs < NH; ++hs) {
+          *reinterpret_cast<f32x4_v *>(pk + hs * 16) = (red[(2 * hs) * 256] + dK[hs]) * a.scale;
+          *reinterpret_cast<f32x4_v *>(pv + hs * 16) = red[(2 * hs + 1) * 256] + dV[hs];
+        }
+      }
+    }
+  }
+}
+
 template <typename T, int HD> hipError_t fwd_t(const AttnArgs &a, hipStream_t st) {
   dim3 grid((a.n + 127) / 128, a.H, a.nsplit);
   // bf16 mode hands the O projection an fp16 operand; fp32 mode keeps fp32
@@ -1343,8 +1692,23 @@ hipError_t dq_hd(bool bf, int hd, const AttnArgs &a, hipStream_t st) {
   }
   HD_SWITCH_F32(dq_t)
 }
+template <int HD> hipError_t dkdv2_t(const AttnArgs &a, hipStream_t st) {
+  dim3 grid(((a.n + 63) / 64 + 1) / 2, a.H);
+  hipLaunchKernelGGL((attn_bwd_dkdv2_kernel<HD>), grid, dim3(512), 0, st, a);
+  return hipGetLastError();
+}
 hipError_t dkdv_hd(bool bf, int hd, const AttnArgs &a, hipStream_t st) {
-  if (bf) { HD_SWITCH(dkdv_t, bf16_t) }
+  if (bf) {
+    switch (hd) {
+      case 16: return dkdv2_t<16>(a, st);
+      case 32: return dkdv2_t<32>(a, st);
+      case 64: return dkdv2_t<64>(a, st);
+      case 80: return dkdv2_t<80>(a, st);
+      case 96: return dkdv2_t<96>(a, st);
+      case 128: return dkdv_t<bf16_t, 128>(a, st);  // its tiles would not fit two LDS stages
+    }
+    return hipErrorInvalidValue;
+  }
   HD_SWITCH_F32(dkdv_t)
 }
 
