@@ -156,7 +156,18 @@ def algorithmic_bytes(cfg, T, update=True):
     return b
 
 
-def gpu_bench(cfg, steps, warmup, profile=True):
+def steady_start(cfg):
+    """First position of the first chunk whose window is full (chunk index ceil(k/b)),
+    or None when the sequence has no such chunk."""
+    s = -(-cfg.window // cfg.chunk) * cfg.chunk
+    return s if s < cfg.seq_len else None
+
+
+def gpu_bench(cfg, steps, warmup, profile=True, gains=None):
+    """Times the prefill of cfg's sequence with inner updates and with eta = 0 (no
+    backward, no update), and, when the sequence has chunks with a full window, the
+    prefill of its first s tokens (s = ceil(k/b) b): the difference prices the
+    steady-state chunks (chunk index >= k/b) alone."""
     import torch
     from ttt_inputs import make_weights_torch, make_tokens
     from test_lm_prefill_amd import Session
@@ -165,7 +176,7 @@ def gpu_bench(cfg, steps, warmup, profile=True):
     T = cfg.seq_len
     log(f"[bench] workload {cfg.name}: L={cfg.n_layers} d={cfg.d_model} T={T} b={cfg.chunk} k={cfg.window}")
     t0 = time.time()
-    w = make_weights_torch(cfg, "cuda", seed=0)
+    w = make_weights_torch(cfg, "cuda", seed=0, gains=gains)
     tok_np = make_tokens(cfg, seed=1)
     tok = torch.from_numpy(tok_np).cuda()
     torch.cuda.synchronize()
@@ -173,41 +184,46 @@ def gpu_bench(cfg, steps, warmup, profile=True):
     sess = Session(cfg, w, max_tokens=T)
     stream = torch.cuda.current_stream()
 
-    def timed(flags, K, W):
+    def timed(flags, K, W, t=tok):
         for i in range(W):
-            sess.prefill(tok, flags=flags, want_fast=False, check=False)
+            sess.prefill(t, flags=flags, want_fast=False, check=False)
             torch.cuda.synchronize()
-            log(f"[bench] warmup {i + 1}/{W} flags={flags} done")
+            log(f"[bench] warmup {i + 1}/{W} flags={flags} T={t.numel() - 1} done")
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(K):
-            sess.prefill(tok, flags=flags, want_fast=False, check=False)
+            sess.prefill(t, flags=flags, want_fast=False, check=False)
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
-        log(f"[bench] timed {K} steps flags={flags}: {ms / K:.2f} ms/step")
-        return ms
+        log(f"[bench] timed {K} steps flags={flags} T={t.numel() - 1}: {ms / K:.2f} ms/step")
+        return ms / K
 
-    ms_ttt = timed(0, steps, warmup)
-    from test_lm_prefill_amd.ttt import ttt_check_finite
+    res = {"ms_ttt": timed(0, steps, warmup)}
     losses, _ = sess.prefill(tok, want_fast=False, check=True)
-    mean_loss = float(losses.mean().item())
-    ms_swa = timed(TTT_NO_UPDATE, steps, 1)
-
-    ktimes = {}
+    res["mean_loss"] = float(losses.mean().item())
+    res["ms_swa"] = timed(TTT_NO_UPDATE, steps, 1)
+    s0 = steady_start(cfg)
+    if s0 is not None:
+        head = tok[:s0 + 1].contiguous()
+        res["steady_s0"] = s0
+        res["ms_ttt_head"] = timed(0, max(2, steps), 1, head)
+        res["ms_swa_head"] = timed(TTT_NO_UPDATE, max(2, steps), 1, head)
+    res["kt"] = {}
     if profile:
         sess.set_kernel_timing(True)
         sess.prefill(tok, want_fast=False, check=False)
         torch.cuda.synchronize()
-        ktimes = sess.kernel_times()
+        res["kt"] = sess.kernel_times()
         sess.set_kernel_timing(False)
         log("[bench] kernel timing pass done")
     sess.close()
     del w
     torch.cuda.empty_cache()
-    return ms_ttt, ms_swa, ktimes, mean_loss, tok_np
+    res["tok_np"] = tok_np
+    return res
 
 
 def time_prefill(cfg, flags, steps, warmup, n_seq=1):
@@ -403,32 +419,256 @@ def stored_traffic(kernel, workload):
     return float(fields["bytes_per_launch"])
 
 
-def cpu_baseline(cfg, tok_np, n_tokens):
-    """The oracle (numpy fp64) on the first n_tokens positions of the same workload,
-    as one chunk of that size: forward, losses, backward and one update."""
+def host_info():
+    """CPU model, logical / physical / usable cores and the BLAS numpy calls."""
+    info = {"cpu_model": None, "logical_cores": os.cpu_count(), "physical_cores": None,
+            "usable_cores": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+    try:
+        phys, pid, cid = set(), None, None
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key = line.split(":", 1)[0].strip()
+                if key == "model name" and info["cpu_model"] is None:
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                elif key == "physical id":
+                    pid = line.split(":", 1)[1].strip()
+                elif key == "core id":
+                    cid = line.split(":", 1)[1].strip()
+                elif not line.strip():
+                    if cid is not None:
+                        phys.add((pid, cid))
+                    pid, cid = None, None
+        if cid is not None:
+            phys.add((pid, cid))
+        info["physical_cores"] = len(phys) or None
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = {"vendor": blas[0].get("internal_api"), "version": blas[0].get("version"),
+                            "threads": blas[0].get("num_threads"),
+                            "architecture": blas[0].get("architecture")}
+    except Exception:
+        pass
+    return info
+
+
+def cpu_baseline(cfg, tok_np, gains=None, seed=7, n_max=128):
+    """The oracle (numpy float64, as it is) on a bounded sample of the same workload.
+
+    Workloads with chunks whose window is full: the first n_max positions of one such
+    steady-state chunk (chunk index ceil(k/b)), run as a chunk of their own (forward,
+    losses, backward and the SGD step; the work per position is that of the full chunk:
+    every query sees k keys, every product has the same shapes per row), with the k-1
+    cached positions per layer filled with seeded random keys and values in place of
+    the earlier chunks' own (their values do not change the work).  Workloads without
+    such a chunk: the whole prefill when it is short (up to 4 chunks), else the first
+    n_max positions of its last chunk the same way.
+    """
     from ttt_inputs import make_weights_torch
-    from oracle.ttt_oracle import Oracle
+    from oracle.ttt_oracle import Oracle, sgd_step
     import torch
     t0 = time.time()
-    w = make_weights_torch(cfg, "cuda", seed=0)
+    w = make_weights_torch(cfg, "cuda" if torch.cuda.is_available() else "cpu", seed=0, gains=gains)
     wn = {k: v.float().cpu().numpy() for k, v in w.items()}
     del w
     torch.cuda.empty_cache()
     log(f"[bench] cpu baseline: weights on host in {time.time() - t0:.1f}s")
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = os.cpu_count()
-    c = cfg.with_(chunk=n_tokens)
-    orc = Oracle(c, wn)
-    t1 = time.time()
-    orc.prefill(tok_np[:n_tokens + 1])
-    dt = time.time() - t1
-    log(f"[bench] cpu baseline: {n_tokens} tokens in {dt:.1f}s")
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n_tokens} positions of the same sequence as one chunk "
-                      f"(forward, losses, backward, one SGD step), numpy float64, {dt:.1f} s"}
+    orc = Oracle(cfg, wn)
+    T, b, k = cfg.seq_len, cfg.chunk, cfg.window
+    hi = host_info()
+    threads = (hi.get("blas") or {}).get("threads") or hi["usable_cores"]
+    s0 = steady_start(cfg)
+    if s0 is None and cfg.n_chunks <= 4:
+        t1 = time.time()
+        orc.prefill(tok_np[:T + 1])
+        dt = time.time() - t1
+        n, what = T, f"the whole prefill ({cfg.n_chunks} chunks of {b})"
+    else:
+        if s0 is None:
+            s0 = (cfg.n_chunks - 1) * b
+            kind = "the last chunk"
+        else:
+            kind = "one steady-state chunk (chunk index ceil(k/b))"
+        n = min(b, T - s0, n_max)
+        rng = np.random.default_rng(seed)
+        lo = max(0, s0 - k + 1)
+        shape = (s0 - lo, cfg.n_heads, cfg.head_dim)
+        cache = [{"pos": np.arange(lo, s0, dtype=np.int64), "k": rng.standard_normal(shape),
+                  "v": 0.05 * rng.standard_normal(shape)} for _ in range(cfg.n_layers)]
+        W = orc.init_fast()
+        t1 = time.time()
+        _, saved, _ = orc.chunk_forward(W, cache, tok_np[s0:s0 + n], tok_np[s0 + 1:s0 + n + 1], s0)
+        if cfg.n_update > 0:
+            G = orc.chunk_grad(W, saved)
+            W = [[sgd_step(x, g, cfg.eta) for x, g in zip(ws, gs)] for ws, gs in zip(W, G)]
+        dt = time.time() - t1
+        what = (f"the first {n} positions of {kind}, run as a chunk of their own: positions {s0}..{s0 + n - 1} "
+                f"with {s0 - lo} cached positions per layer (seeded random keys and values), forward, losses, "
+                f"backward and one SGD step")
+    log(f"[bench] cpu baseline: {n} tokens in {dt:.1f}s")
+    return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "ms_per_1k_tokens": round(dt * 1e3 * 1024 / n, 1),
+            "projected_whole_prefill_s": round(dt * T / n, 1),  # every chunk priced as a steady-state one
+            "sample": f"{what}; numpy float64; {dt:.1f} s",
+            "host": hi}
+
+
+def attention_path(cfg, gains):
+    """Which forward attention kernel the library picks for these QK-norm gains (its
+    rule: bound B = 1.01 max|g_q| max|g_k| sqrt(hd) log2(e) of the scaled scores in
+    log2 units; fp16 bounded softmax for B <= 14.5, bf16 bounded for B <= 48, else the
+    online-max kernel), per layer, counted."""
+    if cfg.dtype != "bf16":
+        return {"fp32 online max": cfg.n_layers}
+    out = {}
+    for l in range(cfg.n_layers):
+        gq = 1.0 if gains is None else float(np.abs(gains[f"l{l}.q_norm"]).max())
+        gk = 1.0 if gains is None else float(np.abs(gains[f"l{l}.k_norm"]).max())
+        B = 1.01 * gq * gk * np.sqrt(cfg.head_dim) * 1.4426950408889634
+        path = "fp16 bounded softmax" if B <= 14.5 else ("bf16 bounded softmax" if B <= 48 else "bf16 online max")
+        out[path] = out.get(path, 0) + 1
+    return out
+
+
+def qk_gains(cfg, product):
+    """Unit block-norm gains and QK-norm gains sqrt(product) each (bf16-rounded)."""
+    from ttt_inputs.weights import tensor_specs, round_bf16_np
+    g = {}
+    for name, _, shape, kind in tensor_specs(cfg):
+        if kind == "gain":
+            v = np.sqrt(product) if name.endswith(("q_norm", "k_norm")) else 1.0
+            g[name] = round_bf16_np(np.full(shape, v, dtype=np.float32))
+    return g
+
+
+def overhead_flops(cfg, T):
+    """MFMA work the path does beyond the algorithmic count: the bf16 workloads' fast
+    MLP forward runs over the hi | lo working copy, doubling the reduction of the fast
+    gate/up (4 d F per token per fast block) and fast down (2 d F) products."""
+    if cfg.dtype != "bf16" or cfg.n_update == 0:
+        return {}
+    return {"gemm_gate_up_swiglu": T * cfg.n_update * 4 * cfg.d_model * cfg.d_ff,
+            "gemm_down_residual": T * cfg.n_update * 2 * cfg.d_model * cfg.d_ff}
+
+
+def summarize(cfg, r, steps):
+    """The per-workload figures from one gpu_bench result."""
+    T = cfg.seq_len
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    flops = algorithmic_flops(cfg, T, update=True)
+    total_tf = sum(flops.values()) / 1e12
+    swa_tf = sum(algorithmic_flops(cfg, T, update=False).values()) / 1e12
+    ov = overhead_flops(cfg, T)
+    rflops = recompute_flops(cfg, T, update=True)
+    out = {
+        "ms_per_step": round(r["ms_ttt"], 3),
+        "ms_per_1k_tokens": round(r["ms_ttt"] * 1024 / T, 4),
+        "tokens_per_s": round(T / (r["ms_ttt"] / 1e3), 1),
+        "mfma_util_pct": round(100 * total_tf / (r["ms_ttt"] / 1e3) / peak, 2),
+        "algorithmic_tflop_per_step": round(total_tf, 2),
+        "overhead_tflop_per_step": {"hilo_fast_forward": round(sum(ov.values()) / 1e12, 2),
+                                    "head_backward_logits_recompute": round(sum(rflops.values()) / 1e12, 2)},
+        "swa_only": {"ms_per_step": round(r["ms_swa"], 3), "ms_per_1k_tokens": round(r["ms_swa"] * 1024 / T, 4),
+                     "tokens_per_s": round(T / (r["ms_swa"] / 1e3), 1),
+                     "mfma_util_pct": round(100 * swa_tf / (r["ms_swa"] / 1e3) / peak, 2)},
+        "ttt_over_swa": round(r["ms_ttt"] / r["ms_swa"], 3),
+    }
+    if "steady_s0" in r:
+        n = T - r["steady_s0"]
+        out["steady_state"] = {
+            "chunks": f"{r['steady_s0'] // cfg.chunk}..{cfg.n_chunks - 1}",
+            "ms_per_1k_tokens": round((r["ms_ttt"] - r["ms_ttt_head"]) * 1024 / n, 4),
+            "swa_only_ms_per_1k_tokens": round((r["ms_swa"] - r["ms_swa_head"]) * 1024 / n, 4),
+            "how": f"(prefill of T tokens - prefill of the first {r['steady_s0']}) / {n} tokens"}
+    kt = r["kt"]
+    kernels = {}
+    if kt:
+        hbm = algorithmic_bytes(cfg, T, update=True)
+        tot_prof = sum(v[0] for v in kt.values())
+        for nm, (ms, cnt) in sorted(kt.items(), key=lambda x: -x[1][0]):
+            if cnt == 0:
+                continue
+            ent = {"ms": round(ms, 3), "launches": cnt, "share": round(ms / tot_prof, 4)}
+            if nm in flops and ms > 0:
+                ent["tflops"] = round(flops[nm] / 1e12 / (ms / 1e3), 1)
+                ent["mfma_frac"] = round(flops[nm] / 1e12 / (ms / 1e3) / peak, 4)
+            if nm in ov and ms > 0:  # the hi | lo work: its own entry, outside the algorithmic rate
+                ent["overhead_tflop"] = round(ov[nm] / 1e12, 2)
+                ent["tflops_incl_overhead"] = round((flops[nm] + ov[nm]) / 1e12 / (ms / 1e3), 1)
+            if nm in rflops and ms > 0:
+                ent["recompute_tflops"] = round(rflops[nm] / 1e12 / (ms / 1e3), 1)
+            ub = hbm.get("update_in_gemm_dw_sgd") if nm == "gemm_dw_sgd" else None
+            if (nm in hbm or ub) and ms > 0:
+                by = ub if ub else hbm[nm]
+                key = "update_" if ub else ""
+                ent[key + "gbytes"] = round(by / 1e9, 3)
+                ent[key + "gbps"] = round(by / 1e9 / (ms / 1e3), 1)
+                ent[key + "hbm_frac"] = round(by / 1e9 / (ms / 1e3) / PEAK_HBM_GBS, 4)
+            kernels[nm] = ent
+
+        def util(names):
+            f = sum(flops[nm] for nm in names if nm in kt)
+            t = sum(kt[nm][0] for nm in names if nm in kt)
+            return round(f / 1e12 / (t / 1e3) / peak, 4) if t > 0 else None
+        out["mfma_frac_by_family"] = {
+            "gemm": util([nm for nm in flops if nm.startswith("gemm_")]),
+            "attention": util([nm for nm in flops if nm.startswith("attn_")])}
+        out["hbm_gbps"] = {nm: kernels[nm].get("gbps") or kernels[nm].get("update_gbps")
+                           for nm in ("rmsnorm", "rmsnorm_bwd", "ce_reduce", "gemm_dw_sgd") if nm in kernels}
+    out["kernels"] = kernels
+    return out, flops, peak
+
+
+def roofline_entry(cfg, r, flops, peak):
+    kt = r["kt"]
+    if not kt:
+        return None
+    dom = max((nm for nm in kt if nm in flops and kt[nm][1] > 0), key=lambda nm: kt[nm][0])
+    ms_d, n_d = kt[dom]
+    per_launch = flops[dom] / n_d
+    achieved = per_launch / 1e12 / (ms_d / n_d / 1e3)
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": stored_traffic(dom, cfg.name), "kernel": dom,
+            "flop_per_launch": per_launch, "avg_launch_ms": round(ms_d / n_d, 4)}
+
+
+def precision(cfg, gains):
+    if cfg.dtype != "bf16":
+        return "fp32", {"all": "fp32"}
+    return "fp16", {"weights": "bf16 values", "forward_gemm_operands": "fp16",
+                    "attention_forward": attention_path(cfg, gains),
+                    "mlp_backward_operands": "fp16 (loss scaled by 2^12)",
+                    "attention_and_vocab_backward_operands": "bf16", "accumulate": "fp32",
+                    "fast_weight_master": "fp32", "residual_stream_and_losses": "fp32"}
+
+
+BASELINE_WORKLOADS = ("tiny", "125m", "760m", "1.3b_b256", "1.3b_b1024", "1.3b_b4096", "2.7b_8k", "2.7b_32k")
+
+
+def suite_configs(steps, warmup, with_cpu=True):
+    """Every listed workload besides the headline one: whole-sequence and steady-state
+    ms per 1K tokens with inner updates and with eta = 0, MFMA fractions of the GEMM and
+    attention families, HBM rates of the norm, CE and update kernels, and the oracle on
+    its bounded sample."""
+    from ttt_inputs import get
+    rows = []
+    for name in BASELINE_WORKLOADS:
+        cfg = get(name)
+        r = gpu_bench(cfg, steps, warmup, profile=True)
+        row, _, _ = summarize(cfg, r, steps)
+        row = {"workload": name, "seq_len": cfg.seq_len, "chunk": cfg.chunk, "window": cfg.window,
+               "n_update": cfg.n_update, **row}
+        row.pop("kernels")
+        row["dtype"] = precision(cfg, None)[0]
+        row["mean_loss"] = round(r["mean_loss"], 4)
+        if with_cpu:
+            row["cpu_baseline"] = cpu_baseline(cfg, r["tok_np"])
+        rows.append(row)
+        log(f"[bench] {name}: {row['ms_per_1k_tokens']} ms/1K (swa {row['swa_only']['ms_per_1k_tokens']})")
+    return {"suite": "workloads", "rows": rows}
 
 
 def main():
@@ -437,16 +677,17 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="2.7b_128k")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--qk-gain", type=float, default=None,
+                    help="QK-norm gains sqrt(G) for q and k (product G) instead of unit gains")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
                     help="run a calibration kernel and one prefill only (for counter runs)")
-    ap.add_argument("--suite", choices=["full_attention", "sweep", "decode", "batch"],
+    ap.add_argument("--suite", choices=["full_attention", "sweep", "decode", "batch", "workloads"],
                     help="instead of the benchmark line: the full-attention baseline at the 2.7B shape, "
-                         "the n_update / window sweep at the 760M shape, or decoding with periodic "
-                         "updates after an 8K prompt at the 2.7B shape, or batched sequences at 131072 "
-                         "tokens per call at the 2.7B shape (one JSON line)")
+                         "the n_update / window sweep at the 760M shape, decoding with periodic "
+                         "updates after an 8K prompt at the 2.7B shape, batched sequences at 131072 "
+                         "tokens per call at the 2.7B shape, or every other listed workload (one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: a TTT prefill sequence is a recurrence over chunks and "
@@ -458,82 +699,42 @@ def main():
         profile_pass(cfg)
         return
     if args.suite:
+        if args.suite == "workloads":
+            print(json.dumps(suite_configs(args.steps, args.warmup, with_cpu=not args.no_cpu_baseline)), flush=True)
+            return
         fn = {"full_attention": suite_full_attention, "sweep": suite_sweep, "decode": suite_decode,
               "batch": suite_batch}[args.suite]
         print(json.dumps(fn(args.steps, args.warmup)), flush=True)
         return
     T = cfg.seq_len
-    ms_ttt, ms_swa, kt, mean_loss, tok_np = gpu_bench(cfg, args.steps, args.warmup,
-                                                      profile=not args.no_kernel_timing)
-    ms_step = ms_ttt / args.steps
-    ms_swa_step = ms_swa / args.steps
-    flops = algorithmic_flops(cfg, T, update=True)
-    total_tf = sum(flops.values()) / 1e12
-    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
-    mfma_util = total_tf / (ms_step / 1e3) / peak
-    swa_tf = sum(algorithmic_flops(cfg, T, update=False).values()) / 1e12
-
-    roof = None
-    kernels = {}
-    hbm = algorithmic_bytes(cfg, T, update=True)
-    rflops = recompute_flops(cfg, T, update=True)
-    if kt:
-        tot_prof = sum(v[0] for v in kt.values())
-        for nm, (ms, n) in sorted(kt.items(), key=lambda x: -x[1][0]):
-            if n == 0:
-                continue
-            ent = {"ms": round(ms, 3), "launches": n, "share": round(ms / tot_prof, 4)}
-            if nm in flops and ms > 0:
-                ent["tflops"] = round(flops[nm] / 1e12 / (ms / 1e3), 1)
-                ent["mfma_frac"] = round(flops[nm] / 1e12 / (ms / 1e3) / peak, 4)
-            if nm in rflops and ms > 0:  # recomputation: its rate, outside the utilisation numerator
-                ent["recompute_tflops"] = round(rflops[nm] / 1e12 / (ms / 1e3), 1)
-            ub = hbm.get("update_in_gemm_dw_sgd") if nm == "gemm_dw_sgd" else None
-            if (nm in hbm or ub) and ms > 0:
-                by = ub if ub else hbm[nm]
-                key = "update_" if ub else ""
-                ent[key + "gbytes"] = round(by / 1e9, 3)
-                ent[key + "gbps"] = round(by / 1e9 / (ms / 1e3), 1)
-                ent[key + "hbm_frac"] = round(by / 1e9 / (ms / 1e3) / PEAK_HBM_GBS, 4)
-            kernels[nm] = ent
-        dom = max((nm for nm in kernels if nm in flops), key=lambda nm: kernels[nm]["ms"])
-        ms_d, n_d = kt[dom]
-        per_launch = flops[dom] / n_d
-        achieved = per_launch / 1e12 / (ms_d / n_d / 1e3)
-        traffic = stored_traffic(dom, cfg.name)
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
-                "flop_per_launch": per_launch, "avg_launch_ms": round(ms_d / n_d, 4)}
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, tok_np, min(args.cpu_tokens, T))
+    gains = qk_gains(cfg, args.qk_gain) if args.qk_gain is not None else None
+    r = gpu_bench(cfg, args.steps, args.warmup, profile=not args.no_kernel_timing, gains=gains)
+    summ, flops, peak = summarize(cfg, r, args.steps)
+    roof = roofline_entry(cfg, r, flops, peak)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, r["tok_np"], gains=gains)
+    dtype, prec = precision(cfg, gains)
     out = {
         "metric": "TTT prefill tokens/s and ms per 1K tokens at 128K ctx; MFMA util %",
-        "value": round(T * args.steps / (ms_ttt / 1e3), 1),
+        "value": round(T / (r["ms_ttt"] / 1e3), 1),
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 3),
-        "ms_per_1k_tokens": round(ms_step * 1024 / T, 4),
-        "mfma_util_pct": round(100 * mfma_util, 2),
-        "algorithmic_tflop_per_step": round(total_tf, 2),
-        "swa_only": {"ms_per_step": round(ms_swa_step, 3), "ms_per_1k_tokens": round(ms_swa_step * 1024 / T, 4),
-                     "tokens_per_s": round(T / (ms_swa_step / 1e3), 1),
-                     "mfma_util_pct": round(100 * swa_tf / (ms_swa_step / 1e3) / peak, 2)},
+        "ms_per_step": summ.pop("ms_per_step"),
+        "ms_per_1k_tokens": summ.pop("ms_per_1k_tokens"),
+        "mfma_util_pct": summ.pop("mfma_util_pct"),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": cfg.dtype, "data": "synthetic (seeded Zipf+span-copy ids, seeded random-init weights)",
-        "precision": ({"weights": "bf16 values", "forward_operands": "fp16",
-                       "mlp_backward_operands": "fp16 (loss scaled by 2^12)",
-                       "attention_and_vocab_backward_operands": "bf16", "accumulate": "fp32",
-                       "fast_weight_master": "fp32", "residual_stream_and_losses": "fp32"}
-                      if cfg.dtype == "bf16" else {"all": "fp32"}),
-        "config": {"workload": cfg.name, "n_layers": cfg.n_layers, "d_model": cfg.d_model, "n_heads": cfg.n_heads,
+        "dtype": dtype, "data": "synthetic (seeded Zipf+span-copy ids, seeded random-init weights)",
+        "precision": prec,
+        "config": {"workload": cfg.name + (f"_qkgain{args.qk_gain:g}" if gains is not None else ""),
+                   "n_layers": cfg.n_layers, "d_model": cfg.d_model, "n_heads": cfg.n_heads,
                    "d_ff": cfg.d_ff, "vocab": cfg.vocab, "seq_len": T, "window": cfg.window, "chunk": cfg.chunk,
-                   "n_update": cfg.n_update, "eta": cfg.eta},
-        "mean_loss": round(mean_loss, 4),
+                   "n_update": cfg.n_update, "eta": cfg.eta,
+                   "qk_gain_product": args.qk_gain if gains is not None else 1.0},
+        "mean_loss": round(r["mean_loss"], 4),
         "roofline": roof,
-        "kernels": kernels,
         "cpu_baseline": cpu,
     }
+    summ.pop("tokens_per_s")
+    out.update(summ)
     print(json.dumps(out), flush=True)
 
 
