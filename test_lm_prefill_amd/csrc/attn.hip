@@ -12,6 +12,7 @@
 // (4g..4g+3, 16+4g..16+4g+3) for lane group g, which is why V (and K for dQ)
 // are read transposed from LDS.  Softmax statistics stay per lane (one query).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "attn.h"
@@ -500,9 +501,21 @@ template <int HD, typename TF> struct F2State {
   using C = F2<HD>;
   Frag<TF> qf[4][C::NC];
   f32x4_v O[C::NH][4];
+  // row sums of the 16-bit weights.  Up to hd 80: an MFMA of each P fragment against a
+  // fragment of ones, so every lane holds its query's sum over all keys (4 equal values);
+  // above (where registers are short): per lane over its 8 keys, v_dot2 against (1, 1)
+  static constexpr bool MSUM = C::NH <= 5;
+  f32x4_v ls[4];
   float lsum[4];
   int kb[2], vb;  // per-lane byte offsets of the fragment reads (kb by parity of the 32-dim step)
 };
+
+// fp16 queries are stored pre-multiplied by scale * log2(e) (rounded to fp16) in the
+// forward's registers, and the score accumulators start at -B, so that the MFMA gives
+// the exponent s * scale * log2(e) - B directly and each weight costs one v_exp_f32;
+// bf16 keeps its queries as they are (one more bf16 rounding of q would cost precision)
+template <typename TF> struct F2Pre { static constexpr bool v = false; };
+template <> struct F2Pre<f16_t> { static constexpr bool v = true; };
 
 // Tiles t0 .. t1-1 of 32 keys.  FULL tiles have every (query, key) pair of
 // the work-group inside the window; otherwise each wave skips the MFMAs of a
@@ -513,6 +526,11 @@ DEVI void fwd2_range(F2State<HD, TF> &st, const F2Issue<HD> &is, char *stage, in
                      int pq, int lr, int lg, const AttnArgs &a) {
   using C = F2<HD>;
   const float sl2 = a.scale * LOG2E_F, B = a.sbound - P16Off<TF>::v;
+  constexpr bool PRE = F2Pre<TF>::v;
+  const float s_init = PRE ? -B : 0.f;
+  Frag<TF> ones;
+  ones.v = std::is_same<TF, f16_t>::value ? make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u)
+                                          : make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
   for (int t = t0; t < t1; ++t) {
     const int jt = jt0 + 32 * t;
     wait_vm<0>();
@@ -533,7 +551,7 @@ DEVI void fwd2_range(F2State<HD, TF> &st, const F2Issue<HD> &is, char *stage, in
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int qs = 0; qs < 4; ++qs) S[ks][qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+      for (int qs = 0; qs < 4; ++qs) S[ks][qs] = f32x4_v{s_init, s_init, s_init, s_init};
 #pragma unroll
     for (int c = 0; c < C::NC; ++c)
 #pragma unroll
@@ -549,7 +567,7 @@ DEVI void fwd2_range(F2State<HD, TF> &st, const F2Issue<HD> &is, char *stage, in
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float e = fast_exp2(__builtin_fmaf(S[ks][qs][r], sl2, -B));
+          float e = PRE ? fast_exp2(S[ks][qs][r]) : fast_exp2(__builtin_fmaf(S[ks][qs][r], sl2, -B));
           if (!FULL) {
             const int j = jt + 8 * lg + 4 * ks + r;
             e = (j > p || j <= p - a.window) ? 0.f : e;
@@ -557,13 +575,17 @@ DEVI void fwd2_range(F2State<HD, TF> &st, const F2Issue<HD> &is, char *stage, in
           x[4 * ks + r] = e;
         }
       pack_frag(pf[qs], x);
-      // row sum from the packed 16-bit p (the values the PV product uses), two per dot2
-      st.lsum[qs] = sum_pairs(pf[qs], st.lsum[qs]);
+      // row sums of the packed 16-bit p (the values the PV product uses)
+      if constexpr (!F2State<HD, TF>::MSUM) st.lsum[qs] = sum_pairs(pf[qs], st.lsum[qs]);
     }
 #pragma unroll
     for (int hs = 0; hs < C::NH; ++hs)
 #pragma unroll
       for (int qs = 0; qs < 4; ++qs) mma(st.O[hs][qs], vf[hs], pf[qs]);
+    if constexpr (F2State<HD, TF>::MSUM) {
+#pragma unroll
+      for (int qs = 0; qs < 4; ++qs) mma(st.ls[qs], ones, pf[qs]);
+    }
   }
 }
 
@@ -605,8 +627,26 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd2_kernel(const AttnArgs a) {
       else
         zero_frag(st.qf[qs][c]);
     }
+  if constexpr (F2Pre<TF>::v) {
+    // q <- fp16(q * scale * log2 e)
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    const _Float16 sc = (_Float16)(a.scale * LOG2E_F);
+    const h2_t s2 = {sc, sc};
+#pragma unroll
+    for (int qs = 0; qs < 4; ++qs)
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+        uint4 v = st.qf[qs][c].v;
+        v.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, v.x) * s2);
+        v.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, v.y) * s2);
+        v.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, v.z) * s2);
+        v.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, v.w) * s2);
+        st.qf[qs][c].v = v;
+      }
+  }
 #pragma unroll
   for (int qs = 0; qs < 4; ++qs) {
+    st.ls[qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
     st.lsum[qs] = 0.f;
 #pragma unroll
     for (int hs = 0; hs < C::NH; ++hs) st.O[hs][qs] = f32x4_v{0.f, 0.f, 0.f, 0.f};
@@ -656,7 +696,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd2_kernel(const AttnArgs a) {
   TO *Out = reinterpret_cast<TO *>(a.o);
 #pragma unroll
   for (int qs = 0; qs < 4; ++qs) {
-    const float lt = group4_sum(st.lsum[qs]);
+    const float lt = F2State<HD, TF>::MSUM ? st.ls[qs][0] : group4_sum(st.lsum[qs]);
     const int q = qw + qs * 16 + lr;
     if (q < a.n) {
       // a split may see no key of this query: weight 0 in the merge
