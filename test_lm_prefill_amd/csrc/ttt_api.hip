@@ -830,6 +830,37 @@ void scratch_setup(ttt_handle *h, hipStream_t st) {
   h->scratch = g_scratch_ptr[h->dev];
 }
 
+// Tokens per sequence in a frozen-prefix group.  The group's products run unsplit on the
+// 256 x 256 tile (one work-group per CU), so how full their last round of tiles is depends
+// on the row count: at 2.7B (d = 2560) 8192 rows give the d-wide O and down products 320
+// tiles, 1.25 rounds of 256 CUs with the second three-quarters idle, and 12288 rows 480
+// (1.9 rounds; measured 54 ms per 128K prefill faster).  Among row counts from 8192 to
+// 16384 (multiples of the chunk over the B sequences) this takes the one whose QKV, O,
+// gate/up and down products fill their rounds best, weighted by their FLOPs, the smallest
+// on ties: 12288 at d = 2560, 8192 at d = 2048 (8 column tiles: exactly one round of O),
+// 10240 at d = 1536.
+long frozen_group_tokens(int d, int F, int b, int B, int cus) {
+  const int tw = 256;
+  const long nt[4] = {(3L * d + tw - 1) / tw, ((long)d + tw - 1) / tw, (2L * F + tw - 1) / tw, ((long)d + tw - 1) / tw};
+  const double w[4] = {3.0 * d * d, 1.0 * d * d, 2.0 * d * F, 1.0 * d * F};
+  const long step = (long)b * B;
+  long best = std::max(1L, 8192 / step) * b;
+  double best_s = -1.0;
+  for (long rows = step * std::max(1L, 8192 / step); rows <= 16384; rows += step) {
+    double sc = 0.0;
+    for (int p = 0; p < 4; ++p) {
+      const long tiles = (rows + tw - 1) / tw * nt[p];
+      const long rounds = (tiles + cus - 1) / cus;
+      sc += w[p] * (double)tiles / (double)(rounds * cus);
+    }
+    if (sc > best_s + 1e-9) {
+      best_s = sc;
+      best = rows / B;
+    }
+  }
+  return best;
+}
+
 void free_all(ttt_handle *h) {
   for (int i = 0; i < 6; ++i)
     if (h->gexec[i]) hipGraphExecDestroy(h->gexec[i]);
@@ -983,17 +1014,17 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
   h->nu = c.n_update;
   h->R = c.window + c.chunk;  // positions s-k+1 .. s+b-1 must coexist; multiple of 64
   h->B = c.n_seq > 0 ? c.n_seq : 1;
-  // frozen-prefix groups: about 12288 rows per pass (B sequences of G tokens), never
-  // longer than the longest sequence.  With the 256 x 256 tile on 256 CUs, the d-wide
-  // products (O, down: d / 256 = 10 column tiles at d = 2560) take 480 tiles over 12288
-  // rows, 1.9 rounds of the GPU, where 8192 rows gave 320 tiles (1.25 rounds, the second
-  // one three-quarters idle); 40-60 ms less per 128K prefill at 2.7B than 8192 rows, the
-  // same as 32768 rows with less ring memory.
+  // frozen-prefix groups of G tokens per sequence (B G rows per pass), never longer than
+  // the longest sequence: frozen_group_tokens picks G.
   h->Lf = c.n_layers - c.n_update;
   {
-    const int gc = std::max(1, 12288 / (h->B * c.chunk));
+    int cus = 256, dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess) {
+      int v = 0;
+      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
     const long gmax = (c.max_tokens + c.chunk - 1) / c.chunk * (long)c.chunk;
-    h->G = (int)std::min<long>((long)gc * c.chunk, gmax);
+    h->G = (int)std::min<long>(frozen_group_tokens(c.d_model, c.d_ff, c.chunk, h->B, cus), gmax);
     if (h->Lf == 0 || h->G <= c.chunk) h->G = 0;
   }
   h->ld_tok = c.max_tokens + 1;

@@ -66,12 +66,13 @@ def test_batch_each_sequence_matches_oracle(dtype, hd, T, B):
 
 
 def test_batch_over_several_groups():
-    # two sequences of 6844 tokens in 256-token chunks: the frozen-prefix pass takes groups of
-    # 6144 tokens per sequence (12288 rows over both), so each sequence spans a whole group and
-    # a ragged one, and every chunk picks its rows from its own sequence's part of the group
+    # two sequences of 8892 tokens in 256-token chunks: the frozen-prefix pass takes groups of
+    # at most 8192 tokens per sequence (at most 16384 rows over both), so each sequence spans a
+    # whole group and a ragged one, and every chunk picks its rows from its own sequence's part
+    # of the group
     from oracle.ttt_oracle import Oracle
     from test_lm_prefill_amd import Session
-    T, B = 6144 + 700, 2
+    T, B = 8192 + 700, 2
     cfg = cfg_b(dtype="fp32", hd=64, T=T, b=256, V=512)
     say(f"case: batch over groups fp32 T={T} B={B} b=256")
     w = make_weights_torch(cfg, "cuda")

@@ -91,8 +91,8 @@ def test_mid_bf16_gains(hd, qk):
 
 
 def test_frozen_prefix_groups_with_gains():
-    """T past one group of 12288 tokens: the frozen blocks run ahead over groups."""
-    T = 12288 + 300
+    """T past the largest group (16384 tokens): the frozen blocks run ahead over groups."""
+    T = 16384 + 300
     cfg = mid(64, T=T, L=3, n_update=2, V=512, k=256, b=256)
     say(f"case: frozen prefix groups bf16 T={T} random gains")
     wt, wn, _ = with_gains(cfg, 7, qk_range=(0.8, 1.05))
