@@ -831,18 +831,18 @@ void scratch_setup(ttt_handle *h, hipStream_t st) {
 }
 
 // Tokens per sequence in a frozen-prefix group.  The group's products run unsplit on the
-// 256 x 256 tile (one work-group per CU), so how full their last round of tiles is depends
-// on the row count: at 2.7B (d = 2560) 8192 rows give the d-wide O and down products 320
-// tiles, 1.25 rounds of 256 CUs with the second three-quarters idle, and 12288 rows 480
-// (1.9 rounds; measured 54 ms per 128K prefill faster).  Among row counts from 8192 to
-// 16384 (multiples of the chunk over the B sequences) this takes the one whose QKV, O,
-// gate/up and down products fill their rounds best, weighted by their FLOPs, the smallest
-// on ties: 12288 at d = 2560, 8192 at d = 2048 (8 column tiles: exactly one round of O),
-// 10240 at d = 1536.
-long frozen_group_tokens(int d, int F, int b, int B, int cus) {
+// 256 x 256 tile (one work-group per CU) and its attention on work-groups of 256 queries of
+// one head (two per CU), so how full their last round is depends on the row count: at 2.7B
+// (d = 2560) 8192 rows give the d-wide O and down products 320 tiles, 1.25 rounds of 256
+// CUs with the second three-quarters idle, and 12288 rows 480 (1.9 rounds; measured 54 ms
+// per 128K prefill faster).  Among row counts from 8192 to 16384 (multiples of the chunk
+// over the B sequences) this takes the one whose QKV, O, gate/up, down and attention work
+// fills its rounds best, weighted by FLOPs per token, the smallest on ties: 12288 at 2.7B,
+// 16384 at 1.3B and 760M.
+long frozen_group_tokens(int d, int F, int H, int k, int b, int B, int cus) {
   const int tw = 256;
   const long nt[4] = {(3L * d + tw - 1) / tw, ((long)d + tw - 1) / tw, (2L * F + tw - 1) / tw, ((long)d + tw - 1) / tw};
-  const double w[4] = {3.0 * d * d, 1.0 * d * d, 2.0 * d * F, 1.0 * d * F};
+  const double w[5] = {6.0 * d * d, 2.0 * d * d, 4.0 * d * F, 2.0 * d * F, 4.0 * d * k};
   const long step = (long)b * B;
   long best = std::max(1L, 8192 / step) * b;
   double best_s = -1.0;
@@ -853,6 +853,8 @@ long frozen_group_tokens(int d, int F, int b, int B, int cus) {
       const long rounds = (tiles + cus - 1) / cus;
       sc += w[p] * (double)tiles / (double)(rounds * cus);
     }
+    const long wg = (rows / B + 255) / 256 * H * B;  // attention work-groups, two per CU
+    sc += w[4] * (double)wg / (double)((wg + 2L * cus - 1) / (2L * cus) * 2L * cus);
     if (sc > best_s + 1e-9) {
       best_s = sc;
       best = rows / B;
@@ -1024,7 +1026,7 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
       if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
     const long gmax = (c.max_tokens + c.chunk - 1) / c.chunk * (long)c.chunk;
-    h->G = (int)std::min<long>(frozen_group_tokens(c.d_model, c.d_ff, c.chunk, h->B, cus), gmax);
+    h->G = (int)std::min<long>(frozen_group_tokens(c.d_model, c.d_ff, c.n_heads, c.window, c.chunk, h->B, cus), gmax);
     if (h->Lf == 0 || h->G <= c.chunk) h->G = 0;
   }
   h->ld_tok = c.max_tokens + 1;
