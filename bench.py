@@ -120,11 +120,11 @@ def algorithmic_bytes(cfg, T, update=True):
             return 1
         return rnd(min(-(-400 // tiles), K // 512, 4))
     b_rows = cfg.chunk
-    # the frozen blocks below the updated ones run ahead over groups of about 12288 tokens
-    # (the library's rule for one sequence) with unsplit products; their outputs are then
-    # copied into each chunk's residual rows (fp32 read + write, timed with the embedding)
-    gc = max(1, 12288 // cfg.chunk)
-    G = min(gc * cfg.chunk, n_chunks * cfg.chunk)
+    # the frozen blocks below the updated ones run ahead over groups of 8192 to 16384 tokens
+    # (the library picks the count per shape; only whether there is more than one chunk's
+    # worth matters here) with unsplit products; their outputs are then copied into each
+    # chunk's residual rows (fp32 read + write, timed with the embedding)
+    G = min(max(1, 8192 // cfg.chunk) * cfg.chunk, n_chunks * cfg.chunk)
     grouped = (L - nu) > 0 and G > cfg.chunk
     sp_o = split_k(b_rows, d, d)
     sp_dn = split_k(b_rows, d, F)
