@@ -20,7 +20,7 @@ TTT_NO_UPDATE, TTT_NO_GRAPH = 1, 2
 def mid(hd, dtype="bf16", T=600, n_update=2, L=3, eta=0.5, std=0.02, V=1024, k=256, b=128):
     H = 4
     d = H * hd
-    F = {16: 192, 64: 512, 80: 704, 96: 768, 128: 1024}[hd]
+    F = {16: 192, 32: 384, 64: 512, 80: 704, 96: 768, 128: 1024}[hd]
     return TTTConfig(f"mid{hd}_{dtype}", L, d, H, hd, F, V, T, k, b, n_update, eta, dtype, init_std=std)
 
 
@@ -57,7 +57,7 @@ def test_tiny_fp32_full_sequence():
     assert dwr <= 1e-3
 
 
-@pytest.mark.parametrize("hd", [64, 80, 96, 128])
+@pytest.mark.parametrize("hd", [16, 32, 64, 80, 96, 128])
 def test_mid_bf16_ragged(hd):
     cfg = mid(hd)
     say(f"case: mid hd={hd} bf16 T={cfg.seq_len} b={cfg.chunk} k={cfg.window}")
