@@ -134,7 +134,7 @@ def test_empty_and_single_chunk():
     assert dl <= 2e-2 and dwr <= 5e-2
 
 
-@pytest.mark.parametrize("hd", [64, 80])
+@pytest.mark.parametrize("hd", [64, 80, 96, 128])
 def test_long_window_split_attention(hd):
     """A window of 1024 with 128-token chunks: the attention passes split the
     key range over several work-groups and the ring wraps (T > k + b)."""
@@ -226,7 +226,7 @@ def test_n_update_extremes(n_update, L):
 GROUP = 16384
 
 
-@pytest.mark.parametrize("dtype,hd,T", [("fp32", 16, GROUP + 300), ("bf16", 64, GROUP + 300)])
+@pytest.mark.parametrize("dtype,hd,T", [("fp32", 16, GROUP + 300), ("bf16", 64, GROUP + 300), ("bf16", 80, GROUP + 300)])
 def test_frozen_prefix_over_several_groups(dtype, hd, T):
     # T spans at least two groups (the last one ragged), so the blocks below the
     # updated ones run ahead over each group and the chunks pick their rows from it
