@@ -23,7 +23,7 @@ TTT_NO_UPDATE, TTT_NO_GRAPH = 1, 2
 
 def cfg_b(dtype="bf16", hd=64, T=600, L=3, n_update=2, k=256, b=128, V=1024, eta=0.5):
     H = 4
-    F = {64: 512, 80: 704}[hd]
+    F = {64: 512, 80: 704, 96: 768}[hd]
     return TTTConfig(f"batch{hd}_{dtype}", L, H * hd, H, hd, F, V, T, k, b, n_update, eta, dtype, init_std=0.02)
 
 
@@ -43,7 +43,7 @@ def _run(sess, tok, flags=0):
     return l.double().cpu().numpy(), [[x.double().cpu().numpy() for x in fs] for fs in f]
 
 
-@pytest.mark.parametrize("dtype,hd,T,B", [("bf16", 64, 600, 3), ("bf16", 80, 512, 2), ("fp32", 64, 450, 2)])
+@pytest.mark.parametrize("dtype,hd,T,B", [("bf16", 64, 600, 3), ("bf16", 80, 512, 2), ("bf16", 96, 700, 2), ("fp32", 64, 450, 2)])
 def test_batch_each_sequence_matches_oracle(dtype, hd, T, B):
     from oracle.ttt_oracle import Oracle
     from test_lm_prefill_amd import Session

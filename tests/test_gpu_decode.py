@@ -24,7 +24,7 @@ TTT_NO_UPDATE, TTT_NO_GRAPH = 1, 2
 
 def cfg_dec(dtype="bf16", hd=64, L=3, n_update=2, k=256, b=128, V=1024, eta=0.5):
     H = 4
-    F = {64: 512, 80: 704}[hd]
+    F = {64: 512, 80: 704, 96: 768, 128: 1024}[hd]
     return TTTConfig(f"dec{hd}_{dtype}", L, H * hd, H, hd, F, V, 2048, k, b, n_update, eta, dtype, init_std=0.02)
 
 
@@ -56,7 +56,7 @@ def _gpu_decode(sess, prompt, n, forced=None, flags=0):
             [x.double().cpu().numpy() for x in fast] if fast is not None else None)
 
 
-@pytest.mark.parametrize("hd,P", [(64, 256), (80, 200)])
+@pytest.mark.parametrize("hd,P", [(64, 256), (80, 200), (96, 300), (128, 384)])
 def test_decode_forced_bf16(hd, P):
     """Prompt of P positions (a whole number of chunks, or not), then 300 forced
     steps: two decode updates and an open chunk at the end."""

@@ -33,7 +33,7 @@ def _gpu():
 
 def mid(hd, dtype="bf16", T=600, n_update=2, L=3, eta=0.5, V=1024, k=256, b=128):
     H = 4
-    F = {16: 192, 64: 512, 80: 704, 96: 768}[hd]
+    F = {16: 192, 64: 512, 80: 704, 96: 768, 128: 1024}[hd]
     return TTTConfig(f"gains{hd}_{dtype}", L, H * hd, H, hd, F, V, T, k, b, n_update, eta, dtype, init_std=0.02)
 
 
@@ -76,7 +76,7 @@ def test_mid_fp32_gains_two_updated_blocks():
     check(cfg, gl, gf, ol, of, wn, "mid fp32 gains")
 
 
-@pytest.mark.parametrize("hd,qk", [(80, "small"), (64, "wide"), (96, "small")])
+@pytest.mark.parametrize("hd,qk", [(80, "small"), (64, "wide"), (96, "small"), (128, "small")])
 def test_mid_bf16_gains(hd, qk):
     """qk "small": q/k gains in [0.8, 1.05], whose score bound keeps the attention
     forward in fp16; "wide": q/k gains in [0.5, 1.5] as well, which moves it to bf16."""
