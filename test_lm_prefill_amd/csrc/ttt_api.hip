@@ -830,34 +830,48 @@ void scratch_setup(ttt_handle *h, hipStream_t st) {
   h->scratch = g_scratch_ptr[h->dev];
 }
 
+// Modelled time of one frozen block over a pass of `rows` rows (B sequences of `seq` rows
+// each), in units of one k-step of the 256 x 256 GEMM tile.  Each product takes
+// ceil(tiles / CUs) rounds, a round costing its K steps plus a fixed part (prologue,
+// epilogue, dispatch: about 609 steps, measured as 14.5 us against 24.4 us per 1024 of
+// K); the attention takes ceil(work-groups / 2 CUs) rounds of (k + 256) / 32 key tiles of
+// 256 queries, about 1.51 (k + 256) steps at head dim 80 (1.15 us per tile), scaled by hd.
+static double frozen_pass_cost(long rows, long seq, int d, int F, int H, int k, int cus) {
+  if (rows <= 0) return 0.0;
+  const int tw = 256;
+  const long rt = (rows + tw - 1) / tw;
+  const long N[4] = {3L * d, d, 2L * F, d}, K[4] = {d, d, d, F};
+  double t = 0.0;
+  for (int p = 0; p < 4; ++p) {
+    const long tiles = rt * ((N[p] + tw - 1) / tw);
+    t += (double)((tiles + cus - 1) / cus) * (609.0 + (double)K[p]);
+  }
+  const long wg = (seq + 255) / 256 * H * (rows / seq);
+  t += (double)((wg + 2L * cus - 1) / (2L * cus)) * 1.51 * (k + 256) * ((double)d / H) / 80.0;
+  return t;
+}
+
 // Tokens per sequence in a frozen-prefix group.  The group's products run unsplit on the
 // 256 x 256 tile (one work-group per CU) and its attention on work-groups of 256 queries of
-// one head (two per CU), so how full their last round is depends on the row count: at 2.7B
-// (d = 2560) 8192 rows give the d-wide O and down products 320 tiles, 1.25 rounds of 256
-// CUs with the second three-quarters idle, and 12288 rows 480 (1.9 rounds; measured 54 ms
-// per 128K prefill faster).  Among row counts from 8192 to 16384 (multiples of the chunk
-// over the B sequences) this takes the one whose QKV, O, gate/up, down and attention work
-// fills its rounds best, weighted by FLOPs per token, the smallest on ties: 12288 at 2.7B,
-// 16384 at 1.3B and 760M.
-long frozen_group_tokens(int d, int F, int H, int k, int b, int B, int cus) {
-  const int tw = 256;
-  const long nt[4] = {(3L * d + tw - 1) / tw, ((long)d + tw - 1) / tw, (2L * F + tw - 1) / tw, ((long)d + tw - 1) / tw};
-  const double w[5] = {6.0 * d * d, 2.0 * d * d, 4.0 * d * F, 2.0 * d * F, 4.0 * d * k};
+// one head (two per CU), so how full their rounds are depends on the row count, and a
+// ragged last group pays whole rounds for a few rows: at 2.7B 8192 rows leave the d-wide
+// O and down products at 1.25 rounds of 256 CUs.  Among row counts from 8192 to 16384
+// (multiples of the chunk over the B sequences) this takes the one whose groups over T
+// tokens cost least in the model above, the smallest on ties: 12288 at 2.7B and 128K (8192
+// and 16384 measured 55 and 35 ms slower per prefill), 16384 at 1.3B, 760M and 125M (125M:
+// 1.5 ms faster than 10240, whose last group is 2048 rows) and at 2.7B and 32K (the same
+// time as 12288 there).
+long frozen_group_tokens(int d, int F, int H, int k, int b, int B, long T, int cus) {
   const long step = (long)b * B;
   long best = std::max(1L, 8192 / step) * b;
-  double best_s = -1.0;
+  double best_t = -1.0;
   for (long rows = step * std::max(1L, 8192 / step); rows <= 16384; rows += step) {
-    double sc = 0.0;
-    for (int p = 0; p < 4; ++p) {
-      const long tiles = (rows + tw - 1) / tw * nt[p];
-      const long rounds = (tiles + cus - 1) / cus;
-      sc += w[p] * (double)tiles / (double)(rounds * cus);
-    }
-    const long wg = (rows / B + 255) / 256 * H * B;  // attention work-groups, two per CU
-    sc += w[4] * (double)wg / (double)((wg + 2L * cus - 1) / (2L * cus) * 2L * cus);
-    if (sc > best_s + 1e-9) {
-      best_s = sc;
-      best = rows / B;
+    const long G = rows / B, full = T / G, last = T % G;
+    const double t = (double)full * frozen_pass_cost(rows, G, d, F, H, k, cus) +
+                     frozen_pass_cost(last * B, last, d, F, H, k, cus);
+    if (best_t < 0.0 || t < best_t - 1e-9) {
+      best_t = t;
+      best = G;
     }
   }
   return best;
@@ -1026,7 +1040,8 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
       if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
     const long gmax = (c.max_tokens + c.chunk - 1) / c.chunk * (long)c.chunk;
-    h->G = (int)std::min<long>(frozen_group_tokens(c.d_model, c.d_ff, c.n_heads, c.window, c.chunk, h->B, cus), gmax);
+    h->G = (int)std::min<long>(frozen_group_tokens(c.d_model, c.d_ff, c.n_heads, c.window, c.chunk, h->B, gmax, cus),
+                               gmax);
     if (h->Lf == 0 || h->G <= c.chunk) h->G = 0;
   }
   h->ld_tok = c.max_tokens + 1;
