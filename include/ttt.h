@@ -126,9 +126,10 @@ typedef struct ttt_handle ttt_handle;
  * one vocabulary slab when n_update > 0 - no logits are kept, the backward
  * computes each slab's again; fp32 master fast weights) and copies/repacks
  * the weights.
- * G is 8192 to 16384 rows over all sequences (the count whose GEMM tiles fill the
- * GPU best), at most max_tokens rounded up to
- * a chunk, and 0 (no group pass) when that is not more than one chunk.
+ * G is 8192 to 16384 rows over all sequences (the count for which a model of the
+ * frozen pass over max_tokens tokens, in whole rounds of GEMM tiles and attention
+ * work-groups, is fastest), at most max_tokens rounded up to a chunk, and 0 (no
+ * group pass) when that is not more than one chunk.
  * `stream` is a hipStream_t (NULL = default stream); the call synchronises it
  * before returning.  *out receives the handle (NULL on failure).
  */
