@@ -221,8 +221,27 @@ def test_n_update_extremes(n_update, L):
     assert dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
 
 
+@pytest.mark.parametrize("dtype,k,b", [("bf16", 128, 128), ("fp32", 64, 64), ("bf16", 64, 64)])
+def test_window_equal_to_chunk(dtype, k, b):
+    """The smallest window the library accepts, k = b: a chunk's last query sees only
+    its own chunk, its first query the whole previous chunk but one key, and the ring
+    (k + b rows) holds exactly two chunks.  T is ragged."""
+    T = 9 * b + 37
+    cfg = mid(64, dtype=dtype, T=T, k=k, b=b)
+    say(f"case: window = chunk {dtype} k={k} b={b} T={T}")
+    tok = rand_tokens(T + 1, cfg.vocab, seed=400 + k)
+    sess, _ = gpu_session(cfg)
+    gl, gf = run_gpu(sess, tok)
+    ol, of, w = run_oracle(cfg, tok)
+    dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, w), f"k=b={k} {dtype}")
+    if dtype == "fp32":
+        assert dl <= 1e-4 and wr <= 1e-5 and dwr <= 1e-3
+    else:
+        assert dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
+
+
 # the largest frozen-prefix group the library forms for one sequence (it picks 8192 to
-# 16384 rows by how full the group's GEMM tile rounds are)
+# 16384 rows from a time model of the frozen pass)
 GROUP = 16384
 
 
