@@ -240,6 +240,26 @@ def test_window_equal_to_chunk(dtype, k, b):
         assert dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
 
 
+@pytest.mark.parametrize("dtype,V,b", [("bf16", 1040, 128), ("fp32", 1008, 128), ("bf16", 40016, 1024)])
+def test_ragged_vocab(dtype, V, b):
+    """A vocabulary that is a multiple of 16 but not of 128: the head's last column tile
+    and its cross-entropy partials are ragged; at b = 1024 the head backward streams the
+    vocabulary in slabs of 32768 columns, so the second slab is ragged too."""
+    T = 2 * b + 52
+    cfg = mid(64, dtype=dtype, T=T, V=V, b=b, k=max(256, b))
+    say(f"case: ragged vocab {dtype} V={V} b={b} T={T}")
+    tok = rand_tokens(cfg.seq_len + 1, V, seed=500 + V)
+    tok[::7] = V - 1  # the last vocabulary rows are labels too
+    sess, _ = gpu_session(cfg)
+    gl, gf = run_gpu(sess, tok)
+    ol, of, w = run_oracle(cfg, tok)
+    dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, w), f"V={V} {dtype}")
+    if dtype == "fp32":
+        assert dl <= 1e-4 and wr <= 1e-5 and dwr <= 1e-3
+    else:
+        assert dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
+
+
 # the largest frozen-prefix group the library forms for one sequence (it picks 8192 to
 # 16384 rows from a time model of the frozen pass)
 GROUP = 16384
