@@ -260,6 +260,21 @@ def test_ragged_vocab(dtype, V, b):
         assert dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
 
 
+def test_fp32_shapes_off_the_64_grid():
+    """fp32 mode accepts d_model, d_ff and vocab that are multiples of 16 only: three heads
+    of 16 (d = 48), d_ff = 208, V = 1008, T = 1 (one scored position) and a ragged T."""
+    cfg = TTTConfig("odd_fp32", 2, 48, 3, 16, 208, 1008, 345, 128, 64, 1, 0.5, "fp32", init_std=0.05)
+    say("case: fp32 d=48 F=208 V=1008")
+    sess, _ = gpu_session(cfg)
+    for T, seed in ((1, 601), (345, 602)):
+        tok = rand_tokens(T + 1, cfg.vocab, seed=seed)
+        gl, gf = run_gpu(sess, tok)
+        ol, of, w = run_oracle(cfg, tok)
+        dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, w), f"odd fp32 T={T}")
+        assert len(gl) == T
+        assert dl <= 1e-4 and wr <= 1e-5 and dwr <= 1e-3
+
+
 # the largest frozen-prefix group the library forms for one sequence (it picks 8192 to
 # 16384 rows from a time model of the frozen pass)
 GROUP = 16384
