@@ -64,6 +64,9 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
   // lane holds C[m][n .. n+3] for m = m0 + wm*64 + 16 j + lr, n = n0 + wn*WN + 16 i + 4 lq
   const int g4 = lq * 4;
   if constexpr (EPI == EPI_CE) {
+    // partial slots exist for both 64-column halves of every 128-column tile of N (what
+    // the 128-wide kernels write); the second half of a 256-wide tile past them has none
+    const bool slot = n0 + wn * WN < (g.N + 127) / 128 * 128;
     const int lab_base = *g.pos0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -88,7 +91,7 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
             if (n < g.N && acc[i][j][r] == mx) ai = n;
           }
         ai = group4_min_int(ai);
-        if (m < g.M && lq == 0) g.part_arg[(long)m * g.part_ld + tn * 2 + wn] = ai + g.col_off;
+        if (m < g.M && lq == 0 && slot) g.part_arg[(long)m * g.part_ld + tn * 2 + wn] = ai + g.col_off;
       }
       float s = 0.f;
 #pragma unroll
@@ -102,7 +105,7 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
           }
         }
       s = group4_sum(s);
-      if (m < g.M && lq == 0) g.part[(long)m * g.part_ld + tn * 2 + wn] = make_float2(mx, s);
+      if (m < g.M && lq == 0 && slot) g.part[(long)m * g.part_ld + tn * 2 + wn] = make_float2(mx, s);
     }
     return;
   }

@@ -245,14 +245,21 @@ def test_ragged_vocab(dtype, V, b):
     """A vocabulary that is a multiple of 16 but not of 128: the head's last column tile
     and its cross-entropy partials are ragged; at b = 1024 the head backward streams the
     vocabulary in slabs of 32768 columns, so the second slab is ragged too."""
+    from ttt_inputs import make_weights_np, make_weights_torch
     T = 2 * b + 52
     cfg = mid(64, dtype=dtype, T=T, V=V, b=b, k=max(256, b))
     say(f"case: ragged vocab {dtype} V={V} b={b} T={T}")
     tok = rand_tokens(cfg.seq_len + 1, V, seed=500 + V)
     tok[::7] = V - 1  # the last vocabulary rows are labels too
-    sess, _ = gpu_session(cfg)
+    # the first 128 head rows scaled by 8 (exact): their logits dominate every row's
+    # softmax, so a partial slot of them lost or overwritten would move the losses by O(1)
+    wt = make_weights_torch(cfg, "cuda")
+    wn = make_weights_np(cfg)
+    wt["lm_head"][:128] *= 8
+    wn["lm_head"][:128] *= 8
+    sess, _ = gpu_session(cfg, weights=wt)
     gl, gf = run_gpu(sess, tok)
-    ol, of, w = run_oracle(cfg, tok)
+    ol, of, w = run_oracle(cfg, tok, weights_np=wn)
     dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, w), f"V={V} {dtype}")
     if dtype == "fp32":
         assert dl <= 1e-4 and wr <= 1e-5 and dwr <= 1e-3
