@@ -76,13 +76,25 @@ def algorithmic_flops(cfg, T, update=True):
     return f
 
 
-def recompute_flops(cfg, T, update=True):
-    """FLOPs the path spends again on purpose and that are not algorithmic: the head
-    backward computes each vocabulary slab's logits a second time (2 d V per token)
-    instead of keeping the [b, V] logits of the forward."""
-    if not update or cfg.n_update == 0:
+def head_single_pass(cfg, w):
+    """Whether the library runs the head's loss and gradient in one pass for these weights:
+    its create-time test, 2 * 1.01 sqrt(d) max|g_final| max_v |W_v| + ln V <= 126, which
+    bounds every row's logit spread around its label's logit (only used here to book the
+    head's FLOPs)."""
+    import torch
+    wn = float(torch.linalg.vector_norm(w["lm_head"].float(), dim=1).max())
+    gm = float(w["final_norm"].float().abs().max())
+    b = 1.01 * wn * gm * np.sqrt(cfg.d_model)
+    return bool(np.isfinite(b) and 2 * b + np.log(cfg.vocab) <= 126.0)
+
+
+def recompute_flops(cfg, T, update=True, single_pass=True):
+    """FLOPs the path spends again on purpose and that are not algorithmic: none when the
+    head runs its loss and gradient in one pass; otherwise the head backward computes each
+    vocabulary slab's logits a second time after the cross-entropy pass (2 d V per token)."""
+    if not update or cfg.n_update == 0 or single_pass:
         return {}
-    return {"gemm_dlogits": 2 * cfg.d_model * cfg.vocab * T}
+    return {"gemm_lmhead_ce": 2 * cfg.d_model * cfg.vocab * T}
 
 
 def algorithmic_bytes(cfg, T, update=True):
@@ -201,7 +213,7 @@ def gpu_bench(cfg, steps, warmup, profile=True, gains=None):
         log(f"[bench] timed {K} steps flags={flags} T={t.numel() - 1}: {ms / K:.2f} ms/step")
         return ms / K
 
-    res = {"ms_ttt": timed(0, steps, warmup)}
+    res = {"ms_ttt": timed(0, steps, warmup), "head_single_pass": head_single_pass(cfg, w)}
     losses, _ = sess.prefill(tok, want_fast=False, check=True)
     res["mean_loss"] = float(losses.mean().item())
     res["ms_swa"] = timed(TTT_NO_UPDATE, steps, 1)
@@ -562,7 +574,7 @@ def summarize(cfg, r, steps):
     total_tf = sum(flops.values()) / 1e12
     swa_tf = sum(algorithmic_flops(cfg, T, update=False).values()) / 1e12
     ov = overhead_flops(cfg, T)
-    rflops = recompute_flops(cfg, T, update=True)
+    rflops = recompute_flops(cfg, T, update=True, single_pass=r.get("head_single_pass", True))
     out = {
         "ms_per_step": round(r["ms_ttt"], 3),
         "ms_per_1k_tokens": round(r["ms_ttt"] * 1024 / T, 4),
@@ -571,6 +583,7 @@ def summarize(cfg, r, steps):
         "algorithmic_tflop_per_step": round(total_tf, 2),
         "overhead_tflop_per_step": {"hilo_fast_forward": round(sum(ov.values()) / 1e12, 2),
                                     "head_backward_logits_recompute": round(sum(rflops.values()) / 1e12, 2)},
+        "head_single_pass": r.get("head_single_pass"),
         "swa_only": {"ms_per_step": round(r["ms_swa"], 3), "ms_per_1k_tokens": round(r["ms_swa"] * 1024 / T, 4),
                      "tokens_per_s": round(T / (r["ms_swa"] / 1e3), 1),
                      "mfma_util_pct": round(100 * swa_tf / (r["ms_swa"] / 1e3) / peak, 2)},

@@ -122,10 +122,14 @@ typedef struct ttt_handle ttt_handle;
  * Creates a handle on the current HIP device: validates cfg, allocates the
  * bounded state (per-layer key/value rings of k+b rows, or k+G rows for the
  * blocks below the updated ones, which run ahead over groups of G tokens;
- * activations of one chunk and of one group; the cross-entropy gradient of
- * one vocabulary slab when n_update > 0 - no logits are kept, the backward
- * computes each slab's again; fp32 master fast weights) and copies/repacks
- * the weights.
+ * activations of one chunk and of one group; the exponentiated logits of
+ * one vocabulary slab when n_update > 0 - no [b, V] logits are kept; fp32
+ * master fast weights) and copies/repacks the weights.  It reads the head and
+ * final-norm weights once to decide how the head runs: one pass over the
+ * vocabulary for losses and gradient when the weights bound how far any
+ * logit can lie from its row's label logit, 2.02 sqrt(d) max|final_norm|
+ * max_v |lm_head row v|, by 126 - ln V; else a cross-entropy pass first and
+ * a second pass for the gradient (same results up to rounding).
  * G is 8192 to 16384 rows over all sequences (the count for which a model of the
  * frozen pass over max_tokens tokens, in whole rounds of GEMM tiles and attention
  * work-groups, is fastest), at most max_tokens rounded up to a chunk, and 0 (no

@@ -66,6 +66,13 @@ hipError_t swiglu_bwd_launch(int dtype, const void *GU, const void *dhmid, void 
 
 // Combines per-row partials (max, sum exp) into lse[m] and
 // losses[*pos0 + m] = lse - zlab[m].
+// Per-row shift of the single-pass head: shift[m] = n_f[m] . W[label] + off (one wave per
+// row; f16: both operands fp16 in bf16 mode, else the working dtype).
+hipError_t head_shift_launch(int dtype, bool f16, const void *nf, const void *W, const int *labs, const int *pos0,
+                             float *shift, int n, int d, float off, hipStream_t st);
+// dn[m] = alpha (dn[m] exp(shift[m] - lse[m]) - W[label of m]) over the d columns of each row.
+hipError_t head_grad_finish_launch(int dtype, bool f16, float *dn, const float *shift, const float *lse, const void *W,
+                                   const int *labs, const int *pos0, int n, int d, float alpha, hipStream_t st);
 hipError_t ce_reduce_launch(const float2 *part, int P, const float *zlab, const int *pos0, float *lse,
                             float *losses, int n, hipStream_t st);
 
@@ -114,6 +121,8 @@ hipError_t bf16_to_f16_launch(const void *src, long lds, void *dst, long ldd, in
                               float scale = 1.f);
 // *out = max(*out, bit pattern of max |x|) over a [rows][cols] block with row
 // stride ld (dtype 0 fp32, 1 bf16); *out must start at 0.  NaN counts as largest.
+// *out = max(*out, largest row norm of x [rows][cols]) as float bits (set *out to 0 first).
+hipError_t rownorm_max_launch(int dtype, const void *x, long ld, int rows, int cols, unsigned *out, hipStream_t st);
 hipError_t absmax_launch(int dtype, const void *x, long ld, int rows, int cols, unsigned *out, hipStream_t st);
 
 hipError_t set_int_launch(int *p, int v, hipStream_t st);

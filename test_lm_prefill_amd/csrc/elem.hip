@@ -334,6 +334,47 @@ __global__ __launch_bounds__(256) void ce_reduce_kernel(const float2 *part, int 
   }
 }
 
+// ----------------------------------------------------------------- head softmax shift and gradient
+// shift[m] = n_f[m] . W[label of m] + off: the label's logit (in fp32, from the head's own
+// operands) plus a margin, the per-row shift of the single-pass head.  One wave per row.
+template <typename TA, typename TW>
+__global__ __launch_bounds__(256) void head_shift_kernel(const TA *nf, const TW *W, const int *labs, const int *pos0,
+                                                         float *shift, int n, int d, float off) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= n) return;
+  const long lab = labs[*pos0 + m];
+  float acc = 0.f;
+  for (int i = lane * 4; i < d; i += 256) {
+    float a[4], w[4];
+    load4<TA>(nf + (long)m * d + i, a);
+    load4<TW>(W + lab * d + i, w);
+    acc += a[0] * w[0] + a[1] * w[1] + a[2] * w[2] + a[3] * w[3];
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) shift[m] = acc + off;
+}
+
+// dn[m] = alpha (dn[m] exp(shift[m] - lse[m]) - W[label of m]): the unnormalised softmax
+// product over the vocabulary divided by its sum (sum = exp(lse - shift)), minus the
+// label's row.  One work-group per row.
+template <typename TW>
+__global__ __launch_bounds__(256) void head_grad_finish_kernel(float *dn, const float *shift, const float *lse,
+                                                               const TW *W, const int *labs, const int *pos0, int d,
+                                                               float alpha) {
+  const int m = blockIdx.x;
+  const long lab = labs[*pos0 + m];
+  const float sc = __expf(shift[m] - lse[m]);
+  for (int i = threadIdx.x * 4; i < d; i += 1024) {
+    float w[4];
+    load4<TW>(W + lab * d + i, w);
+    float4 *p = reinterpret_cast<float4 *>(dn + (long)m * d + i);
+    const float4 v = *p;
+    *p = make_float4(alpha * (v.x * sc - w[0]), alpha * (v.y * sc - w[1]), alpha * (v.z * sc - w[2]),
+                     alpha * (v.w * sc - w[3]));
+  }
+}
+
 __global__ void rope_table_kernel(float2 *cs, long max_pos, int hd, double theta) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   const int half = hd / 2;
@@ -442,6 +483,22 @@ __global__ void bf16_to_f16_kernel(const bf16_t *src, long lds, f16_t *dst, long
 
 // *out = max(*out, bits of max |x|) over x[r * ld + c], r < rows, c < cols
 // (non-negative floats order like their bit patterns; a NaN compares highest).
+// out = max(out, largest Euclidean norm of a row) as float bits (norms are non-negative, so
+// their bit patterns order like the values; NaN rows give NaN bits, which compare above).
+template <typename T>
+__global__ __launch_bounds__(256) void rownorm_max_kernel(const T *x, long ld, int rows, int cols, unsigned *out) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  float s = 0.f;
+  for (int i = lane; i < cols; i += 64) {
+    const float v = to_f(x[(long)r * ld + i]);
+    s += v * v;
+  }
+  s = wave_sum(s);
+  if (lane == 0) atomicMax(out, __float_as_uint(sqrtf(s)));
+}
+
 template <typename T>
 __global__ void absmax_kernel(const T *x, long ld, int rows, int cols, unsigned *out) {
   float m = 0.f;
@@ -684,6 +741,43 @@ hipError_t decode_pick_launch(const float2 *part, const int *part_arg, int P, co
   return hipGetLastError();
 }
 
+hipError_t head_shift_launch(int dtype, bool f16, const void *nf, const void *W, const int *labs, const int *pos0,
+                             float *shift, int n, int d, float off, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (d % 4 != 0) return hipErrorInvalidValue;
+  const dim3 grid((n + 3) / 4);
+  if (f16) {
+    if (dtype != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((head_shift_kernel<f16_t, f16_t>), grid, dim3(256), 0, st, (const f16_t *)nf, (const f16_t *)W,
+                       labs, pos0, shift, n, d, off);
+  } else if (dtype == 0) {
+    hipLaunchKernelGGL((head_shift_kernel<float, float>), grid, dim3(256), 0, st, (const float *)nf, (const float *)W,
+                       labs, pos0, shift, n, d, off);
+  } else {
+    hipLaunchKernelGGL((head_shift_kernel<bf16_t, bf16_t>), grid, dim3(256), 0, st, (const bf16_t *)nf,
+                       (const bf16_t *)W, labs, pos0, shift, n, d, off);
+  }
+  return hipGetLastError();
+}
+
+hipError_t head_grad_finish_launch(int dtype, bool f16, float *dn, const float *shift, const float *lse, const void *W,
+                                   const int *labs, const int *pos0, int n, int d, float alpha, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (d % 4 != 0) return hipErrorInvalidValue;
+  if (f16) {
+    if (dtype != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(head_grad_finish_kernel<f16_t>, dim3(n), dim3(256), 0, st, dn, shift, lse, (const f16_t *)W, labs,
+                       pos0, d, alpha);
+  } else if (dtype == 0) {
+    hipLaunchKernelGGL(head_grad_finish_kernel<float>, dim3(n), dim3(256), 0, st, dn, shift, lse, (const float *)W, labs,
+                       pos0, d, alpha);
+  } else {
+    hipLaunchKernelGGL(head_grad_finish_kernel<bf16_t>, dim3(n), dim3(256), 0, st, dn, shift, lse, (const bf16_t *)W,
+                       labs, pos0, d, alpha);
+  }
+  return hipGetLastError();
+}
+
 hipError_t ce_reduce_launch(const float2 *part, int P, const float *zlab, const int *pos0, float *lse, float *losses,
                             int n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
@@ -773,6 +867,15 @@ hipError_t bf16_to_f16_launch(const void *src, long lds, void *dst, long ldd, in
   if (tot <= 0) return hipSuccess;
   hipLaunchKernelGGL(bf16_to_f16_kernel, dim3(blocks_for(tot)), dim3(256), 0, st, (const bf16_t *)src, lds,
                      (f16_t *)dst, ldd, rows, cols, scale);
+  return hipGetLastError();
+}
+
+hipError_t rownorm_max_launch(int dtype, const void *x, long ld, int rows, int cols, unsigned *out, hipStream_t st) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  const dim3 grid((rows + 3) / 4);
+#define K_(T, ...) hipLaunchKernelGGL(rownorm_max_kernel<T>, grid, dim3(256), 0, st, (const T *)x, ld, rows, cols, out)
+  DT_DISPATCH(dtype, K_, 0);
+#undef K_
   return hipGetLastError();
 }
 

@@ -11,8 +11,12 @@ enum GemmEpi {
   EPI_SWIGLU = 3,    // C (T)[m, unit] = silu(gate) * up over 16-row interleaved gate/up
                      // blocks of B; C2 (T, optional) = raw gate/up pre-activations
   EPI_CE = 4,        // per-row partial (max, sum exp) over the tile's columns and the
-                     // label logit -> part / zlab   (cross-entropy, first pass)
-  EPI_DLOGITS = 5,   // C (T) = (exp(acc - lse[m]) - [n + col_off == label]) * alpha
+                     // label logit -> part / zlab   (cross-entropy)
+  EPI_PROBS = 5,     // C (T) = exp(acc - rowf[m]) with a per-row shift rowf; per row and
+                     // 64-column slot the partial (rowf[m], sum of those exponentials in
+                     // fp32) at slot col_off / 64 + local slot, and the label logit -> zlab
+                     // (cross-entropy and the unnormalised softmax in one pass; C, part and
+                     // zlab may each be null)
   EPI_SGD = 6,       // Cf (fp32 master) -= alpha * acc; C (T) = hi = round(c_scale * Cf) and,
                      // when C2 is set, C2 (T) = round(c_scale * Cf - hi): the working copy as
                      // hi + lo, scaled by c_scale (inner SGD); when CT is set, also
@@ -30,12 +34,12 @@ struct GemmArgs {
   long ldcf;
   void *C2;
   long ldc2;
-  const float *rowf;  // lse per row (EPI_DLOGITS)
+  const float *rowf;  // per-row shift (EPI_PROBS)
   const int *rowi;    // labels: label of row m = rowi[*pos0 + m]
   const int *pos0;
-  float2 *part;       // EPI_CE partials [M][part_ld]
+  float2 *part;       // EPI_CE / EPI_PROBS partials [M][part_ld]
   int part_ld;
-  float *zlab;        // EPI_CE label logits [M]
+  float *zlab;        // EPI_CE / EPI_PROBS label logits [M]
   int *part_arg;      // EPI_CE, optional: per-tile argmax column (+ col_off) beside each partial, lowest on ties
   float alpha;
   int col_off;

@@ -244,6 +244,38 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const GemmArgs g) {
     }
     return;
   }
+  if constexpr (EPI == EPI_PROBS) {
+    // the partial slots of EPI_CE (every 64-column half of a 128-column tile), from slot
+    // col_off / 64 on; every partial of a row carries the row's shift
+    const int lab_base = *g.pos0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wm * 64 + j * 16 + lr;
+      const bool mok = m < g.M;
+      const int lab = mok ? g.rowi[lab_base + m] : -1;
+      const float c = mok ? g.rowf[m] : 0.f;
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + wn * 64 + i * 16 + g4;
+        float e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e[r] = 0.f;
+          if (n + r < g.N) {
+            e[r] = exp2f((acc[i][j][r] - c) * LOG2E_F);
+            s += e[r];
+            if (g.zlab && n + r + g.col_off == lab) g.zlab[m] = acc[i][j][r];
+          }
+        }
+        if (g.C && mok && n < g.N) store4<T>(reinterpret_cast<T *>(g.C) + (long)m * g.ldc + n, e);
+      }
+      s = group4_sum(s);
+      if (g.part && mok && (lane >> 4) == 0)
+        g.part[(long)m * g.part_ld + g.col_off / 64 + tn * 2 + wn] = make_float2(c, s);
+    }
+    return;
+  }
   if constexpr (EPI == EPI_SWIGLU) {
     T *Hm = reinterpret_cast<T *>(g.C);
     T *GU = reinterpret_cast<T *>(g.C2);
@@ -276,12 +308,6 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const GemmArgs g) {
   for (int j = 0; j < 4; ++j) {
     const int m = m0 + wm * 64 + j * 16 + lr;
     if (m >= g.M) continue;
-    int lab = -1;
-    float lse = 0.f;
-    if constexpr (EPI == EPI_DLOGITS) {
-      lab = g.rowi[*g.pos0 + m];
-      lse = g.rowf[m];
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int n = n0 + wn * 64 + i * 16 + g4;
@@ -298,14 +324,6 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const GemmArgs g) {
         *p = make_float4(o.x + v[0] * sc, o.y + v[1] * sc, o.z + v[2] * sc, o.w + v[3] * sc);
       } else if constexpr (EPI == EPI_PARTIAL) {
         store4<float>(g.ws + ((long)blockIdx.z * g.M + m) * g.N + n, v);
-      } else if constexpr (EPI == EPI_DLOGITS) {
-        float d[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float p = __expf(v[r] - lse);
-          d[r] = (p - ((n + r + g.col_off == lab) ? 1.f : 0.f)) * g.alpha;
-        }
-        store4<T>(reinterpret_cast<T *>(g.C) + (long)m * g.ldc + n, d);
       } else if constexpr (EPI == EPI_SGD) {
         float4 *pw = reinterpret_cast<float4 *>(g.Cf + (long)m * g.ldcf + n);
         float4 w = *pw;
@@ -375,7 +393,7 @@ hipError_t dispatch_epi(int epi, const GemmArgs &g, hipStream_t st, int split) {
     case EPI_ADD_F32: return launch_t<T, AK, BKc, EPI_ADD_F32>(g, st, 1);
     case EPI_SWIGLU: return launch_t<T, AK, BKc, EPI_SWIGLU>(g, st, 1);
     case EPI_CE: return launch_t<T, AK, BKc, EPI_CE>(g, st, 1);
-    case EPI_DLOGITS: return launch_t<T, AK, BKc, EPI_DLOGITS>(g, st, 1);
+    case EPI_PROBS: return launch_t<T, AK, BKc, EPI_PROBS>(g, st, 1);
     case EPI_SGD: return launch_t<T, AK, BKc, EPI_SGD>(g, st, 1);
   }
   return hipErrorInvalidValue;

@@ -109,6 +109,39 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
     }
     return;
   }
+  if constexpr (EPI == EPI_PROBS) {
+    // same partial slots as EPI_CE (every 64-column half of a 128-column tile of N), at
+    // slot col_off / 64 onwards; every partial of a row carries the row's shift
+    const bool slot = n0 + wn * WN < (g.N + 127) / 128 * 128;
+    const int lab_base = *g.pos0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wm * 64 + j * 16 + lr;
+      const bool mok = m < g.M;
+      const int lab = mok ? g.rowi[lab_base + m] : -1;
+      const float c = mok ? g.rowf[m] : 0.f;
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int n = n0 + wn * WN + i * 16 + g4;
+        float e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e[r] = 0.f;
+          if (n + r < g.N) {
+            e[r] = fast_exp2((acc[i][j][r] - c) * LOG2E_F);
+            s += e[r];
+            if (g.zlab && n + r + g.col_off == lab) g.zlab[m] = acc[i][j][r];
+          }
+        }
+        if (g.C && mok && n < g.N) store_c4(g, g.C, (long)m * g.ldc + n, e);
+      }
+      s = group4_sum(s);
+      if (g.part && mok && lq == 0 && slot)
+        g.part[(long)m * g.part_ld + g.col_off / 64 + tn * 2 + wn] = make_float2(c, s);
+    }
+    return;
+  }
   if constexpr (EPI == EPI_SWIGLU) {
     void *GU = g.C2;
 #pragma unroll
@@ -140,12 +173,6 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
   for (int j = 0; j < 4; ++j) {
     const int m = m0 + wm * 64 + j * 16 + lr;
     if (m >= g.M) continue;
-    int lab = -1;
-    float lse = 0.f;
-    if constexpr (EPI == EPI_DLOGITS) {
-      lab = g.rowi[*g.pos0 + m];
-      lse = g.rowf[m];
-    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int n = n0 + wn * WN + i * 16 + g4;
@@ -162,14 +189,6 @@ DEVI void gemm2_epilogue(const GemmArgs &g, Acc &acc, int m0, int n0, int tn, in
         *p = make_float4(o.x + v[0] * sc, o.y + v[1] * sc, o.z + v[2] * sc, o.w + v[3] * sc);
       } else if constexpr (EPI == 100) {  // split-K partial
         store4<float>(g.ws + ((long)blockIdx.z * g.M + m) * g.N + n, v);
-      } else if constexpr (EPI == EPI_DLOGITS) {
-        float d[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __expf(v[r] - lse);
-          d[r] = (p - ((n + r + g.col_off == lab) ? 1.f : 0.f)) * g.alpha;
-        }
-        store_c4(g, g.C, (long)m * g.ldc + n, d);
       } else if constexpr (EPI == EPI_SGD) {
         float4 *pw = reinterpret_cast<float4 *>(g.Cf + (long)m * g.ldcf + n);
         float4 w;
@@ -425,7 +444,7 @@ __global__ __launch_bounds__(NT, 2) void gemm5_kernel(const GemmArgs g) {
   template __global__ void gemm5_kernel<TI, EPI_ADD_F32>(const GemmArgs);   \
   template __global__ void gemm5_kernel<TI, EPI_SWIGLU>(const GemmArgs);    \
   template __global__ void gemm5_kernel<TI, EPI_CE>(const GemmArgs);        \
-  template __global__ void gemm5_kernel<TI, EPI_DLOGITS>(const GemmArgs);   \
+  template __global__ void gemm5_kernel<TI, EPI_PROBS>(const GemmArgs);   \
   template __global__ void gemm5_kernel<TI, EPI_SGD>(const GemmArgs);       \
   template __global__ void gemm5_kernel<TI, 100>(const GemmArgs);
 G5_INST(bf16_t)
@@ -446,7 +465,7 @@ template <typename TI> hipError_t launch5(int epi, const GemmArgs &g, hipStream_
     case EPI_ADD_F32: return launch5_e<TI, EPI_ADD_F32>(g, st);
     case EPI_SWIGLU: return launch5_e<TI, EPI_SWIGLU>(g, st);
     case EPI_CE: return launch5_e<TI, EPI_CE>(g, st);
-    case EPI_DLOGITS: return launch5_e<TI, EPI_DLOGITS>(g, st);
+    case EPI_PROBS: return launch5_e<TI, EPI_PROBS>(g, st);
     case EPI_SGD: return launch5_e<TI, EPI_SGD>(g, st);
   }
   return hipErrorInvalidValue;
@@ -683,7 +702,7 @@ __global__ __launch_bounds__(g8::NT8, 1) void gemm8_kernel(const GemmArgs g) {
   template __global__ void gemm8_kernel<TI, EPI_ADD_F32>(const GemmArgs);   \
   template __global__ void gemm8_kernel<TI, EPI_SWIGLU>(const GemmArgs);    \
   template __global__ void gemm8_kernel<TI, EPI_CE>(const GemmArgs);        \
-  template __global__ void gemm8_kernel<TI, EPI_DLOGITS>(const GemmArgs);   \
+  template __global__ void gemm8_kernel<TI, EPI_PROBS>(const GemmArgs);   \
   template __global__ void gemm8_kernel<TI, 100>(const GemmArgs);
 G8_INST(bf16_t)
 G8_INST(f16_t)
@@ -702,7 +721,7 @@ template <typename TI> hipError_t launch8(int epi, const GemmArgs &g, hipStream_
     case EPI_ADD_F32: return launch8_e<TI, EPI_ADD_F32>(g, st);
     case EPI_SWIGLU: return launch8_e<TI, EPI_SWIGLU>(g, st);
     case EPI_CE: return launch8_e<TI, EPI_CE>(g, st);
-    case EPI_DLOGITS: return launch8_e<TI, EPI_DLOGITS>(g, st);
+    case EPI_PROBS: return launch8_e<TI, EPI_PROBS>(g, st);
   }
   return hipErrorInvalidValue;
 }

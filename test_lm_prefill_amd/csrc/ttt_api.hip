@@ -5,10 +5,12 @@
 //   forward  embed -> L x [RMSNorm, QKV GEMM, QK-norm + rotary + ring write,
 //            window attention, O GEMM (+residual), RMSNorm, gate|up GEMM with
 //            fused SwiGLU, down GEMM (+residual)] -> final RMSNorm ->
-//            LM-head GEMM with fused cross-entropy partials -> row reduce
-//            (losses recorded here, before any update: Alg. 1 step 3.3)
-//   backward (skipped with TTT_NO_UPDATE) dlogits slab by slab and dX of the
-//            head -> final RMSNorm backward -> for blocks L-1 .. L-n_u: MLP
+//            LM-head GEMM, slab by slab, with the cross-entropy partials and
+//            the shifted exponentials fused, and the product of those with the
+//            head (dX of the head) -> row reduce (losses recorded here, before
+//            any update: Alg. 1 step 3.3)
+//   backward (skipped with TTT_NO_UPDATE) the head's dX finished from the
+//            losses -> final RMSNorm backward -> for blocks L-1 .. L-n_u: MLP
 //            backward with the fast-weight gradient GEMMs carrying the SGD
 //            step in their epilogue (Eq. 9), then (above block L-n_u) the
 //            attention sub-block backward; keys/values of earlier chunks are
@@ -128,6 +130,8 @@ struct ttt_handle {
   void *ring_base = nullptr;
   size_t ring_bytes = 0;
   float *h = nullptr, *lse2 = nullptr, *hf = nullptr, *rf = nullptr, *zlab = nullptr, *lse = nullptr;
+  float *shift = nullptr;  // per-row shift of the single-pass head [B b]
+  bool head1 = false;      // the head's loss and gradient in one pass (exact for these weights)
   float *qkv = nullptr;  // [b][3d] fp32
   void *a = nullptr, *qh = nullptr, *o = nullptr, *m = nullptr, *hmid = nullptr, *nf = nullptr;
   float2 *part = nullptr;
@@ -222,12 +226,12 @@ char *off(void *p, size_t bytes) { return reinterpret_cast<char *>(p) + bytes; }
 
 enum KClass {
   K_EMBED, K_RMSNORM, K_GEMM_QKV, K_ROPE, K_ATTN_FWD, K_GEMM_O, K_GEMM_GATE_UP, K_GEMM_DOWN, K_GEMM_HEAD_CE,
-  K_CE_REDUCE, K_GEMM_DLOGITS, K_GEMM_DN, K_RMSNORM_BWD, K_GEMM_DHMID, K_GEMM_DW_SGD, K_SWIGLU_BWD, K_GEMM_DM,
+  K_CE_REDUCE, K_GEMM_DN, K_RMSNORM_BWD, K_GEMM_DHMID, K_GEMM_DW_SGD, K_SWIGLU_BWD, K_GEMM_DM,
   K_GEMM_DO, K_ATTN_BWD_PRE, K_ATTN_BWD_DQ, K_ATTN_BWD_DKDV, K_ROPE_BWD, K_GEMM_DA, K_TRANSPOSE, K_SPLITK_REDUCE, K_ATTN_MERGE, K_MISC, K_NCLASS
 };
 const char *const kclass_names[K_NCLASS] = {
     "embed", "rmsnorm", "gemm_qkv", "qknorm_rope_ring", "attn_fwd", "gemm_o_residual", "gemm_gate_up_swiglu",
-    "gemm_down_residual", "gemm_lmhead_ce", "ce_reduce", "gemm_dlogits", "gemm_dn", "rmsnorm_bwd", "gemm_dhmid",
+    "gemm_down_residual", "gemm_lmhead_ce", "ce_reduce", "gemm_dn", "rmsnorm_bwd", "gemm_dhmid",
     "gemm_dw_sgd", "swiglu_bwd", "gemm_dm", "gemm_do", "attn_bwd_pre", "attn_bwd_dq", "attn_bwd_dkdv",
     "qknorm_rope_bwd", "gemm_da", "transpose", "splitk_reduce", "attn_merge", "misc"};
 
@@ -317,7 +321,9 @@ ResidualPartials gemm_residual(ttt_handle *h, int cls, GemmArgs g, hipStream_t s
 enum ChunkMode {
   MODE_PREFILL = 0,   // losses[pos] = loss of the stored label
   MODE_GREEDY = 1,    // decode: also picks the argmax as the next token (tok[pos + n]) with its loss
-  MODE_RECOMPUTE = 2  // a decoded chunk run again for its update; losses go to rlosses
+  MODE_RECOMPUTE = 2, // a decoded chunk run again for its update; losses go to rlosses
+  MODE_FORCED = 3     // decode of a given token: losses[pos] as MODE_PREFILL, computed as a greedy step
+                      // computes them (so that forced and greedy decodes agree bit for bit)
 };
 
 // lb > 0: blocks below lb were run ahead by the frozen-prefix pass (lead); the chunk's
@@ -513,48 +519,82 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
                               eps, st, f16, pend));
     pend = ResidualPartials();
   }
-  {
+  const bool head_bwd = update && h->nu > 0;
+  if (mode == MODE_GREEDY || mode == MODE_FORCED) {
+    // a decode step: per-tile (max, sum) partials and each tile's argmax for the pick
     GemmArgs g = gargs(h->nf, d, h->lm_head, d, Bn, h->V, d);
     g.rowi = h->labs;  // label of row r = labs[*zero + r]
     g.pos0 = h->zero;
     g.part = h->part;
     g.part_ld = h->P;
     g.zlab = h->zlab;
-    if (mode == MODE_GREEDY) g.part_arg = h->part_arg;
-    // with an update the backward computes these logits again slab by slab with the tiled
-    // kernel: the forward takes the same kernel (never the few-row one), so both see the
-    // same values
-    gemm(h, K_GEMM_HEAD_CE, true, true, EPI_CE, g, st, true, update && h->nu > 0);
-  }
-  {
-    PROF(K_CE_REDUCE);
-    HIPCHK(ce_reduce_launch(h->part, h->P, h->zlab, h->zero, h->lse, h->closs, Bn, st));
-    HIPCHK(scatter_chunk_losses_launch(h->closs, mode == MODE_RECOMPUTE ? h->rlosses : h->losses, h->cfg.max_tokens,
-                                       h->pos0, n, B, st));
-    if (mode == MODE_GREEDY)  // one sequence
-      HIPCHK(decode_pick_launch(h->part, h->part_arg, h->P, h->lse, h->pos0, n, h->tok, h->losses, st));
-  }
-  h->launches += mode == MODE_GREEDY ? 4 : 3;
-
-  if (update && h->nu > 0) {
-    const int np = (n + 63) / 64 * 64;  // token count padded for the weight-gradient GEMMs
-    // --- dlogits (softmax - onehot) * 2^s / n, streamed over vocab slabs, and dn = dz W_lm.
-    // No logits are kept from the forward: each slab's logits are computed again by the
-    // LM-head product (the forward's kernel and reduction order, so the same values) and
-    // turned into the gradient in its epilogue with the saved log-sum-exp; only the
-    // slab's [B b, Vs] gradient goes to memory before the dn product reads it.
+    g.part_arg = h->part_arg;
+    gemm(h, K_GEMM_HEAD_CE, true, true, EPI_CE, g, st, true);
+  } else if (!head_bwd) {
+    // losses only, computed as the update path of this handle computes them (so that the
+    // losses match a prefill with eta = 0 bit for bit): the partials of the single pass
+    // without its exponentials stored, or the cross-entropy pass
+    GemmArgs g = gargs(h->nf, d, h->lm_head, d, Bn, h->V, d);
+    g.rowi = h->labs;  // label of row r = labs[*zero + r]
+    g.pos0 = h->zero;
+    g.part = h->part;
+    g.part_ld = h->P;
+    g.zlab = h->zlab;
+    if (h->head1) {
+      {
+        PROF(K_CE_REDUCE);
+        HIPCHK(head_shift_launch(dt, f16, h->nf, h->lm_head, h->labs, h->zero, h->shift, Bn, d, 40.f, st));
+      }
+      h->launches++;
+      g.rowf = h->shift;
+      gemm(h, K_GEMM_HEAD_CE, true, true, EPI_PROBS, g, st, true, true);
+    } else {
+      gemm(h, K_GEMM_HEAD_CE, true, true, EPI_CE, g, st, true, true);
+    }
+  } else {
+    // losses and the head's gradient.  Single pass (head1): with a per-row shift c (the
+    // label's logit + 40) the epilogue writes p = exp(z - c) for a vocabulary slab, the loss
+    // partials (c, sum p) and the label logit, and dn accumulates p W over the slabs; once
+    // the losses are reduced, dn = (dn / sum p - W[label]) 2^s / n.  That is exact while no
+    // logit of a row exceeds its label's logit by about 128 - ln V, which the handle checks
+    // once from the weights: |z_v - z_label| <= 2 sqrt(d) max|g_final| max_v |W_v|.
+    // Otherwise the cross-entropy pass gives the losses (lse) first and the slabs write the
+    // softmax itself, p = exp(z - lse), with sum p = 1.
+    {
+      PROF(K_CE_REDUCE);
+      if (h->head1)
+        HIPCHK(head_shift_launch(dt, f16, h->nf, h->lm_head, h->labs, h->zero, h->shift, Bn, d, 40.f, st));
+    }
+    if (h->head1) {
+      h->launches++;
+    } else {
+      GemmArgs g = gargs(h->nf, d, h->lm_head, d, Bn, h->V, d);
+      g.rowi = h->labs;
+      g.pos0 = h->zero;
+      g.part = h->part;
+      g.part_ld = h->P;
+      g.zlab = h->zlab;
+      gemm(h, K_GEMM_HEAD_CE, true, true, EPI_CE, g, st, true, true);
+      {
+        PROF(K_CE_REDUCE);
+        HIPCHK(ce_reduce_launch(h->part, h->P, h->zlab, h->zero, h->lse, h->closs, Bn, st));
+      }
+      h->launches++;
+    }
     for (int v0 = 0, sl = 0; v0 < h->V; v0 += h->Vs, ++sl) {
       const int vs = std::min(h->Vs, h->V - v0);
       {
         GemmArgs g = gargs(h->nf, d, off(h->lm_head, (size_t)v0 * d * es), d, Bn, vs, d);
-        g.C = h->dz;
+        g.C = h->dz;  // p in the working dtype
         g.ldc = h->Vs;
-        g.rowf = h->lse;
+        g.rowf = h->head1 ? h->shift : h->lse;
         g.rowi = h->labs;  // label of row r = labs[*zero + r]
         g.pos0 = h->zero;
+        g.part = h->head1 ? h->part : nullptr;
+        g.part_ld = h->P;
+        g.zlab = h->head1 ? h->zlab : nullptr;
         g.col_off = v0;
-        g.alpha = h->gscale / (float)n;
-        gemm(h, K_GEMM_DLOGITS, true, true, EPI_DLOGITS, g, st, true);  // dz in the working dtype
+        gemm(h, K_GEMM_HEAD_CE, true, true, EPI_PROBS, g, st, true);
       }
       {
         // B[n = model dim][k = vocab] from the transposed head [d][V]
@@ -564,6 +604,26 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
         gemm(h, K_GEMM_DN, true, true, sl == 0 ? EPI_STORE_F32 : EPI_ADD_F32, g, st);
       }
     }
+  }
+  {
+    PROF(K_CE_REDUCE);
+    if (!head_bwd || h->head1)
+      HIPCHK(ce_reduce_launch(h->part, h->P, h->zlab, h->zero, h->lse, h->closs, Bn, st));
+    HIPCHK(scatter_chunk_losses_launch(h->closs, mode == MODE_RECOMPUTE ? h->rlosses : h->losses, h->cfg.max_tokens,
+                                       h->pos0, n, B, st));
+    if (mode == MODE_GREEDY)  // one sequence
+      HIPCHK(decode_pick_launch(h->part, h->part_arg, h->P, h->lse, h->pos0, n, h->tok, h->losses, st));
+  }
+  h->launches += (mode == MODE_GREEDY ? 3 : 2) - (head_bwd && !h->head1 ? 1 : 0);
+
+  if (head_bwd) {
+    const int np = (n + 63) / 64 * 64;  // token count padded for the weight-gradient GEMMs
+    {
+      PROF(K_CE_REDUCE);
+      HIPCHK(head_grad_finish_launch(dt, f16, h->dn, h->head1 ? h->shift : h->lse, h->lse, h->lm_head, h->labs, h->zero, Bn, d,
+                                     h->gscale / (float)n, st));
+    }
+    h->launches++;
     {
       PROF(K_RMSNORM_BWD);
       HIPCHK(rmsnorm_bwd_launch(dt, h->dn, h->hf, h->rf, h->final_norm, nullptr, h->dh, h->dy, Bn, d, st, f16));
@@ -934,7 +994,7 @@ void run_step(ttt_handle *h, int n, bool update, int mode, bool use_graph, hipSt
     } else {
       if (mode == MODE_PREFILL && n == h->b && grouped == (h->G > 0)) gi = update ? 0 : 1;
       if (mode == MODE_GREEDY && n == 1 && !update) gi = 2;
-      if (mode == MODE_PREFILL && n == 1 && !update) gi = 3;
+      if (mode == MODE_FORCED && n == 1 && !update) gi = 3;
       if (mode == MODE_RECOMPUTE && n == h->b && update) gi = 4;
     }
   }
@@ -1045,10 +1105,11 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     if (h->Lf == 0 || h->G <= c.chunk) h->G = 0;
   }
   h->ld_tok = c.max_tokens + 1;
-  // vocabulary slab of the head backward: its [B b, Vs] gradient is about 64 MiB or less
+  // vocabulary slab of the head: its [B b, Vs] unnormalised softmax is about 64 MiB or less
   // (32768 columns at B b = 1024; measured 13 ms per 128K prefill faster than 16384, and
-  // 65536 no better)
-  h->Vs = std::min(h->V, std::max(1024, (32768 * 1024 / std::max(1, h->B * c.chunk)) / 128 * 128));
+  // 65536 no better); a multiple of 256 columns, so that every slab starts at a partial slot
+  // of the 256-wide tile
+  h->Vs = std::min(h->V, std::max(1024, (32768 * 1024 / std::max(1, h->B * c.chunk)) / 256 * 256));
   h->P = 2 * ((h->V + 127) / 128);
   hipStream_t st = (hipStream_t)stream;
   const int d = h->d, F = h->F, b = h->b, L = h->L, V = h->V;
@@ -1076,6 +1137,25 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
       lw.fwd16 = attn_fwd_f16_ok(h->dt, lw.sbound, h->hd);
       lw.R = (h->G > 0 && l < h->Lf) ? c.window + h->G : h->R;
       ring_sb += (size_t)h->H * lw.R * h->hd * es * (2 + (lw.bwd_attn ? (lw.fwd16 ? 3 : 2) : 0));
+    }
+    {
+      // the single-pass head is exact when every row's logits lie within a band of the
+      // label's logit: |z_v - z_label| <= |W_v - W_label| |g_final * x / rms(x)| <=
+      // 2 max_v |W_v| max|g_final| sqrt(d) = 2 bound (1% headroom for the rounding of the
+      // normalised rows); with the shift label + 40, exp(z - shift) summed over V columns
+      // stays below fp32's (and bf16's) largest value while 2 bound + ln V <= 126
+      unsigned *hm = (unsigned *)dalloc(h, 64, false);
+      HIPCHK(hipMemsetAsync(hm, 0, 8, st));
+      HIPCHK(rownorm_max_launch(h->dt, w->lm_head, d, V, d, hm, st));
+      HIPCHK(absmax_launch(h->dt, w->final_norm, d, 1, d, hm + 1, st));
+      unsigned bits[2] = {0, 0};
+      HIPCHK(hipMemcpyAsync(bits, hm, 8, hipMemcpyDeviceToHost, st));
+      HIPCHK(hipStreamSynchronize(st));
+      float wn, gm;
+      std::memcpy(&wn, &bits[0], 4);
+      std::memcpy(&gm, &bits[1], 4);
+      const double bound = 1.01 * (double)wn * (double)gm * std::sqrt((double)d);
+      h->head1 = std::isfinite(bound) && 2.0 * bound + std::log((double)V) <= 126.0;
     }
     if (h->dt == 1 && h->nu > 0) {
       // largest |w| over the weights whose forward copies are stored scaled
@@ -1235,6 +1315,7 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     h->rf = (float *)dalloc(h, Bb * 4);
     h->zlab = (float *)dalloc(h, Bb * 4);
     h->lse = (float *)dalloc(h, Bb * 4);
+    h->shift = (float *)dalloc(h, Bb * 4);
     h->part = (float2 *)dalloc(h, (size_t)Bb * h->P * sizeof(float2));
     h->part_arg = (int *)dalloc(h, (size_t)Bb * h->P * sizeof(int));
     h->rlosses = (float *)dalloc(h, c.max_tokens * sizeof(float));
@@ -1293,7 +1374,7 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
       h->hmidT = dalloc(h, (size_t)b * F * es);
       h->dguT = dalloc(h, (size_t)b * 2 * F * es);
     }
-    // the LM head's forward copy (cross-entropy and the recomputed logits) is fp16 in bf16 mode
+    // the LM head's forward copy (the logits of the cross-entropy and of the softmax) is fp16 in bf16 mode
     if (h->dt == 1) HIPCHK(bf16_to_f16_launch(h->lm_head, d, h->lm_head, d, 1, V * d, st));
     h->ws_elems = gemm_ws_elems(b, d);
     h->ws = (float *)dalloc(h, h->ws_elems * 4);
@@ -1445,7 +1526,7 @@ ttt_status ttt_decode(ttt_handle *h, int64_t n_steps, const int32_t *d_forced, i
       HIPCHK(hipMemcpyAsync(h->tok + len0 + 1, d_forced, (size_t)n_steps * sizeof(int), hipMemcpyDeviceToDevice, st));
     for (int64_t j = 0; j < n_steps; ++j) {
       // position len: predict the token after it (the forced one's loss, or the argmax)
-      run_step(h, 1, false, d_forced ? MODE_PREFILL : MODE_GREEDY, use_graph, st);
+      run_step(h, 1, false, d_forced ? MODE_FORCED : MODE_GREEDY, use_graph, st);
       h->len += 1;
       if (h->len - h->dstart == h->b) {
         // every target of the open chunk is known: its update (Algorithm 3 step 3)

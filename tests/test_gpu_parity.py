@@ -240,27 +240,42 @@ def test_window_equal_to_chunk(dtype, k, b):
         assert dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
 
 
-@pytest.mark.parametrize("dtype,V,b", [("bf16", 1040, 128), ("fp32", 1008, 128), ("bf16", 40016, 1024)])
-def test_ragged_vocab(dtype, V, b):
+def head_bound_test(cfg, w):
+    """The library's create-time test for running the head's loss and gradient in one pass:
+    every row's logits lie within 2 * 1.01 sqrt(d) max|g_final| max_v |W_v| of its label's
+    logit, and that spread plus ln V stays at or below 126."""
+    wn = float(np.max(np.linalg.norm(w["lm_head"].astype(np.float64), axis=1)))
+    gm = float(np.max(np.abs(w["final_norm"])))
+    return 2 * 1.01 * wn * gm * np.sqrt(cfg.d_model) + np.log(cfg.vocab) <= 126.0
+
+
+@pytest.mark.parametrize("dtype,V,b,scale", [("bf16", 1040, 128, 8), ("fp32", 1008, 128, 8), ("bf16", 40016, 1024, 8),
+                                             ("bf16", 1040, 128, 12), ("fp32", 1008, 128, 16),
+                                             ("bf16", 40016, 1024, 12)])
+def test_ragged_vocab(dtype, V, b, scale):
     """A vocabulary that is a multiple of 16 but not of 128: the head's last column tile
     and its cross-entropy partials are ragged; at b = 1024 the head backward streams the
-    vocabulary in slabs of 32768 columns, so the second slab is ragged too."""
+    vocabulary in slabs of 32768 columns, so the second slab is ragged too.  The first 128
+    head rows are scaled (the oracle takes the scaled values as stored): their logits dominate
+    every row's softmax, so a partial slot of them lost or overwritten would move the
+    losses by O(1).  At scale 8 the weights pass the single-pass head's bound; at 12 and 16
+    they do not, and the head computes the losses first and the softmax after."""
     from ttt_inputs import make_weights_np, make_weights_torch
     T = 2 * b + 52
     cfg = mid(64, dtype=dtype, T=T, V=V, b=b, k=max(256, b))
-    say(f"case: ragged vocab {dtype} V={V} b={b} T={T}")
+    say(f"case: ragged vocab {dtype} V={V} b={b} T={T} head rows x{scale}")
     tok = rand_tokens(cfg.seq_len + 1, V, seed=500 + V)
     tok[::7] = V - 1  # the last vocabulary rows are labels too
-    # the first 128 head rows scaled by 8 (exact): their logits dominate every row's
-    # softmax, so a partial slot of them lost or overwritten would move the losses by O(1)
     wt = make_weights_torch(cfg, "cuda")
     wn = make_weights_np(cfg)
-    wt["lm_head"][:128] *= 8
-    wn["lm_head"][:128] *= 8
+    wt["lm_head"][:128] *= scale
+    # the oracle takes the stored (rounded, for bf16) values
+    wn["lm_head"][:128] = wt["lm_head"][:128].float().cpu().numpy()
+    assert head_bound_test(cfg, wn) == (scale == 8)
     sess, _ = gpu_session(cfg, weights=wt)
     gl, gf = run_gpu(sess, tok)
     ol, of, w = run_oracle(cfg, tok, weights_np=wn)
-    dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, w), f"V={V} {dtype}")
+    dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, w), f"V={V} {dtype} x{scale}")
     if dtype == "fp32":
         assert dl <= 1e-4 and wr <= 1e-5 and dwr <= 1e-3
     else:
