@@ -149,8 +149,14 @@ def algorithmic_bytes(cfg, T, update=True):
     # QK-norm + RoPE: read fp32 q, k, v; write q and the ring's K and V^T; the backward's
     # copies (V, K^T, 16-bit K) of back-propagated blocks, and with the update q copies
     rope = L * (12 + 3 * a) * d + nb * 3 * a * d + (nb * 2 * a * d if update else 0)
+    # the head's row kernels (timed as one class with the loss reduce): the per-row shift reads
+    # the normalised row and the label's head row (the 16-bit forward copy: 2 bytes in bf16
+    # workloads) and writes 4 bytes; with updates the finish reads and writes the fp32 dn row
+    # and reads the label's head row again
+    wh = 2 if cfg.dtype == "bf16" else 4
+    head_rows = (a + wh) * d + 8 + ((8 + wh) * d + 12 if update and nu > 0 else 0)
     b = {"embed": T * (a + 4) * d + (T * 8 * d if grouped else 0), "rmsnorm": T * rms, "qknorm_rope_ring": T * rope,
-         "ce_reduce": T * (8 * P + 12)}
+         "ce_reduce": T * (8 * P + 12 + head_rows)}
     if update and nu > 0:
         b.update({
             # final norm (dy, x, out fp32 + 16-bit) and two norms per back-propagated block (+ dh_in)
