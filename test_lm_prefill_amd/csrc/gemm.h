@@ -65,6 +65,14 @@ struct GemmArgs {
   float *ws;
 };
 
+// Up to GEMM_GROUP_MAX products run as one launch (gemm_group_launch).
+#define GEMM_GROUP_MAX 8
+struct GemmGroup {
+  GemmArgs g[GEMM_GROUP_MAX];
+  int beg[GEMM_GROUP_MAX];  // first block of each product (set by the launcher)
+  int n;
+};
+
 // dtype (operand type): 0 = fp32, 1 = bf16, 2 = fp16.  a_kc / b_kc select the
 // operand layouts.  fp16 operands need the streaming kernel's shapes (both
 // k-contiguous, K and a_kwrap multiples of 64, leading dimensions multiples of 8).
@@ -94,3 +102,11 @@ GemmPlan gemm_plan(int dtype, bool a_kc, bool b_kc, int epi, const GemmArgs &g, 
 hipError_t gemm_main_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, float *ws, GemmPlan plan,
                             hipStream_t st, bool allow_gemv = true);
 hipError_t gemm_reduce_launch(int dtype, int epi, GemmArgs g, float *ws, int split, hipStream_t st);
+
+// n products with the same operand type, layouts and epilogue, each with results
+// identical to its own gemm_launch: one launch of the 256 x 256 tile over all their tiles
+// when every product is a 16-bit k-contiguous product that needs no K split (so that
+// products too small to fill the chip share its rounds of tiles), else one launch each.
+// Implemented for EPI_SWIGLU.
+hipError_t gemm_group_launch(int dtype, int epi, const GemmArgs *gs, int n, float *ws, size_t ws_elems,
+                             hipStream_t st);

@@ -17,6 +17,7 @@
 // m-fastest order; the tiles sharing one block of B (the weights) then sit on
 // one XCD and share its L2.
 #include <algorithm>
+#include <cstring>
 
 #include "common.h"
 #include "gemm.h"
@@ -433,6 +434,7 @@ size_t gemm_ws_elems(int M, int N) { return (size_t)8 * M * N; }
 
 hipError_t gemm_dma_launch(bool f16, int epi, const GemmArgs &g, hipStream_t st);
 hipError_t gemm_dma256_launch(bool f16, int epi, const GemmArgs &g, hipStream_t st);
+hipError_t gemm_dma256_group_launch(bool f16, int epi, GemmGroup &gg, hipStream_t st);
 // few-row products (gemv.hip): M <= 4, 16-bit k-contiguous operands, fp32 / SwiGLU / CE epilogues
 bool gemv_ok(int dtype, bool a_kc, bool b_kc, int epi, const GemmArgs &g);
 hipError_t gemv_launch(bool f16, int epi, const GemmArgs &g, hipStream_t st);
@@ -511,6 +513,31 @@ hipError_t gemm_reduce_launch(int dtype, int epi, GemmArgs g, float *ws, int spl
   g.ws = ws;
   if (g.c_f16) return reduce_launch<f16_t>(epi, g, split, st);
   return dtype == 0 ? reduce_launch<float>(epi, g, split, st) : reduce_launch<bf16_t>(epi, g, split, st);
+}
+
+hipError_t gemm_group_launch(int dtype, int epi, const GemmArgs *gs, int n, float *ws, size_t ws_elems,
+                             hipStream_t st) {
+  if (n < 0 || n > GEMM_GROUP_MAX) return hipErrorInvalidValue;
+  bool one = epi == EPI_SWIGLU && n > 1;
+  for (int p = 0; p < n && one; ++p)
+    one = use_dma(dtype, true, true, gs[p]) && gs[p].M > 0 && gs[p].N > 0 &&
+          !gemv_ok(dtype, true, true, epi, gs[p]) && (gs[p].a_kwrap == 0 || gs[p].a_kwrap % 8 == 0);
+  if (!one) {
+    for (int p = 0; p < n; ++p) {
+      hipError_t e = gemm_launch(dtype, true, true, epi, gs[p], ws, ws_elems, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  GemmGroup gg;
+  memset(&gg, 0, sizeof(gg));
+  gg.n = n;
+  for (int p = 0; p < n; ++p) {
+    gg.g[p] = gs[p];
+    gg.g[p].ksplit = 1;
+    gg.g[p].ws = ws;
+  }
+  return gemm_dma256_group_launch(dtype == 2, epi, gg, st);
 }
 
 hipError_t gemm_launch(int dtype, bool a_kc, bool b_kc, int epi, GemmArgs g, float *ws, size_t ws_elems,

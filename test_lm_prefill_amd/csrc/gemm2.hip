@@ -612,8 +612,9 @@ DEVI void main_loop(f32x4_v (&acc)[8][4], const uint32_t (&vo)[LPH], const uint3
 #undef G8_INS
 }  // namespace g8
 
+// One 256 x 256 output tile of g: block bx of the product's tiles (bx < tiles).
 template <typename TI, int EPI>
-__global__ __launch_bounds__(g8::NT8, 1) void gemm8_kernel(const GemmArgs g) {
+DEVI void gemm8_tile(const GemmArgs &g, const int bx) {
   using namespace g8;
   __shared__ __align__(1024) char sm[2 * SBYTES];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -621,7 +622,7 @@ __global__ __launch_bounds__(g8::NT8, 1) void gemm8_kernel(const GemmArgs g) {
   const int wn = wave >> 2, wm = wave & 3;  // weight half, token quarter
   const int mt = (g.M + TX - 1) / TX, ntl = (g.N + TW - 1) / TW;
   constexpr int GM = 8;
-  const int tile = remap_tile2(blockIdx.x, mt * ntl);
+  const int tile = remap_tile2(bx, mt * ntl);
   const int band = tile / (GM * ntl), in_band = tile % (GM * ntl);
   const int bm = min(GM, mt - band * GM);
   const int tm = band * GM + in_band % bm, tn = in_band / bm;
@@ -696,6 +697,26 @@ __global__ __launch_bounds__(g8::NT8, 1) void gemm8_kernel(const GemmArgs g) {
   }
 }
 
+template <typename TI, int EPI>
+__global__ __launch_bounds__(g8::NT8, 1) void gemm8_kernel(const GemmArgs g) {
+  gemm8_tile<TI, EPI>(g, blockIdx.x);
+}
+
+// Several products with the same epilogue in one launch: problem p owns blocks
+// beg[p] .. beg[p] + its tile count - 1; every beg[p] is a multiple of 8, so that a
+// problem's block index modulo 8 is still the XCD that runs it (the tile remap keeps each
+// XCD's tiles together); blocks between problems exit at once.
+template <typename TI, int EPI>
+__global__ __launch_bounds__(g8::NT8, 1) void gemm8_group_kernel(const GemmGroup gg) {
+  const int bx = blockIdx.x;
+  int p = 0;
+  while (p + 1 < gg.n && bx >= gg.beg[p + 1]) ++p;
+  const GemmArgs &g = gg.g[p];
+  const int i = bx - gg.beg[p];
+  if (i >= ((g.M + g8::TX - 1) / g8::TX) * ((g.N + g8::TW - 1) / g8::TW)) return;
+  gemm8_tile<TI, EPI>(g, i);
+}
+
 #define G8_INST(TI)                                                      \
   template __global__ void gemm8_kernel<TI, EPI_STORE>(const GemmArgs);     \
   template __global__ void gemm8_kernel<TI, EPI_STORE_F32>(const GemmArgs); \
@@ -707,6 +728,8 @@ __global__ __launch_bounds__(g8::NT8, 1) void gemm8_kernel(const GemmArgs g) {
 G8_INST(bf16_t)
 G8_INST(f16_t)
 #undef G8_INST
+template __global__ void gemm8_group_kernel<f16_t, EPI_SWIGLU>(const GemmGroup);
+template __global__ void gemm8_group_kernel<bf16_t, EPI_SWIGLU>(const GemmGroup);
 
 template <typename TI, int EPI> hipError_t launch8_e(const GemmArgs &g, hipStream_t st) {
   const int tiles = ((g.M + g8::TX - 1) / g8::TX) * ((g.N + g8::TW - 1) / g8::TW);
@@ -739,4 +762,23 @@ hipError_t gemm_dma_launch(bool f16, int epi, const GemmArgs &g, hipStream_t st)
 // The 256 x 256 tile (same operand conditions as gemm_dma_launch; no EPI_SGD).
 hipError_t gemm_dma256_launch(bool f16, int epi, const GemmArgs &g, hipStream_t st) {
   return f16 ? launch8<f16_t>(epi, g, st) : launch8<bf16_t>(epi, g, st);
+}
+
+// Several SwiGLU products of the 256 x 256 tile in one launch (each meets the conditions
+// of gemm_dma_launch and has ksplit 1); fills gg.beg.
+hipError_t gemm_dma256_group_launch(bool f16, int epi, GemmGroup &gg, hipStream_t st) {
+  if (epi != EPI_SWIGLU || gg.n < 1 || gg.n > GEMM_GROUP_MAX) return hipErrorInvalidValue;
+  int blocks = 0;
+  for (int p = 0; p < gg.n; ++p) {
+    const GemmArgs &g = gg.g[p];
+    if (g.ksplit > 1) return hipErrorInvalidValue;
+    gg.beg[p] = blocks;
+    const int tiles = ((g.M + g8::TX - 1) / g8::TX) * ((g.N + g8::TW - 1) / g8::TW);
+    blocks += (tiles + 7) / 8 * 8;
+  }
+  if (f16)
+    hipLaunchKernelGGL((gemm8_group_kernel<f16_t, EPI_SWIGLU>), dim3(blocks), dim3(g8::NT8), 0, st, gg);
+  else
+    hipLaunchKernelGGL((gemm8_group_kernel<bf16_t, EPI_SWIGLU>), dim3(blocks), dim3(g8::NT8), 0, st, gg);
+  return hipGetLastError();
 }

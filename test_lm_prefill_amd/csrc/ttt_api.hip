@@ -294,6 +294,24 @@ void gemm(ttt_handle *h, int cls, bool akc, bool bkc, int epi, GemmArgs g, hipSt
   h->launches += split > 1 ? 2 : 1;
 }
 
+// Products with the same epilogue and k-contiguous operands that each fill less of the GPU
+// than one round of tiles: one launch over all their 256 x 256 tiles when they have at
+// least 200 together, else one launch each (the same results either way).
+void gemm_group(ttt_handle *h, int cls, int epi, const GemmArgs *gs, int n, hipStream_t st, bool f16op = false) {
+  const int odt = (f16op && h->dt == 1) ? 2 : h->dt;
+  long t256 = 0;
+  for (int p = 0; p < n; ++p) t256 += (long)((gs[p].M + 255) / 256) * ((gs[p].N + 255) / 256);
+  if (n < 2 || t256 < 200) {
+    for (int p = 0; p < n; ++p) gemm(h, cls, true, true, epi, gs[p], st, f16op);
+    return;
+  }
+  {
+    Prof prof_(h, cls, st);
+    HIPCHK(gemm_group_launch(odt, epi, gs, n, h->ws, h->ws_elems, st));
+  }
+  h->launches += 1;
+}
+
 // A residual product h += A B^T (EPI_ADD_F32, 16-bit operands) whose split-K reduction
 // is left to the RMSNorm that reads h next: returns the pending fp32 partials, or an
 // empty descriptor when the product was not split (then h is already updated).  The
@@ -476,19 +494,21 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
         pend = gemm_residual(h, K_GEMM_DOWN, g2, st);
       h->launches += 4;
     } else {
-      // static units [F, 2F), all sequences at once
-      GemmArgs gs = gargs(m, d, lw.wgu_s, d, Bn, 2 * F, d);
-      gs.C = off(hm, (size_t)F * es);
-      gs.ldc = 2 * F;
-      gs.C2 = S ? off(S->gu, (size_t)2 * F * es) : nullptr;
-      gs.ldc2 = 4 * F;
-      gs.c_f16 = f16;
-      gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, gs, st, true);
+      // gate/up: the static units [F, 2F) for all sequences at once and each sequence's
+      // fast units [0, F), launched together in groups of up to GEMM_GROUP_MAX products
+      GemmArgs gs[GEMM_GROUP_MAX];
+      int ng = 0;
+      gs[ng] = gargs(m, d, lw.wgu_s, d, Bn, 2 * F, d);
+      gs[ng].C = off(hm, (size_t)F * es);
+      gs[ng].ldc = 2 * F;
+      gs[ng].C2 = S ? off(S->gu, (size_t)2 * F * es) : nullptr;
+      gs[ng].ldc2 = 4 * F;
+      gs[ng].c_f16 = f16;
+      ++ng;
       for (int s = 0; s < B; ++s) {
-        void *wgu = off(lw.wgu, s * h->fgu_sb);
-        void *wd = off(lw.wd, s * h->fd_sb);
-        // fast units [0, F): bf16 runs the reduction over [m | m] x [hi | lo]
-        GemmArgs g = gargs(off(m, rows(s, d, es)), d, wgu, 2 * d, n, 2 * F, dt == 1 ? 2 * d : d);
+        // fast units: bf16 runs the reduction over [m | m] x [hi | lo]
+        GemmArgs &g = gs[ng++];
+        g = gargs(off(m, rows(s, d, es)), d, off(lw.wgu, s * h->fgu_sb), 2 * d, n, 2 * F, dt == 1 ? 2 * d : d);
         g.a_kwrap = dt == 1 ? d : 0;
         g.C = off(hm, rows(s, 2 * F, es));
         g.ldc = 2 * F;
@@ -496,7 +516,13 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
         g.ldc2 = 4 * F;
         g.c_f16 = f16;
         g.acc_scale = 1.f / h->wscale;
-        gemm(h, K_GEMM_GATE_UP, true, true, EPI_SWIGLU, g, st, true);
+        if (ng == GEMM_GROUP_MAX || s == B - 1) {
+          gemm_group(h, K_GEMM_GATE_UP, EPI_SWIGLU, gs, ng, st, true);
+          ng = 0;
+        }
+      }
+      for (int s = 0; s < B; ++s) {
+        void *wd = off(lw.wd, s * h->fd_sb);
         // down: [fast | static | fast] units x [hi | static | lo] columns (bf16 mode)
         GemmArgs g2 = gargs(off(hm, rows(s, 2 * F, es)), 2 * F, wd, 3 * F, n, d, dt == 1 ? 3 * F : 2 * F);
         g2.a_kwrap = dt == 1 ? 2 * F : 0;

@@ -282,6 +282,40 @@ def test_ragged_vocab(dtype, V, b, scale):
         assert dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
 
 
+def wide_tiles(M, N):
+    return -(-M // 256) * -(-N // 256)
+
+
+@pytest.mark.parametrize("B,b", [(1, 1024), (2, 512)])
+def test_grouped_gate_up_launch(B, b):
+    """An updated block's static gate/up product (all sequences) and each sequence's fast
+    one fill less than the GPU's 256 CUs with 256 x 256 tiles alone; with at least 200 such
+    tiles together they run as one launch (d = 1024, 2F = 6656: 104 tiles for each of the
+    static and the fast product at 1024 rows; B = 2 at b = 512: three products)."""
+    from test_lm_prefill_amd import Session
+    from ttt_inputs import make_weights_np, make_weights_torch
+    T = 2 * b + 100
+    cfg = TTTConfig("grouped_bf16", 2, 1024, 8, 128, 3328, 1024, T, b, b, 1, 0.5, "bf16", init_std=0.02)
+    static = wide_tiles(B * b, 2 * cfg.d_ff)
+    fast = B * wide_tiles(b, 2 * cfg.d_ff)
+    assert static < 200 and fast // B < 200 and static + fast >= 200
+    say(f"case: grouped gate/up B={B} b={b} T={T} ({static} + {fast} wide tiles)")
+    w = make_weights_torch(cfg, "cuda")
+    wn = make_weights_np(cfg)
+    toks = [rand_tokens(T + 1, cfg.vocab, seed=700 + s) for s in range(B)]
+    sess = Session(cfg, w, max_tokens=T, n_seq=B)
+    l, f = sess.prefill(torch.from_numpy(np.stack(toks)).cuda() if B > 1 else torch.from_numpy(toks[0]).cuda(),
+                        want_fast=True)
+    torch.cuda.synchronize()
+    sess.close()
+    for s in range(B):
+        gl = (l[s] if B > 1 else l).double().cpu().numpy()
+        gf = [x.double().cpu().numpy() for x in (f[s] if B > 1 else f)]
+        ol, of, _ = run_oracle(cfg, toks[s], weights_np=wn)
+        dl, wr, dwr = compare(cfg, gl, gf, ol, of, fast_init(cfg, wn), f"grouped B={B} seq {s}")
+        assert dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
+
+
 def test_fp32_shapes_off_the_64_grid():
     """fp32 mode accepts d_model, d_ff and vocab that are multiples of 16 only: three heads
     of 16 (d = 48), d_ff = 208, V = 1008, T = 1 (one scored position) and a ragged T."""
