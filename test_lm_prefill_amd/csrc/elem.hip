@@ -135,72 +135,111 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float *dy, const
 }
 
 // ----------------------------------------------------------------- QK-norm + rotary (+ ring write)
-// grid (ceil(n/32), H); wave w handles tokens 8w..8w+7 of the block; lane
-// i < hd/2 handles the rotary pair (i, i + hd/2).
+// grid (ceil(n/32), H): 32 tokens of one head per block.  Each wave handles 8 tokens, four at
+// a time: 16-lane group g takes one token, and lane j < hd/8 of the group the elements
+// 4j..4j+3 and their rotary partners 4j+hd/2.. (16-byte loads and 8-byte stores; the
+// norms reduce over the group).
 template <typename T, typename TF>
 __global__ __launch_bounds__(256) void qk_rope_fwd_kernel(const RopeArgs a) {
   extern __shared__ float sm[];  // [3][hd][33]: Vt, Kt, Qt tiles
   const int hd = a.hd, half = hd / 2, h = blockIdx.y, t0 = blockIdx.x * 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane >> 4, i0 = (lane & 15) * 4;
   const int pos0 = *a.pos0;
   const float *qkv = reinterpret_cast<const float *>(a.qkv);
-  const T *gq = reinterpret_cast<const T *>(a.gq);
-  const T *gk = reinterpret_cast<const T *>(a.gk);
   float *sV = sm, *sK = sm + hd * 33, *sQ = sm + 2 * hd * 33;
-  const bool act = lane < half;
-  const float gqi = act ? to_f(gq[lane]) : 0.f, gqj = act ? to_f(gq[lane + half]) : 0.f;
-  const float gki = act ? to_f(gk[lane]) : 0.f, gkj = act ? to_f(gk[lane + half]) : 0.f;
-  // all loads of the wave's 8 tokens are issued first (one memory round trip, not eight)
-  float ld[8][6];
+  const bool act = i0 < half;
+  float gq[2][4] = {}, gk[2][4] = {};
+  if (act) {
+    load4<T>(reinterpret_cast<const T *>(a.gq) + i0, gq[0]);
+    load4<T>(reinterpret_cast<const T *>(a.gq) + i0 + half, gq[1]);
+    load4<T>(reinterpret_cast<const T *>(a.gk) + i0, gk[0]);
+    load4<T>(reinterpret_cast<const T *>(a.gk) + i0 + half, gk[1]);
+  }
+  // all loads of the wave's 8 tokens are issued first (one memory round trip)
+  float4 ld[2][6];
 #pragma unroll
-  for (int tt = 0; tt < 8; ++tt) {
-    const int t = t0 + wave * 8 + tt;
-    const long base = (long)t * 3 * a.d + h * hd;
+  for (int it = 0; it < 2; ++it) {
+    const int t = t0 + wave * 8 + it * 4 + grp;
     const bool ok = act && t < a.n;
+    const float *base = qkv + (long)t * 3 * a.d + h * hd + i0;
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
-      ld[tt][2 * c] = ok ? qkv[base + c * a.d + lane] : 0.f;
-      ld[tt][2 * c + 1] = ok ? qkv[base + c * a.d + lane + half] : 0.f;
+      ld[it][2 * c] = ok ? *reinterpret_cast<const float4 *>(base + c * a.d) : make_float4(0.f, 0.f, 0.f, 0.f);
+      ld[it][2 * c + 1] =
+          ok ? *reinterpret_cast<const float4 *>(base + c * a.d + half) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
 #pragma unroll
-  for (int tt = 0; tt < 8; ++tt) {
-    const int tl = wave * 8 + tt, t = t0 + tl;
-    if (t >= a.n) break;
-    const int p = pos0 + t;
-    const float qi = ld[tt][0], qj = ld[tt][1], ki = ld[tt][2], kj = ld[tt][3], vi = ld[tt][4], vj = ld[tt][5];
-    const float sq = wave_sum(qi * qi + qj * qj), sk = wave_sum(ki * ki + kj * kj);
+  for (int it = 0; it < 2; ++it) {
+    const int tl = wave * 8 + it * 4 + grp, t = t0 + tl;
+    const bool ok = act && t < a.n;
+    const float q[2][4] = {{ld[it][0].x, ld[it][0].y, ld[it][0].z, ld[it][0].w},
+                           {ld[it][1].x, ld[it][1].y, ld[it][1].z, ld[it][1].w}};
+    const float k[2][4] = {{ld[it][2].x, ld[it][2].y, ld[it][2].z, ld[it][2].w},
+                           {ld[it][3].x, ld[it][3].y, ld[it][3].z, ld[it][3].w}};
+    const float v[2][4] = {{ld[it][4].x, ld[it][4].y, ld[it][4].z, ld[it][4].w},
+                           {ld[it][5].x, ld[it][5].y, ld[it][5].z, ld[it][5].w}};
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sq += q[x][e] * q[x][e];
+        sk += k[x][e] * k[x][e];
+      }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {  // within the 16-lane group
+      sq += __shfl_xor(sq, o, 64);
+      sk += __shfl_xor(sk, o, 64);
+    }
     const float rq = 1.f / sqrtf(sq / (float)hd + a.eps), rk = 1.f / sqrtf(sk / (float)hd + a.eps);
-    if (act) {
-      const float2 cs = a.cs[(long)p * half + lane];
-      const float qa = qi * rq * gqi, qb = qj * rq * gqj, ka = ki * rk * gki, kb = kj * rk * gkj;
-      const float q1 = qa * cs.x - qb * cs.y, q2 = qa * cs.y + qb * cs.x;
-      const float k1 = ka * cs.x - kb * cs.y, k2 = ka * cs.y + kb * cs.x;
-      TF *qh = reinterpret_cast<TF *>(a.qh) + (long)t * a.d + h * hd;
-      qh[lane] = from_f<TF>(q1);
-      qh[lane + half] = from_f<TF>(q2);
+    if (ok) {
+      const int p = pos0 + t;
+      const float4 *csp = reinterpret_cast<const float4 *>(a.cs + (long)p * half + i0);
+      const float4 c01 = csp[0], c23 = csp[1];
+      const float cs_c[4] = {c01.x, c01.z, c23.x, c23.z}, cs_s[4] = {c01.y, c01.w, c23.y, c23.w};
+      float q1[4], q2[4], k1[4], k2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float qa = q[0][e] * rq * gq[0][e], qb = q[1][e] * rq * gq[1][e];
+        const float ka = k[0][e] * rk * gk[0][e], kb = k[1][e] * rk * gk[1][e];
+        q1[e] = qa * cs_c[e] - qb * cs_s[e];
+        q2[e] = qa * cs_s[e] + qb * cs_c[e];
+        k1[e] = ka * cs_c[e] - kb * cs_s[e];
+        k2[e] = ka * cs_s[e] + kb * cs_c[e];
+      }
+      TF *qh = reinterpret_cast<TF *>(a.qh) + (long)t * a.d + h * hd + i0;
+      store4<TF>(qh, q1);
+      store4<TF>(qh + half, q2);
       if (a.qhb) {
-        T *qb = reinterpret_cast<T *>(a.qhb) + (long)t * a.d + h * hd;
-        qb[lane] = from_f<T>(q1);
-        qb[lane + half] = from_f<T>(q2);
+        T *qb = reinterpret_cast<T *>(a.qhb) + (long)t * a.d + h * hd + i0;
+        store4<T>(qb, q1);
+        store4<T>(qb + half, q2);
       }
       const long slot = p % a.R;
-      TF *kr = reinterpret_cast<TF *>(a.K) + ((long)h * a.R + slot) * hd;
-      kr[lane] = from_f<TF>(k1);
-      kr[lane + half] = from_f<TF>(k2);
+      TF *kr = reinterpret_cast<TF *>(a.K) + ((long)h * a.R + slot) * hd + i0;
+      store4<TF>(kr, k1);
+      store4<TF>(kr + half, k2);
       if (a.Kb) {
-        T *kb = reinterpret_cast<T *>(a.Kb) + ((long)h * a.R + slot) * hd;
-        kb[lane] = from_f<T>(k1);
-        kb[lane + half] = from_f<T>(k2);
+        T *kb = reinterpret_cast<T *>(a.Kb) + ((long)h * a.R + slot) * hd + i0;
+        store4<T>(kb, k1);
+        store4<T>(kb + half, k2);
       }
       if (a.V) {
-        T *vr = reinterpret_cast<T *>(a.V) + ((long)h * a.R + slot) * hd;
-        vr[lane] = from_f<T>(vi);
-        vr[lane + half] = from_f<T>(vj);
+        T *vr = reinterpret_cast<T *>(a.V) + ((long)h * a.R + slot) * hd + i0;
+        store4<T>(vr, v[0]);
+        store4<T>(vr + half, v[1]);
       }
-      sV[lane * 33 + tl] = vi; sV[(lane + half) * 33 + tl] = vj;
-      sK[lane * 33 + tl] = k1; sK[(lane + half) * 33 + tl] = k2;
-      sQ[lane * 33 + tl] = q1; sQ[(lane + half) * 33 + tl] = q2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sV[(i0 + e) * 33 + tl] = v[0][e];
+        sV[(i0 + half + e) * 33 + tl] = v[1][e];
+        sK[(i0 + e) * 33 + tl] = k1[e];
+        sK[(i0 + half + e) * 33 + tl] = k2[e];
+        sQ[(i0 + e) * 33 + tl] = q1[e];
+        sQ[(i0 + half + e) * 33 + tl] = q2[e];
+      }
     }
   }
   __syncthreads();
