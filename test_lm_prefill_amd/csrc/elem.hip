@@ -255,46 +255,77 @@ __global__ __launch_bounds__(256) void qk_rope_fwd_kernel(const RopeArgs a) {
   }
 }
 
-// grid (ceil(n/4), H): one wave per (token, head).
+// grid (ceil(n/16), H): one 16-lane group per (token, head), lanes as in the forward.
 template <typename T>
 __global__ __launch_bounds__(256) void qk_rope_bwd_kernel(const RopeArgs a) {
   const int hd = a.hd, half = hd / 2, h = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.n) return;
-  const int p = *a.pos0 + t;
-  const bool act = lane < half;
+  const int lane = threadIdx.x & 63, i0 = (lane & 15) * 4;
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool ok = i0 < half && t < a.n;
   const float *qkv = reinterpret_cast<const float *>(a.qkv);
-  const long base = (long)t * 3 * a.d + h * hd;
-  const long ob = (long)t * a.d + h * hd;
-  float qi = 0, qj = 0, ki = 0, kj = 0, dqi = 0, dqj = 0, dki = 0, dkj = 0;
-  float2 cs = make_float2(1.f, 0.f);
-  float gqi = 0, gqj = 0, gki = 0, gkj = 0;
-  if (act) {
-    qi = qkv[base + lane]; qj = qkv[base + lane + half];
-    ki = qkv[base + a.d + lane]; kj = qkv[base + a.d + lane + half];
-    cs = a.cs[(long)p * half + lane];
-    // transpose of the rotation
-    const float ai = a.dqh[ob + lane], aj = a.dqh[ob + lane + half];
-    dqi = ai * cs.x + aj * cs.y; dqj = -ai * cs.y + aj * cs.x;
-    const float bi = a.dkh[ob + lane], bj = a.dkh[ob + lane + half];
-    dki = bi * cs.x + bj * cs.y; dkj = -bi * cs.y + bj * cs.x;
-    gqi = to_f(reinterpret_cast<const T *>(a.gq)[lane]); gqj = to_f(reinterpret_cast<const T *>(a.gq)[lane + half]);
-    gki = to_f(reinterpret_cast<const T *>(a.gk)[lane]); gkj = to_f(reinterpret_cast<const T *>(a.gk)[lane + half]);
+  const long base = (long)t * 3 * a.d + h * hd + i0;
+  const long ob = (long)t * a.d + h * hd + i0;
+  float q[2][4] = {}, k[2][4] = {}, gyq[2][4] = {}, gyk[2][4] = {};
+  float sq = 0.f, sk = 0.f, dotq = 0.f, dotk = 0.f;
+  if (ok) {
+    float gq[2][4], gk[2][4], dqh[2][4], dkh[2][4];
+    load4<float>(qkv + base, q[0]);
+    load4<float>(qkv + base + half, q[1]);
+    load4<float>(qkv + base + a.d, k[0]);
+    load4<float>(qkv + base + a.d + half, k[1]);
+    load4<float>(a.dqh + ob, dqh[0]);
+    load4<float>(a.dqh + ob + half, dqh[1]);
+    load4<float>(a.dkh + ob, dkh[0]);
+    load4<float>(a.dkh + ob + half, dkh[1]);
+    load4<T>(reinterpret_cast<const T *>(a.gq) + i0, gq[0]);
+    load4<T>(reinterpret_cast<const T *>(a.gq) + i0 + half, gq[1]);
+    load4<T>(reinterpret_cast<const T *>(a.gk) + i0, gk[0]);
+    load4<T>(reinterpret_cast<const T *>(a.gk) + i0 + half, gk[1]);
+    const float4 *csp = reinterpret_cast<const float4 *>(a.cs + (long)(*a.pos0 + t) * half + i0);
+    const float4 c01 = csp[0], c23 = csp[1];
+    const float cs_c[4] = {c01.x, c01.z, c23.x, c23.z}, cs_s[4] = {c01.y, c01.w, c23.y, c23.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // transpose of the rotation, then the gain
+      gyq[0][e] = (dqh[0][e] * cs_c[e] + dqh[1][e] * cs_s[e]) * gq[0][e];
+      gyq[1][e] = (-dqh[0][e] * cs_s[e] + dqh[1][e] * cs_c[e]) * gq[1][e];
+      gyk[0][e] = (dkh[0][e] * cs_c[e] + dkh[1][e] * cs_s[e]) * gk[0][e];
+      gyk[1][e] = (-dkh[0][e] * cs_s[e] + dkh[1][e] * cs_c[e]) * gk[1][e];
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sq += q[x][e] * q[x][e];
+        sk += k[x][e] * k[x][e];
+        dotq += q[x][e] * gyq[x][e];
+        dotk += k[x][e] * gyk[x][e];
+      }
   }
-  const float sq = wave_sum(qi * qi + qj * qj), sk = wave_sum(ki * ki + kj * kj);
-  const float rq = 1.f / sqrtf(sq / (float)hd + a.eps), rk = 1.f / sqrtf(sk / (float)hd + a.eps);
-  const float gyqi = dqi * gqi, gyqj = dqj * gqj, gyki = dki * gki, gykj = dkj * gkj;
-  const float dotq = wave_sum(qi * gyqi + qj * gyqj), dotk = wave_sum(ki * gyki + kj * gykj);
-  if (act) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) {  // within the 16-lane group
+    sq += __shfl_xor(sq, o, 64);
+    sk += __shfl_xor(sk, o, 64);
+    dotq += __shfl_xor(dotq, o, 64);
+    dotk += __shfl_xor(dotk, o, 64);
+  }
+  if (ok) {
+    const float rq = 1.f / sqrtf(sq / (float)hd + a.eps), rk = 1.f / sqrtf(sk / (float)hd + a.eps);
     const float cq = rq * rq * rq * dotq / (float)hd, ck = rk * rk * rk * dotk / (float)hd;
     T *o = reinterpret_cast<T *>(a.dqkv) + base;
-    o[lane] = from_f<T>(rq * gyqi - qi * cq);
-    o[lane + half] = from_f<T>(rq * gyqj - qj * cq);
-    o[a.d + lane] = from_f<T>(rk * gyki - ki * ck);
-    o[a.d + lane + half] = from_f<T>(rk * gykj - kj * ck);
-    o[2 * a.d + lane] = from_f<T>(a.dv[ob + lane]);
-    o[2 * a.d + lane + half] = from_f<T>(a.dv[ob + lane + half]);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      float oq[4], ok4[4], ov[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        oq[e] = rq * gyq[x][e] - q[x][e] * cq;
+        ok4[e] = rk * gyk[x][e] - k[x][e] * ck;
+      }
+      load4<float>(a.dv + ob + x * half, ov);
+      store4<T>(o + x * half, oq);
+      store4<T>(o + a.d + x * half, ok4);
+      store4<T>(o + 2 * a.d + x * half, ov);
+    }
   }
 }
 
@@ -305,17 +336,41 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const T *dO, const TO
   extern __shared__ float sm[];  // [hd][65]
   const int h = blockIdx.y, t0 = blockIdx.x * 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int tt = 0; tt < 16; ++tt) {
-    const int tl = wave * 16 + tt, t = t0 + tl;
-    if (t >= n) break;
-    float acc = 0.f;
-    for (int i = lane; i < hd; i += 64) {
-      const float a = to_f(dO[(long)t * d + h * hd + i]);
-      acc += a * to_f(O[(long)t * d + h * hd + i]);
-      sm[i * 65 + tl] = a;
+  // 16-lane group g of wave w takes tokens 16 it + 4 w + g (it = 0..3); lane j < hd/8 of the
+  // group the elements 8j..8j+7
+  const int grp = lane >> 4, i0 = (lane & 15) * 8;
+  const bool act = i0 < hd;
+  float a[4][8], o[4][8];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int t = t0 + it * 16 + wave * 4 + grp;
+    const bool ok = act && t < n;
+    const long off = (long)t * d + h * hd + i0;
+    if (ok) {
+      load4<T>(dO + off, a[it]);
+      load4<T>(dO + off + 4, a[it] + 4);
+      load4<TO>(O + off, o[it]);
+      load4<TO>(O + off + 4, o[it] + 4);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[it][e] = o[it][e] = 0.f;
     }
-    acc = wave_sum(acc);
-    if (lane == 0) Dq[(long)h * ldl + t] = acc;
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int tl = it * 16 + wave * 4 + grp, t = t0 + tl;
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += a[it][e] * o[it][e];
+#pragma unroll
+    for (int m = 8; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);  // within the 16-lane group
+    if (t < n) {
+      if ((lane & 15) == 0) Dq[(long)h * ldl + t] = acc;
+      if (act) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm[(i0 + e) * 65 + tl] = a[it][e];
+      }
+    }
   }
   __syncthreads();
   const int cnt = min(64, n - t0);
@@ -708,7 +763,7 @@ hipError_t qk_rope_fwd_launch(int dtype, const RopeArgs &a, hipStream_t st) {
 
 hipError_t qk_rope_bwd_launch(int dtype, const RopeArgs &a, hipStream_t st) {
   if (a.n <= 0) return hipSuccess;
-  dim3 grid(blocks_for(a.n, 4), a.H);
+  dim3 grid(blocks_for(a.n, 16), a.H);
 #define K_(T, ...) hipLaunchKernelGGL(qk_rope_bwd_kernel<T>, grid, dim3(256), 0, st, a)
   DT_DISPATCH(dtype, K_, 0);
 #undef K_
