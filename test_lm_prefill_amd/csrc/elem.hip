@@ -406,23 +406,45 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T *GU, const T *d
 }
 
 // ----------------------------------------------------------------- cross-entropy reduce
+// (mx, s) <- the pair for the union of the terms of (mx, s) and one partial (x, y): a sum of
+// exponentials y e^x held as s e^mx.  Partials with y <= 0 hold no terms.
+DEVI void ce_combine(float &mx, float &s, float x, float y) {
+  if (y > 0.f) {
+    if (x > mx) {
+      s = s * __expf(mx - x) + y;
+      mx = x;
+    } else {
+      s += y * __expf(x - mx);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void ce_reduce_kernel(const float2 *part, int P, const float *zlab, const int *pos0,
                                                         float *lse, float *losses, int n) {
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= n) return;
-  const float2 *pr = part + (long)m * P;
-  float mx = -INFINITY;
-  for (int i = lane; i < P; i += 64) mx = fmaxf(mx, pr[i].x);
-  mx = wave_max(mx);
-  float s = 0.f;
-  for (int i = lane; i < P; i += 64) {
-    const float2 v = pr[i];
-    if (v.y > 0.f) s += v.y * __expf(v.x - mx);
+  // one pass, two partials per 16-byte load (P is even), eight loads in flight per lane
+  const float4 *pr = reinterpret_cast<const float4 *>(part + (long)m * P);
+  const int P2 = P / 2;
+  float mx = -INFINITY, s = 0.f;
+  for (int i0 = 0; i0 < P2; i0 += 8 * 64) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 64 + lane;
+      v[u] = i < P2 ? pr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      ce_combine(mx, s, v[u].x, v[u].y);
+      ce_combine(mx, s, v[u].z, v[u].w);
+    }
   }
-  s = wave_sum(s);
+  const float M = wave_max(mx);
+  s = wave_sum(s > 0.f ? s * __expf(mx - M) : 0.f);
   if (lane == 0) {
-    const float l = mx + logf(s);
+    const float l = M + logf(s);
     lse[m] = l;
     losses[*pos0 + m] = l - zlab[m];
   }
@@ -875,7 +897,8 @@ hipError_t head_grad_finish_launch(int dtype, bool f16, float *dn, const float *
 hipError_t ce_reduce_launch(const float2 *part, int P, const float *zlab, const int *pos0, float *lse, float *losses,
                             int n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ce_reduce_kernel, dim3(n), dim3(256), 0, st, part, P, zlab, pos0, lse, losses, n);
+  if (P % 2 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ce_reduce_kernel, dim3((n + 3) / 4), dim3(256), 0, st, part, P, zlab, pos0, lse, losses, n);
   return hipGetLastError();
 }
 
