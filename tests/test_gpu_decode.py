@@ -38,10 +38,10 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def _oracle_decode(cfg, prompt, n, forced=None):
+def _oracle_decode(cfg, prompt, n, forced=None, w=None):
     from oracle.ttt_oracle import Oracle
     from ttt_inputs import make_weights_np
-    w = make_weights_np(cfg)
+    w = make_weights_np(cfg) if w is None else w
     pre, ids, sl, margins, W = Oracle(cfg, w).decode(prompt, n, forced=forced)
     return pre, ids, sl, margins, [x for ws in W for x in ws], w
 
@@ -73,6 +73,36 @@ def test_decode_forced_bf16(hd, P):
     dl, wr, dwr = compare(cfg, gsl, gf, osl, of, fast_init(cfg, w), f"decode forced hd={hd}")
     say(f"prefill max|dloss|={dl_pre:.3e}")
     assert dl_pre <= 2e-2 and dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
+    sess.close()
+
+
+def test_decode_two_pass_head_bf16():
+    """Head row 0 scaled by 13 (the oracle takes the stored value): the weights fail the
+    single-pass head's bound, so each decode update's head runs the cross-entropy pass and
+    then the softmax pass.  Forced steps against the oracle, and a greedy decode equal to
+    a forced decode of the ids it chose, bit for bit."""
+    from ttt_inputs import make_weights_np, make_weights_torch
+    cfg = cfg_dec(hd=64)
+    n, P = 300, 256
+    wt = make_weights_torch(cfg, "cuda")
+    wt["lm_head"][:1] *= 13
+    wn = make_weights_np(cfg)
+    wn["lm_head"][:1] = wt["lm_head"][:1].float().cpu().numpy()
+    bound = 2 * 1.01 * np.max(np.linalg.norm(wn["lm_head"].astype(np.float64), axis=1)) * np.sqrt(cfg.d_model)
+    assert bound + np.log(cfg.vocab) > 126.0
+    prompt = rand_tokens(P + 1, cfg.vocab, seed=77)
+    forced = rand_tokens(n, cfg.vocab, seed=78)
+    say(f"case: decode forced bf16, two-pass head, P={P} n={n}")
+    sess, _ = gpu_session(cfg, weights=wt)
+    gpre, gids, gsl, gf = _gpu_decode(sess, prompt, n, forced)
+    opre, oids, osl, _, of, w = _oracle_decode(cfg, prompt, n, forced, w=wn)
+    dl_pre = float(np.max(np.abs(gpre - opre)))
+    dl, wr, dwr = compare(cfg, gsl, gf, osl, of, fast_init(cfg, w), "decode forced, two-pass head")
+    say(f"prefill max|dloss|={dl_pre:.3e}")
+    assert dl_pre <= 2e-2 and dl <= 2e-2 and wr <= 1e-2 and dwr <= 5e-2
+    _, ids, sl, f = _gpu_decode(sess, prompt, n)
+    _, ids3, sl3, f3 = _gpu_decode(sess, prompt, n, forced=ids)
+    assert np.array_equal(sl, sl3) and all(np.array_equal(x, y) for x, y in zip(f, f3))
     sess.close()
 
 

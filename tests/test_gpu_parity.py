@@ -83,11 +83,20 @@ def test_mid_fp32_hd64():
     assert dwr <= 1e-3
 
 
-def test_no_update_equals_eta0_and_bitwise_invariants():
+@pytest.mark.parametrize("head_scale", [1, 12])
+def test_no_update_equals_eta0_and_bitwise_invariants(head_scale):
+    # head_scale 12: the first 128 head rows scaled so that the weights fail the single-pass
+    # head's bound, and the head runs its two-pass form
+    from ttt_inputs import make_weights_np, make_weights_torch
     cfg = mid(80, T=512)
-    say("case: invariants hd=80 bf16 T=512")
+    say(f"case: invariants hd=80 bf16 T=512 head rows x{head_scale}")
     tok = rand_tokens(cfg.seq_len + 1, cfg.vocab, seed=11)
-    sess, w = gpu_session(cfg)
+    wt = make_weights_torch(cfg, "cuda")
+    wt["lm_head"][:128] *= head_scale
+    wn = make_weights_np(cfg)
+    wn["lm_head"][:128] = wt["lm_head"][:128].float().cpu().numpy()
+    assert head_bound_test(cfg, wn) == (head_scale == 1)
+    sess, w = gpu_session(cfg, weights=wt)
     sess0, _ = gpu_session(cfg.with_(eta=0.0), weights=w)
     l_upd, f1 = run_gpu(sess, tok)
     l_upd2, f2 = run_gpu(sess, tok)
