@@ -371,7 +371,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
     else
       HIPCHK(lead_rows_launch(h->h_lead, h->lead_n, h->G, h->pos0, h->h, n, d, B, st));
   }
-  h->launches += 2;
+  h->launches += lead ? 3 : 2;
   for (int l = lb; l < le; ++l) {
     LayerBuf &lw = h->layers[l];
     // blocks below Lf: unsplit products and one key range per head, so that a token's
@@ -458,8 +458,8 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
           PROF(K_ATTN_MERGE);
           HIPCHK(attn_merge_launch(dt, hd, false, aa, st));
         }
+        h->launches += aa.nsplit > 1 ? 3 : 2;  // QK-norm + RoPE, attention, merge
       }
-      h->launches += 3;
     }
     {
       GemmArgs g = gargs(o, d, lw.wo, d, Bn, d, d);
@@ -492,7 +492,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
         gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st, true, true);
       else
         pend = gemm_residual(h, K_GEMM_DOWN, g2, st);
-      h->launches += 4;
+      h->launches += 2;  // the block's two RMSNorms (the GEMM helpers count their own launches)
     } else {
       // gate/up: the static units [F, 2F) for all sequences at once and each sequence's
       // fast units [0, F), launched together in groups of up to GEMM_GROUP_MAX products
@@ -534,7 +534,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
         else
           gemm(h, K_GEMM_DOWN, true, true, EPI_ADD_F32, g2, st, true);
       }
-      h->launches += 2 + 2 * B;
+      h->launches += 2;  // the block's two RMSNorms
     }
   }
   if (lead) return;  // the frozen prefix of a group: its residual rows stay in h_lead
@@ -545,6 +545,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
                               eps, st, f16, pend));
     pend = ResidualPartials();
   }
+  h->launches++;
   const bool head_bwd = update && h->nu > 0;
   if (mode == MODE_GREEDY || mode == MODE_FORCED) {
     // a decode step: per-tile (max, sum) partials and each tile's argmax for the pick
@@ -582,7 +583,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
     // label's logit + 40) the epilogue writes p = exp(z - c) for a vocabulary slab, the loss
     // partials (c, sum p) and the label logit, and dn accumulates p W over the slabs; once
     // the losses are reduced, dn = (dn / sum p - W[label]) 2^s / n.  That is exact while no
-    // logit of a row exceeds its label's logit by about 128 - ln V, which the handle checks
+    // logit of a row exceeds its label's logit by more than 126 - ln V, which the handle checks
     // once from the weights: |z_v - z_label| <= 2 sqrt(d) max|g_final| max_v |W_v|.
     // Otherwise the cross-entropy pass gives the losses (lse) first and the slabs write the
     // softmax itself, p = exp(z - lse), with sum p = 1.
@@ -695,7 +696,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
           g.ldct = d;
           gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st, true);
         }
-        h->launches += 4;
+        h->launches += 2;  // the transposes
       }
       {
         PROF(K_SWIGLU_BWD);
@@ -735,7 +736,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
           g.ldct = 4 * F;
           gemm(h, K_GEMM_DW_SGD, true, true, EPI_SGD, g, st, true);
         }
-        h->launches += last ? 3 : 4;
+        h->launches += 2;  // the transposes
       }
       if (last) break;
       {
@@ -749,7 +750,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
         g.ldc = d;
         gemm(h, K_GEMM_DO, true, true, EPI_STORE, g, st, true);  // dO itself is bf16
       }
-      h->launches += 2;
+      h->launches += 1;
       for (int s = 0; s < B; ++s) {
         const size_t rs = s * h->ring_sbytes;
         void *dO = off(h->dO, rows(s, d, es));
@@ -830,7 +831,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
         PROF(K_RMSNORM_BWD);
         HIPCHK(rmsnorm_bwd_launch(dt, h->da, S.h_in, S.r1, lw.attn_norm, h->dh, h->dh, h->dy, Bn, d, st, f16));
       }
-      h->launches += 2;
+      h->launches += 1;
     }
   }
   {
