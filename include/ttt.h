@@ -122,7 +122,8 @@ typedef struct ttt_handle ttt_handle;
  * Creates a handle on the current HIP device: validates cfg, allocates the
  * bounded state (per-layer key/value rings of k+b rows, or k+G rows for the
  * blocks below the updated ones, which run ahead over groups of G tokens;
- * activations of one chunk and of one group; the exponentiated logits of
+ * activations of one chunk and of two groups, the current one and the next,
+ * whose frozen-block pass runs beside the current one's chunks; the exponentiated logits of
  * one vocabulary slab when n_update > 0 - no [b, V] logits are kept; fp32
  * master fast weights) and copies/repacks the weights.  It reads the head and
  * final-norm weights once to decide how the head runs: one pass over the
@@ -154,7 +155,10 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
  *              order gate[F,d], up[F,d], down[d,F] for block L-n_u, then
  *              L-n_u+1, ..., sequence 0 first.
  *   flags      TTT_NO_UPDATE / TTT_NO_GRAPH, OR-ed with cfg.flags.
- *   stream     hipStream_t to enqueue on (NULL = default stream).
+ *   stream     hipStream_t to enqueue on (NULL = default stream).  With graph
+ *              replay the frozen blocks' pass over the next group of G tokens runs
+ *              on a stream the handle owns, ordered against `stream` by events;
+ *              all of the call's work is complete when `stream` reaches its end.
  * Starts from W_init and an empty ring every call.  Returns after enqueueing
  * (no host synchronisation) unless the non-finite check is requested with
  * ttt_check_finite().  Token ids are not range-checked on the device; ids

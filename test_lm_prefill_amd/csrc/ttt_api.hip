@@ -149,7 +149,19 @@ struct ttt_handle {
   // h_lead [B][G][d].  G = 0: no grouping (every chunk step runs all blocks).
   int G = 0, Lf = 0;
   float *h_lead = nullptr;
-  int *lead_n = nullptr;  // device: rows per sequence of the last frozen-prefix pass (G, or fewer at the end)
+  int *lead_n = nullptr;  // device: rows per sequence of the current group (G, or fewer at the end)
+  // The frozen-prefix pass writes its own scratch rows and residual rows (ls.h) and
+  // keeps its own position counter (ls.pos0, advanced by each pass), so that the next
+  // group's pass can run on lead_st beside the current group's chunk steps; ls.h is
+  // copied into h_lead when those steps are done.
+  struct LeadScratch {
+    int *pos0 = nullptr, *ids = nullptr, *labs = nullptr;
+    float *h = nullptr, *lse2 = nullptr, *qkv = nullptr;
+    void *a = nullptr, *qh = nullptr, *o = nullptr, *m = nullptr, *hmid = nullptr;
+  } ls;
+  hipStream_t lead_st = nullptr;
+  // [0] a frozen-prefix pass is done (lead_st), [1] the prefill's stream has taken its rows
+  hipEvent_t ev_lead[2] = {nullptr, nullptr};
   float *attn_ws = nullptr;
   size_t attn_ws_n = 0;      // floats of attn_ws
   int dev = 0;               // device the handle lives on
@@ -346,7 +358,8 @@ enum ChunkMode {
 
 // lb > 0: blocks below lb were run ahead by the frozen-prefix pass (lead); the chunk's
 // residual rows are taken from h_lead.  lead: run only the frozen prefix over n rows per
-// sequence (a group), into h_lead, with no head, backward or position advance.
+// sequence (a group) with the frozen-prefix scratch, into ls.h, advancing ls.pos0 by n
+// (no head, no backward).
 void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode = MODE_PREFILL, int lb = 0,
                    bool lead = false) {
   const int d = h->d, F = h->F, L = h->L, dt = h->dt, B = h->B, H = h->H, hd = h->hd, b = h->b;
@@ -358,20 +371,22 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
   auto rows = [n](int s, long cols, size_t esz) { return (size_t)s * n * cols * esz; };
   h->launches = 0;
   ResidualPartials pend;  // split-K partials of the last residual product, reduced by the next RMSNorm
-  float *const hres = lead ? h->h_lead : h->h;  // the residual stream of this pass
+  float *const hres = lead ? h->ls.h : h->h;  // the residual stream of this pass
+  int *const pos0 = lead ? h->ls.pos0 : h->pos0;
+  int *const ids = lead ? h->ls.ids : h->ids;
+  void *const act = lead ? h->ls.a : h->a;
   const int ldr = lead ? h->G : b;              // rows per sequence of the per-row statistics buffers
   const int le = lead ? h->Lf : L;
 
   {
     PROF(K_EMBED);
-    HIPCHK(gather_chunk_ids_launch(h->tok, h->ld_tok, h->pos0, n, B, h->ids, h->labs, st));
-    if (lead) HIPCHK(set_int_launch(h->lead_n, n, st));
+    HIPCHK(gather_chunk_ids_launch(h->tok, h->ld_tok, pos0, n, B, ids, lead ? h->ls.labs : h->labs, st));
     if (lb == 0)
-      HIPCHK(embed_launch(dt, h->tok_emb, h->ids, h->zero, hres, Bn, d, st));
+      HIPCHK(embed_launch(dt, h->tok_emb, ids, h->zero, hres, Bn, d, st));
     else
       HIPCHK(lead_rows_launch(h->h_lead, h->lead_n, h->G, h->pos0, h->h, n, d, B, st));
   }
-  h->launches += lead ? 3 : 2;
+  h->launches += 2;
   for (int l = lb; l < le; ++l) {
     LayerBuf &lw = h->layers[l];
     // blocks below Lf: unsplit products and one key range per head, so that a token's
@@ -385,20 +400,21 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
     // --- attention sub-block
     {
       PROF(K_RMSNORM);
-      HIPCHK(rmsnorm_fwd_launch(dt, hres, lw.attn_norm, h->a, sb ? S->r1 : nullptr, sb ? S->h_in : nullptr, Bn, d, eps,
+      HIPCHK(rmsnorm_fwd_launch(dt, hres, lw.attn_norm, act, sb ? S->r1 : nullptr, sb ? S->h_in : nullptr, Bn, d, eps,
                                 st, f16, pend));
       pend = ResidualPartials();
     }
-    float *qkv = sb ? S->qkv : h->qkv;  // fp32: q, k, v are normalised / cached without a 16-bit rounding first
+    // fp32: q, k, v are normalised / cached without a 16-bit rounding first
+    float *qkv = sb ? S->qkv : lead ? h->ls.qkv : h->qkv;
     {
-      GemmArgs g = gargs(h->a, d, lw.wqkv, d, Bn, 3 * d, d);
+      GemmArgs g = gargs(act, d, lw.wqkv, d, Bn, 3 * d, d);
       g.Cf = qkv;
       g.ldcf = 3 * d;
       gemm(h, K_GEMM_QKV, true, true, EPI_STORE_F32, g, st, true, frozen_whole);
     }
-    void *qh = sb ? S->qh : h->qh;
-    void *o = sb ? S->o : h->o;
-    float *lse2 = sb ? S->lse2 : h->lse2;
+    void *qh = sb ? S->qh : lead ? h->ls.qh : h->qh;
+    void *o = sb ? S->o : lead ? h->ls.o : h->o;
+    float *lse2 = sb ? S->lse2 : lead ? h->ls.lse2 : h->lse2;
     for (int s = 0; s < B; ++s) {  // per sequence: its ring and its positions
       const size_t rs = s * h->ring_sbytes;
       {
@@ -408,7 +424,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
         ra.gq = lw.q_norm;
         ra.gk = lw.k_norm;
         ra.cs = h->rope;
-        ra.pos0 = h->pos0;
+        ra.pos0 = pos0;
         ra.n = n;
         ra.d = d;
         ra.H = H;
@@ -443,7 +459,7 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
         aa.window = h->k;
         aa.ldl = ldr;
         aa.ldt = b;
-        aa.pos0 = h->pos0;
+        aa.pos0 = pos0;
         aa.scale = 1.f / sqrtf((float)hd);
         aa.nsplit = frozen_whole ? 1 : n <= 16 ? std::max(lw.fsplit, h->dec_split) : lw.fsplit;
         aa.sbound = lw.sbound;
@@ -471,14 +487,14 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
         pend = gemm_residual(h, K_GEMM_O, g, st);
     }
     // --- MLP sub-block (fast + static summed on one norm for updated blocks)
-    void *m = S ? S->m : h->m;
+    void *m = S ? S->m : lead ? h->ls.m : h->m;
     {
       PROF(K_RMSNORM);
       HIPCHK(rmsnorm_fwd_launch(dt, hres, lw.mlp_norm, m, S ? S->r2 : nullptr, S ? S->h1 : nullptr, Bn, d, eps, st, f16,
                                 pend));
       pend = ResidualPartials();
     }
-    void *hm = S ? S->hmid : h->hmid;  // hidden units: F (frozen) or 2F = fast then static
+    void *hm = S ? S->hmid : lead ? h->ls.hmid : h->hmid;  // hidden units: F (frozen) or 2F = fast then static
     if (!lw.fast) {
       GemmArgs g = gargs(m, d, lw.wgu, d, Bn, 2 * F, d);
       g.C = hm;
@@ -537,7 +553,11 @@ void enqueue_chunk(ttt_handle *h, int n, bool update, hipStream_t st, int mode =
       h->launches += 2;  // the block's two RMSNorms
     }
   }
-  if (lead) return;  // the frozen prefix of a group: its residual rows stay in h_lead
+  if (lead) {  // the frozen prefix of a group: its residual rows stay in ls.h
+    HIPCHK(add_int_launch(h->ls.pos0, n, st));
+    h->launches++;
+    return;
+  }
   // --- head: final norm, LM head + cross-entropy (losses written before any update)
   {
     PROF(K_RMSNORM);
@@ -968,8 +988,11 @@ void free_all(ttt_handle *h) {
   for (int i = 0; i < 6; ++i)
     if (h->gexec[i]) hipGraphExecDestroy(h->gexec[i]);
   if (h->cap) hipStreamDestroy(h->cap);
-  for (int i = 0; i < 2; ++i)
+  if (h->lead_st) hipStreamDestroy(h->lead_st);
+  for (int i = 0; i < 2; ++i) {
     if (h->ev_pf[i]) hipEventDestroy(h->ev_pf[i]);
+    if (h->ev_lead[i]) hipEventDestroy(h->ev_lead[i]);
+  }
   for (void *p : h->allocs) hipFree(p);
   h->allocs.clear();
 }
@@ -1327,8 +1350,20 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     HIPCHK(rope_table_launch(h->rope, c.max_tokens, h->hd, (double)c.rope_theta, st));
     h->h = (float *)dalloc(h, Bbd * 4);
     if (h->G > 0) {
-      h->h_lead = (float *)dalloc(h, (size_t)h->B * h->G * d * 4);
+      const size_t Gr = (size_t)h->B * h->G;  // rows of a frozen-prefix group
+      h->h_lead = (float *)dalloc(h, Gr * d * 4);
       h->lead_n = (int *)dalloc(h, 64);
+      h->ls.pos0 = (int *)dalloc(h, 64);
+      h->ls.ids = (int *)dalloc(h, Gr * sizeof(int));
+      h->ls.labs = (int *)dalloc(h, Gr * sizeof(int));
+      h->ls.h = (float *)dalloc(h, Gr * d * 4);
+      h->ls.lse2 = (float *)dalloc(h, (size_t)h->H * Gr * 4);
+      h->ls.qkv = (float *)dalloc(h, 3 * Gr * d * 4);
+      h->ls.a = dalloc(h, Gr * d * es);
+      h->ls.qh = dalloc(h, Gr * d * es);
+      h->ls.o = dalloc(h, Gr * d * es);
+      h->ls.m = dalloc(h, Gr * d * es);
+      h->ls.hmid = dalloc(h, Gr * F * es);
     }
     h->lse2 = (float *)dalloc(h, (size_t)h->H * Br * 4);
     h->a = dalloc(h, Brd * es);
@@ -1410,6 +1445,11 @@ ttt_status ttt_create(const ttt_config *cfg, const ttt_weights *w, void *stream,
     for (auto &z : h->zero_list) HIPCHK(hipMemsetAsync(z.first, 0, z.second, st));
     HIPCHK(hipStreamSynchronize(st));
     HIPCHK(hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking));
+    if (h->G > 0) {
+      HIPCHK(hipStreamCreateWithFlags(&h->lead_st, hipStreamNonBlocking));
+      HIPCHK(hipEventCreateWithFlags(&h->ev_lead[0], hipEventDisableTiming));
+      HIPCHK(hipEventCreateWithFlags(&h->ev_lead[1], hipEventDisableTiming));
+    }
     HIPCHK(hipEventCreate(&h->ev_pf[0]));
     HIPCHK(hipEventCreate(&h->ev_pf[1]));
     HIPCHK(hipGetDevice(&h->dev));
@@ -1481,12 +1521,36 @@ ttt_status prefill_impl(ttt_handle *h, const int32_t *d_tokens, int64_t T, float
     const int64_t nfull = T / b;
     const int tail = (int)(T % b);
     if (h->G > 0) {
-      // the frozen prefix of each group of G tokens, then the group's chunks from block Lf
+      // The frozen prefix of each group of G tokens, then the group's chunks from block Lf.
+      // With graph replay the next group's frozen prefix runs on lead_st while this group's
+      // chunk steps run on st (it reads only ids, frozen weights and the frozen blocks'
+      // rings, and writes only its own scratch); otherwise everything runs on st in the
+      // same order.  Results are the same either way.
+      const bool ovl = use_graph;
+      hipStream_t lst = ovl ? h->lead_st : st;
+      HIPCHK(set_int_launch(h->ls.pos0, 0, st));
+      if (ovl) {  // after the ids, the ring reset and the counter
+        HIPCHK(hipEventRecord(h->ev_lead[1], st));
+        HIPCHK(hipStreamWaitEvent(lst, h->ev_lead[1], 0));
+      }
+      if (T > 0) run_step(h, (int)std::min<int64_t>(h->G, T), false, MODE_PREFILL, use_graph, lst, true);
+      if (ovl) HIPCHK(hipEventRecord(h->ev_lead[0], lst));
       for (int64_t g0 = 0; g0 < T; g0 += h->G) {
         const int gn = (int)std::min<int64_t>(h->G, T - g0);
-        run_step(h, gn, false, MODE_PREFILL, use_graph, st, true);
+        if (ovl) HIPCHK(hipStreamWaitEvent(st, h->ev_lead[0], 0));
+        HIPCHK(hipMemcpyAsync(h->h_lead, h->ls.h, (size_t)h->B * h->G * h->d * 4, hipMemcpyDeviceToDevice, st));
+        HIPCHK(set_int_launch(h->lead_n, gn, st));
+        if (g0 + h->G < T) {
+          if (ovl) {
+            HIPCHK(hipEventRecord(h->ev_lead[1], st));
+            HIPCHK(hipStreamWaitEvent(lst, h->ev_lead[1], 0));
+          }
+          run_step(h, (int)std::min<int64_t>(h->G, T - g0 - h->G), false, MODE_PREFILL, use_graph, lst, true);
+          if (ovl) HIPCHK(hipEventRecord(h->ev_lead[0], lst));
+        }
         for (int c0 = 0; c0 < gn; c0 += b) run_step(h, std::min(b, gn - c0), update, MODE_PREFILL, use_graph, st, false, true);
       }
+      if (ovl) HIPCHK(hipStreamWaitEvent(st, h->ev_lead[0], 0));  // lead_st joins st (already, unless T = 0)
     } else {
       for (int64_t c = 0; c < nfull; ++c) run_step(h, b, update, MODE_PREFILL, use_graph, st);
       if (tail > 0) run_step(h, tail, update, MODE_PREFILL, use_graph, st);
