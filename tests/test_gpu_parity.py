@@ -371,3 +371,8 @@ def test_frozen_prefix_over_several_groups(dtype, hd, T):
             l_p, _ = run_gpu(sess, tok[:n + 1])
             bad = np.nonzero(l_p[:m] != gl[:m])[0]
             assert bad.size == 0, (n, bad[:5])
+    # with graph replay the next group's frozen-prefix pass runs on a second stream beside
+    # the chunk steps; launched one by one, everything runs on one stream: same bits
+    l_ng, f_ng = run_gpu(sess, tok, flags=TTT_NO_GRAPH)
+    assert np.array_equal(l_ng, gl)
+    assert all(np.array_equal(a, c) for a, c in zip(f_ng, gf))
